@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA hot path on one MI355X.  Prints ONE JSON line.
+
+A step is one ``dsa_prefill`` (Lightning Indexer -> top-k -> sparse GQA attention) over the
+128K-token video-like prefill workload (131072 tokens = 128 frames x (16 timestamp-text +
+1008 vision tokens), k = 2048, indexer 64 heads x 128 fp8, GQA 32q/4kv, d = 128 bf16), with
+all inputs resident in HBM.  ``value`` is prefill tokens/s.  The same line also reports, from
+the same run: per-stage times with HIP events, the indexer's roofline fraction, the dense
+causal attention time on the same inputs (DSA/dense ratio), the decode step time for 16
+sequences x 128K cached tokens over 64 steps (with the dense-decode ratio), the packed 256K
+varlen prefill throughput, and the CPU oracle timed on a bounded row sample.
+
+    python bench.py [--gpus 1] [--steps 3] [--warmup 1] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA prefill tokens/s & decode µs/step at 128K ctx; % MFMA/HBM peak; ratio vs dense"
+PEAK_FP8 = 5.0e15      # MI355X dense fp8 MFMA, FLOP/s
+PEAK_BF16 = 2.5e15     # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12      # MI355X HBM3E, B/s
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def pairs_of(lengths):
+    return sum(L * (L + 1) // 2 for L in lengths)
+
+
+def selected_of(lengths, k):
+    return sum(sum(min(k, i + 1) for i in range(L)) if L <= k else k * (k + 1) // 2 + (L - k) * k
+               for L in lengths)
+
+
+def ms_between(a, b):
+    return a.elapsed_time(b)
+
+
+def bench_prefill(name, steps, warmup, with_dense=True):
+    import torch
+    from sparse_attention_long_04_amd import workloads
+    from sparse_attention_long_04_amd.runtime import PrefillBatch, timing_events
+
+    t0 = time.time()
+    p = workloads.make(name)
+    log(f"{name}: inputs generated in {time.time() - t0:.1f}s, T={p.total_tokens}, lengths={list(p.lengths)}")
+    pb = PrefillBatch(p)
+    torch.cuda.synchronize()
+    log(f"{name}: resident in HBM (workspace {pb.ws.numel() / 2**30:.1f} GiB)")
+    st = torch.cuda.current_stream()
+    ev = [timing_events(4) for _ in range(steps)]
+    for _ in range(warmup):
+        pb.prefill()
+    torch.cuda.synchronize()
+    start, end = timing_events(2)
+    start.record(st)
+    for s in range(steps):
+        pb.prefill_timed(ev[s])
+    end.record(st)
+    torch.cuda.synchronize()
+    total_ms = ms_between(start, end)
+    # per-stage: [0]=after schedule, [1]=after indexer, [2]=after top-k, [3]=after attention
+    idx_ms = [ms_between(e[0], e[1]) for e in ev]
+    topk_ms = [ms_between(e[1], e[2]) for e in ev]
+    attn_ms = [ms_between(e[2], e[3]) for e in ev]
+    log(f"{name}: {total_ms / steps:.2f} ms/step  indexer {np.mean(idx_ms):.2f}  topk {np.mean(topk_ms):.2f}  "
+        f"attention {np.mean(attn_ms):.2f}")
+    res = dict(p=p, T=p.total_tokens, lengths=[int(x) for x in p.lengths], ms=total_ms / steps,
+               indexer_ms=float(np.mean(idx_ms)), topk_ms=float(np.mean(topk_ms)), attn_ms=float(np.mean(attn_ms)))
+    if with_dense:
+        out = torch.empty_like(pb.out)
+        pb.dense(out=out)
+        torch.cuda.synchronize()
+        a, b = timing_events(2)
+        a.record(st)
+        for _ in range(steps):
+            pb.dense(out=out)
+        b.record(st)
+        torch.cuda.synchronize()
+        res["dense_ms"] = ms_between(a, b) / steps
+        log(f"{name}: dense causal {res['dense_ms']:.2f} ms")
+    del pb
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(steps_total=64):
+    import torch
+    from sparse_attention_long_04_amd import workloads
+    from sparse_attention_long_04_amd.runtime import DecodeState, timing_events
+
+    t0 = time.time()
+    d = workloads.make(workloads.DECODE)
+    log(f"decode: caches generated in {time.time() - t0:.1f}s")
+    st_ = DecodeState(d)
+    steps = []
+    for i in range(steps_total):
+        st_.load_step(i)
+        steps.append(st_.step_dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [timing_events(4) for _ in range(steps_total)]
+    dense_ms = []
+    dout = torch.empty_like(st_.out)
+    for i in range(steps_total):
+        st_.step_dev = steps[i]
+        st_.append()
+        evs[i][0].record(stream)
+        st_.decode_timed(evs[i][1:])
+        if i in (0, steps_total // 2, steps_total - 1):
+            a, b = timing_events(2)
+            a.record(stream)
+            st_.dense(out=dout)
+            b.record(stream)
+            torch.cuda.synchronize()
+            dense_ms.append(ms_between(a, b))
+    torch.cuda.synchronize()
+    us = np.array([ms_between(e[0], e[3]) * 1e3 for e in evs])
+    idx_us = np.array([ms_between(e[0], e[1]) * 1e3 for e in evs])
+    topk_us = np.array([ms_between(e[1], e[2]) * 1e3 for e in evs])
+    attn_us = np.array([ms_between(e[2], e[3]) * 1e3 for e in evs])
+    # the first step also pays one-time costs; report mean over steps 1..63 and p50 over all
+    res = dict(us_mean=float(us[1:].mean()), us_p50=float(np.median(us)), indexer_us=float(idx_us[1:].mean()),
+               topk_us=float(topk_us[1:].mean()), attn_us=float(attn_us[1:].mean()),
+               dense_us=float(np.mean(dense_ms) * 1e3), batch=d.batch, ctx=d.ctx_len)
+    n_mean = d.ctx_len + steps_total / 2
+    bytes_step = d.batch * (n_mean * d.idx_dim + d.topk * d.kv_heads * d.head_dim * 2 * 2 + n_mean * 4 * 2)
+    res["hbm_gbs"] = bytes_step / (res["us_mean"] * 1e-6) / 1e9
+    log(f"decode: {res['us_mean']:.1f} us/step (p50 {res['us_p50']:.1f}) indexer {res['indexer_us']:.1f} "
+        f"topk {res['topk_us']:.1f} attn {res['attn_us']:.1f}; dense {res['dense_us']:.1f} us")
+    del st_
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(p, seconds=15.0, max_rows=4000, seed=0):
+    """The oracle (as is) on a uniform random sample of the workload's rows, for a bounded time."""
+    from oracle import dsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    o = O.Prefill(p.cu_seqlens, p.q_idx, p.k_idx, p.w_idx, p.q, p.k, p.v, p.idx_dtype, p.topk, p.softmax_scale)
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, p.total_tokens, size=max_rows)
+    o.row(int(rows[0]))  # decode the sequence's keys outside the timed part
+    t0 = time.perf_counter()
+    n = 0
+    for t in rows:
+        o.row(int(t))
+        n += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"{n} uniformly drawn rows of the 131072-token prefill (indexer + top-k + attention per "
+                       f"row, float64), {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--quick", action="store_true", help="prefill only (no dense/decode/varlen/cpu)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--workload", default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the DSA path here runs on a single GPU with no collectives)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_attention_long_04_amd import workloads
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    name = args.workload or workloads.P128K
+    w = workloads.WORKLOADS[name]
+    quick = args.quick
+
+    pre = bench_prefill(name, args.steps, args.warmup, with_dense=not quick)
+    T = pre["T"]
+    value = T / (pre["ms"] * 1e-3)
+    flops_idx = pairs_of(pre["lengths"]) * w["idx_heads"] * w["idx_dim"] * 2
+    peak = PEAK_FP8 if w["idx_dtype"] == "fp8_e4m3" else PEAK_BF16
+    achieved = flops_idx / (pre["indexer_ms"] * 1e-3)
+    sel = selected_of(pre["lengths"], w["topk"])
+    attn_flops = sel * 32 * 128 * 4
+    gathered = sel * 4 * 128 * 2 * 2
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3+bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "seq_len": T, "global_batch": len(pre["lengths"]), "topk": w["topk"],
+                   "indexer": f"{w['idx_heads']}x{w['idx_dim']} {w['idx_dtype']}", "attention": "GQA 32q/4kv d128 bf16"},
+        "roofline": {"bound": "mfma", "kernel": "indexer_prefill", "achieved": round(achieved / 1e12, 1),
+                     "peak": PEAK_FP8 / 1e12 if peak == PEAK_FP8 else PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None},
+        "stages_ms": {"indexer": round(pre["indexer_ms"], 3), "topk": round(pre["topk_ms"], 3),
+                      "sparse_attention": round(pre["attn_ms"], 3)},
+        "sparse_attention": {"tflops": round(attn_flops / (pre["attn_ms"] * 1e-3) / 1e12, 1),
+                             "frac_bf16_peak": round(attn_flops / (pre["attn_ms"] * 1e-3) / PEAK_BF16, 4),
+                             "gathered_GBps": round(gathered / (pre["attn_ms"] * 1e-3) / 1e9, 1)},
+    }
+    if not quick:
+        line["dense"] = {"ms": round(pre["dense_ms"], 3), "ratio_dsa_over_dense": round(pre["ms"] / pre["dense_ms"], 4),
+                         "dense_frac_bf16_peak": round(pairs_of(pre["lengths"]) * 32 * 128 * 4 /
+                                                       (pre["dense_ms"] * 1e-3) / PEAK_BF16, 4)}
+        dec = bench_decode()
+        line["decode"] = {"us_per_step": round(dec["us_mean"], 2), "us_p50": round(dec["us_p50"], 2),
+                          "stages_us": {"indexer": round(dec["indexer_us"], 2), "topk": round(dec["topk_us"], 2),
+                                        "sparse_attention": round(dec["attn_us"], 2)},
+                          "hbm_GBps": round(dec["hbm_gbs"], 1), "hbm_frac": round(dec["hbm_gbs"] * 1e9 / PEAK_HBM, 4),
+                          "dense_us": round(dec["dense_us"], 2),
+                          "ratio_dsa_over_dense": round(dec["us_mean"] / dec["dense_us"], 4),
+                          "workload": workloads.DECODE}
+        vl = bench_prefill(workloads.VARLEN, max(1, args.steps - 1), 1, with_dense=False)
+        line["varlen"] = {"workload": workloads.VARLEN, "tokens_per_s": round(vl["T"] / (vl["ms"] * 1e-3), 1),
+                          "ms": round(vl["ms"], 3), "lengths": vl["lengths"]}
+        if not args.no_cpu:
+            line["cpu_baseline"] = cpu_baseline(pre["p"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

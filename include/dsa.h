@@ -1,0 +1,179 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DeepSeek Sparse Attention hot path.
+ *
+ * The operation (Keye-VL-2.0 summary page, gsyq.cn):
+ *   section 一: a lightweight, MQA-shared "Lightning Indexer" scans every position and
+ *     scores which ones deserve attention (one indexer key per token, shared by all
+ *     indexer heads);
+ *   section 一 and the second Q&A: every current token keeps the 2048 most relevant positions
+ *     of its context, so attention costs O(Lk) instead of O(L^2);
+ *   section 一: attention then runs only among the kept positions, on a GQA base model;
+ *   section 一: prefill and decode costs are quoted against standard full attention;
+ *   section 八: the selection is deterministic.
+ *
+ * Readings fixed by this library where the pages are silent:
+ *   score  I[t,s] = sum_h w[t,h] * max(0, q_I[t,h,:] . k_I[s,:])  for keys s <= t of t's own
+ *     sequence (the token sees itself); fp32, exact for integer-valued inputs;
+ *   selection: the first min(k, t+1) keys in the order (score descending, index ascending),
+ *     written in ascending index order, -1 padded; index = position within the sequence;
+ *   attention: one index set per token shared by all query heads; query head h reads KV
+ *     head h / (q_heads / kv_heads); softmax scale given; fp32 softmax, bf16 output (RNE).
+ *
+ * Conventions for every entry point:
+ *   - all tensor pointers are DEVICE pointers, row-major and contiguous, 16-byte aligned,
+ *     owned by the caller; the library never allocates or frees device memory;
+ *   - `stream` is a hipStream_t (NULL = the default stream); every call only enqueues work on
+ *     it and returns without synchronising; nothing is copied between host and device;
+ *   - bf16 tensors are uint16 bit patterns; fp8 tensors are OCP E4M3 ("e4m3fn") codes;
+ *   - return DSA_OK (0) or a positive dsa_status.  Argument checks happen on the host
+ *     before anything is enqueued; on error nothing is enqueued.  Contents of device arrays
+ *     (cu_seqlens, cache_lens) are the caller's contract and are not checked;
+ *   - identical inputs give bit-identical outputs (no float atomics anywhere);
+ *   - the library keeps no mutable global state; calls on different streams may overlap as
+ *     long as they do not share output or workspace buffers.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, inconsistent shape */
+  DSA_ERR_UNSUPPORTED = 2,        /* valid but not compiled (e.g. head_dim != 128) */
+  DSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  DSA_ERR_HIP = 4                 /* a HIP launch failed; see dsa_last_hip_error() */
+};
+
+enum dsa_idx_dtype { DSA_IDX_BF16 = 0, DSA_IDX_FP8_E4M3 = 1 };
+
+/* One packed prefill batch of num_seqs causal sequences (block-diagonal causal mask). */
+typedef struct dsa_prefill_shape {
+  int32_t num_seqs;           /* B >= 1 */
+  const int32_t* cu_seqlens;  /* DEVICE int32 [B+1]: 0 = cu[0] <= cu[1] <= ... <= cu[B] = total_tokens */
+  int64_t total_tokens;       /* T >= 0 */
+  int32_t max_seqlen;         /* host-known bound on every sequence length (sizes the grids) */
+  int32_t topk;               /* k: 1..4096 */
+  int32_t idx_heads;          /* H_I: multiple of 16, 16..64 */
+  int32_t idx_dim;            /* d_I: 64 or 128 (fp8 needs 128) */
+  int32_t idx_dtype;          /* enum dsa_idx_dtype */
+  int32_t q_heads;            /* Hq */
+  int32_t kv_heads;           /* Hkv: 1..8, Hq % Hkv == 0, Hq / Hkv <= 16 */
+  int32_t head_dim;           /* d: 128 */
+  float softmax_scale;        /* > 0, e.g. 1/sqrt(d) */
+} dsa_prefill_shape;
+
+/* A batch of decode sequences, each with its own cache of `cache_capacity` rows. */
+typedef struct dsa_decode_shape {
+  int32_t batch;              /* B >= 1 */
+  int32_t cache_capacity;     /* rows per sequence in every cache */
+  const int32_t* cache_lens;  /* DEVICE int32 [B]: valid rows, the newest token included, 1..capacity */
+  int32_t max_cache_len;      /* host-known bound on cache_lens (<= cache_capacity) */
+  int32_t topk, idx_heads, idx_dim, idx_dtype, q_heads, kv_heads, head_dim;  /* as for prefill */
+  float softmax_scale;
+} dsa_decode_shape;
+
+/* Text of a status code (static storage). */
+const char* dsa_status_string(int status);
+/* hipError_t of the last DSA_ERR_HIP returned on the calling thread (0 if none). */
+int dsa_last_hip_error(void);
+
+/* ---------------------------------------------------------------------------------------
+ * Prefill
+ * ------------------------------------------------------------------------------------- */
+
+/* Workspace bytes needed by dsa_index_scores / dsa_index_topk / dsa_prefill /
+ * dense_causal_attention for `shape`.  cu_seqlens_host (HOST int32 [B+1], nullable) gives the
+ * exact size; without it a bound from total_tokens, num_seqs and max_seqlen is returned.
+ * The workspace holds the causal indexer score triangle (fp32, in 16-row blocks), a work
+ * schedule and, for dsa_prefill with topk_idx == NULL, the index array. */
+int dsa_prefill_workspace_size(const dsa_prefill_shape* shape, const int32_t* cu_seqlens_host,
+                               size_t* bytes);
+
+/* Debug/verification export of the Lightning Indexer scores (summary page section 一).
+ * q_idx [T, H_I, d_I], k_idx [T, d_I] (bf16 or fp8 per idx_dtype), w_idx fp32 [T, H_I].
+ * scores fp32 [T, max_seqlen]: row t holds I[t, s] for s = 0..i (i = t's position in its
+ * sequence) and -inf for s > i. */
+int dsa_index_scores(const dsa_prefill_shape* shape, const void* q_idx, const void* k_idx,
+                     const float* w_idx, float* scores, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Lightning Indexer + per-token top-k (summary page sections 一 and 八).
+ * topk_idx int32 [T, k]: the min(k, i+1) selected positions of each token, ascending,
+ * then -1. */
+int dsa_index_topk(const dsa_prefill_shape* shape, const void* q_idx, const void* k_idx,
+                   const float* w_idx, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Sparse GQA attention over given index sets (summary page section 一: attention only among
+ * the selected positions).  q bf16 [T, Hq, d], k/v bf16 [T, Hkv, d], topk_idx int32 [T, k]
+ * as produced by dsa_index_topk (entries < 0 are ignored; valid entries must be in
+ * 0..i); out bf16 [T, Hq, d].  No workspace. */
+int dsa_sparse_attention(const dsa_prefill_shape* shape, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, const int32_t* topk_idx, uint16_t* out, void* stream);
+
+/* The whole prefill hot path: dsa_index_topk then dsa_sparse_attention.  topk_idx may be
+ * NULL (the workspace then holds the indices). */
+int dsa_prefill(const dsa_prefill_shape* shape, const void* q_idx, const void* k_idx,
+                const float* w_idx, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                uint16_t* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* dsa_prefill that also records caller-created hipEvent_t events[0..3] on `stream` after the
+ * work schedule, the indexer, the top-k and the attention kernels (per-stage timing). */
+int dsa_prefill_timed(const dsa_prefill_shape* shape, const void* q_idx, const void* k_idx,
+                      const float* w_idx, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      uint16_t* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                      void* stream, void* const* events);
+
+/* Standard full causal GQA attention (the cost reference of summary page section 一), same
+ * tensors as dsa_sparse_attention without indices.  Uses the prefill workspace. */
+int dense_causal_attention(const dsa_prefill_shape* shape, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, uint16_t* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Decode
+ * ------------------------------------------------------------------------------------- */
+
+/* Workspace bytes for dsa_decode / dense_decode_attention. */
+int dsa_decode_workspace_size(const dsa_decode_shape* shape, size_t* bytes);
+
+/* Append one token per sequence to the caches at row positions[b] (DEVICE int32 [B],
+ * 0 <= positions[b] < cache_capacity): k_idx_new [B, d_I] -> k_idx_cache [B, cap, d_I],
+ * k_new/v_new bf16 [B, Hkv, d] -> k_cache/v_cache bf16 [B, cap, Hkv, d]. */
+int dsa_kv_append(const dsa_decode_shape* shape, const void* k_idx_new, const uint16_t* k_new,
+                  const uint16_t* v_new, const int32_t* positions, void* k_idx_cache,
+                  uint16_t* k_cache, uint16_t* v_cache, void* stream);
+
+/* One DSA decode step (summary page sections 一 and 八): for each sequence b the newest token
+ * (cache row cache_lens[b]-1, already appended) scores cache rows 0..n-1 with the indexer,
+ * keeps the top-k and attends over them.  q_idx [B, H_I, d_I], w_idx fp32 [B, H_I],
+ * q bf16 [B, Hq, d]; out bf16 [B, Hq, d]; topk_idx int32 [B, k] (nullable). */
+int dsa_decode(const dsa_decode_shape* shape, const void* q_idx, const float* w_idx,
+               const uint16_t* q, const void* k_idx_cache, const uint16_t* k_cache,
+               const uint16_t* v_cache, uint16_t* out, int32_t* topk_idx, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/* dsa_decode that also records caller-created hipEvent_t events[0..2] on `stream` after the
+ * indexer, the top-k and the attention kernels (per-stage timing). */
+int dsa_decode_timed(const dsa_decode_shape* shape, const void* q_idx, const float* w_idx,
+                     const uint16_t* q, const void* k_idx_cache, const uint16_t* k_cache,
+                     const uint16_t* v_cache, uint16_t* out, int32_t* topk_idx, void* workspace,
+                     size_t workspace_bytes, void* stream, void* const* events);
+
+/* Full attention of the newest token over its whole cache (decode cost reference). */
+int dense_decode_attention(const dsa_decode_shape* shape, const uint16_t* q,
+                           const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

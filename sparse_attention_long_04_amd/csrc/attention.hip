@@ -1,0 +1,421 @@
+// Sparse GQA attention over the selected keys, and the dense causal reference
+// (Keye-VL-2.0 summary page, gsyq.cn, section 一: attention only among the selected positions;
+// the base LLM uses GQA; costs are quoted against standard full attention).
+//
+// gather_attention_kernel -- one workgroup per query row (a prefill token or a decode
+//   sequence) and optional key split; one wave per KV head.  The wave's query heads (Hq/Hkv,
+//   padded to 16) share the row's index set.  Per 32-key tile:
+//     S^T = K Q^T   bf16 MFMA 16x16x32, K rows gathered from HBM straight into A registers;
+//     online softmax in fp32 (exp2, running max/sum per head);
+//     O^T += V^T P^T  fp16 MFMA 16x16x32: V rows are gathered, converted to fp16 and written
+//                     transposed into the wave's LDS tile; P is rounded to fp16 (11-bit
+//                     mantissa, far below the bf16 output rounding).
+//   With several splits the wave writes (unnormalised O, running max, sum) partials that
+//   combine_kernel merges by log-sum-exp; with one split it writes bf16 output directly.
+//   idx == nullptr means "keys 0..n-1" (dense decode).
+//
+// dense_prefill_kernel -- FlashAttention-style causal attention: a workgroup owns 128 query
+//   tokens of one query head (4 waves x 32 queries); 64-key K and V^T tiles are staged in LDS
+//   and shared by the 4 waves; S^T and O^T use 32x32x16 MFMAs (bf16 for QK, fp16 for PV).
+#include "common.h"
+
+namespace dsa {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_f16_16x16x32(i32x4 a, i32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f16_32x32x16(i32x4 a, i32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// 8 fp32 -> 8 fp16 (round to nearest even), packed as 4 dwords.
+__device__ __forceinline__ i32x4 pack_f16x8(const float* p) {
+  f16x8 h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (_Float16)p[i];
+  return __builtin_bit_cast(i32x4, h);
+}
+
+__device__ __forceinline__ uint16_t bf16_lane(const i32x4& v, int e) {
+  const uint32_t w = uint32_t(v[e >> 1]);
+  return uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+
+constexpr int kVtStride = 40;  // halfs per transposed-V row (32 keys + 8 pad)
+
+struct RowInfo {
+  int64_t kv_row0;  // row of key 0 in the K/V arrays (units of Hkv*D elements)
+  int n;            // causal context length
+};
+
+__device__ __forceinline__ RowInfo row_info(int mode, int64_t r, const int32_t* cu, int nseq,
+                                            const int32_t* cache_lens, int cap) {
+  RowInfo ri;
+  if (mode == 0) {
+    const int b = find_seq(cu, nseq, r);
+    ri.kv_row0 = cu[b];
+    ri.n = int(r - cu[b]) + 1;
+  } else {
+    ri.kv_row0 = r * (int64_t)cap;
+    ri.n = cache_lens[r];
+  }
+  return ri;
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ idx, int K, int mode, const int32_t* __restrict__ cu, int nseq,
+    const int32_t* __restrict__ cache_lens, int cap, int Hq, int Hkv, float scale_log2,
+    int keys_per_split, int nsplit, uint16_t* __restrict__ out, float* __restrict__ o_part,
+    float2* __restrict__ ml_part) {
+  static_assert(D == 128, "head_dim 128 only");
+  __shared__ __attribute__((aligned(16))) _Float16 vt_lds[NW][D * kVtStride];
+  const int64_t r = blockIdx.x;
+  const int split = blockIdx.y;
+  const int g = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int kg = lane & 3, dc = lane >> 2;  // V-load mapping: keys 8kg..8kg+7, dims 8dc..8dc+7
+  const int G = Hq / Hkv;
+  const RowInfo ri = row_info(mode, r, cu, nseq, cache_lens, cap);
+  const int m_all = idx ? min(K, ri.n) : ri.n;
+  const int p_begin = split * keys_per_split;
+  const int p_end = min(m_all, p_begin + keys_per_split);
+  const int32_t* __restrict__ irow = idx ? idx + r * K : nullptr;
+  _Float16* __restrict__ vt = vt_lds[g];
+
+  // Q^T operand: lane holds head lr, dims 32c + 8lg .. +7
+  i32x4 qf[4];
+  {
+    const bool hv = lr < G;
+    const uint16_t* qp = q + (r * Hq + g * G + (hv ? lr : 0)) * D + 8 * lg;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      qf[c] = *reinterpret_cast<const i32x4*>(qp + 32 * c);
+      if (!hv) qf[c] = (i32x4){0, 0, 0, 0};
+    }
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  const int64_t kvs = (int64_t)Hkv * D;
+  const uint16_t* __restrict__ kg_base = k + ri.kv_row0 * kvs + g * D;
+  const uint16_t* __restrict__ vg_base = v + ri.kv_row0 * kvs + g * D;
+
+  for (int tile = p_begin; tile < p_end; tile += 32) {
+    // ---- gather K rows for the two 16-key S sub-tiles (row lr <-> slot 8(lr/4)+4h+(lr%4))
+    i32x4 kf[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int p = tile + 8 * (lr >> 2) + 4 * h + (lr & 3);
+      int s = (p < p_end) ? (irow ? irow[p] : p) : 0;
+      s = max(s, 0);
+      const uint16_t* kp = kg_base + (int64_t)s * kvs + 8 * lg;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kf[h][c] = *reinterpret_cast<const i32x4*>(kp + 32 * c);
+    }
+    // ---- gather V rows: slots 8kg + mm, dims 8dc .. 8dc+7
+    i32x4 vf[8];
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) {
+      const int p = tile + 8 * kg + mm;
+      int s = (p < p_end) ? (irow ? irow[p] : p) : 0;
+      s = max(s, 0);
+      vf[mm] = *reinterpret_cast<const i32x4*>(vg_base + (int64_t)s * kvs + 8 * dc);
+    }
+    // ---- validity of this lane's score slots 8lg + 4h + i
+    bool valid[8];
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) {
+      const int p = tile + 8 * lg + mm;
+      valid[mm] = (p < p_end) && (irow ? irow[p] >= 0 : true);
+    }
+    // ---- S^T = K Q^T
+    float z[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) c4 = mfma_bf16_16x16x32(kf[h][c], qf[c], c4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[4 * h + i] = valid[4 * h + i] ? c4[i] * scale_log2 : -__builtin_inff();
+    }
+    // ---- online softmax (per head = per lane column; keys over registers and lane groups)
+    float mt = z[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, z[i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const bool live = m_new != -__builtin_inff();
+    const float alpha = live ? exp2f(m_run - m_new) : 1.f;
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = live ? exp2f(z[i] - m_new) : 0.f;
+      ps += p[i];
+    }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    // ---- V^T tile into LDS (fp16): vt[dim][slot]
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      float col[8];
+#pragma unroll
+      for (int mm = 0; mm < 8; ++mm) col[mm] = bf16_to_f32(bf16_lane(vf[mm], d));
+      *reinterpret_cast<i32x4*>(vt + (8 * dc + d) * kVtStride + 8 * kg) = pack_f16x8(col);
+    }
+    // the tile is private to this wave and LDS executes a wave's accesses in order: only
+    // compiler reordering has to be fenced off
+    __builtin_amdgcn_wave_barrier();
+    // ---- O^T += V^T P^T
+    const i32x4 pf = pack_f16x8(p);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const i32x4 a = *reinterpret_cast<const i32x4*>(vt + (16 * dt + lr) * kVtStride + 8 * lg);
+      o[dt] = mfma_f16_16x16x32(a, pf, o[dt]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (lr >= G) return;
+  const int head = g * G + lr;
+  if (nsplit == 1) {
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    uint16_t* op = out + (r * Hq + head) * D + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      uint32_t lo = f32_to_bf16(o[dt][0] * inv) | (uint32_t(f32_to_bf16(o[dt][1] * inv)) << 16);
+      uint32_t hi = f32_to_bf16(o[dt][2] * inv) | (uint32_t(f32_to_bf16(o[dt][3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(op + 16 * dt) = make_uint2(lo, hi);
+    }
+  } else {
+    const int64_t slot = (r * nsplit + split) * Hq + head;
+    float* pp = o_part + slot * D + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(pp + 16 * dt) = o[dt];
+    if (lg == 0) ml_part[slot] = make_float2(m_run, l_tot);
+  }
+}
+
+// Merge split partials: out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+__global__ void combine_kernel(const float* __restrict__ o_part, const float2* __restrict__ ml_part,
+                               int nsplit, int Hq, int D, uint16_t* __restrict__ out) {
+  const int64_t r = blockIdx.x;
+  const int h = blockIdx.y;
+  const int d = threadIdx.x;
+  float M = -__builtin_inff();
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml_part[(r * nsplit + s) * Hq + h].x);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float2 ml = ml_part[(r * nsplit + s) * Hq + h];
+    if (ml.y == 0.f) continue;
+    const float wgt = exp2f(ml.x - M);
+    L += ml.y * wgt;
+    acc += o_part[((r * nsplit + s) * Hq + h) * (int64_t)D + d] * wgt;
+  }
+  if (d < D) out[(r * Hq + h) * D + d] = f32_to_bf16(L > 0.f ? acc / L : 0.f);
+}
+
+// ------------------------------------------------------------------------------------------
+// Dense causal prefill (FlashAttention-style), head_dim 128.
+// 32x32 MFMA output layout: lane l holds column l%32 and rows 8(i/4) + 4(l/32) + i%4, i<16.
+// S^T = K Q^T: A row rr of a 32-key block loads key kperm(rr) so that, per lane half, the 8
+// registers used by one PV k-step hold 8 consecutive keys.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ int kperm(int rr) {
+  const int a = rr >> 3, hh = (rr >> 2) & 1, bb = rr & 3;
+  return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + bb;
+}
+
+constexpr int kKStride = 136;  // bf16 per K row in LDS (128 + 8 pad)
+constexpr int kVStride = 72;   // halfs per V^T row in LDS (64 keys + 8 pad)
+
+__global__ __launch_bounds__(256) void dense_prefill_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ cu, int Hq, int Hkv, float scale_log2, const int2* __restrict__ sched,
+    const int* __restrict__ sched_count, uint16_t* __restrict__ out) {
+  constexpr int D = 128, BM = 128, BN = 64;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * kKStride];
+  __shared__ __attribute__((aligned(16))) _Float16 v_lds[D * kVStride];
+  const int n = blockIdx.x;
+  if (n >= *sched_count) return;
+  const int2 e = sched[n];
+  const int b = e.x, j = e.y;
+  const int h = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int g = h / G;
+  const int64_t seq0 = cu[b];
+  const int L = cu[b + 1] - cu[b];
+  const int q0 = BM * j;
+  const int rows = min(BM, L - q0);
+  const int kend = q0 + rows;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int qc = lane & 31, hf = lane >> 5;
+  const int64_t kvs = (int64_t)Hkv * D;
+
+  const int my_q = q0 + 32 * w + qc;  // local query index of this lane's column
+  i32x4 qf[8];
+  {
+    const int qq = min(my_q, kend - 1);
+    const uint16_t* qp = q + ((seq0 + qq) * Hq + h) * D + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const i32x4*>(qp + 16 * s);
+  }
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  const int wave_qmax = q0 + 32 * w + 31;
+
+  for (int kt = 0; kt < kend; kt += BN) {
+    // K tile: 64 keys x 256 B, 16-byte units
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int u = tid + 256 * x;
+      const int key = u >> 4, c = u & 15;
+      const int kk = min(kt + key, kend - 1);
+      *reinterpret_cast<i32x4*>(k_lds + key * kKStride + 8 * c) =
+          *reinterpret_cast<const i32x4*>(k + (seq0 + kk) * kvs + g * D + 8 * c);
+    }
+    // V^T tile: thread -> keys 8*kg8..+7, dims 4*dq..+3
+    {
+      const int kg8 = tid >> 5, dq = tid & 31;
+      uint2 vv[8];
+#pragma unroll
+      for (int mm = 0; mm < 8; ++mm) {
+        const int kk = min(kt + 8 * kg8 + mm, kend - 1);
+        vv[mm] = *reinterpret_cast<const uint2*>(v + (seq0 + kk) * kvs + g * D + 4 * dq);
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        float col[8];
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) {
+          const uint32_t wd = (d < 2) ? vv[mm].x : vv[mm].y;
+          col[mm] = bf16_to_f32(uint16_t((d & 1) ? (wd >> 16) : (wd & 0xFFFFu)));
+        }
+        *reinterpret_cast<i32x4*>(v_lds + (4 * dq + d) * kVStride + 8 * kg8) = pack_f16x8(col);
+      }
+    }
+    __syncthreads();
+    if (kt <= wave_qmax) {
+      // S^T for two 32-key blocks
+      f32x16 sacc[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[rb][i] = 0.f;
+        const uint16_t* ka = k_lds + (32 * rb + kperm(qc)) * kKStride + 8 * hf;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sacc[rb] = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(ka + 16 * s), qf[s], sacc[rb]);
+      }
+      // mask + scale; C row (reg i, half hf) of block rb <-> key kt + 32rb + kperm(8(i/4)+4hf+i%4)
+      float z[2][16];
+      float mt = -__builtin_inff();
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt + 32 * rb + kperm(8 * (i >> 2) + 4 * hf + (i & 3));
+          const float zz = (key <= my_q) ? sacc[rb][i] * scale_log2 : -__builtin_inff();
+          z[rb][i] = zz;
+          mt = fmaxf(mt, zz);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = fmaxf(m_run, mt);
+      const bool live = m_new != -__builtin_inff();
+      const float alpha = live ? exp2f(m_run - m_new) : 1.f;
+      float ps = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float pv = live ? exp2f(z[rb][i] - m_new) : 0.f;
+          z[rb][i] = pv;
+          ps += pv;
+        }
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      // O^T += V^T P^T, k-step (rb, kk2): keys kt + 32rb + 16kk2 + 8hf .. +7 = regs 8kk2..8kk2+7
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kk2 = 0; kk2 < 2; ++kk2) {
+          const i32x4 pf = pack_f16x8(&z[rb][8 * kk2]);
+          const _Float16* va = v_lds + qc * kVStride + 32 * rb + 16 * kk2 + 8 * hf;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            o[db] = mfma_f16_32x32x16(*reinterpret_cast<const i32x4*>(va + 32 * db * kVStride), pf, o[db]);
+        }
+    }
+    __syncthreads();
+  }
+  float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (my_q >= kend) return;
+  const float inv = 1.f / l_tot;
+  uint16_t* op = out + ((seq0 + my_q) * Hq + h) * D;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int dim = 32 * db + 8 * a + 4 * hf;
+      uint32_t lo = f32_to_bf16(o[db][4 * a + 0] * inv) | (uint32_t(f32_to_bf16(o[db][4 * a + 1] * inv)) << 16);
+      uint32_t hi = f32_to_bf16(o[db][4 * a + 2] * inv) | (uint32_t(f32_to_bf16(o[db][4 * a + 3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(op + dim) = make_uint2(lo, hi);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int32_t* idx, int K, int mode, const int32_t* cu, int nseq,
+                                   const int32_t* cache_lens, int cap, int64_t rows, int Hq, int Hkv,
+                                   float scale, int keys_per_split, int nsplit, uint16_t* out,
+                                   float* o_part, float2* ml_part, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  dim3 grid((unsigned)rows, nsplit);
+#define DSA_GATHER(NW)                                                                                   \
+  gather_attention_kernel<128, NW><<<grid, 64 * NW, 0, st>>>(q, k, v, idx, K, mode, cu, nseq, cache_lens, \
+                                                            cap, Hq, Hkv, scale_log2, keys_per_split,    \
+                                                            nsplit, out, o_part, ml_part)
+  switch (Hkv) {
+    case 1: DSA_GATHER(1); break;
+    case 2: DSA_GATHER(2); break;
+    case 3: DSA_GATHER(3); break;
+    case 4: DSA_GATHER(4); break;
+    case 5: DSA_GATHER(5); break;
+    case 6: DSA_GATHER(6); break;
+    case 7: DSA_GATHER(7); break;
+    case 8: DSA_GATHER(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef DSA_GATHER
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || nsplit == 1) return err;
+  combine_kernel<<<dim3((unsigned)rows, Hq), 128, 0, st>>>(o_part, ml_part, nsplit, Hq, 128, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu,
+                                int Hq, int Hkv, float scale, const int2* sched, const int* count,
+                                int nb_bound, uint16_t* out, hipStream_t st) {
+  if (nb_bound == 0) return hipSuccess;
+  dense_prefill_kernel<<<dim3(nb_bound, Hq), 256, 0, st>>>(q, k, v, cu, Hq, Hkv, scale * 1.4426950408889634f,
+                                                           sched, count, out);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

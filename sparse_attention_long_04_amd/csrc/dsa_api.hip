@@ -1,0 +1,409 @@
+// C-ABI host layer of the DSA hot path: argument checks, workspace layout, launch order.
+// Every entry point validates on the host, then only enqueues kernels on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/dsa.h"
+#include "common.h"
+
+namespace dsa {
+hipError_t launch_build_schedule(const int32_t* cu, int nseq, int bq, int nb_bound, int2* sched, int* count,
+                                 int64_t* seqoff, hipStream_t st);
+hipError_t launch_indexer_prefill(bool fp8, int di, const void* q_idx, const void* k_idx, const float* w,
+                                  const int32_t* cu, int H, const int2* sched, const int* count, int nb_bound,
+                                  const int64_t* seqoff, float* scores, hipStream_t st);
+hipError_t launch_unpack_scores(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq, int64_t T,
+                                int ldo, float* out, hipStream_t st);
+hipError_t launch_indexer_decode(const void* q_idx, const float* w, const void* k_cache, const int32_t* cache_lens,
+                                 int B, int cap, int max_len, int H, int64_t score_ld, float* scores, hipStream_t st);
+hipError_t launch_topk_prefill(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq, int64_t T, int K,
+                               int32_t* out, hipStream_t st);
+hipError_t launch_topk_decode(const float* scores, int64_t ld, const int32_t* cache_lens, int B, int K, int32_t* out,
+                              hipStream_t st);
+hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx, int K,
+                                   int mode, const int32_t* cu, int nseq, const int32_t* cache_lens, int cap,
+                                   int64_t rows, int Hq, int Hkv, float scale, int keys_per_split, int nsplit,
+                                   uint16_t* out, float* o_part, float2* ml_part, hipStream_t st);
+hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu, int Hq,
+                                int Hkv, float scale, const int2* sched, const int* count, int nb_bound,
+                                uint16_t* out, hipStream_t st);
+
+// Copy one new token per sequence into the caches at row positions[b].
+__global__ void kv_append_kernel(const uint8_t* __restrict__ kin, const uint16_t* __restrict__ knew,
+                                 const uint16_t* __restrict__ vnew, const int32_t* __restrict__ pos,
+                                 int cap, int idx_row_bytes, int kv_row_elems, uint8_t* __restrict__ kic,
+                                 uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
+  const int b = blockIdx.x;
+  const int64_t row = (int64_t)b * cap + pos[b];
+  for (int i = threadIdx.x; i < idx_row_bytes; i += blockDim.x) kic[row * idx_row_bytes + i] = kin[(int64_t)b * idx_row_bytes + i];
+  for (int i = threadIdx.x; i < kv_row_elems; i += blockDim.x) {
+    kc[row * kv_row_elems + i] = knew[(int64_t)b * kv_row_elems + i];
+    vc[row * kv_row_elems + i] = vnew[(int64_t)b * kv_row_elems + i];
+  }
+}
+}  // namespace dsa
+
+using namespace dsa;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return DSA_OK;
+  g_last_hip_error = int(e);
+  return DSA_ERR_HIP;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int check_heads(int32_t topk, int32_t H, int32_t dI, int32_t dtype, int32_t Hq, int32_t Hkv, int32_t d,
+                float scale, bool need_indexer) {
+  if (topk < 1 || topk > 4096) return DSA_ERR_INVALID_ARGUMENT;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f) || !isfinite(scale)) return DSA_ERR_INVALID_ARGUMENT;
+  if (Hkv > 8 || Hq / Hkv > 16) return DSA_ERR_UNSUPPORTED;
+  if (d != 128) return DSA_ERR_UNSUPPORTED;
+  if (need_indexer) {
+    if (H < 1 || dI < 1) return DSA_ERR_INVALID_ARGUMENT;
+    if (dtype != DSA_IDX_BF16 && dtype != DSA_IDX_FP8_E4M3) return DSA_ERR_INVALID_ARGUMENT;
+    if (H % 16 != 0 || H > 64) return DSA_ERR_UNSUPPORTED;
+    if (dtype == DSA_IDX_FP8_E4M3 && dI != 128) return DSA_ERR_UNSUPPORTED;
+    if (dtype == DSA_IDX_BF16 && dI != 64 && dI != 128) return DSA_ERR_UNSUPPORTED;
+    if (dtype == DSA_IDX_BF16 && dI == 128 && H > 32) return DSA_ERR_UNSUPPORTED;
+  }
+  return DSA_OK;
+}
+
+int check_prefill(const dsa_prefill_shape* s, bool need_indexer) {
+  if (!s || !s->cu_seqlens || s->num_seqs < 1 || s->total_tokens < 0 || s->max_seqlen < 0)
+    return DSA_ERR_INVALID_ARGUMENT;
+  if (s->total_tokens > 0 && s->max_seqlen < 1) return DSA_ERR_INVALID_ARGUMENT;
+  if (s->max_seqlen > s->total_tokens) return DSA_ERR_INVALID_ARGUMENT;
+  if (s->total_tokens > (int64_t(1) << 31) - 1) return DSA_ERR_UNSUPPORTED;
+  return check_heads(s->topk, s->idx_heads, s->idx_dim, s->idx_dtype, s->q_heads, s->kv_heads, s->head_dim,
+                     s->softmax_scale, need_indexer);
+}
+
+// Prefill workspace layout (all offsets 256-byte aligned):
+//   counts int[64] | seqoff int64[B+1] | sched16 int2[nb16] | sched128 int2[nb128] |
+//   scores float[score_floats] | topk int32[T*k]
+struct PrefillWs {
+  size_t counts, seqoff, sched16, sched128, scores, topk, total;
+  int nb16, nb128;
+  int64_t score_floats;
+};
+
+PrefillWs prefill_layout(const dsa_prefill_shape* s, const int32_t* cu_host) {
+  PrefillWs w{};
+  const int64_t T = s->total_tokens;
+  const int B = s->num_seqs;
+  int64_t nb16 = 0, nb128 = 0, sq = 0;
+  if (cu_host) {
+    for (int b = 0; b < B; ++b) {
+      const int64_t L = cu_host[b + 1] - cu_host[b];
+      const int64_t n16 = (L + 15) / 16;
+      nb16 += n16;
+      nb128 += (L + 127) / 128;
+      sq += n16 * (n16 + 1);
+    }
+  } else {
+    nb16 = (T + 15) / 16 + B;
+    nb128 = (T + 127) / 128 + B;
+    const int64_t M = (int64_t(s->max_seqlen) + 15) / 16;
+    if (M > 0) {
+      const int64_t q = nb16 / M, rem = nb16 % M;
+      sq = q * M * (M + 1) + rem * (rem + 1);
+    }
+  }
+  w.nb16 = int(nb16);
+  w.nb128 = int(nb128);
+  w.score_floats = 128 * sq;
+  size_t off = 0;
+  w.counts = off; off = align_up(off + 64 * sizeof(int), 256);
+  w.seqoff = off; off = align_up(off + size_t(B + 1) * sizeof(int64_t), 256);
+  w.sched16 = off; off = align_up(off + size_t(nb16) * sizeof(int2), 256);
+  w.sched128 = off; off = align_up(off + size_t(nb128) * sizeof(int2), 256);
+  w.scores = off; off = align_up(off + size_t(w.score_floats) * sizeof(float), 256);
+  w.topk = off; off = align_up(off + size_t(T) * size_t(s->topk) * sizeof(int32_t), 256);
+  w.total = off;
+  return w;
+}
+
+template <typename T>
+T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+
+int run_index_scores_tri(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
+                         void* ws, const PrefillWs& L, hipStream_t st) {
+  hipError_t e = launch_build_schedule(s->cu_seqlens, s->num_seqs, 16, L.nb16, at<int2>(ws, L.sched16),
+                                       at<int>(ws, L.counts), at<int64_t>(ws, L.seqoff), st);
+  if (e != hipSuccess) return hip_status(e);
+  if (L.nb16 == 0) return DSA_OK;
+  e = launch_indexer_prefill(s->idx_dtype == DSA_IDX_FP8_E4M3, s->idx_dim, q_idx, k_idx, w_idx, s->cu_seqlens,
+                             s->idx_heads, at<int2>(ws, L.sched16), at<int>(ws, L.counts), L.nb16,
+                             at<int64_t>(ws, L.seqoff), at<float>(ws, L.scores), st);
+  return hip_status(e);
+}
+
+int check_prefill_ws(const dsa_prefill_shape* s, void* ws, size_t ws_bytes, PrefillWs* L) {
+  *L = prefill_layout(s, nullptr);
+  if (!ws || !aligned16(ws)) return DSA_ERR_INVALID_ARGUMENT;
+  // the exact layout (from device cu_seqlens) never exceeds the host bound
+  if (ws_bytes < L->total) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  return DSA_OK;
+}
+
+int check_decode(const dsa_decode_shape* s, bool need_indexer) {
+  if (!s || !s->cache_lens || s->batch < 1 || s->cache_capacity < 1) return DSA_ERR_INVALID_ARGUMENT;
+  if (s->max_cache_len < 1 || s->max_cache_len > s->cache_capacity) return DSA_ERR_INVALID_ARGUMENT;
+  int rc = check_heads(s->topk, s->idx_heads, s->idx_dim, s->idx_dtype, s->q_heads, s->kv_heads, s->head_dim,
+                       s->softmax_scale, need_indexer);
+  if (rc) return rc;
+  if (need_indexer && s->idx_dtype != DSA_IDX_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+constexpr int kDecodeSparseSplit = 128;   // selected keys per split (decode)
+constexpr int kDecodeDenseSplit = 2048;   // cache rows per split (dense decode)
+
+struct DecodeWs {
+  size_t scores, topk, opart, mlpart, total;
+  int64_t ld;
+  int nsplit_sparse, nsplit_dense;
+};
+
+DecodeWs decode_layout(const dsa_decode_shape* s) {
+  DecodeWs w{};
+  w.ld = (int64_t(s->cache_capacity) + 63) / 64 * 64;
+  w.nsplit_sparse = (s->topk + kDecodeSparseSplit - 1) / kDecodeSparseSplit;
+  w.nsplit_dense = (s->max_cache_len + kDecodeDenseSplit - 1) / kDecodeDenseSplit;
+  const int ns = w.nsplit_sparse > w.nsplit_dense ? w.nsplit_sparse : w.nsplit_dense;
+  const size_t B = size_t(s->batch);
+  size_t off = 0;
+  w.scores = off; off = align_up(off + B * size_t(w.ld) * sizeof(float), 256);
+  w.topk = off; off = align_up(off + B * size_t(s->topk) * sizeof(int32_t), 256);
+  w.opart = off; off = align_up(off + B * ns * size_t(s->q_heads) * s->head_dim * sizeof(float), 256);
+  w.mlpart = off; off = align_up(off + B * ns * size_t(s->q_heads) * sizeof(float2), 256);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case DSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int dsa_last_hip_error(void) { return g_last_hip_error; }
+
+int dsa_prefill_workspace_size(const dsa_prefill_shape* s, const int32_t* cu_seqlens_host, size_t* bytes) {
+  if (!bytes) return DSA_ERR_INVALID_ARGUMENT;
+  int rc = check_prefill(s, false);
+  if (rc) return rc;
+  *bytes = prefill_layout(s, cu_seqlens_host).total;
+  // the library only checks the host bound, so never report less than it
+  const size_t bound = prefill_layout(s, nullptr).total;
+  if (*bytes < bound) *bytes = bound;
+  return DSA_OK;
+}
+
+int dsa_index_scores(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
+                     float* scores, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_prefill(s, true);
+  if (rc) return rc;
+  if (!q_idx || !k_idx || !w_idx || !scores) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx)) return DSA_ERR_INVALID_ARGUMENT;
+  PrefillWs L;
+  if ((rc = check_prefill_ws(s, ws, ws_bytes, &L))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = run_index_scores_tri(s, q_idx, k_idx, w_idx, ws, L, st))) return rc;
+  return hip_status(launch_unpack_scores(at<float>(ws, L.scores), at<int64_t>(ws, L.seqoff), s->cu_seqlens,
+                                         s->num_seqs, s->total_tokens, s->max_seqlen, scores, st));
+}
+
+int dsa_index_topk(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
+                   int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_prefill(s, true);
+  if (rc) return rc;
+  if (!q_idx || !k_idx || !w_idx || !topk_idx) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx)) return DSA_ERR_INVALID_ARGUMENT;
+  PrefillWs L;
+  if ((rc = check_prefill_ws(s, ws, ws_bytes, &L))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = run_index_scores_tri(s, q_idx, k_idx, w_idx, ws, L, st))) return rc;
+  return hip_status(launch_topk_prefill(at<float>(ws, L.scores), at<int64_t>(ws, L.seqoff), s->cu_seqlens,
+                                        s->num_seqs, s->total_tokens, s->topk, topk_idx, st));
+}
+
+int dsa_sparse_attention(const dsa_prefill_shape* s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const int32_t* topk_idx, uint16_t* out, void* stream) {
+  int rc = check_prefill(s, false);
+  if (rc) return rc;
+  if (!q || !k || !v || !topk_idx || !out) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return DSA_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_gather_attention(q, k, v, topk_idx, s->topk, 0, s->cu_seqlens, s->num_seqs, nullptr, 0,
+                                            s->total_tokens, s->q_heads, s->kv_heads, s->softmax_scale, 1 << 30, 1,
+                                            out, nullptr, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+int record(void* const* ev, int i, hipStream_t st) {
+  if (!ev) return DSA_OK;
+  return hip_status(hipEventRecord(static_cast<hipEvent_t>(ev[i]), st));
+}
+
+int prefill_impl(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
+                 const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int32_t* topk_idx,
+                 void* ws, size_t ws_bytes, void* stream, void* const* ev) {
+  int rc = check_prefill(s, true);
+  if (rc) return rc;
+  if (!q_idx || !k_idx || !w_idx || !q || !k || !v || !out) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx) || !aligned16(q) || !aligned16(k) ||
+      !aligned16(v) || !aligned16(out))
+    return DSA_ERR_INVALID_ARGUMENT;
+  PrefillWs L;
+  if ((rc = check_prefill_ws(s, ws, ws_bytes, &L))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.topk);
+  hipError_t e = launch_build_schedule(s->cu_seqlens, s->num_seqs, 16, L.nb16, at<int2>(ws, L.sched16),
+                                       at<int>(ws, L.counts), at<int64_t>(ws, L.seqoff), st);
+  if (e != hipSuccess) return hip_status(e);
+  if ((rc = record(ev, 0, st))) return rc;
+  if (L.nb16 > 0) {
+    e = launch_indexer_prefill(s->idx_dtype == DSA_IDX_FP8_E4M3, s->idx_dim, q_idx, k_idx, w_idx, s->cu_seqlens,
+                               s->idx_heads, at<int2>(ws, L.sched16), at<int>(ws, L.counts), L.nb16,
+                               at<int64_t>(ws, L.seqoff), at<float>(ws, L.scores), st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if ((rc = record(ev, 1, st))) return rc;
+  if ((rc = hip_status(launch_topk_prefill(at<float>(ws, L.scores), at<int64_t>(ws, L.seqoff), s->cu_seqlens,
+                                           s->num_seqs, s->total_tokens, s->topk, idx, st))))
+    return rc;
+  if ((rc = record(ev, 2, st))) return rc;
+  if ((rc = hip_status(launch_gather_attention(q, k, v, idx, s->topk, 0, s->cu_seqlens, s->num_seqs, nullptr, 0,
+                                               s->total_tokens, s->q_heads, s->kv_heads, s->softmax_scale, 1 << 30,
+                                               1, out, nullptr, nullptr, st))))
+    return rc;
+  return record(ev, 3, st);
+}
+
+int decode_impl(const dsa_decode_shape* s, const void* q_idx, const float* w_idx, const uint16_t* q,
+                const void* k_idx_cache, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
+                int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream, void* const* ev) {
+  int rc = check_decode(s, true);
+  if (rc) return rc;
+  if (!q_idx || !w_idx || !q || !k_idx_cache || !k_cache || !v_cache || !out || !ws) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q_idx) || !aligned16(w_idx) || !aligned16(q) || !aligned16(k_idx_cache) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(out) || !aligned16(ws))
+    return DSA_ERR_INVALID_ARGUMENT;
+  const DecodeWs L = decode_layout(s);
+  if (ws_bytes < L.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.topk);
+  float* scores = at<float>(ws, L.scores);
+  if ((rc = hip_status(launch_indexer_decode(q_idx, w_idx, k_idx_cache, s->cache_lens, s->batch, s->cache_capacity,
+                                             s->max_cache_len, s->idx_heads, L.ld, scores, st))))
+    return rc;
+  if ((rc = record(ev, 0, st))) return rc;
+  if ((rc = hip_status(launch_topk_decode(scores, L.ld, s->cache_lens, s->batch, s->topk, idx, st)))) return rc;
+  if ((rc = record(ev, 1, st))) return rc;
+  if ((rc = hip_status(launch_gather_attention(q, k_cache, v_cache, idx, s->topk, 1, nullptr, 0, s->cache_lens,
+                                               s->cache_capacity, s->batch, s->q_heads, s->kv_heads,
+                                               s->softmax_scale, kDecodeSparseSplit, L.nsplit_sparse, out,
+                                               at<float>(ws, L.opart), at<float2>(ws, L.mlpart), st))))
+    return rc;
+  return record(ev, 2, st);
+}
+}  // namespace
+
+int dsa_prefill(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
+                const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int32_t* topk_idx,
+                void* ws, size_t ws_bytes, void* stream) {
+  return prefill_impl(s, q_idx, k_idx, w_idx, q, k, v, out, topk_idx, ws, ws_bytes, stream, nullptr);
+}
+
+int dsa_prefill_timed(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
+                      const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int32_t* topk_idx,
+                      void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  if (!events) return DSA_ERR_INVALID_ARGUMENT;
+  return prefill_impl(s, q_idx, k_idx, w_idx, q, k, v, out, topk_idx, ws, ws_bytes, stream, events);
+}
+
+int dense_causal_attention(const dsa_prefill_shape* s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_prefill(s, false);
+  if (rc) return rc;
+  if (!q || !k || !v || !out) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return DSA_ERR_INVALID_ARGUMENT;
+  PrefillWs L;
+  if ((rc = check_prefill_ws(s, ws, ws_bytes, &L))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_build_schedule(s->cu_seqlens, s->num_seqs, 128, L.nb128, at<int2>(ws, L.sched128),
+                                       at<int>(ws, L.counts) + 1, nullptr, st);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_dense_prefill(q, k, v, s->cu_seqlens, s->q_heads, s->kv_heads, s->softmax_scale,
+                                         at<int2>(ws, L.sched128), at<int>(ws, L.counts) + 1, L.nb128, out, st));
+}
+
+int dsa_decode_workspace_size(const dsa_decode_shape* s, size_t* bytes) {
+  if (!bytes) return DSA_ERR_INVALID_ARGUMENT;
+  int rc = check_decode(s, false);
+  if (rc) return rc;
+  *bytes = decode_layout(s).total;
+  return DSA_OK;
+}
+
+int dsa_kv_append(const dsa_decode_shape* s, const void* k_idx_new, const uint16_t* k_new, const uint16_t* v_new,
+                  const int32_t* positions, void* k_idx_cache, uint16_t* k_cache, uint16_t* v_cache, void* stream) {
+  if (!s || s->batch < 1 || s->cache_capacity < 1 || s->idx_dim < 1 || s->kv_heads < 1 || s->head_dim < 1)
+    return DSA_ERR_INVALID_ARGUMENT;
+  if (s->idx_dtype != DSA_IDX_BF16 && s->idx_dtype != DSA_IDX_FP8_E4M3) return DSA_ERR_INVALID_ARGUMENT;
+  if (!k_idx_new || !k_new || !v_new || !positions || !k_idx_cache || !k_cache || !v_cache)
+    return DSA_ERR_INVALID_ARGUMENT;
+  const int idx_row_bytes = s->idx_dim * (s->idx_dtype == DSA_IDX_BF16 ? 2 : 1);
+  kv_append_kernel<<<s->batch, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const uint8_t*>(k_idx_new), k_new, v_new, positions, s->cache_capacity, idx_row_bytes,
+      s->kv_heads * s->head_dim, static_cast<uint8_t*>(k_idx_cache), k_cache, v_cache);
+  return hip_status(hipGetLastError());
+}
+
+int dsa_decode(const dsa_decode_shape* s, const void* q_idx, const float* w_idx, const uint16_t* q,
+               const void* k_idx_cache, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
+               int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl(s, q_idx, w_idx, q, k_idx_cache, k_cache, v_cache, out, topk_idx, ws, ws_bytes, stream, nullptr);
+}
+
+int dsa_decode_timed(const dsa_decode_shape* s, const void* q_idx, const float* w_idx, const uint16_t* q,
+                     const void* k_idx_cache, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
+                     int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  if (!events) return DSA_ERR_INVALID_ARGUMENT;
+  return decode_impl(s, q_idx, w_idx, q, k_idx_cache, k_cache, v_cache, out, topk_idx, ws, ws_bytes, stream, events);
+}
+
+int dense_decode_attention(const dsa_decode_shape* s, const uint16_t* q, const uint16_t* k_cache,
+                           const uint16_t* v_cache, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_decode(s, false);
+  if (rc) return rc;
+  if (!q || !k_cache || !v_cache || !out || !ws) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(ws))
+    return DSA_ERR_INVALID_ARGUMENT;
+  const DecodeWs L = decode_layout(s);
+  if (ws_bytes < L.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(launch_gather_attention(q, k_cache, v_cache, nullptr, s->topk, 1, nullptr, 0, s->cache_lens,
+                                            s->cache_capacity, s->batch, s->q_heads, s->kv_heads, s->softmax_scale,
+                                            kDecodeDenseSplit, L.nsplit_dense, out, at<float>(ws, L.opart),
+                                            at<float2>(ws, L.mlpart), static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

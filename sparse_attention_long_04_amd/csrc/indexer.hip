@@ -1,0 +1,290 @@
+// Lightning Indexer scores for packed prefill (Keye-VL-2.0 summary page, gsyq.cn, section 一:
+// one MQA-shared indexer key per position, scored by every indexer head):
+//
+//     I[t, s] = sum_h w[t, h] * max(0, q_I[t, h, :] . k_I[s, :]),   s <= t in t's sequence.
+//
+// Work unit: one workgroup owns a block of 16 query tokens of one sequence and sweeps all of
+// their causal keys.  The block's indexer queries (16 tokens x H_I heads x d_I) sit in LDS;
+// each wave streams 16-key tiles of k_I from HBM/L2 straight into MFMA operand registers.
+// For every head, q_h (16 tokens) x k (16 keys) is ONE dense MFMA contraction over d_I
+// (fp8: v_mfma_f32_16x16x128_f8f6f4; bf16: 16x16x32 steps); ReLU and the head weight are
+// applied to the fp32 accumulator in registers and summed over heads without leaving VGPRs.
+//
+// Scores go to a triangle of 16-row blocks: block j of a sequence holds rows 16j..16j+15 with
+// a row stride of 16(j+1) floats, at offset seqoff[b] + 128 j (j+1).
+#include "common.h"
+
+namespace dsa {
+
+// ------------------------------------------------------------------------------------------
+// Work schedule: (sequence, block) pairs of BQ query rows, longest (largest block index) first.
+// Also writes seqoff[b] = start of sequence b's score triangle (16-row blocks, in floats).
+// ------------------------------------------------------------------------------------------
+__global__ void build_schedule_kernel(const int32_t* __restrict__ cu, int nseq, int bq,
+                                      int nb_bound, int2* __restrict__ sched,
+                                      int* __restrict__ sched_count, int64_t* __restrict__ seqoff) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (seqoff != nullptr && n <= nseq) {
+    int64_t off = 0;
+    for (int b = 0; b < n; ++b) {
+      const int64_t nb16 = (cu[b + 1] - cu[b] + 15) / 16;
+      off += 128 * nb16 * (nb16 + 1);
+    }
+    seqoff[n] = off;
+  }
+  if (n >= nb_bound) return;
+  int acc = 0, b = -1, j = 0;
+  for (int s = 0; s < nseq; ++s) {
+    const int nb = (cu[s + 1] - cu[s] + bq - 1) / bq;
+    if (b < 0 && n < acc + nb) { b = s; j = n - acc; }
+    acc += nb;
+  }
+  if (n == 0) *sched_count = acc;
+  if (b < 0) return;
+  // rank in the order (block index descending, sequence ascending)
+  int rank = 0;
+  for (int s = 0; s < nseq; ++s) {
+    const int nb = (cu[s + 1] - cu[s] + bq - 1) / bq;
+    if (nb > j + 1) rank += nb - j - 1;
+    if (s < b && nb > j) rank += 1;
+  }
+  sched[rank] = make_int2(b, j);
+}
+
+// ------------------------------------------------------------------------------------------
+// Indexer kernel.
+//   FP8 = true : e4m3fn inputs, DI = 128, one 16x16x128 MFMA per (head, key tile).
+//   FP8 = false: bf16 inputs, DI = 64 or 128, DI/32 16x16x32 MFMAs per (head, key tile).
+// Lane layout (16x16 MFMA): lane l -> r = l & 15, g = l >> 4.  A (queries) lane holds token
+// row r, B (keys) lane holds key r; both take bytes [g*CH, (g+1)*CH) of their d_I row, so
+// every MFMA pairs identical d_I positions.  Output C[i] of lane l = (token 4g+i, key r).
+// ------------------------------------------------------------------------------------------
+template <bool FP8, int DI, int HMAX, int NWAVES, int NT>
+__global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
+    const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx,
+    const float* __restrict__ w_idx, const int32_t* __restrict__ cu, int H,
+    const int2* __restrict__ sched, const int* __restrict__ sched_count,
+    const int64_t* __restrict__ seqoff, float* __restrict__ scores) {
+  constexpr int ROWB = DI * (FP8 ? 1 : 2);   // bytes of one d_I row
+  constexpr int UNITS = ROWB / 16;           // 16-byte units per row
+  constexpr int CH = ROWB / 4;               // bytes per lane group
+  constexpr int CHU = CH / 16;               // 16-byte units per lane group
+  static_assert(UNITS >= 8, "swizzle needs >= 8 units per row");
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[HMAX * 16 * ROWB];
+  __shared__ __attribute__((aligned(16))) float w_lds[HMAX * 16];
+
+  const int n = blockIdx.x;
+  if (n >= *sched_count) return;
+  const int2 e = sched[n];
+  const int b = e.x, j = e.y;
+  const int64_t seq0 = cu[b];
+  const int L = cu[b + 1] - cu[b];
+  const int i0 = 16 * j;
+  const int rows = min(16, L - i0);
+  const int kend = i0 + rows;  // keys [0, kend) are needed by this block
+  const int tid = threadIdx.x;
+
+  // stage queries: lds[(h*16 + t)*ROWB + ((u ^ (t&7)) * 16)] <- q_idx[seq0+i0+t][h][u*16..]
+  {
+    const int per_tok = H * UNITS;
+    const int total = 16 * per_tok;
+    for (int u = tid; u < total; u += NWAVES * 64) {
+      const int t = u / per_tok;
+      const int rem = u - t * per_tok;
+      const int h = rem / UNITS;
+      const int c = rem - h * UNITS;
+      i32x4 val = {0, 0, 0, 0};
+      if (t < rows)
+        val = *reinterpret_cast<const i32x4*>(q_idx + ((seq0 + i0 + t) * H + h) * (int64_t)ROWB + c * 16);
+      *reinterpret_cast<i32x4*>(q_lds + (h * 16 + t) * ROWB + ((c ^ (t & 7)) * 16)) = val;
+    }
+    for (int u = tid; u < 16 * H; u += NWAVES * 64) {
+      const int h = u >> 4, t = u & 15;
+      w_lds[u] = (t < rows) ? w_idx[(seq0 + i0 + t) * H + h] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t stride = 16 * (int64_t)(j + 1);
+  float* __restrict__ sblk = scores + seqoff[b] + score_block_offset(j);
+
+  for (int kb = wave * NT * 16; kb < kend; kb += NWAVES * NT * 16) {
+    // key tiles -> B operand registers
+    i32x4 bfr[NT][CHU];
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+      const int key = min(kb + 16 * jt + r, kend - 1);
+      const uint8_t* p = k_idx + (seq0 + key) * (int64_t)ROWB + g * CH;
+#pragma unroll
+      for (int c = 0; c < CHU; ++c) bfr[jt][c] = *reinterpret_cast<const i32x4*>(p + 16 * c);
+    }
+    f32x4 acc[NT];
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) acc[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    for (int h = 0; h < H; ++h) {
+      i32x4 afr[CHU];
+      const uint8_t* qa = q_lds + (h * 16 + r) * ROWB;
+#pragma unroll
+      for (int c = 0; c < CHU; ++c) {
+        const int unit = g * CHU + c;
+        afr[c] = *reinterpret_cast<const i32x4*>(qa + ((unit ^ (r & 7)) * 16));
+      }
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(w_lds + h * 16 + 4 * g);
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) {
+        f32x4 cacc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (FP8) {
+          const i32x8 a8 = {afr[0][0], afr[0][1], afr[0][2], afr[0][3], afr[1][0], afr[1][1], afr[1][2], afr[1][3]};
+          const i32x8 b8 = {bfr[jt][0][0], bfr[jt][0][1], bfr[jt][0][2], bfr[jt][0][3],
+                            bfr[jt][1][0], bfr[jt][1][1], bfr[jt][1][2], bfr[jt][1][3]};
+          cacc = mfma_fp8_16x16x128(a8, b8, cacc);
+        } else {
+#pragma unroll
+          for (int c = 0; c < CHU; ++c) cacc = mfma_bf16_16x16x32(afr[c], bfr[jt][c], cacc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[jt][i] = fmaf(wv[i], fmaxf(cacc[i], 0.f), acc[jt][i]);
+      }
+    }
+
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+      const int key = kb + 16 * jt + r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * g + i;
+        if (row < rows && key <= i0 + row) sblk[row * stride + key] = acc[jt][i];
+      }
+    }
+  }
+}
+
+// Expand the score triangle into a dense [T, ldo] matrix with -inf outside the causal context.
+__global__ void unpack_scores_kernel(const float* __restrict__ tri, const int64_t* __restrict__ seqoff,
+                                     const int32_t* __restrict__ cu, int nseq, int ldo,
+                                     float* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  const int b = find_seq(cu, nseq, t);
+  const int i = int(t - cu[b]);
+  const int j = i >> 4;
+  const float* src = tri + seqoff[b] + score_block_offset(j) + (i & 15) * 16 * (int64_t)(j + 1);
+  for (int s = threadIdx.x; s < ldo; s += blockDim.x)
+    out[t * ldo + s] = (s <= i) ? src[s] : -__builtin_inff();
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode indexer: one query token per sequence against its whole cache.  A = the token's
+// queries (16 heads per MFMA, from LDS), B = 16 cached keys; C[i] of lane l = (head 4g+i,
+// key r).  The weighted ReLU sum over heads runs in registers, then across the 4 lane groups.
+// ------------------------------------------------------------------------------------------
+template <int HMAX, int NT>
+__global__ __launch_bounds__(256) void indexer_decode_kernel(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const uint8_t* __restrict__ k_cache, const int32_t* __restrict__ cache_lens, int cap, int H,
+    int64_t score_ld, float* __restrict__ scores) {
+  constexpr int ROWB = 128, UNITS = 8, CH = 32;
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[HMAX * ROWB];
+  __shared__ float w_lds[HMAX];
+  const int b = blockIdx.y;
+  const int n = cache_lens[b];
+  const int key0 = blockIdx.x * (4 * NT * 16);
+  if (key0 >= n) return;
+  const int tid = threadIdx.x;
+  for (int u = tid; u < H * UNITS; u += 256) {
+    const int h = u / UNITS, c = u - h * UNITS;
+    *reinterpret_cast<i32x4*>(q_lds + h * ROWB + ((c ^ (h & 7)) * 16)) =
+        *reinterpret_cast<const i32x4*>(q_idx + ((int64_t)b * H + h) * ROWB + c * 16);
+  }
+  for (int h = tid; h < H; h += 256) w_lds[h] = w_idx[(int64_t)b * H + h];
+  __syncthreads();
+  const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int kb = key0 + wave * NT * 16;
+  if (kb >= n) return;
+  i32x8 bfr[NT];
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) {
+    const int key = min(kb + 16 * jt + r, n - 1);
+    const uint8_t* p = k_cache + ((int64_t)b * cap + key) * ROWB + g * CH;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
+    bfr[jt] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  float acc[NT];
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) acc[jt] = 0.f;
+  for (int hb = 0; hb < H; hb += 16) {
+    const uint8_t* qa = q_lds + (hb + r) * ROWB;
+    const int hr = (hb + r) & 7;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(qa + (((2 * g) ^ hr) * 16));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(qa + (((2 * g + 1) ^ hr) * 16));
+    const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const f32x4 wv = *reinterpret_cast<const f32x4*>(w_lds + hb + 4 * g);
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+      f32x4 c = mfma_fp8_16x16x128(a8, bfr[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[jt] = fmaf(wv[i], fmaxf(c[i], 0.f), acc[jt]);
+    }
+  }
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) {
+    float v = acc[jt];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    const int key = kb + 16 * jt + r;
+    if (g == 0 && key < n) scores[(int64_t)b * score_ld + key] = v;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// host-side launchers
+// ------------------------------------------------------------------------------------------
+hipError_t launch_build_schedule(const int32_t* cu, int nseq, int bq, int nb_bound, int2* sched,
+                                 int* count, int64_t* seqoff, hipStream_t st) {
+  const int threads = 256;
+  const int work = max(nb_bound, nseq + 1);
+  build_schedule_kernel<<<(work + threads - 1) / threads, threads, 0, st>>>(cu, nseq, bq, nb_bound,
+                                                                            sched, count, seqoff);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_prefill(bool fp8, int di, const void* q_idx, const void* k_idx,
+                                  const float* w, const int32_t* cu, int H, const int2* sched,
+                                  const int* count, int nb_bound, const int64_t* seqoff,
+                                  float* scores, hipStream_t st) {
+  const auto* q = static_cast<const uint8_t*>(q_idx);
+  const auto* k = static_cast<const uint8_t*>(k_idx);
+  if (fp8 && di == 128)
+    indexer_prefill_kernel<true, 128, 64, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores);
+  else if (!fp8 && di == 64)
+    indexer_prefill_kernel<false, 64, 64, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores);
+  else if (!fp8 && di == 128)
+    indexer_prefill_kernel<false, 128, 32, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_scores(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq,
+                                int64_t T, int ldo, float* out, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  unpack_scores_kernel<<<(unsigned)T, 256, 0, st>>>(tri, seqoff, cu, nseq, ldo, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_decode(const void* q_idx, const float* w, const void* k_cache,
+                                 const int32_t* cache_lens, int B, int cap, int max_len, int H,
+                                 int64_t score_ld, float* scores, hipStream_t st) {
+  constexpr int NT = 4;
+  const int per_block = 4 * NT * 16;
+  dim3 grid((max_len + per_block - 1) / per_block, B);
+  indexer_decode_kernel<64, NT><<<grid, 256, 0, st>>>(static_cast<const uint8_t*>(q_idx), w,
+                                                      static_cast<const uint8_t*>(k_cache), cache_lens,
+                                                      cap, H, score_ld, scores);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,142 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol, and rejects bad
+arguments on the host before touching the GPU.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sparse_attention_long_04_amd import dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dsa.lib_path()), reason="libdsa.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if",)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["dsa_index_topk", "dsa_prefill", "dsa_decode", "dense_causal_attention", "dsa_sparse_attention",
+              "dense_decode_attention", "dsa_kv_append", "dsa_index_scores", "dsa_prefill_workspace_size",
+              "dsa_decode_workspace_size", "dsa_status_string", "dsa_last_hip_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(dsa.lib_path())
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    # and the binding wraps each of them
+    assert set(declared_functions()) <= set(dsa.EXPORTS)
+
+
+def test_status_strings():
+    assert dsa.dsa_status_string(0) == "ok"
+    assert "workspace" in dsa.dsa_status_string(3)
+    assert dsa.dsa_status_string(99) == "unknown status"
+
+
+FAKE = 1 << 20  # a non-null, 16-byte aligned "device pointer" that is never dereferenced
+WS = (FAKE, 1 << 62)
+
+
+def shape(**kw):
+    base = dict(topk=2048, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", q_heads=32, kv_heads=4,
+                head_dim=128, softmax_scale=128 ** -0.5)
+    base.update(kw)
+    T = base.pop("T", 4096)
+    ms = base.pop("max_seqlen", 4096)
+    ns = base.pop("num_seqs", 1)
+    return dsa.prefill_shape(FAKE, T, ms, num_seqs=ns, **base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(topk=0), 1), (dict(topk=5000), 1), (dict(kv_heads=3), 1), (dict(head_dim=64), 2),
+    (dict(idx_heads=24), 2), (dict(idx_heads=128), 2), (dict(idx_dim=64), 2), (dict(idx_dtype=7), 1),
+    (dict(softmax_scale=0.0), 1), (dict(softmax_scale=float("nan")), 1), (dict(kv_heads=1), 2),
+    (dict(max_seqlen=5000), 1), (dict(num_seqs=0), 1), (dict(T=-1), 1),
+])
+def test_prefill_rejects_bad_shapes_before_launch(kw, code):
+    s = shape(**kw)
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_prefill(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, stream=0)
+    assert ei.value.status == code
+
+
+def test_prefill_rejects_null_and_misaligned_pointers():
+    s = shape()
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_prefill(s, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, stream=0)
+    assert ei.value.status == 1
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_index_topk(s, FAKE + 4, FAKE, FAKE, FAKE, WS, stream=0)
+    assert ei.value.status == 1
+
+
+def test_workspace_too_small_is_reported():
+    s = shape()
+    L = dsa.lib()
+    need = dsa.dsa_prefill_workspace_size(s)
+    rc = L.dsa_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 0)
+    assert rc == 3
+
+
+def test_workspace_size_covers_the_score_triangle():
+    T = 131072
+    s = shape(T=T, max_seqlen=T)
+    n = dsa.dsa_prefill_workspace_size(s, np.array([0, T]))
+    nb = T // 16
+    tri = 128 * nb * (nb + 1) * 4
+    assert n >= tri + T * 2048 * 4
+    assert n < tri * 1.01 + T * 2048 * 4 + (1 << 22)
+
+
+def test_varlen_workspace_bound_holds_for_any_split():
+    rng = np.random.default_rng(0)
+    for _ in range(50):
+        lens = rng.integers(0, 3000, size=int(rng.integers(1, 8)))
+        T = int(lens.sum())
+        if T == 0:
+            continue
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        s = shape(T=T, max_seqlen=int(lens.max()), num_seqs=len(lens), topk=64)
+        bound = dsa.dsa_prefill_workspace_size(s)
+        exact = dsa.dsa_prefill_workspace_size(s, cu)
+        nb = (lens + 15) // 16
+        assert bound >= 4 * 128 * int((nb * (nb + 1)).sum())
+        assert exact == bound
+
+
+def test_decode_rejects_bad_shapes():
+    s = dsa.decode_shape(FAKE, 1000, 2000, batch=2, topk=64, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3")
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_decode_workspace_size(s)
+    assert ei.value.status == 1
+    s = dsa.decode_shape(FAKE, 1000, 900, batch=2, topk=64, idx_heads=64, idx_dim=64, idx_dtype="bf16")
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_decode(s, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, WS, stream=0)
+    assert ei.value.status == 2
+
+
+def test_schedule_rank_is_a_longest_first_permutation():
+    """Host model of the device work schedule: ranks of (sequence, block) pairs ordered by
+    block index descending then sequence ascending form a permutation."""
+    rng = np.random.default_rng(1)
+    for _ in range(100):
+        nbs = rng.integers(0, 20, size=int(rng.integers(1, 6)))
+        pairs = [(b, j) for b, nb in enumerate(nbs) for j in range(nb)]
+        ranks = []
+        for b, j in pairs:
+            r = sum(max(0, int(nb) - j - 1) for nb in nbs) + sum(1 for s in range(b) if nbs[s] > j)
+            ranks.append(r)
+        assert sorted(ranks) == list(range(len(pairs)))
+        order = [p for _, p in sorted(zip(ranks, pairs))]
+        assert order == sorted(pairs, key=lambda p: (-p[1], p[0]))

@@ -7,9 +7,13 @@
 //   padded to 16) share the row's index set.  Per 32-key tile:
 //     S^T = K Q^T   bf16 MFMA 16x16x32, K rows gathered from HBM straight into A registers;
 //     online softmax in fp32 (exp2, running max/sum per head);
-//     O^T += V^T P^T  fp16 MFMA 16x16x32: V rows are gathered, converted to fp16 and written
-//                     transposed into the wave's LDS tile; P is rounded to fp16 (11-bit
-//                     mantissa, far below the bf16 output rounding).
+//     O^T += V^T P^T  bf16 MFMA 16x16x32 with P split as hi + lo bf16 (two MFMAs, relative
+//                     error ~2^-16).  V needs keys along the MFMA k dimension: each lane
+//                     gathers 8 keys x 8 consecutive dims and the head-dim order is permuted
+//                     (dim tile dt holds dims 8*row + dt), so the transpose happens inside the
+//                     lane's registers -- no LDS round trip for V.
+//   The next tile's K/V rows are loaded while the current one is computed; the row's key
+//   indices are staged in LDS once per workgroup.
 //   With several splits the wave writes (unnormalised O, running max, sum) partials that
 //   combine_kernel merges by log-sum-exp; with one split it writes bf16 output directly.
 //   idx == nullptr means "keys 0..n-1" (dense decode).
@@ -43,8 +47,6 @@ __device__ __forceinline__ uint16_t bf16_lane(const i32x4& v, int e) {
   return uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFFu));
 }
 
-constexpr int kVtStride = 40;  // halfs per transposed-V row (32 keys + 8 pad)
-
 struct RowInfo {
   int64_t kv_row0;  // row of key 0 in the K/V arrays (units of Hkv*D elements)
   int n;            // causal context length
@@ -64,6 +66,43 @@ __device__ __forceinline__ RowInfo row_info(int mode, int64_t r, const int32_t* 
   return ri;
 }
 
+constexpr int kMaxSplitKeys = 4096;  // LDS index slots per workgroup
+
+// bf16 pair (lo from a, hi from b): element e of 8-element vectors a and b.
+__device__ __forceinline__ uint32_t pair_bf16(const i32x4& a, const i32x4& b, int e) {
+  const uint32_t x = uint32_t(a[e >> 1]), y = uint32_t(b[e >> 1]);
+  return (e & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+}
+
+// One tile of 32 gathered keys in registers.  Lane (lr, lg):
+//   kf[h][c]: K row of key slot 8(lr/4)+4h+(lr%4), dims 32c+8lg .. +7  (S^T A operand)
+//   vf[m]   : V row of key slot 8lg+m, dims 8lr .. 8lr+7             (transposed in registers)
+//   sv[m]   : index of key slot 8lg+m (-1 = masked)
+struct GatherTile {
+  i32x4 kf[2][4];
+  i32x4 vf[8];
+  int sv[8];
+};
+
+__device__ __forceinline__ void load_tile(GatherTile& t, const int* __restrict__ il, int tl,
+                                          const uint16_t* __restrict__ kg_base,
+                                          const uint16_t* __restrict__ vg_base, int64_t kvs, int lr, int lg) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int s = max(il[tl + 8 * (lr >> 2) + 4 * h + (lr & 3)], 0);
+    const uint16_t* kp = kg_base + (int64_t)s * kvs + 8 * lg;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) t.kf[h][c] = *reinterpret_cast<const i32x4*>(kp + 32 * c);
+  }
+  const i32x4 s0 = *reinterpret_cast<const i32x4*>(il + tl + 8 * lg);
+  const i32x4 s1 = *reinterpret_cast<const i32x4*>(il + tl + 8 * lg + 4);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) { t.sv[m] = s0[m]; t.sv[4 + m] = s1[m]; }
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+    t.vf[m] = *reinterpret_cast<const i32x4*>(vg_base + (int64_t)max(t.sv[m], 0) * kvs + 8 * lr);
+}
+
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -72,19 +111,26 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
     int keys_per_split, int nsplit, uint16_t* __restrict__ out, float* __restrict__ o_part,
     float2* __restrict__ ml_part) {
   static_assert(D == 128, "head_dim 128 only");
-  __shared__ __attribute__((aligned(16))) _Float16 vt_lds[NW][D * kVtStride];
+  __shared__ __attribute__((aligned(16))) int il[kMaxSplitKeys + 32];
   const int64_t r = blockIdx.x;
   const int split = blockIdx.y;
   const int g = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int kg = lane & 3, dc = lane >> 2;  // V-load mapping: keys 8kg..8kg+7, dims 8dc..8dc+7
   const int G = Hq / Hkv;
   const RowInfo ri = row_info(mode, r, cu, nseq, cache_lens, cap);
   const int m_all = idx ? min(K, ri.n) : ri.n;
   const int p_begin = split * keys_per_split;
   const int p_end = min(m_all, p_begin + keys_per_split);
-  const int32_t* __restrict__ irow = idx ? idx + r * K : nullptr;
-  _Float16* __restrict__ vt = vt_lds[g];
+  const int cnt = max(0, p_end - p_begin);
+  const int cnt32 = (cnt + 31) & ~31;
+
+  // stage this split's key indices in LDS; slots past the end hold -1
+  for (int j = threadIdx.x; j < cnt32; j += 64 * NW) {
+    int s = -1;
+    if (j < cnt) s = idx ? __builtin_nontemporal_load(idx + r * K + p_begin + j) : p_begin + j;
+    il[j] = s;
+  }
+  __syncthreads();
 
   // Q^T operand: lane holds head lr, dims 32c + 8lg .. +7
   i32x4 qf[4];
@@ -93,10 +139,11 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
     const uint16_t* qp = q + (r * Hq + g * G + (hv ? lr : 0)) * D + 8 * lg;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      qf[c] = *reinterpret_cast<const i32x4*>(qp + 32 * c);
+      qf[c] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(qp + 32 * c));
       if (!hv) qf[c] = (i32x4){0, 0, 0, 0};
     }
   }
+  // O accumulator: o[dt][i] = O[head lr][dim 32lg + 8i + dt]
   f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -105,82 +152,57 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
   const uint16_t* __restrict__ kg_base = k + ri.kv_row0 * kvs + g * D;
   const uint16_t* __restrict__ vg_base = v + ri.kv_row0 * kvs + g * D;
 
-  for (int tile = p_begin; tile < p_end; tile += 32) {
-    // ---- gather K rows for the two 16-key S sub-tiles (row lr <-> slot 8(lr/4)+4h+(lr%4))
-    i32x4 kf[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int p = tile + 8 * (lr >> 2) + 4 * h + (lr & 3);
-      int s = (p < p_end) ? (irow ? irow[p] : p) : 0;
-      s = max(s, 0);
-      const uint16_t* kp = kg_base + (int64_t)s * kvs + 8 * lg;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kf[h][c] = *reinterpret_cast<const i32x4*>(kp + 32 * c);
-    }
-    // ---- gather V rows: slots 8kg + mm, dims 8dc .. 8dc+7
-    i32x4 vf[8];
-#pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
-      const int p = tile + 8 * kg + mm;
-      int s = (p < p_end) ? (irow ? irow[p] : p) : 0;
-      s = max(s, 0);
-      vf[mm] = *reinterpret_cast<const i32x4*>(vg_base + (int64_t)s * kvs + 8 * dc);
-    }
-    // ---- validity of this lane's score slots 8lg + 4h + i
-    bool valid[8];
-#pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
-      const int p = tile + 8 * lg + mm;
-      valid[mm] = (p < p_end) && (irow ? irow[p] >= 0 : true);
-    }
-    // ---- S^T = K Q^T
+  GatherTile cur, nxt;
+  if (cnt32 > 0) load_tile(cur, il, 0, kg_base, vg_base, kvs, lr, lg);
+  for (int tl = 0; tl < cnt32; tl += 32) {
+    if (tl + 32 < cnt32) load_tile(nxt, il, tl + 32, kg_base, vg_base, kvs, lr, lg);
+    // ---- S^T = K Q^T for the two 16-key sub-tiles; lane slot 8lg + 4h + i
     float z[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) c4 = mfma_bf16_16x16x32(kf[h][c], qf[c], c4);
+      for (int c = 0; c < 4; ++c) c4 = mfma_bf16_16x16x32(cur.kf[h][c], qf[c], c4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[4 * h + i] = valid[4 * h + i] ? c4[i] * scale_log2 : -__builtin_inff();
+      for (int i = 0; i < 4; ++i) z[4 * h + i] = (cur.sv[4 * h + i] >= 0) ? c4[i] * scale_log2 : -__builtin_inff();
     }
-    // ---- online softmax (per head = per lane column; keys over registers and lane groups)
+    // ---- online softmax (per head = lane column; keys over registers and the 4 lane groups)
     float mt = z[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mt = fmaxf(mt, z[i]);
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m_run, mt);
-    const bool live = m_new != -__builtin_inff();
-    const float alpha = live ? exp2f(m_run - m_new) : 1.f;
-    float p[8], ps = 0.f;
+    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float ps = 0.f;
+    uint32_t phi[8], plo[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = live ? exp2f(z[i] - m_new) : 0.f;
-      ps += p[i];
+      const float pv = __builtin_amdgcn_exp2f(z[i] - m_use);
+      ps += pv;
+      // p = hi + lo: hi = p truncated to bf16, lo = the remainder truncated to bf16
+      const uint32_t hb = __float_as_uint(pv) & 0xFFFF0000u;
+      phi[i] = hb;
+      plo[i] = __float_as_uint(pv - __uint_as_float(hb)) & 0xFFFF0000u;
     }
     l_run = l_run * alpha + ps;
     m_run = m_new;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-    // ---- V^T tile into LDS (fp16): vt[dim][slot]
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      float col[8];
-#pragma unroll
-      for (int mm = 0; mm < 8; ++mm) col[mm] = bf16_to_f32(bf16_lane(vf[mm], d));
-      *reinterpret_cast<i32x4*>(vt + (8 * dc + d) * kVtStride + 8 * kg) = pack_f16x8(col);
-    }
-    // the tile is private to this wave and LDS executes a wave's accesses in order: only
-    // compiler reordering has to be fenced off
-    __builtin_amdgcn_wave_barrier();
-    // ---- O^T += V^T P^T
-    const i32x4 pf = pack_f16x8(p);
+    const i32x4 bh = {int((phi[0] >> 16) | phi[1]), int((phi[2] >> 16) | phi[3]), int((phi[4] >> 16) | phi[5]),
+                      int((phi[6] >> 16) | phi[7])};
+    const i32x4 bl = {int((plo[0] >> 16) | plo[1]), int((plo[2] >> 16) | plo[3]), int((plo[4] >> 16) | plo[5]),
+                      int((plo[6] >> 16) | plo[7])};
+    // ---- O^T += V^T P^T; dim tile dt holds dims 8*row + dt, row = 0..15
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const i32x4 a = *reinterpret_cast<const i32x4*>(vt + (16 * dt + lr) * kVtStride + 8 * lg);
-      o[dt] = mfma_f16_16x16x32(a, pf, o[dt]);
+      const i32x4 a = {int(pair_bf16(cur.vf[0], cur.vf[1], dt)), int(pair_bf16(cur.vf[2], cur.vf[3], dt)),
+                       int(pair_bf16(cur.vf[4], cur.vf[5], dt)), int(pair_bf16(cur.vf[6], cur.vf[7], dt))};
+      o[dt] = mfma_bf16_16x16x32(a, bh, o[dt]);
+      o[dt] = mfma_bf16_16x16x32(a, bl, o[dt]);
     }
-    __builtin_amdgcn_wave_barrier();
+    cur = nxt;
   }
 
   float l_tot = l_run;
@@ -190,18 +212,25 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
   const int head = g * G + lr;
   if (nsplit == 1) {
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    uint16_t* op = out + (r * Hq + head) * D + 4 * lg;
+    uint16_t* op = out + (r * Hq + head) * D + 32 * lg;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      uint32_t lo = f32_to_bf16(o[dt][0] * inv) | (uint32_t(f32_to_bf16(o[dt][1] * inv)) << 16);
-      uint32_t hi = f32_to_bf16(o[dt][2] * inv) | (uint32_t(f32_to_bf16(o[dt][3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(op + 16 * dt) = make_uint2(lo, hi);
+    for (int i = 0; i < 4; ++i) {
+      i32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = int(uint32_t(f32_to_bf16(o[2 * e][i] * inv)) | (uint32_t(f32_to_bf16(o[2 * e + 1][i] * inv)) << 16));
+      __builtin_nontemporal_store(w, reinterpret_cast<i32x4*>(op + 8 * i));
     }
   } else {
     const int64_t slot = (r * nsplit + split) * Hq + head;
-    float* pp = o_part + slot * D + 4 * lg;
+    float* pp = o_part + slot * D + 32 * lg;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(pp + 16 * dt) = o[dt];
+    for (int i = 0; i < 4; ++i) {
+      f32x4 a = {o[0][i], o[1][i], o[2][i], o[3][i]};
+      f32x4 b = {o[4][i], o[5][i], o[6][i], o[7][i]};
+      *reinterpret_cast<f32x4*>(pp + 8 * i) = a;
+      *reinterpret_cast<f32x4*>(pp + 8 * i + 4) = b;
+    }
     if (lg == 0) ml_part[slot] = make_float2(m_run, l_tot);
   }
 }

@@ -11,15 +11,18 @@ hipError_t launch_build_schedule(const int32_t* cu, int nseq, int bq, int nb_bou
                                  int64_t* seqoff, hipStream_t st);
 hipError_t launch_indexer_prefill(bool fp8, int di, const void* q_idx, const void* k_idx, const float* w,
                                   const int32_t* cu, int H, const int2* sched, const int* count, int nb_bound,
-                                  const int64_t* seqoff, float* scores, hipStream_t st);
+                                  const int64_t* seqoff, float* scores, float2* rowrange, hipStream_t st);
 hipError_t launch_unpack_scores(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq, int64_t T,
                                 int ldo, float* out, hipStream_t st);
 hipError_t launch_indexer_decode(const void* q_idx, const float* w, const void* k_cache, const int32_t* cache_lens,
-                                 int B, int cap, int max_len, int H, int64_t score_ld, float* scores, hipStream_t st);
+                                 int B, int cap, int max_len, int H, int64_t score_ld, float* scores, int* ghist,
+                                 uint32_t* keyrange, hipStream_t st);
 hipError_t launch_topk_prefill(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq, int64_t T, int K,
-                               int32_t* out, hipStream_t st);
-hipError_t launch_topk_decode(const float* scores, int64_t ld, const int32_t* cache_lens, int B, int K, int32_t* out,
-                              hipStream_t st);
+                               const float2* rowrange, int32_t* out, hipStream_t st);
+int topk_decode_nchunk(int max_len);
+hipError_t launch_topk_decode(const float* scores, int64_t ld, const int32_t* cache_lens, int B, int max_len, int K,
+                              const uint32_t* keyrange, int* ghist, uint32_t* lkeys, int* lids, int* counts,
+                              int* spill, int32_t* out, hipStream_t st);
 hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx, int K,
                                    int mode, const int32_t* cu, int nseq, const int32_t* cache_lens, int cap,
                                    int64_t rows, int Hq, int Hkv, float scale, int keys_per_split, int nsplit,
@@ -89,9 +92,9 @@ int check_prefill(const dsa_prefill_shape* s, bool need_indexer) {
 
 // Prefill workspace layout (all offsets 256-byte aligned):
 //   counts int[64] | seqoff int64[B+1] | sched16 int2[nb16] | sched128 int2[nb128] |
-//   scores float[score_floats] | topk int32[T*k]
+//   rowrange float2[T] | scores float[score_floats] | topk int32[T*k]
 struct PrefillWs {
-  size_t counts, seqoff, sched16, sched128, scores, topk, total;
+  size_t counts, seqoff, sched16, sched128, rowrange, scores, topk, total;
   int nb16, nb128;
   int64_t score_floats;
 };
@@ -126,6 +129,7 @@ PrefillWs prefill_layout(const dsa_prefill_shape* s, const int32_t* cu_host) {
   w.seqoff = off; off = align_up(off + size_t(B + 1) * sizeof(int64_t), 256);
   w.sched16 = off; off = align_up(off + size_t(nb16) * sizeof(int2), 256);
   w.sched128 = off; off = align_up(off + size_t(nb128) * sizeof(int2), 256);
+  w.rowrange = off; off = align_up(off + size_t(T) * sizeof(float2), 256);
   w.scores = off; off = align_up(off + size_t(w.score_floats) * sizeof(float), 256);
   w.topk = off; off = align_up(off + size_t(T) * size_t(s->topk) * sizeof(int32_t), 256);
   w.total = off;
@@ -143,7 +147,7 @@ int run_index_scores_tri(const dsa_prefill_shape* s, const void* q_idx, const vo
   if (L.nb16 == 0) return DSA_OK;
   e = launch_indexer_prefill(s->idx_dtype == DSA_IDX_FP8_E4M3, s->idx_dim, q_idx, k_idx, w_idx, s->cu_seqlens,
                              s->idx_heads, at<int2>(ws, L.sched16), at<int>(ws, L.counts), L.nb16,
-                             at<int64_t>(ws, L.seqoff), at<float>(ws, L.scores), st);
+                             at<int64_t>(ws, L.seqoff), at<float>(ws, L.scores), at<float2>(ws, L.rowrange), st);
   return hip_status(e);
 }
 
@@ -158,6 +162,7 @@ int check_prefill_ws(const dsa_prefill_shape* s, void* ws, size_t ws_bytes, Pref
 int check_decode(const dsa_decode_shape* s, bool need_indexer) {
   if (!s || !s->cache_lens || s->batch < 1 || s->cache_capacity < 1) return DSA_ERR_INVALID_ARGUMENT;
   if (s->max_cache_len < 1 || s->max_cache_len > s->cache_capacity) return DSA_ERR_INVALID_ARGUMENT;
+  if (s->max_cache_len > 256 * 4096) return DSA_ERR_UNSUPPORTED;
   int rc = check_heads(s->topk, s->idx_heads, s->idx_dim, s->idx_dtype, s->q_heads, s->kv_heads, s->head_dim,
                        s->softmax_scale, need_indexer);
   if (rc) return rc;
@@ -169,9 +174,9 @@ constexpr int kDecodeSparseSplit = 128;   // selected keys per split (decode)
 constexpr int kDecodeDenseSplit = 2048;   // cache rows per split (dense decode)
 
 struct DecodeWs {
-  size_t scores, topk, opart, mlpart, total;
+  size_t scores, topk, opart, mlpart, ghist, keyrange, lkeys, lids, counts, spill, total;
   int64_t ld;
-  int nsplit_sparse, nsplit_dense;
+  int nsplit_sparse, nsplit_dense, nchunk;
 };
 
 DecodeWs decode_layout(const dsa_decode_shape* s) {
@@ -186,6 +191,14 @@ DecodeWs decode_layout(const dsa_decode_shape* s) {
   w.topk = off; off = align_up(off + B * size_t(s->topk) * sizeof(int32_t), 256);
   w.opart = off; off = align_up(off + B * ns * size_t(s->q_heads) * s->head_dim * sizeof(float), 256);
   w.mlpart = off; off = align_up(off + B * ns * size_t(s->q_heads) * sizeof(float2), 256);
+  w.nchunk = topk_decode_nchunk(s->max_cache_len);
+  const size_t lst = B * size_t(w.nchunk) * 4096;
+  w.ghist = off; off = align_up(off + B * 2048 * sizeof(int), 256);
+  w.keyrange = off; off = align_up(off + B * 2 * sizeof(uint32_t), 256);
+  w.lkeys = off; off = align_up(off + lst * sizeof(uint32_t), 256);
+  w.lids = off; off = align_up(off + lst * sizeof(int), 256);
+  w.counts = off; off = align_up(off + B * size_t(w.nchunk) * sizeof(int), 256);
+  w.spill = off; off = align_up(off + 2 * lst * sizeof(int), 256);
   w.total = off;
   return w;
 }
@@ -243,7 +256,7 @@ int dsa_index_topk(const dsa_prefill_shape* s, const void* q_idx, const void* k_
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((rc = run_index_scores_tri(s, q_idx, k_idx, w_idx, ws, L, st))) return rc;
   return hip_status(launch_topk_prefill(at<float>(ws, L.scores), at<int64_t>(ws, L.seqoff), s->cu_seqlens,
-                                        s->num_seqs, s->total_tokens, s->topk, topk_idx, st));
+                                        s->num_seqs, s->total_tokens, s->topk, at<float2>(ws, L.rowrange), topk_idx, st));
 }
 
 int dsa_sparse_attention(const dsa_prefill_shape* s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -283,12 +296,12 @@ int prefill_impl(const dsa_prefill_shape* s, const void* q_idx, const void* k_id
   if (L.nb16 > 0) {
     e = launch_indexer_prefill(s->idx_dtype == DSA_IDX_FP8_E4M3, s->idx_dim, q_idx, k_idx, w_idx, s->cu_seqlens,
                                s->idx_heads, at<int2>(ws, L.sched16), at<int>(ws, L.counts), L.nb16,
-                               at<int64_t>(ws, L.seqoff), at<float>(ws, L.scores), st);
+                               at<int64_t>(ws, L.seqoff), at<float>(ws, L.scores), at<float2>(ws, L.rowrange), st);
     if (e != hipSuccess) return hip_status(e);
   }
   if ((rc = record(ev, 1, st))) return rc;
   if ((rc = hip_status(launch_topk_prefill(at<float>(ws, L.scores), at<int64_t>(ws, L.seqoff), s->cu_seqlens,
-                                           s->num_seqs, s->total_tokens, s->topk, idx, st))))
+                                           s->num_seqs, s->total_tokens, s->topk, at<float2>(ws, L.rowrange), idx, st))))
     return rc;
   if ((rc = record(ev, 2, st))) return rc;
   if ((rc = hip_status(launch_gather_attention(q, k, v, idx, s->topk, 0, s->cu_seqlens, s->num_seqs, nullptr, 0,
@@ -313,10 +326,15 @@ int decode_impl(const dsa_decode_shape* s, const void* q_idx, const float* w_idx
   int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.topk);
   float* scores = at<float>(ws, L.scores);
   if ((rc = hip_status(launch_indexer_decode(q_idx, w_idx, k_idx_cache, s->cache_lens, s->batch, s->cache_capacity,
-                                             s->max_cache_len, s->idx_heads, L.ld, scores, st))))
+                                             s->max_cache_len, s->idx_heads, L.ld, scores, at<int>(ws, L.ghist),
+                                             at<uint32_t>(ws, L.keyrange), st))))
     return rc;
   if ((rc = record(ev, 0, st))) return rc;
-  if ((rc = hip_status(launch_topk_decode(scores, L.ld, s->cache_lens, s->batch, s->topk, idx, st)))) return rc;
+  if ((rc = hip_status(launch_topk_decode(scores, L.ld, s->cache_lens, s->batch, s->max_cache_len, s->topk,
+                                          at<uint32_t>(ws, L.keyrange), at<int>(ws, L.ghist),
+                                          at<uint32_t>(ws, L.lkeys), at<int>(ws, L.lids),
+                                          at<int>(ws, L.counts), at<int>(ws, L.spill), idx, st))))
+    return rc;
   if ((rc = record(ev, 1, st))) return rc;
   if ((rc = hip_status(launch_gather_attention(q, k_cache, v_cache, idx, s->topk, 1, nullptr, 0, s->cache_lens,
                                                s->cache_capacity, s->batch, s->q_heads, s->kv_heads,

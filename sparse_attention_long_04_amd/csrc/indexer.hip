@@ -64,7 +64,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ w_idx, const int32_t* __restrict__ cu, int H,
     const int2* __restrict__ sched, const int* __restrict__ sched_count,
-    const int64_t* __restrict__ seqoff, float* __restrict__ scores) {
+    const int64_t* __restrict__ seqoff, float* __restrict__ scores, float2* __restrict__ rowrange) {
   constexpr int ROWB = DI * (FP8 ? 1 : 2);   // bytes of one d_I row
   constexpr int UNITS = ROWB / 16;           // 16-byte units per row
   constexpr int CH = ROWB / 4;               // bytes per lane group
@@ -72,6 +72,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   static_assert(UNITS >= 8, "swizzle needs >= 8 units per row");
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[HMAX * 16 * ROWB];
   __shared__ __attribute__((aligned(16))) float w_lds[HMAX * 16];
+  __shared__ float2 range_lds[NWAVES][16];
 
   const int n = blockIdx.x;
   if (n >= *sched_count) return;
@@ -109,6 +110,11 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   const int r = lane & 15, g = lane >> 4;
   const int64_t stride = 16 * (int64_t)(j + 1);
   float* __restrict__ sblk = scores + seqoff[b] + score_block_offset(j);
+  // per-row score range (min, max) over this lane's written scores; the top-k uses it to bin
+  // scores by value
+  float rmin[4], rmax[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { rmin[i] = __builtin_inff(); rmax[i] = -__builtin_inff(); }
 
   for (int kb = wave * NT * 16; kb < kend; kb += NWAVES * NT * 16) {
     // key tiles -> B operand registers
@@ -156,9 +162,31 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 4 * g + i;
-        if (row < rows && key <= i0 + row) sblk[row * stride + key] = acc[jt][i];
+        if (row < rows && key <= i0 + row) {
+          sblk[row * stride + key] = acc[jt][i];
+          rmin[i] = fminf(rmin[i], acc[jt][i]);
+          rmax[i] = fmaxf(rmax[i], acc[jt][i]);
+        }
       }
     }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      rmin[i] = fminf(rmin[i], __shfl_xor(rmin[i], o));
+      rmax[i] = fmaxf(rmax[i], __shfl_xor(rmax[i], o));
+    }
+    if (r == 0) range_lds[wave][4 * g + i] = make_float2(rmin[i], rmax[i]);
+  }
+  __syncthreads();
+  if (tid < rows) {
+    float2 acc2 = range_lds[0][tid];
+    for (int w = 1; w < NWAVES; ++w) {
+      acc2.x = fminf(acc2.x, range_lds[w][tid].x);
+      acc2.y = fmaxf(acc2.y, range_lds[w][tid].y);
+    }
+    rowrange[seq0 + i0 + tid] = acc2;
   }
 }
 
@@ -184,15 +212,16 @@ template <int HMAX, int NT>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_cache, const int32_t* __restrict__ cache_lens, int cap, int H,
-    int64_t score_ld, float* __restrict__ scores) {
+    int64_t score_ld, float* __restrict__ scores, int* __restrict__ ghist, uint32_t* __restrict__ keyrange) {
   constexpr int ROWB = 128, UNITS = 8, CH = 32;
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[HMAX * ROWB];
   __shared__ float w_lds[HMAX];
   const int b = blockIdx.y;
   const int n = cache_lens[b];
   const int key0 = blockIdx.x * (4 * NT * 16);
-  if (key0 >= n) return;
   const int tid = threadIdx.x;
+  // the top-k that follows merges chunk histograms into ghist[b] with atomics: clear it here
+  if (key0 >= n) return;
   for (int u = tid; u < H * UNITS; u += 256) {
     const int h = u / UNITS, c = u - h * UNITS;
     *reinterpret_cast<i32x4*>(q_lds + h * ROWB + ((c ^ (h & 7)) * 16)) =
@@ -229,13 +258,39 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
       for (int i = 0; i < 4; ++i) acc[jt] = fmaf(wv[i], fmaxf(c[i], 0.f), acc[jt]);
     }
   }
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int jt = 0; jt < NT; ++jt) {
     float v = acc[jt];
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
     const int key = kb + 16 * jt + r;
-    if (g == 0 && key < n) scores[(int64_t)b * score_ld + key] = v;
+    if (g == 0 && key < n) {
+      scores[(int64_t)b * score_ld + key] = v;
+      const uint32_t kk = score_key(v);
+      kmin = min(kmin, kk);
+      kmax = max(kmax, kk);
+    }
+  }
+  // row range for the top-k's value binning (integer atomics: order-independent)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  }
+  if (lane == 0) {
+    atomicMin(&keyrange[2 * b], kmin);
+    atomicMax(&keyrange[2 * b + 1], kmax);
+  }
+}
+
+// Reset the decode top-k's per-row state: histogram and key range.
+__global__ void decode_topk_reset_kernel(int* __restrict__ ghist, uint32_t* __restrict__ keyrange) {
+  const int b = blockIdx.x;
+  for (int i = threadIdx.x; i < 2048; i += blockDim.x) ghist[b * 2048 + i] = 0;
+  if (threadIdx.x == 0) {
+    keyrange[2 * b] = 0xFFFFFFFFu;
+    keyrange[2 * b + 1] = 0u;
   }
 }
 
@@ -254,15 +309,15 @@ hipError_t launch_build_schedule(const int32_t* cu, int nseq, int bq, int nb_bou
 hipError_t launch_indexer_prefill(bool fp8, int di, const void* q_idx, const void* k_idx,
                                   const float* w, const int32_t* cu, int H, const int2* sched,
                                   const int* count, int nb_bound, const int64_t* seqoff,
-                                  float* scores, hipStream_t st) {
+                                  float* scores, float2* rowrange, hipStream_t st) {
   const auto* q = static_cast<const uint8_t*>(q_idx);
   const auto* k = static_cast<const uint8_t*>(k_idx);
   if (fp8 && di == 128)
-    indexer_prefill_kernel<true, 128, 64, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores);
+    indexer_prefill_kernel<true, 128, 64, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores, rowrange);
   else if (!fp8 && di == 64)
-    indexer_prefill_kernel<false, 64, 64, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores);
+    indexer_prefill_kernel<false, 64, 64, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores, rowrange);
   else if (!fp8 && di == 128)
-    indexer_prefill_kernel<false, 128, 32, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores);
+    indexer_prefill_kernel<false, 128, 32, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores, rowrange);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -277,13 +332,15 @@ hipError_t launch_unpack_scores(const float* tri, const int64_t* seqoff, const i
 
 hipError_t launch_indexer_decode(const void* q_idx, const float* w, const void* k_cache,
                                  const int32_t* cache_lens, int B, int cap, int max_len, int H,
-                                 int64_t score_ld, float* scores, hipStream_t st) {
+                                 int64_t score_ld, float* scores, int* ghist, uint32_t* keyrange,
+                                 hipStream_t st) {
   constexpr int NT = 4;
   const int per_block = 4 * NT * 16;
   dim3 grid((max_len + per_block - 1) / per_block, B);
+  decode_topk_reset_kernel<<<B, 256, 0, st>>>(ghist, keyrange);
   indexer_decode_kernel<64, NT><<<grid, 256, 0, st>>>(static_cast<const uint8_t*>(q_idx), w,
                                                       static_cast<const uint8_t*>(k_cache), cache_lens,
-                                                      cap, H, score_ld, scores);
+                                                      cap, H, score_ld, scores, ghist, keyrange);
   return hipGetLastError();
 }
 

@@ -5,23 +5,44 @@
 // Rule: the first min(k, n) keys in the order (score descending, index ascending), written in
 // ascending index order and padded with -1.
 //
-// One workgroup (256 threads) per row.  Scores are mapped to order-preserving uint32 keys and
-// the k-th largest key T is found by a most-significant-digit radix select (digits of 12, 12
-// and 8 bits, histograms in LDS).  Then one ordered stream compaction keeps every key > T and
-// the lowest-index keys == T until k are kept; a block-wide prefix sum gives each kept key its
-// output slot, so the output comes out sorted with no sort pass.
+// Scores map to order-preserving uint32 keys.  The k-th largest key T is found by a most-
+// significant-digit radix select (digits of 11, 11 and 10 bits; histograms in LDS); then an
+// ordered stream compaction keeps every key > T and the lowest-index keys == T until k are
+// kept.  A block-wide prefix sum gives every kept key its output slot, so the output is
+// sorted without a sort pass.  No float atomics anywhere; integer histogram atomics commute.
+//
+// Scores of one row crowd into a few float exponents, so the first pass bins by VALUE:
+// bin(x) = floor((x - lo) * 2048 / (hi - lo)) with the row's min lo and max hi (written by the
+// indexer).  The map is monotone, so every element of a bin above the threshold bin is kept and
+// only the threshold bin needs a closer look.
+//
+// Prefill (one workgroup per row): pass 1 histograms the value bins over the row in HBM;
+// pass 2 compacts every element whose bin is >= the threshold bin into LDS (in index order);
+// the exact radix select and the output compaction then run on that short LDS list.  Rows whose
+// list would not fit (heavy ties) fall back to radix passes over HBM; rows whose scores are all
+// equal keep their first k keys directly.
+//
+// Decode (few rows of ~10^5 keys): the row is split into 4096-key chunks handled by separate
+// workgroups -- chunk histograms are merged with integer atomics, every chunk compacts its
+// candidates into its own list, and one workgroup per row finishes the select over the
+// concatenated lists.
 #include "common.h"
 
 namespace dsa {
 
 constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kListCap = 4096;     // LDS candidate list capacity (prefill)
+constexpr int kBins = 2048;        // value bins / radix digit size
+constexpr int kChunk = 4096;       // decode chunk
+constexpr int kFinalCap = 12288;   // LDS list capacity of the decode finalize step
 
 struct TopkSmem {
-  int hist[4096];
+  int hist[kBins];
   int wave_tot[kTopkWaves];
   int sel_digit;
   int sel_above;
+  int list_n;
 };
 
 // Block-wide inclusive scan (256 threads).  Returns the inclusive prefix, *total = block sum.
@@ -42,79 +63,63 @@ __device__ __forceinline__ int block_incl_scan(int v, int* wave_tot, int* total)
   return incl + before;
 }
 
-__device__ void select_row(const float* __restrict__ row, int n, int K, int32_t* __restrict__ out,
-                           TopkSmem& sm) {
+// Given sm.hist[0..nb) filled, find the digit d with  above(d) < krem <= above(d) + hist[d],
+// above(d) = sum of hist over digits > d.  Results in sm.sel_digit / sm.sel_above.
+__device__ void find_digit(TopkSmem& sm, int nb, int krem) {
   const int tid = threadIdx.x;
-  if (n <= K) {
-    for (int s = tid; s < K; s += kTopkThreads) out[s] = (s < n) ? s : -1;
-    return;
+  const int bpt = nb / kTopkThreads;
+  const int top = nb - bpt * tid;
+  int local = 0;
+  for (int i = 1; i <= bpt; ++i) local += sm.hist[top - i];
+  int total;
+  const int incl = block_incl_scan(local, sm.wave_tot, &total);
+  const int excl = incl - local;
+  if (excl < krem && krem <= incl) {
+    int c = excl;
+    for (int i = 1; i <= bpt; ++i) {
+      const int h = sm.hist[top - i];
+      if (c + h >= krem) {
+        sm.sel_digit = top - i;
+        sm.sel_above = c;
+        break;
+      }
+      c += h;
+    }
   }
-  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-  uint32_t prefix = 0, hi_mask = 0;
-  int krem = K;
-  const int shifts[3] = {20, 8, 0};
-  const int widths[3] = {12, 12, 8};
-  for (int d = 0; d < 3; ++d) {
-    const int shift = shifts[d];
-    const int nb = 1 << widths[d];
-    const uint32_t dmask = uint32_t(nb - 1);
-    for (int i = tid; i < nb; i += kTopkThreads) sm.hist[i] = 0;
-    __syncthreads();
-    if (aligned) {
-      const int n4 = n >> 2;
-      for (int q = tid; q < n4; q += kTopkThreads) {
-        const f32x4 v = reinterpret_cast<const f32x4*>(row)[q];
+  __syncthreads();
+}
+
+__device__ __forceinline__ void clear_hist(TopkSmem& sm, int nb) {
+  for (int i = threadIdx.x; i < nb; i += kTopkThreads) sm.hist[i] = 0;
+  __syncthreads();
+}
+
+// Monotone value bin of score x in a row with range [lo, lo + 1/sc].
+__device__ __forceinline__ int value_bin(float x, float lo, float sc) {
+  return min(kBins - 1, int((x - lo) * sc));
+}
+
+__device__ __forceinline__ float key_to_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// ---- element sources: a raw score row (index = position) or a (key, index) list ----------
+struct RowSrc {
+  const float* __restrict__ row;
+  bool vec;  // 16-byte aligned
+  __device__ __forceinline__ void quadf(int n, int s0, float* x) const {
+    if (vec && s0 + 3 < n) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(row + s0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t key = score_key(v[e]);
-          if ((key & hi_mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & dmask], 1);
-        }
-      }
-      for (int s = (n4 << 2) + tid; s < n; s += kTopkThreads) {
-        const uint32_t key = score_key(row[s]);
-        if ((key & hi_mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & dmask], 1);
-      }
+      for (int e = 0; e < 4; ++e) x[e] = v[e];
     } else {
-      for (int s = tid; s < n; s += kTopkThreads) {
-        const uint32_t key = score_key(row[s]);
-        if ((key & hi_mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & dmask], 1);
-      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (s0 + e < n) ? row[s0 + e] : 0.f;
     }
-    __syncthreads();
-    // thread tid owns bins [nb - bpt*(tid+1), nb - bpt*tid), scanned from the top
-    const int bpt = nb / kTopkThreads;
-    const int top = nb - bpt * tid;
-    int local = 0;
-    for (int i = 1; i <= bpt; ++i) local += sm.hist[top - i];
-    int total;
-    const int incl = block_incl_scan(local, sm.wave_tot, &total);
-    const int excl = incl - local;
-    if (excl < krem && krem <= incl) {
-      int c = excl;
-      for (int i = 1; i <= bpt; ++i) {
-        const int h = sm.hist[top - i];
-        if (c + h >= krem) {
-          sm.sel_digit = top - i;
-          sm.sel_above = c;
-          break;
-        }
-        c += h;
-      }
-    }
-    __syncthreads();
-    const int digit = sm.sel_digit;
-    krem -= sm.sel_above;
-    prefix |= uint32_t(digit) << shift;
-    hi_mask |= dmask << shift;
-    __syncthreads();
   }
-  // prefix = key of the k-th largest score; krem = how many keys equal to it are kept.
-  const uint32_t T = prefix;
-  int base_gt = 0, base_eq = 0;
-  for (int c0 = 0; c0 < n; c0 += 4 * kTopkThreads) {
-    const int s0 = c0 + 4 * tid;
-    uint32_t keys[4];
-    if (aligned && s0 + 3 < n) {
+  // visit elements [c0 + 4*tid, +4) of a 1024-element chunk in index order
+  __device__ __forceinline__ void quad(int n, int s0, uint32_t* keys, int* ids) const {
+    if (vec && s0 + 3 < n) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(row + s0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) keys[e] = score_key(v[e]);
@@ -122,12 +127,78 @@ __device__ void select_row(const float* __restrict__ row, int n, int K, int32_t*
 #pragma unroll
       for (int e = 0; e < 4; ++e) keys[e] = (s0 + e < n) ? score_key(row[s0 + e]) : 0u;
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ids[e] = s0 + e;
+  }
+};
+
+struct ListSrc {
+  const uint32_t* __restrict__ keys;
+  const int* __restrict__ ids;
+  __device__ __forceinline__ void quad(int n, int s0, uint32_t* k, int* id) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool ok = s0 + e < n;
+      k[e] = ok ? keys[s0 + e] : 0u;
+      id[e] = ok ? ids[s0 + e] : -1;
+    }
+  }
+};
+
+// Histogram of digit (key >> shift) & dmask over elements with (key & hmask) == prefix.
+template <class Src>
+__device__ void hist_pass(const Src& src, int n, uint32_t prefix, uint32_t hmask, int shift, uint32_t dmask,
+                          TopkSmem& sm) {
+  for (int c0 = 0; c0 < n; c0 += 4 * kTopkThreads) {
+    uint32_t k[4];
+    int id[4];
+    const int s0 = c0 + 4 * threadIdx.x;
+    src.quad(n, s0, k, id);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (s0 + e < n && (k[e] & hmask) == prefix) atomicAdd(&sm.hist[(k[e] >> shift) & dmask], 1);
+  }
+  __syncthreads();
+}
+
+// Radix select digits [d0, 3) over src.  On entry prefix/hmask describe the already fixed high
+// bits and krem the number still to take among matching elements.  On exit prefix = T (the
+// k-th largest key) and krem = how many keys equal to T are kept.
+template <class Src>
+__device__ void radix_rest(const Src& src, int n, int d0, uint32_t& prefix, uint32_t& hmask, int& krem,
+                           TopkSmem& sm) {
+  const int shifts[3] = {21, 10, 0};
+  const int widths[3] = {11, 11, 10};
+  for (int d = d0; d < 3; ++d) {
+    const int nb = 1 << widths[d];
+    const uint32_t dmask = uint32_t(nb - 1);
+    clear_hist(sm, nb);
+    hist_pass(src, n, prefix, hmask, shifts[d], dmask, sm);
+    find_digit(sm, nb, krem);
+    krem -= sm.sel_above;
+    prefix |= uint32_t(sm.sel_digit) << shifts[d];
+    hmask |= dmask << shifts[d];
+    __syncthreads();
+  }
+}
+
+// Ordered compaction: call emit(slot, key, id) for every element kept by keep(key) in index
+// order; slot counts kept elements.  Elements with key == T are kept only while fewer than
+// krem of them have been seen (lowest indices first); keys > T are always kept.
+template <class Src, class Emit>
+__device__ void ordered_emit(const Src& src, int n, uint32_t T, int krem, Emit emit, TopkSmem& sm) {
+  int base_gt = 0, base_eq = 0;
+  for (int c0 = 0; c0 < n; c0 += 4 * kTopkThreads) {
+    uint32_t k[4];
+    int id[4];
+    const int s0 = c0 + 4 * threadIdx.x;
+    src.quad(n, s0, k, id);
     int cgt = 0, ceq = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool valid = s0 + e < n;
-      cgt += (valid && keys[e] > T);
-      ceq += (valid && keys[e] == T);
+      const bool ok = s0 + e < n;
+      cgt += (ok && k[e] > T);
+      ceq += (ok && k[e] == T);
     }
     const int packed = cgt | (ceq << 16);
     int total;
@@ -138,51 +209,254 @@ __device__ void select_row(const float* __restrict__ row, int n, int K, int32_t*
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (s0 + e >= n) break;
-      if (keys[e] > T) {
-        out[gt_before + min(eq_before, krem)] = s0 + e;
+      if (k[e] > T) {
+        emit(gt_before + min(eq_before, krem), k[e], id[e]);
         ++gt_before;
-      } else if (keys[e] == T) {
-        if (eq_before < krem) out[gt_before + eq_before] = s0 + e;
+      } else if (k[e] == T) {
+        if (eq_before < krem) emit(gt_before + eq_before, k[e], id[e]);
         ++eq_before;
       }
     }
     base_gt += total & 0xFFFF;
     base_eq += total >> 16;
   }
+  __syncthreads();
+}
+
+// Histogram of value bins over a raw row.
+__device__ void value_hist_pass(const RowSrc& src, int n, float lo, float sc, int* hist) {
+  for (int c0 = 0; c0 < n; c0 += 4 * kTopkThreads) {
+    float x[4];
+    const int s0 = c0 + 4 * threadIdx.x;
+    src.quadf(n, s0, x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (s0 + e < n) atomicAdd(&hist[value_bin(x[e], lo, sc)], 1);
+  }
+  __syncthreads();
+}
+
+// Ordered compaction of every element whose value bin is >= b1 (no tie limit): emit(slot, key,
+// id) in index order.  Returns the count.
+template <class Emit>
+__device__ int ordered_emit_bin_ge(const RowSrc& src, int n, float lo, float sc, int b1, Emit emit, TopkSmem& sm) {
+  int base = 0;
+  for (int c0 = 0; c0 < n; c0 += 4 * kTopkThreads) {
+    float x[4];
+    const int s0 = c0 + 4 * threadIdx.x;
+    src.quadf(n, s0, x);
+    bool keep[4];
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      keep[e] = s0 + e < n && value_bin(x[e], lo, sc) >= b1;
+      c += keep[e];
+    }
+    int total;
+    const int incl = block_incl_scan(c, sm.wave_tot, &total);
+    int pos = base + incl - c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (keep[e]) emit(pos++, score_key(x[e]), s0 + e);
+    base += total;
+  }
+  __syncthreads();
+  return base;
+}
+
+struct TopkRowSmem {
+  TopkSmem s;
+  uint32_t lkeys[kListCap];
+  int lids[kListCap];
+};
+
+__device__ __forceinline__ void first_k(int n, int K, int32_t* __restrict__ out) {
+  for (int s = threadIdx.x; s < K; s += kTopkThreads) out[s] = (s < n) ? s : -1;
+}
+
+__device__ void select_row(const float* __restrict__ row, int n, int K, float lo, float hi,
+                           int32_t* __restrict__ out, TopkRowSmem& sm) {
+  if (n <= K || !(hi > lo)) {  // everything kept, or every score equal: the first k keys win
+    first_k(n, K, out);
+    return;
+  }
+  const RowSrc src{row, (reinterpret_cast<uintptr_t>(row) & 15) == 0};
+  const float sc = float(kBins) / (hi - lo);
+  clear_hist(sm.s, kBins);
+  value_hist_pass(src, n, lo, sc, sm.s.hist);
+  find_digit(sm.s, kBins, K);
+  const int b1 = sm.s.sel_digit;
+  const int cand = sm.s.sel_above + sm.s.hist[b1];
+  __syncthreads();
+  uint32_t prefix = 0, hmask = 0;
+  int krem = K;
+  if (cand <= kListCap) {
+    ordered_emit_bin_ge(src, n, lo, sc, b1, [&](int slot, uint32_t key, int id) {
+      sm.lkeys[slot] = key;
+      sm.lids[slot] = id;
+    }, sm.s);
+    const ListSrc ls{sm.lkeys, sm.lids};
+    radix_rest(ls, cand, 0, prefix, hmask, krem, sm.s);
+    ordered_emit(ls, cand, prefix, krem, [&](int slot, uint32_t, int id) { out[slot] = id; }, sm.s);
+  } else {
+    radix_rest(src, n, 0, prefix, hmask, krem, sm.s);
+    ordered_emit(src, n, prefix, krem, [&](int slot, uint32_t, int id) { out[slot] = id; }, sm.s);
+  }
 }
 
 // Prefill rows: one workgroup per token, longest rows first (row t = T-1-blockIdx.x).
 __global__ __launch_bounds__(kTopkThreads) void topk_prefill_kernel(
     const float* __restrict__ tri, const int64_t* __restrict__ seqoff, const int32_t* __restrict__ cu,
-    int nseq, int64_t T, int K, int32_t* __restrict__ out) {
-  __shared__ TopkSmem sm;
+    int nseq, int64_t T, int K, const float2* __restrict__ rowrange, int32_t* __restrict__ out) {
+  __shared__ TopkRowSmem sm;
   const int64_t t = T - 1 - (int64_t)blockIdx.x;
   const int b = find_seq(cu, nseq, t);
   const int i = int(t - cu[b]);
   const int j = i >> 4;
   const float* row = tri + seqoff[b] + score_block_offset(j) + (i & 15) * 16 * (int64_t)(j + 1);
-  select_row(row, i + 1, K, out + t * K, sm);
+  const float2 rg = rowrange[t];
+  select_row(row, i + 1, K, rg.x, rg.y, out + t * K, sm);
 }
 
-// Decode rows: one workgroup per sequence, n = cache_lens[b].
-__global__ __launch_bounds__(kTopkThreads) void topk_decode_kernel(
+// ------------------------------------------------------------------------------------------
+// Decode: chunked top-k over rows of n = cache_lens[b] scores.
+//   keyrange [B][2] (min, max order keys, from the decode indexer), ghist [B][kBins] int
+//   (cleared before the indexer), lists [B][nchunk][kChunk] (key, id), counts [B][nchunk].
+// ------------------------------------------------------------------------------------------
+struct RowRange {
+  float lo, sc;
+  bool flat;
+};
+
+__device__ __forceinline__ RowRange decode_range(const uint32_t* keyrange, int b) {
+  RowRange rr;
+  rr.lo = key_to_score(keyrange[2 * b]);
+  const float hi = key_to_score(keyrange[2 * b + 1]);
+  rr.flat = !(hi > rr.lo);
+  rr.sc = rr.flat ? 0.f : float(kBins) / (hi - rr.lo);
+  return rr;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_decode_hist_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cache_lens, int K,
-    int32_t* __restrict__ out) {
+    const uint32_t* __restrict__ keyrange, int* __restrict__ ghist) {
   __shared__ TopkSmem sm;
+  const int b = blockIdx.y;
+  const int n = cache_lens[b];
+  const int c0 = blockIdx.x * kChunk;
+  const RowRange rr = decode_range(keyrange, b);
+  if (n <= K || c0 >= n || rr.flat) return;
+  const int cn = min(kChunk, n - c0);
+  clear_hist(sm, kBins);
+  const RowSrc src{scores + b * ld + c0, true};
+  value_hist_pass(src, cn, rr.lo, rr.sc, sm.hist);
+  for (int i = threadIdx.x; i < kBins; i += kTopkThreads) {
+    const int h = sm.hist[i];
+    if (h) atomicAdd(&ghist[b * kBins + i], h);
+  }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_decode_collect_kernel(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cache_lens, int K,
+    const uint32_t* __restrict__ keyrange, const int* __restrict__ ghist, int nchunk,
+    uint32_t* __restrict__ lkeys, int* __restrict__ lids, int* __restrict__ counts) {
+  __shared__ TopkSmem sm;
+  const int b = blockIdx.y;
+  const int n = cache_lens[b];
+  const int c0 = blockIdx.x * kChunk;
+  const RowRange rr = decode_range(keyrange, b);
+  if (n <= K || rr.flat) return;
+  int cnt = 0;
+  if (c0 < n) {
+    for (int i = threadIdx.x; i < kBins; i += kTopkThreads) sm.hist[i] = ghist[b * kBins + i];
+    __syncthreads();
+    find_digit(sm, kBins, K);
+    const int b1 = sm.sel_digit;
+    const int cn = min(kChunk, n - c0);
+    const RowSrc src{scores + b * ld + c0, true};
+    const int64_t base = ((int64_t)b * nchunk + blockIdx.x) * kChunk;
+    cnt = ordered_emit_bin_ge(src, cn, rr.lo, rr.sc, b1, [&](int slot, uint32_t key, int id) {
+      lkeys[base + slot] = key;
+      lids[base + slot] = c0 + id;
+    }, sm);
+  }
+  if (threadIdx.x == 0) counts[b * nchunk + blockIdx.x] = cnt;
+}
+
+struct TopkFinalSmem {
+  TopkSmem s;
+  uint32_t lkeys[kFinalCap];
+  int lids[kFinalCap];
+  int offs[256];
+};
+
+__global__ __launch_bounds__(kTopkThreads) void topk_decode_final_kernel(
+    const int32_t* __restrict__ cache_lens, int K, const uint32_t* __restrict__ keyrange, int nchunk,
+    const uint32_t* __restrict__ gkeys, const int* __restrict__ gids, const int* __restrict__ counts,
+    int32_t* __restrict__ out, int* __restrict__ spill_keys_ids) {
+  __shared__ TopkFinalSmem sm;
   const int b = blockIdx.x;
-  select_row(scores + b * ld, cache_lens[b], K, out + (int64_t)b * K, sm);
+  const int n = cache_lens[b];
+  int32_t* orow = out + (int64_t)b * K;
+  if (n <= K || decode_range(keyrange, b).flat) {
+    first_k(n, K, orow);
+    return;
+  }
+  // concatenate the chunk lists (chunk order = index order)
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int c = 0; c < nchunk; ++c) {
+      sm.offs[c] = acc;
+      acc += counts[b * nchunk + c];
+    }
+    sm.s.list_n = acc;
+  }
+  __syncthreads();
+  const int total = sm.s.list_n;
+  uint32_t* keys = sm.lkeys;
+  int* ids = sm.lids;
+  if (total > kFinalCap) {  // heavy ties: work from a global spill area instead of LDS
+    keys = reinterpret_cast<uint32_t*>(spill_keys_ids) + (int64_t)b * 2 * nchunk * kChunk;
+    ids = reinterpret_cast<int*>(keys + nchunk * kChunk);
+  }
+  for (int c = 0; c < nchunk; ++c) {
+    const int cnt = counts[b * nchunk + c];
+    const int64_t src = ((int64_t)b * nchunk + c) * kChunk;
+    for (int i = threadIdx.x; i < cnt; i += kTopkThreads) {
+      keys[sm.offs[c] + i] = gkeys[src + i];
+      ids[sm.offs[c] + i] = gids[src + i];
+    }
+  }
+  __syncthreads();
+  const ListSrc ls{keys, ids};
+  uint32_t prefix = 0, hmask = 0;
+  int krem = K;
+  radix_rest(ls, total, 0, prefix, hmask, krem, sm.s);
+  ordered_emit(ls, total, prefix, krem, [&](int slot, uint32_t, int id) { orow[slot] = id; }, sm.s);
 }
 
 hipError_t launch_topk_prefill(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq,
-                               int64_t T, int K, int32_t* out, hipStream_t st) {
+                               int64_t T, int K, const float2* rowrange, int32_t* out, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  topk_prefill_kernel<<<(unsigned)T, kTopkThreads, 0, st>>>(tri, seqoff, cu, nseq, T, K, out);
+  topk_prefill_kernel<<<(unsigned)T, kTopkThreads, 0, st>>>(tri, seqoff, cu, nseq, T, K, rowrange, out);
   return hipGetLastError();
 }
 
-hipError_t launch_topk_decode(const float* scores, int64_t ld, const int32_t* cache_lens, int B, int K,
-                              int32_t* out, hipStream_t st) {
-  topk_decode_kernel<<<B, kTopkThreads, 0, st>>>(scores, ld, cache_lens, K, out);
+int topk_decode_nchunk(int max_len) { return (max_len + kChunk - 1) / kChunk; }
+
+// Workspace needs: ghist B*4096 ints, lists B*nchunk*kChunk*(key+id) twice (chunk lists and
+// the finalize spill area), counts B*nchunk ints.
+hipError_t launch_topk_decode(const float* scores, int64_t ld, const int32_t* cache_lens, int B, int max_len,
+                              int K, const uint32_t* keyrange, int* ghist, uint32_t* lkeys, int* lids, int* counts,
+                              int* spill, int32_t* out, hipStream_t st) {
+  const int nchunk = topk_decode_nchunk(max_len);
+  if (nchunk > 256) return hipErrorInvalidValue;
+  dim3 grid(nchunk, B);
+  topk_decode_hist_kernel<<<grid, kTopkThreads, 0, st>>>(scores, ld, cache_lens, K, keyrange, ghist);
+  topk_decode_collect_kernel<<<grid, kTopkThreads, 0, st>>>(scores, ld, cache_lens, K, keyrange, ghist, nchunk, lkeys,
+                                                            lids, counts);
+  topk_decode_final_kernel<<<B, kTopkThreads, 0, st>>>(cache_lens, K, keyrange, nchunk, lkeys, lids, counts, out,
+                                                       spill);
   return hipGetLastError();
 }
 

@@ -130,7 +130,7 @@ def test_prefill_is_deterministic():
     assert torch.equal(a_idx, pb.topk_idx) and torch.equal(a_out, pb.out)
 
 
-@pytest.mark.parametrize("ctx,cap,k,steps", [(3000, 3100, 256, 2), (500, 520, 2048, 2)])
+@pytest.mark.parametrize("ctx,cap,k,steps", [(3000, 3100, 256, 2), (500, 520, 2048, 2), (9000, 9100, 2048, 2)])
 def test_decode_parity(ctx, cap, k, steps):
     d = gen.make_decode(3, ctx, cap, steps, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", topk=k, seed=5)
     st = DecodeState(d)
@@ -152,3 +152,41 @@ def test_decode_parity(ctx, cap, k, steps):
         assert_out_close(bf16_to_float(st.out), ref, f"decode step {i}")
         dense = bf16_to_float(st.dense(out=torch.empty_like(st.out)))
         assert_out_close(dense, O.dense_decode(kk, vv, st.len_host, s["q"], d.softmax_scale), f"dense decode {i}")
+
+
+def test_topk_all_ties_prefill():
+    """Degenerate case: every score equal (zero indexer queries) -> each row keeps its first
+    min(k, i+1) keys; rows longer than the LDS candidate list take the multi-pass path."""
+    p = gen.make_prefill([9000, 300], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=2048,
+                         seed=9)
+    p.q_idx[:] = 0
+    pb = PrefillBatch(p)
+    pb.prefill()
+    idx = pb.topk_idx.cpu().numpy()
+    o = oracle_of(p)
+    for t in [0, 5, 2046, 2047, 2048, 5000, 8191, 8192, 8999, 9000, 9299]:
+        assert np.array_equal(idx[t], O.select_topk_row(o.scores(t), p.topk)), t
+    rows = np.array([0, 2047, 2048, 8999, 9150])
+    _, ref = o.rows(rows)
+    assert_out_close(bf16_to_float(pb.out)[rows], ref, "all ties")
+
+
+@pytest.mark.parametrize("zero_q", [False, True])
+def test_decode_chunked_topk(zero_q):
+    """Caches of ~20K rows: the decode top-k runs over several 4096-key chunks; with zero
+    queries every score ties and the candidate list spills out of LDS."""
+    d = gen.make_decode(2, 20000, 20064, 1, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", topk=2048, seed=15)
+    st = DecodeState(d)
+    s = st.load_step(0)
+    if zero_q:
+        st.step_dev["q_idx"].zero_()
+        s["q_idx"][:] = 0
+    st.append()
+    st.decode()
+    torch.cuda.synchronize()
+    kc, kk, vv = d.k_idx_cache.copy(), d.k_cache.copy(), d.v_cache.copy()
+    kc[:, 20000], kk[:, 20000], vv[:, 20000] = s["k_idx_new"], s["k_new"], s["v_new"]
+    sel, ref = O.decode_step(kc, kk, vv, st.len_host, s["q_idx"], s["w_idx"], s["q"], d.idx_dtype, d.topk,
+                             d.softmax_scale)
+    assert np.array_equal(st.topk_idx.cpu().numpy(), sel)
+    assert_out_close(bf16_to_float(st.out), ref, f"decode chunked zero_q={zero_q}")

@@ -26,6 +26,7 @@
 namespace dsa {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x4 mfma_f16_16x16x32(i32x4 a, i32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -256,48 +257,69 @@ __global__ void combine_kernel(const float* __restrict__ o_part, const float2* _
 
 // ------------------------------------------------------------------------------------------
 // Dense causal prefill (FlashAttention-style), head_dim 128.
+// Workgroup = 8 waves: 128 query tokens x 2 query heads of one KV group (waves 0-3 head 2p,
+// waves 4-7 head 2p+1, 32 tokens each), so every K/V tile staged in LDS serves both heads.
+// K/V tiles of 64 keys are double-buffered: the next tile is loaded into registers while the
+// current one is computed, then written to the other LDS buffer; one barrier per tile.
 // 32x32 MFMA output layout: lane l holds column l%32 and rows 8(i/4) + 4(l/32) + i%4, i<16.
-// S^T = K Q^T: A row rr of a 32-key block loads key kperm(rr) so that, per lane half, the 8
-// registers used by one PV k-step hold 8 consecutive keys.
+// S^T = K Q^T: A row rr of a 32-key block loads key kperm(rr), so that per lane half the 8
+// registers used by one PV k-step hold 8 consecutive keys.  The V^T operand of O^T += V^T P^T
+// (fp16 P x fp16 V) comes straight from the natural [key][dim] V tile through ds_read_b64_tr_b16: inside each
+// 16-lane group, lane j receives element j%4 of the 4-element rows fetched by lanes j/4,
+// j/4+4, j/4+8 and j/4+12, so lanes that fetch (key k0 + i/4, dims d0 + 4(i%4)..+3) end up with
+// keys k0..k0+3 of dim d0 + j.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ int kperm(int rr) {
   const int a = rr >> 3, hh = (rr >> 2) & 1, bb = rr & 3;
   return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + bb;
 }
 
-constexpr int kKStride = 136;  // bf16 per K row in LDS (128 + 8 pad)
-constexpr int kVStride = 72;   // halfs per V^T row in LDS (64 keys + 8 pad)
+constexpr int kKvRowB = 288;             // bytes per K/V row in LDS (256 + 32 pad)
+constexpr int kKvTileB = 64 * kKvRowB;   // one 64-key tile
 
-__global__ __launch_bounds__(256) void dense_prefill_kernel(
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<uint8_t*>(p)));
+}
+
+// 16-byte unit swizzle inside a K/V row: flips unit bit 0 with key bit 3 (removes the 2-way
+// bank conflict between keys k and k+8 in the K-operand reads).
+__device__ __forceinline__ int kv_off(int key, int byte) { return key * kKvRowB + (byte ^ (((key >> 3) & 1) << 4)); }
+
+__global__ __launch_bounds__(512) void dense_prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu, int Hq, int Hkv, float scale_log2, const int2* __restrict__ sched,
-    const int* __restrict__ sched_count, uint16_t* __restrict__ out) {
+    const int* __restrict__ sched_count, int pair, uint16_t* __restrict__ out) {
   constexpr int D = 128, BM = 128, BN = 64;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * kKStride];
-  __shared__ __attribute__((aligned(16))) _Float16 v_lds[D * kVStride];
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2][2][kKvTileB];  // [buffer][K=0/V=1]
   const int n = blockIdx.x;
   if (n >= *sched_count) return;
   const int2 e = sched[n];
   const int b = e.x, j = e.y;
-  const int h = blockIdx.y;
   const int G = Hq / Hkv;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // pair != 0: waves 0-3 take head 2y, waves 4-7 head 2y+1 (same KV head since G is even);
+  // pair == 0 (odd G): one head per workgroup, waves 4-7 only help stage the tiles
+  const int h = pair ? 2 * blockIdx.y + (w >> 2) : blockIdx.y;
+  const bool active = pair || w < 4;
   const int g = h / G;
   const int64_t seq0 = cu[b];
   const int L = cu[b + 1] - cu[b];
   const int q0 = BM * j;
   const int rows = min(BM, L - q0);
   const int kend = q0 + rows;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int qc = lane & 31, hf = lane >> 5;
   const int64_t kvs = (int64_t)Hkv * D;
+  const int my_q = q0 + 32 * (w & 3) + qc;
 
-  const int my_q = q0 + 32 * w + qc;  // local query index of this lane's column
   i32x4 qf[8];
   {
     const int qq = min(my_q, kend - 1);
     const uint16_t* qp = q + ((seq0 + qq) * Hq + h) * D + 8 * hf;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const i32x4*>(qp + 16 * s);
+    for (int s2 = 0; s2 < 8; ++s2) qf[s2] = *reinterpret_cast<const i32x4*>(qp + 16 * s2);
   }
   f32x16 o[4];
 #pragma unroll
@@ -305,49 +327,54 @@ __global__ __launch_bounds__(256) void dense_prefill_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   float m_run = -__builtin_inff(), l_run = 0.f;
-  const int wave_qmax = q0 + 32 * w + 31;
+  const int wave_qmax = q0 + 32 * (w & 3) + 31;
 
+  // tile loader: 512 threads x (2 K + 2 V) 16-byte units = 64 keys x 256 B each
+  i32x4 pre[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int u = tid + 512 * x;  // unit 0..1023: key = u >> 4, 16-byte column c = u & 15
+      const int kk = min(kt + (u >> 4), kend - 1);
+      pre[x] = *reinterpret_cast<const i32x4*>(k + (seq0 + kk) * kvs + g * D + 8 * (u & 15));
+      pre[2 + x] = *reinterpret_cast<const i32x4*>(v + (seq0 + kk) * kvs + g * D + 8 * (u & 15));
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int u = tid + 512 * x;
+      const int off = kv_off(u >> 4, 16 * (u & 15));
+      *reinterpret_cast<i32x4*>(&kv_lds[buf][0][off]) = pre[x];
+      // V is kept as fp16 (exact for bf16 values in fp16's normal range) for the fp16 P.V MFMA
+      float vf[8];
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) vf[e2] = bf16_to_f32(bf16_lane(pre[2 + x], e2));
+      *reinterpret_cast<i32x4*>(&kv_lds[buf][1][off]) = pack_f16x8(vf);
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  int buf = 0;
   for (int kt = 0; kt < kend; kt += BN) {
-    // K tile: 64 keys x 256 B, 16-byte units
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int u = tid + 256 * x;
-      const int key = u >> 4, c = u & 15;
-      const int kk = min(kt + key, kend - 1);
-      *reinterpret_cast<i32x4*>(k_lds + key * kKStride + 8 * c) =
-          *reinterpret_cast<const i32x4*>(k + (seq0 + kk) * kvs + g * D + 8 * c);
-    }
-    // V^T tile: thread -> keys 8*kg8..+7, dims 4*dq..+3
-    {
-      const int kg8 = tid >> 5, dq = tid & 31;
-      uint2 vv[8];
-#pragma unroll
-      for (int mm = 0; mm < 8; ++mm) {
-        const int kk = min(kt + 8 * kg8 + mm, kend - 1);
-        vv[mm] = *reinterpret_cast<const uint2*>(v + (seq0 + kk) * kvs + g * D + 4 * dq);
-      }
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        float col[8];
-#pragma unroll
-        for (int mm = 0; mm < 8; ++mm) {
-          const uint32_t wd = (d < 2) ? vv[mm].x : vv[mm].y;
-          col[mm] = bf16_to_f32(uint16_t((d & 1) ? (wd >> 16) : (wd & 0xFFFFu)));
-        }
-        *reinterpret_cast<i32x4*>(v_lds + (4 * dq + d) * kVStride + 8 * kg8) = pack_f16x8(col);
-      }
-    }
-    __syncthreads();
-    if (kt <= wave_qmax) {
+    const bool more = kt + BN < kend;
+    if (more) gload(kt + BN);
+    if (active && kt <= wave_qmax) {
+      const uint8_t* kl = kv_lds[buf][0];
+      const uint8_t* vl = kv_lds[buf][1];
       // S^T for two 32-key blocks
       f32x16 sacc[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[rb][i] = 0.f;
-        const uint16_t* ka = k_lds + (32 * rb + kperm(qc)) * kKStride + 8 * hf;
+        const int key = 32 * rb + kperm(qc);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) sacc[rb] = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(ka + 16 * s), qf[s], sacc[rb]);
+        for (int s2 = 0; s2 < 8; ++s2)
+          sacc[rb] = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(kl + kv_off(key, 32 * s2 + 16 * hf)), qf[s2],
+                                        sacc[rb]);
       }
       // mask + scale; C row (reg i, half hf) of block rb <-> key kt + 32rb + kperm(8(i/4)+4hf+i%4)
       float z[2][16];
@@ -363,14 +390,14 @@ __global__ __launch_bounds__(256) void dense_prefill_kernel(
         }
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float m_new = fmaxf(m_run, mt);
-      const bool live = m_new != -__builtin_inff();
-      const float alpha = live ? exp2f(m_run - m_new) : 1.f;
+      const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       float ps = 0.f;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = live ? exp2f(z[rb][i] - m_new) : 0.f;
+          const float pv = __builtin_amdgcn_exp2f(z[rb][i] - m_use);
           z[rb][i] = pv;
           ps += pv;
         }
@@ -378,22 +405,30 @@ __global__ __launch_bounds__(256) void dense_prefill_kernel(
       m_run = m_new;
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[db] *= alpha;
-      // O^T += V^T P^T, k-step (rb, kk2): keys kt + 32rb + 16kk2 + 8hf .. +7 = regs 8kk2..8kk2+7
+      // O^T += V^T P^T; k-step (rb, kk2) covers keys 32rb + 16kk2 + 0..15 = registers 8kk2..8kk2+7
+      const int grp = lane >> 4, jj = lane & 15;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int kk2 = 0; kk2 < 2; ++kk2) {
           const i32x4 pf = pack_f16x8(&z[rb][8 * kk2]);
-          const _Float16* va = v_lds + qc * kVStride + 32 * rb + 16 * kk2 + 8 * hf;
+          const int key_a = 32 * rb + 16 * kk2 + 8 * (grp >> 1) + (jj >> 2);
 #pragma unroll
-          for (int db = 0; db < 4; ++db)
-            o[db] = mfma_f16_32x32x16(*reinterpret_cast<const i32x4*>(va + 32 * db * kVStride), pf, o[db]);
+          for (int db = 0; db < 4; ++db) {
+            const int dim0 = 32 * db + 16 * (grp & 1) + 4 * (jj & 3);
+            const s16x4 lo = lds_tr16(vl + kv_off(key_a, 2 * dim0));
+            const s16x4 hi = lds_tr16(vl + kv_off(key_a + 4, 2 * dim0));
+            const i32x4 a = __builtin_bit_cast(i32x4, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            o[db] = mfma_f16_32x32x16(a, pf, o[db]);
+          }
         }
     }
+    if (more) lstore(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
   float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (my_q >= kend) return;
+  if (!active || my_q >= kend) return;
   const float inv = 1.f / l_tot;
   uint16_t* op = out + ((seq0 + my_q) * Hq + h) * D;
 #pragma unroll
@@ -442,8 +477,9 @@ hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint
                                 int Hq, int Hkv, float scale, const int2* sched, const int* count,
                                 int nb_bound, uint16_t* out, hipStream_t st) {
   if (nb_bound == 0) return hipSuccess;
-  dense_prefill_kernel<<<dim3(nb_bound, Hq), 256, 0, st>>>(q, k, v, cu, Hq, Hkv, scale * 1.4426950408889634f,
-                                                           sched, count, out);
+  const int pair = ((Hq / Hkv) % 2 == 0) ? 1 : 0;
+  dense_prefill_kernel<<<dim3(nb_bound, pair ? Hq / 2 : Hq), 512, 0, st>>>(
+      q, k, v, cu, Hq, Hkv, scale * 1.4426950408889634f, sched, count, pair, out);
   return hipGetLastError();
 }
 

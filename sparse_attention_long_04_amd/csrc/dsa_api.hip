@@ -16,12 +16,12 @@ hipError_t launch_unpack_scores(const float* tri, const int64_t* seqoff, const i
                                 int ldo, float* out, hipStream_t st);
 hipError_t launch_indexer_decode(const void* q_idx, const float* w, const void* k_cache, const int32_t* cache_lens,
                                  int B, int cap, int max_len, int H, int64_t score_ld, float* scores, int* ghist,
-                                 uint32_t* keyrange, hipStream_t st);
+                                 uint2* blkrange, hipStream_t st);
 hipError_t launch_topk_prefill(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq, int64_t T, int K,
                                const float2* rowrange, int32_t* out, hipStream_t st);
 int topk_decode_nchunk(int max_len);
 hipError_t launch_topk_decode(const float* scores, int64_t ld, const int32_t* cache_lens, int B, int max_len, int K,
-                              const uint32_t* keyrange, int* ghist, uint32_t* lkeys, int* lids, int* counts,
+                              const uint2* blkrange, int* ghist, uint32_t* lkeys, int* lids, int* counts,
                               int* spill, int32_t* out, hipStream_t st);
 hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx, int K,
                                    int mode, const int32_t* cu, int nseq, const int32_t* cache_lens, int cap,
@@ -194,7 +194,7 @@ DecodeWs decode_layout(const dsa_decode_shape* s) {
   w.nchunk = topk_decode_nchunk(s->max_cache_len);
   const size_t lst = B * size_t(w.nchunk) * 4096;
   w.ghist = off; off = align_up(off + B * 2048 * sizeof(int), 256);
-  w.keyrange = off; off = align_up(off + B * 2 * sizeof(uint32_t), 256);
+  w.keyrange = off; off = align_up(off + B * size_t((s->max_cache_len + 255) / 256) * sizeof(uint2), 256);
   w.lkeys = off; off = align_up(off + lst * sizeof(uint32_t), 256);
   w.lids = off; off = align_up(off + lst * sizeof(int), 256);
   w.counts = off; off = align_up(off + B * size_t(w.nchunk) * sizeof(int), 256);
@@ -327,11 +327,11 @@ int decode_impl(const dsa_decode_shape* s, const void* q_idx, const float* w_idx
   float* scores = at<float>(ws, L.scores);
   if ((rc = hip_status(launch_indexer_decode(q_idx, w_idx, k_idx_cache, s->cache_lens, s->batch, s->cache_capacity,
                                              s->max_cache_len, s->idx_heads, L.ld, scores, at<int>(ws, L.ghist),
-                                             at<uint32_t>(ws, L.keyrange), st))))
+                                             at<uint2>(ws, L.keyrange), st))))
     return rc;
   if ((rc = record(ev, 0, st))) return rc;
   if ((rc = hip_status(launch_topk_decode(scores, L.ld, s->cache_lens, s->batch, s->max_cache_len, s->topk,
-                                          at<uint32_t>(ws, L.keyrange), at<int>(ws, L.ghist),
+                                          at<uint2>(ws, L.keyrange), at<int>(ws, L.ghist),
                                           at<uint32_t>(ws, L.lkeys), at<int>(ws, L.lids),
                                           at<int>(ws, L.counts), at<int>(ws, L.spill), idx, st))))
     return rc;

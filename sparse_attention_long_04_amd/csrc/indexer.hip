@@ -52,12 +52,52 @@ __global__ void build_schedule_kernel(const int32_t* __restrict__ cu, int nseq, 
 }
 
 // ------------------------------------------------------------------------------------------
+// Exact helpers for OCP e4m3 ("fn") values.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float mag = (e == 0) ? float(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -mag : mag;
+}
+
+// Round to the e4m3 grid (nearest even), |result| <= 448.
+__device__ __forceinline__ float e4m3_round(float v) {
+  const float a = fabsf(v);
+  const int ex = max(int((__float_as_uint(a) >> 23) & 0xFF) - 127, -6);
+  const float qu = __uint_as_float(uint32_t(ex - 3 + 127) << 23);  // spacing of the grid at |v|
+  const float r = fminf(rintf(a / qu) * qu, 448.f);
+  return copysignf(r, v);
+}
+
+// Code of a value that lies on the e4m3 grid.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    code = uint32_t(a * 512.f);
+  } else {
+    const uint32_t bits = __float_as_uint(a);
+    code = ((((bits >> 23) & 0xFFu) - 120u) << 3) | ((bits >> 20) & 7u);
+  }
+  return code | ((__float_as_uint(v) >> 24) & 0x80u);
+}
+
+// ------------------------------------------------------------------------------------------
 // Indexer kernel.
 //   FP8 = true : e4m3fn inputs, DI = 128, one 16x16x128 MFMA per (head, key tile).
 //   FP8 = false: bf16 inputs, DI = 64 or 128, DI/32 16x16x32 MFMAs per (head, key tile).
 // Lane layout (16x16 MFMA): lane l -> r = l & 15, g = l >> 4.  A (queries) lane holds token
 // row r, B (keys) lane holds key r; both take bytes [g*CH, (g+1)*CH) of their d_I row, so
 // every MFMA pairs identical d_I positions.  Output C[i] of lane l = (token 4g+i, key r).
+//
+// ReLU without a max per element: with c_h = q_h . k,
+//     sum_h w_h relu(c_h) = ( sum_h w_h c_h  +  sum_h w_h |c_h| ) / 2 ,
+// the |c_h| sum is one FMA per element (|.| is a free source modifier), and the linear sum is
+// (sum_h w_h q_h) . k -- a per-token vector q_lin, split into NP pieces on the input grid
+// (e4m3 pieces scaled by a power of two per block, or bf16 pieces) and contracted by NP extra
+// MFMAs accumulating in place.  For integer-valued inputs and power-of-two weights every
+// quantity is a multiple of 1/8 below 2^18, so the result is exact in any summation order;
+// otherwise the linear term carries about 20 (fp8) or 24 (bf16) significant bits.
 // ------------------------------------------------------------------------------------------
 template <bool FP8, int DI, int HMAX, int NWAVES, int NT>
 __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
@@ -69,10 +109,15 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   constexpr int UNITS = ROWB / 16;           // 16-byte units per row
   constexpr int CH = ROWB / 4;               // bytes per lane group
   constexpr int CHU = CH / 16;               // 16-byte units per lane group
+  constexpr int NP = FP8 ? 5 : 3;            // pieces of q_lin
+  constexpr int EPU = FP8 ? 16 : 8;          // elements per 16-byte unit
   static_assert(UNITS >= 8, "swizzle needs >= 8 units per row");
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[HMAX * 16 * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[(HMAX + NP) * 16 * ROWB];
   __shared__ __attribute__((aligned(16))) float w_lds[HMAX * 16];
   __shared__ float2 range_lds[NWAVES][16];
+  __shared__ uint32_t qmax_lds;
+  __shared__ float scale_lds;
+  uint8_t* const lin_lds = q_lds + HMAX * 16 * ROWB;
 
   const int n = blockIdx.x;
   if (n >= *sched_count) return;
@@ -103,72 +148,160 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
       const int h = u >> 4, t = u & 15;
       w_lds[u] = (t < rows) ? w_idx[(seq0 + i0 + t) * H + h] : 0.f;
     }
+    if (tid == 0) qmax_lds = 0u;
   }
   __syncthreads();
+
+  // q_lin[t, :] = sum_h w[t,h] q[t,h,:]  (fp32, fixed head order), then its pieces
+  {
+    const bool act = tid < 16 * UNITS;
+    const int t = tid / UNITS, u = tid - (tid / UNITS) * UNITS;
+    float lin[EPU];
+#pragma unroll
+    for (int x = 0; x < EPU; ++x) lin[x] = 0.f;
+    if (act) {
+      for (int h = 0; h < H; ++h) {
+        const i32x4 val = *reinterpret_cast<const i32x4*>(q_lds + (h * 16 + t) * ROWB + ((u ^ (t & 7)) * 16));
+        const float wv = w_lds[h * 16 + t];
+#pragma unroll
+        for (int x = 0; x < EPU; ++x) {
+          const uint32_t word = uint32_t(val[x / (EPU / 4)]);
+          float qv;
+          if constexpr (FP8) qv = e4m3_decode((word >> (8 * (x & 3))) & 0xFFu);
+          else qv = bf16_to_f32(uint16_t((x & 1) ? (word >> 16) : (word & 0xFFFFu)));
+          lin[x] = fmaf(wv, qv, lin[x]);
+        }
+      }
+    }
+    float scale = 1.f;  // q_lin is contracted as sum_p piece_p * scale
+    if constexpr (FP8) {
+      float mx = 0.f;
+#pragma unroll
+      for (int x = 0; x < EPU; ++x) mx = fmaxf(mx, fabsf(lin[x]));
+      if (act) atomicMax(&qmax_lds, __float_as_uint(mx));
+      __syncthreads();
+      // power of two S with max|q_lin| / S in (64, 240]: the block's largest entries use the top
+      // of the e4m3 range (max 448) and small entries stay clear of its subnormal floor
+      const float qm = __uint_as_float(qmax_lds);
+      int es = 0;
+      if (qm > 0.f) {
+        es = int((__float_as_uint(qm) >> 23) & 0xFF) - 127 - 7;
+        if (qm > 240.f * __uint_as_float(uint32_t(127 + max(es, -126)) << 23)) ++es;
+        es = max(-100, min(100, es));
+      }
+      scale = __uint_as_float(uint32_t(127 + es) << 23);
+      const float inv = __uint_as_float(uint32_t(127 - es) << 23);
+#pragma unroll
+      for (int x = 0; x < EPU; ++x) lin[x] *= inv;
+    }
+    if (act) {
+#pragma unroll
+      for (int pc = 0; pc < NP; ++pc) {
+        i32x4 codes = {0, 0, 0, 0};
+#pragma unroll
+        for (int x = 0; x < EPU; ++x) {
+          uint32_t c;
+          float piece;
+          if constexpr (FP8) {
+            piece = e4m3_round(lin[x]);
+            c = e4m3_encode(piece) << (8 * (x & 3));
+          } else {
+            const uint16_t hb = f32_to_bf16(lin[x]);
+            piece = bf16_to_f32(hb);
+            c = uint32_t(hb) << (16 * (x & 1));
+          }
+          lin[x] -= piece;
+          codes[x / (EPU / 4)] |= int(c);
+        }
+        *reinterpret_cast<i32x4*>(lin_lds + (pc * 16 + t) * ROWB + ((u ^ (t & 7)) * 16)) = codes;
+      }
+    }
+    if (tid == 0) scale_lds = scale;
+  }
+  __syncthreads();
+  const float lin_scale = scale_lds;
 
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int64_t stride = 16 * (int64_t)(j + 1);
   float* __restrict__ sblk = scores + seqoff[b] + score_block_offset(j);
-  // per-row score range (min, max) over this lane's written scores; the top-k uses it to bin
-  // scores by value
   float rmin[4], rmax[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) { rmin[i] = __builtin_inff(); rmax[i] = -__builtin_inff(); }
 
-  for (int kb = wave * NT * 16; kb < kend; kb += NWAVES * NT * 16) {
-    // key tiles -> B operand registers
-    i32x4 bfr[NT][CHU];
+  auto load_b = [&](i32x4 (&dst)[NT][CHU], int kb) {
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
       const int key = min(kb + 16 * jt + r, kend - 1);
       const uint8_t* p = k_idx + (seq0 + key) * (int64_t)ROWB + g * CH;
 #pragma unroll
-      for (int c = 0; c < CHU; ++c) bfr[jt][c] = *reinterpret_cast<const i32x4*>(p + 16 * c);
+      for (int c = 0; c < CHU; ++c) dst[jt][c] = *reinterpret_cast<const i32x4*>(p + 16 * c);
     }
-    f32x4 acc[NT];
+  };
+  auto mma = [&](const i32x4 (&a)[CHU], const i32x4 (&bb)[CHU], f32x4 c) -> f32x4 {
+    if constexpr (FP8) {
+      const i32x8 a8 = {a[0][0], a[0][1], a[0][2], a[0][3], a[1][0], a[1][1], a[1][2], a[1][3]};
+      const i32x8 b8 = {bb[0][0], bb[0][1], bb[0][2], bb[0][3], bb[1][0], bb[1][1], bb[1][2], bb[1][3]};
+      return mfma_fp8_16x16x128(a8, b8, c);
+    } else {
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) acc[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int cc = 0; cc < CHU; ++cc) c = mfma_bf16_16x16x32(a[cc], bb[cc], c);
+      return c;
+    }
+  };
+  auto load_a = [&](i32x4 (&dst)[CHU], const uint8_t* base) {
+    const uint8_t* qa = base + r * ROWB;
+#pragma unroll
+    for (int c = 0; c < CHU; ++c) dst[c] = *reinterpret_cast<const i32x4*>(qa + (((g * CHU + c) ^ (r & 7)) * 16));
+  };
 
+  constexpr int STEP = NWAVES * NT * 16;
+  i32x4 bfr[NT][CHU], bnx[NT][CHU];
+  if (wave * NT * 16 < kend) load_b(bfr, wave * NT * 16);
+  for (int kb = wave * NT * 16; kb < kend; kb += STEP) {
+    if (kb + STEP < kend) load_b(bnx, kb + STEP);
+    f32x4 acc_abs[NT], acc_lin[NT];
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+      acc_abs[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      acc_lin[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
     for (int h = 0; h < H; ++h) {
       i32x4 afr[CHU];
-      const uint8_t* qa = q_lds + (h * 16 + r) * ROWB;
-#pragma unroll
-      for (int c = 0; c < CHU; ++c) {
-        const int unit = g * CHU + c;
-        afr[c] = *reinterpret_cast<const i32x4*>(qa + ((unit ^ (r & 7)) * 16));
-      }
+      load_a(afr, q_lds + h * 16 * ROWB);
       const f32x4 wv = *reinterpret_cast<const f32x4*>(w_lds + h * 16 + 4 * g);
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) {
-        f32x4 cacc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (FP8) {
-          const i32x8 a8 = {afr[0][0], afr[0][1], afr[0][2], afr[0][3], afr[1][0], afr[1][1], afr[1][2], afr[1][3]};
-          const i32x8 b8 = {bfr[jt][0][0], bfr[jt][0][1], bfr[jt][0][2], bfr[jt][0][3],
-                            bfr[jt][1][0], bfr[jt][1][1], bfr[jt][1][2], bfr[jt][1][3]};
-          cacc = mfma_fp8_16x16x128(a8, b8, cacc);
-        } else {
+        const f32x4 c = mma(afr, bfr[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int c = 0; c < CHU; ++c) cacc = mfma_bf16_16x16x32(afr[c], bfr[jt][c], cacc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[jt][i] = fmaf(wv[i], fmaxf(cacc[i], 0.f), acc[jt][i]);
+        for (int i = 0; i < 4; ++i) acc_abs[jt][i] = fmaf(wv[i], fabsf(c[i]), acc_abs[jt][i]);
       }
     }
-
+#pragma unroll
+    for (int pc = 0; pc < NP; ++pc) {
+      i32x4 afr[CHU];
+      load_a(afr, lin_lds + pc * 16 * ROWB);
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) acc_lin[jt] = mma(afr, bfr[jt], acc_lin[jt]);
+    }
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
       const int key = kb + 16 * jt + r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 4 * g + i;
+        const float v = 0.5f * fmaf(acc_lin[jt][i], lin_scale, acc_abs[jt][i]);
         if (row < rows && key <= i0 + row) {
-          sblk[row * stride + key] = acc[jt][i];
-          rmin[i] = fminf(rmin[i], acc[jt][i]);
-          rmax[i] = fmaxf(rmax[i], acc[jt][i]);
+          sblk[row * stride + key] = v;
+          rmin[i] = fminf(rmin[i], v);
+          rmax[i] = fmaxf(rmax[i], v);
         }
       }
     }
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+      for (int c = 0; c < CHU; ++c) bfr[jt][c] = bnx[jt][c];
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -212,10 +345,11 @@ template <int HMAX, int NT>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_cache, const int32_t* __restrict__ cache_lens, int cap, int H,
-    int64_t score_ld, float* __restrict__ scores, int* __restrict__ ghist, uint32_t* __restrict__ keyrange) {
+    int64_t score_ld, float* __restrict__ scores, uint2* __restrict__ blkrange, int blk_stride) {
   constexpr int ROWB = 128, UNITS = 8, CH = 32;
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[HMAX * ROWB];
   __shared__ float w_lds[HMAX];
+  __shared__ uint2 red_lds[4];
   const int b = blockIdx.y;
   const int n = cache_lens[b];
   const int key0 = blockIdx.x * (4 * NT * 16);
@@ -231,7 +365,8 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int kb = key0 + wave * NT * 16;
-  if (kb >= n) return;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  if (kb < n) {
   i32x8 bfr[NT];
 #pragma unroll
   for (int jt = 0; jt < NT; ++jt) {
@@ -258,7 +393,6 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
       for (int i = 0; i < 4; ++i) acc[jt] = fmaf(wv[i], fmaxf(c[i], 0.f), acc[jt]);
     }
   }
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
   for (int jt = 0; jt < NT; ++jt) {
     float v = acc[jt];
@@ -272,26 +406,30 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
       kmax = max(kmax, kk);
     }
   }
-  // row range for the top-k's value binning (integer atomics: order-independent)
+  }
+  // this block's score range (order keys) for the top-k's value binning: one slot per block,
+  // reduced by the top-k kernels (no atomics)
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
   }
-  if (lane == 0) {
-    atomicMin(&keyrange[2 * b], kmin);
-    atomicMax(&keyrange[2 * b + 1], kmax);
+  if (lane == 0) red_lds[wave] = make_uint2(kmin, kmax);
+  __syncthreads();
+  if (tid == 0) {
+    uint2 a = red_lds[0];
+    for (int w = 1; w < 4; ++w) {
+      a.x = min(a.x, red_lds[w].x);
+      a.y = max(a.y, red_lds[w].y);
+    }
+    blkrange[(int64_t)b * blk_stride + blockIdx.x] = a;
   }
 }
 
-// Reset the decode top-k's per-row state: histogram and key range.
-__global__ void decode_topk_reset_kernel(int* __restrict__ ghist, uint32_t* __restrict__ keyrange) {
+// Clear the decode top-k's merged histograms.
+__global__ void decode_topk_reset_kernel(int* __restrict__ ghist) {
   const int b = blockIdx.x;
   for (int i = threadIdx.x; i < 2048; i += blockDim.x) ghist[b * 2048 + i] = 0;
-  if (threadIdx.x == 0) {
-    keyrange[2 * b] = 0xFFFFFFFFu;
-    keyrange[2 * b + 1] = 0u;
-  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -332,15 +470,15 @@ hipError_t launch_unpack_scores(const float* tri, const int64_t* seqoff, const i
 
 hipError_t launch_indexer_decode(const void* q_idx, const float* w, const void* k_cache,
                                  const int32_t* cache_lens, int B, int cap, int max_len, int H,
-                                 int64_t score_ld, float* scores, int* ghist, uint32_t* keyrange,
+                                 int64_t score_ld, float* scores, int* ghist, uint2* blkrange,
                                  hipStream_t st) {
   constexpr int NT = 4;
   const int per_block = 4 * NT * 16;
   dim3 grid((max_len + per_block - 1) / per_block, B);
-  decode_topk_reset_kernel<<<B, 256, 0, st>>>(ghist, keyrange);
+  decode_topk_reset_kernel<<<B, 256, 0, st>>>(ghist);
   indexer_decode_kernel<64, NT><<<grid, 256, 0, st>>>(static_cast<const uint8_t*>(q_idx), w,
                                                       static_cast<const uint8_t*>(k_cache), cache_lens,
-                                                      cap, H, score_ld, scores, ghist, keyrange);
+                                                      cap, H, score_ld, scores, blkrange, (int)grid.x);
   return hipGetLastError();
 }
 

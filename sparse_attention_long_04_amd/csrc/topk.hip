@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_prefill_kernel(
 
 // ------------------------------------------------------------------------------------------
 // Decode: chunked top-k over rows of n = cache_lens[b] scores.
-//   keyrange [B][2] (min, max order keys, from the decode indexer), ghist [B][kBins] int
+//   blkrange [B][ceil(n/256)] (min, max order keys per decode-indexer block), ghist [B][kBins] int
 //   (cleared before the indexer), lists [B][nchunk][kChunk] (key, id), counts [B][nchunk].
 // ------------------------------------------------------------------------------------------
 struct RowRange {
@@ -328,10 +328,31 @@ struct RowRange {
   bool flat;
 };
 
-__device__ __forceinline__ RowRange decode_range(const uint32_t* keyrange, int b) {
+// Row range from the decode indexer's per-block (min, max) key slots (256 keys per slot).
+// Every thread of the block must call it.
+__device__ RowRange decode_range(const uint2* __restrict__ blkrange, int stride, int b, int n, TopkSmem& sm) {
+  const int nblk = (n + 255) / 256;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = threadIdx.x; i < nblk; i += kTopkThreads) {
+    const uint2 v = blkrange[(int64_t)b * stride + i];
+    mn = min(mn, v.x);
+    mx = max(mx, v.y);
+  }
+  for (int o = 1; o < 64; o <<= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  }
+  __shared__ uint2 red[kTopkWaves];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_uint2(mn, mx);
+  __syncthreads();
+  for (int w = 0; w < kTopkWaves; ++w) {
+    mn = min(mn, red[w].x);
+    mx = max(mx, red[w].y);
+  }
+  __syncthreads();
   RowRange rr;
-  rr.lo = key_to_score(keyrange[2 * b]);
-  const float hi = key_to_score(keyrange[2 * b + 1]);
+  rr.lo = key_to_score(mn);
+  const float hi = key_to_score(mx);
   rr.flat = !(hi > rr.lo);
   rr.sc = rr.flat ? 0.f : float(kBins) / (hi - rr.lo);
   return rr;
@@ -339,12 +360,12 @@ __device__ __forceinline__ RowRange decode_range(const uint32_t* keyrange, int b
 
 __global__ __launch_bounds__(kTopkThreads) void topk_decode_hist_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cache_lens, int K,
-    const uint32_t* __restrict__ keyrange, int* __restrict__ ghist) {
+    const uint2* __restrict__ blkrange, int blk_stride, int* __restrict__ ghist) {
   __shared__ TopkSmem sm;
   const int b = blockIdx.y;
   const int n = cache_lens[b];
   const int c0 = blockIdx.x * kChunk;
-  const RowRange rr = decode_range(keyrange, b);
+  const RowRange rr = decode_range(blkrange, blk_stride, b, n, sm);
   if (n <= K || c0 >= n || rr.flat) return;
   const int cn = min(kChunk, n - c0);
   clear_hist(sm, kBins);
@@ -358,13 +379,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_hist_kernel(
 
 __global__ __launch_bounds__(kTopkThreads) void topk_decode_collect_kernel(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cache_lens, int K,
-    const uint32_t* __restrict__ keyrange, const int* __restrict__ ghist, int nchunk,
+    const uint2* __restrict__ blkrange, int blk_stride, const int* __restrict__ ghist, int nchunk,
     uint32_t* __restrict__ lkeys, int* __restrict__ lids, int* __restrict__ counts) {
   __shared__ TopkSmem sm;
   const int b = blockIdx.y;
   const int n = cache_lens[b];
   const int c0 = blockIdx.x * kChunk;
-  const RowRange rr = decode_range(keyrange, b);
+  const RowRange rr = decode_range(blkrange, blk_stride, b, n, sm);
   if (n <= K || rr.flat) return;
   int cnt = 0;
   if (c0 < n) {
@@ -391,14 +412,15 @@ struct TopkFinalSmem {
 };
 
 __global__ __launch_bounds__(kTopkThreads) void topk_decode_final_kernel(
-    const int32_t* __restrict__ cache_lens, int K, const uint32_t* __restrict__ keyrange, int nchunk,
+    const int32_t* __restrict__ cache_lens, int K, const uint2* __restrict__ blkrange, int blk_stride, int nchunk,
     const uint32_t* __restrict__ gkeys, const int* __restrict__ gids, const int* __restrict__ counts,
     int32_t* __restrict__ out, int* __restrict__ spill_keys_ids) {
   __shared__ TopkFinalSmem sm;
   const int b = blockIdx.x;
   const int n = cache_lens[b];
   int32_t* orow = out + (int64_t)b * K;
-  if (n <= K || decode_range(keyrange, b).flat) {
+  const RowRange rr = decode_range(blkrange, blk_stride, b, n, sm.s);
+  if (n <= K || rr.flat) {
     first_k(n, K, orow);
     return;
   }
@@ -447,15 +469,16 @@ int topk_decode_nchunk(int max_len) { return (max_len + kChunk - 1) / kChunk; }
 // Workspace needs: ghist B*4096 ints, lists B*nchunk*kChunk*(key+id) twice (chunk lists and
 // the finalize spill area), counts B*nchunk ints.
 hipError_t launch_topk_decode(const float* scores, int64_t ld, const int32_t* cache_lens, int B, int max_len,
-                              int K, const uint32_t* keyrange, int* ghist, uint32_t* lkeys, int* lids, int* counts,
+                              int K, const uint2* blkrange, int* ghist, uint32_t* lkeys, int* lids, int* counts,
                               int* spill, int32_t* out, hipStream_t st) {
+  const int blk_stride = (max_len + 255) / 256;
   const int nchunk = topk_decode_nchunk(max_len);
   if (nchunk > 256) return hipErrorInvalidValue;
   dim3 grid(nchunk, B);
-  topk_decode_hist_kernel<<<grid, kTopkThreads, 0, st>>>(scores, ld, cache_lens, K, keyrange, ghist);
-  topk_decode_collect_kernel<<<grid, kTopkThreads, 0, st>>>(scores, ld, cache_lens, K, keyrange, ghist, nchunk, lkeys,
+  topk_decode_hist_kernel<<<grid, kTopkThreads, 0, st>>>(scores, ld, cache_lens, K, blkrange, blk_stride, ghist);
+  topk_decode_collect_kernel<<<grid, kTopkThreads, 0, st>>>(scores, ld, cache_lens, K, blkrange, blk_stride, ghist, nchunk, lkeys,
                                                             lids, counts);
-  topk_decode_final_kernel<<<B, kTopkThreads, 0, st>>>(cache_lens, K, keyrange, nchunk, lkeys, lids, counts, out,
+  topk_decode_final_kernel<<<B, kTopkThreads, 0, st>>>(cache_lens, K, blkrange, blk_stride, nchunk, lkeys, lids, counts, out,
                                                        spill);
   return hipGetLastError();
 }

@@ -1,0 +1,88 @@
+"""GPU parity at the full workload sizes, through the same entry points and launch
+configuration that bench.py times, checked on rows sampled so that the oracle can compute
+each one by itself: sequence starts and ends, the last rows with fewer than k keys and the
+first with more, frame boundaries, and seeded random rows.
+
+Bars: selected indices bit-exact; bf16 outputs within max-abs 1e-2 and mean-rel 2e-3."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+from sparse_attention_long_04_amd import workloads
+from sparse_attention_long_04_amd.runtime import DecodeState, PrefillBatch, bf16_to_float
+
+from gpu_util import assert_out_close, gpu_available, sample_rows
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _check_prefill(name, with_dense):
+    p = workloads.make(name)
+    print(f"[full] {name}: T={p.total_tokens} lengths={list(p.lengths)}", flush=True)
+    pb = PrefillBatch(p)
+    pb.prefill()
+    rows = sample_rows(p.cu_seqlens, p.topk, seed=len(name))
+    idx = pb.topk_idx[torch.from_numpy(rows).to(pb.topk_idx.device)].cpu().numpy()
+    out = bf16_to_float(pb.out[torch.from_numpy(rows).to(pb.out.device)])
+    dense = None
+    if with_dense:
+        d = pb.dense(out=torch.empty_like(pb.out))
+        dense = bf16_to_float(d[torch.from_numpy(rows).to(d.device)])
+    del pb
+    torch.cuda.empty_cache()
+    o = O.Prefill(p.cu_seqlens, p.q_idx, p.k_idx, p.w_idx, p.q, p.k, p.v, p.idx_dtype, p.topk, p.softmax_scale)
+    print(f"[full] {name}: oracle on {len(rows)} sampled rows", flush=True)
+    sel, ref = o.rows(rows)
+    bad = [int(r) for r, a, b in zip(rows, idx, sel) if not np.array_equal(a, b)]
+    assert not bad, f"index mismatch on rows {bad[:10]}"
+    assert_out_close(out, ref, name)
+    if with_dense:
+        assert_out_close(dense, o.dense_rows(rows), name + " dense")
+
+
+@pytest.mark.timeout(900)
+def test_prefill_32k_full():
+    _check_prefill(workloads.P32K, with_dense=True)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_128k_video_full():
+    _check_prefill(workloads.P128K, with_dense=True)
+
+
+@pytest.mark.timeout(900)
+def test_varlen_256k_full():
+    _check_prefill(workloads.VARLEN, with_dense=False)
+
+
+@pytest.mark.timeout(900)
+def test_decode_16x128k_full():
+    d = workloads.make(workloads.DECODE)
+    st = DecodeState(d)
+    steps = workloads.WORKLOADS[workloads.DECODE]["steps"]
+    checks = {0, steps // 2, steps - 1}
+    kc, kk, vv = d.k_idx_cache, d.k_cache, d.v_cache   # host copies, appended in step
+    for i in range(steps):
+        s = st.load_step(i)
+        st.append()
+        n = int(st.len_host[0])
+        kc[:, n - 1], kk[:, n - 1], vv[:, n - 1] = s["k_idx_new"], s["k_new"], s["v_new"]
+        st.decode()
+        if i in checks:
+            torch.cuda.synchronize()
+            print(f"[full] decode step {i}: n={n}", flush=True)
+            sel, ref = O.decode_step(kc, kk, vv, st.len_host, s["q_idx"], s["w_idx"], s["q"], d.idx_dtype, d.topk,
+                                     d.softmax_scale)
+            assert np.array_equal(st.topk_idx.cpu().numpy(), sel), f"step {i}"
+            assert_out_close(bf16_to_float(st.out), ref, f"decode step {i}")
+            if i == steps - 1:
+                seqs = [0, 7, 15]
+                dense = bf16_to_float(st.dense(out=torch.empty_like(st.out)))[seqs]
+                assert_out_close(dense, O.dense_decode(kk, vv, st.len_host, s["q"], d.softmax_scale, seqs=seqs),
+                                 "dense decode")
+    # appended rows landed where the host copy has them
+    lo, hi = d.ctx_len, d.ctx_len + steps
+    assert np.array_equal(st.k_idx_cache[:, lo:hi].cpu().numpy(), kc[:, lo:hi])
+    assert np.array_equal(st.k_cache[:, lo:hi].cpu().numpy().view(np.uint16), kk[:, lo:hi])
+    assert np.array_equal(st.v_cache[:, lo:hi].cpu().numpy().view(np.uint16), vv[:, lo:hi])

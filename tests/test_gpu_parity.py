@@ -190,3 +190,55 @@ def test_decode_chunked_topk(zero_q):
                              d.softmax_scale)
     assert np.array_equal(st.topk_idx.cpu().numpy(), sel)
     assert_out_close(bf16_to_float(st.out), ref, f"decode chunked zero_q={zero_q}")
+
+
+def test_index_scores_large_linear_term_bitexact():
+    """fp8 queries in [-8, 8] with all weights 1: sum_h w_h q_h reaches several hundred, beyond
+    the e4m3 range, so the indexer's linear term runs with a power-of-two block scale."""
+    p = gen.make_prefill([520, 77], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=8, topk=64, seed=21)
+    p.w_idx[:] = 1.0
+    p.q_idx[:, :, :] = p.q_idx[:1, :1, :]  # same query in every head and token: |q_lin| up to 512
+    pb = PrefillBatch(p)
+    got = pb.index_scores().cpu().numpy().astype(np.float64)
+    ref = O.index_score_matrix(p.cu_seqlens, p.q_idx, p.k_idx, p.w_idx, p.idx_dtype)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+
+
+def test_index_scores_general_weights_close():
+    """Weights that are not powers of two: scores are no longer exactly representable; the
+    GPU path must stay within fp32 rounding of the float64 definition."""
+    p = make("fp8_ragged_700", seed=22)
+    rng = np.random.default_rng(0)
+    p.w_idx[:] = rng.uniform(0.01, 1.0, size=p.w_idx.shape).astype(np.float32)
+    pb = PrefillBatch(p)
+    got = pb.index_scores().cpu().numpy().astype(np.float64)
+    ref = O.index_score_matrix(p.cu_seqlens, p.q_idx, p.k_idx, p.w_idx, p.idx_dtype)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin)
+    # fp32 summation over the heads: |error| <= n * 2^-24 * sum_h w_h |c_h| with n ~ H + pieces;
+    # the bound uses n = 4 * 64 for headroom.
+    q = O.decode(p.q_idx, p.idx_dtype)
+    k = O.decode(p.k_idx, p.idx_dtype)
+    T = p.total_tokens
+    absw = np.zeros_like(ref)
+    for t in range(T):
+        absw[t, : t + 1] = np.abs(k[: t + 1] @ q[t].T) @ p.w_idx[t].astype(np.float64)
+    err = np.abs(got[fin] - ref[fin])
+    assert (err <= 256 * 2.0 ** -24 * absw[fin] + 1e-30).all(), (err.max(), (err / absw[fin].clip(1e-30)).max())
+
+
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (8, 8), (16, 1)])
+def test_other_gqa_shapes(hq, hkv):
+    """Head counts other than 32q/4kv: odd group size (3), plain MHA (1), one KV head (16)."""
+    p = gen.make_prefill([300, 129], idx_heads=16, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=64,
+                         seed=31, q_heads=hq, kv_heads=hkv)
+    pb = PrefillBatch(p)
+    pb.prefill()
+    o = oracle_of(p)
+    sel, ref = o.rows(range(p.total_tokens))
+    assert np.array_equal(pb.topk_idx.cpu().numpy(), sel)
+    assert_out_close(bf16_to_float(pb.out), ref, f"sparse {hq}/{hkv}")
+    dense = bf16_to_float(pb.dense(out=torch.empty_like(pb.out)))
+    assert_out_close(dense, o.dense_rows(range(p.total_tokens)), f"dense {hq}/{hkv}")

@@ -40,12 +40,39 @@ def pairs_of(lengths):
 
 
 def selected_of(lengths, k):
-    return sum(sum(min(k, i + 1) for i in range(L)) if L <= k else k * (k + 1) // 2 + (L - k) * k
-               for L in lengths)
+    """sum over rows of min(k, i+1): the selected (query, key) pairs."""
+    return sum(L * (L + 1) // 2 if L <= k else k * (k + 1) // 2 + (L - k) * k for L in lengths)
 
 
 def ms_between(a, b):
     return a.elapsed_time(b)
+
+
+def roof(bound, achieved, peak, unit, traffic_bytes, work, work_unit):
+    """Roofline entry: achieved/peak in TFLOP/s or GB/s from algorithmic work per launch."""
+    scale = 1e12 if unit == "TFLOP/s" else 1e9
+    return {"bound": bound, "achieved": round(achieved / scale, 1), "peak": round(peak / scale, 1), "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic_bytes, "work_per_launch": work,
+            "work_unit": work_unit}
+
+
+def read_traffic():
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from the committed profile
+    summary; a kernel whose source changed since the counters were taken gets no entry."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "prefill_128k_video_traffic.md")
+    out = {}
+    if not os.path.exists(path):
+        return out
+    for line in open(path):
+        if not line.startswith("traffic "):
+            continue
+        f = dict(kv.split("=", 1) for kv in line.split()[2:])
+        src = os.path.join(ROOT, "sparse_attention_long_04_amd", "csrc", f["source"])
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != f["sha256"]:
+            continue
+        out[line.split()[1]] = int(f["fetch_bytes"]) + int(f["write_bytes"])
+    return out
 
 
 def bench_prefill(name, steps, warmup, with_dense=True):
@@ -178,6 +205,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="prefill only (no dense/decode/varlen/cpu)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -189,6 +218,14 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "copies": 3}), flush=True)
+        return
     name = args.workload or workloads.P128K
     w = workloads.WORKLOADS[name]
     quick = args.quick
@@ -196,12 +233,29 @@ def main():
     pre = bench_prefill(name, args.steps, args.warmup, with_dense=not quick)
     T = pre["T"]
     value = T / (pre["ms"] * 1e-3)
-    flops_idx = pairs_of(pre["lengths"]) * w["idx_heads"] * w["idx_dim"] * 2
-    peak = PEAK_FP8 if w["idx_dtype"] == "fp8_e4m3" else PEAK_BF16
-    achieved = flops_idx / (pre["indexer_ms"] * 1e-3)
+    Hq, Hkv, d = 32, 4, 128
+    pairs = pairs_of(pre["lengths"])
     sel = selected_of(pre["lengths"], w["topk"])
-    attn_flops = sel * 32 * 128 * 4
-    gathered = sel * 4 * 128 * 2 * 2
+    peak_idx = PEAK_FP8 if w["idx_dtype"] == "fp8_e4m3" else PEAK_BF16
+    traffic = read_traffic()
+    # algorithmic work per launch (one launch of each kernel per step)
+    idx_flops = pairs * w["idx_heads"] * w["idx_dim"] * 2
+    idx_bytes = T * (w["idx_heads"] * w["idx_dim"] * (1 if w["idx_dtype"] == "fp8_e4m3" else 2) + w["idx_heads"] * 4) \
+        + 4 * pairs
+    topk_bytes = 4 * pairs + 4 * T * w["topk"]
+    attn_flops = sel * Hq * d * 4
+    attn_bytes = sel * Hkv * d * 2 * 2 + T * (2 * Hq * d * 2 + 4 * w["topk"])
+    rooflines = {
+        "indexer_prefill_kernel": roof("mfma", idx_flops / (pre["indexer_ms"] * 1e-3), peak_idx, "TFLOP/s",
+                                       traffic.get("indexer_prefill_kernel"), idx_flops, "flop"),
+        "topk_prefill_kernel": roof("hbm", topk_bytes / (pre["topk_ms"] * 1e-3), PEAK_HBM, "GB/s",
+                                    traffic.get("topk_prefill_kernel"), topk_bytes, "byte"),
+        "gather_attention_kernel": roof("hbm", attn_bytes / (pre["attn_ms"] * 1e-3), PEAK_HBM, "GB/s",
+                                        traffic.get("gather_attention_kernel"), attn_bytes, "byte"),
+    }
+    stage_ms = {"indexer_prefill_kernel": pre["indexer_ms"], "topk_prefill_kernel": pre["topk_ms"],
+                "gather_attention_kernel": pre["attn_ms"]}
+    dominant = max(stage_ms, key=stage_ms.get)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -217,14 +271,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "seq_len": T, "global_batch": len(pre["lengths"]), "topk": w["topk"],
                    "indexer": f"{w['idx_heads']}x{w['idx_dim']} {w['idx_dtype']}", "attention": "GQA 32q/4kv d128 bf16"},
-        "roofline": {"bound": "mfma", "kernel": "indexer_prefill", "achieved": round(achieved / 1e12, 1),
-                     "peak": PEAK_FP8 / 1e12 if peak == PEAK_FP8 else PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None},
+        "roofline": dict(kernel=dominant, **rooflines[dominant]),
+        "rooflines": rooflines,
         "stages_ms": {"indexer": round(pre["indexer_ms"], 3), "topk": round(pre["topk_ms"], 3),
                       "sparse_attention": round(pre["attn_ms"], 3)},
         "sparse_attention": {"tflops": round(attn_flops / (pre["attn_ms"] * 1e-3) / 1e12, 1),
                              "frac_bf16_peak": round(attn_flops / (pre["attn_ms"] * 1e-3) / PEAK_BF16, 4),
-                             "gathered_GBps": round(gathered / (pre["attn_ms"] * 1e-3) / 1e9, 1)},
+                             "gathered_GBps": round(sel * Hkv * d * 2 * 2 / (pre["attn_ms"] * 1e-3) / 1e9, 1)},
     }
     if not quick:
         line["dense"] = {"ms": round(pre["dense_ms"], 3), "ratio_dsa_over_dense": round(pre["ms"] / pre["dense_ms"], 4),

@@ -256,52 +256,81 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   };
 
   constexpr int STEP = NWAVES * NT * 16;
-  i32x4 bfr[NT][CHU], bnx[NT][CHU];
-  if (wave * NT * 16 < kend) load_b(bfr, wave * NT * 16);
-  for (int kb = wave * NT * 16; kb < kend; kb += STEP) {
-    if (kb + STEP < kend) load_b(bnx, kb + STEP);
+  // one wave step over NT key tiles; the next step's tiles are loaded into the other buffer
+  // (ping-pong, no register copies, so the loads stay in flight across the head loop)
+  auto kb_body = [&](const i32x4 (&cur)[NT][CHU], i32x4 (&nxt)[NT][CHU], int kb) {
+    // unconditional (addresses are clamped): a fixed number of loads in flight lets the
+    // compiler wait only for the current buffer
+    load_b(nxt, kb + STEP);
     f32x4 acc_abs[NT], acc_lin[NT];
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
       acc_abs[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
       acc_lin[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
-    for (int h = 0; h < H; ++h) {
-      i32x4 afr[CHU];
-      load_a(afr, q_lds + h * 16 * ROWB);
-      const f32x4 wv = *reinterpret_cast<const f32x4*>(w_lds + h * 16 + 4 * g);
+    for (int h = 0; h < H; h += 2) {  // H is a multiple of 16: heads in pairs for more ILP
+      i32x4 afr0[CHU], afr1[CHU];
+      load_a(afr0, q_lds + h * 16 * ROWB);
+      load_a(afr1, q_lds + (h + 1) * 16 * ROWB);
+      const f32x4 wv0 = *reinterpret_cast<const f32x4*>(w_lds + h * 16 + 4 * g);
+      const f32x4 wv1 = *reinterpret_cast<const f32x4*>(w_lds + (h + 1) * 16 + 4 * g);
+      f32x4 c0[NT], c1[NT];
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) c0[jt] = mma(afr0, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) {
-        const f32x4 c = mma(afr, bfr[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
+        c1[jt] = mma(afr1, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc_abs[jt][i] = fmaf(wv[i], fabsf(c[i]), acc_abs[jt][i]);
+        for (int i = 0; i < 4; ++i) acc_abs[jt][i] = fmaf(wv0[i], fabsf(c0[jt][i]), acc_abs[jt][i]);
       }
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_abs[jt][i] = fmaf(wv1[i], fabsf(c1[jt][i]), acc_abs[jt][i]);
     }
 #pragma unroll
     for (int pc = 0; pc < NP; ++pc) {
       i32x4 afr[CHU];
       load_a(afr, lin_lds + pc * 16 * ROWB);
 #pragma unroll
-      for (int jt = 0; jt < NT; ++jt) acc_lin[jt] = mma(afr, bfr[jt], acc_lin[jt]);
+      for (int jt = 0; jt < NT; ++jt) acc_lin[jt] = mma(afr, cur[jt], acc_lin[jt]);
     }
+    if (rows == 16 && kb + NT * 16 <= i0 + 1) {
+      // every (row, key) of this step is causal: no masking
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) {
-      const int key = kb + 16 * jt + r;
+      for (int jt = 0; jt < NT; ++jt) {
+        const int key = kb + 16 * jt + r;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * g + i;
-        const float v = 0.5f * fmaf(acc_lin[jt][i], lin_scale, acc_abs[jt][i]);
-        if (row < rows && key <= i0 + row) {
-          sblk[row * stride + key] = v;
+        for (int i = 0; i < 4; ++i) {
+          const float v = 0.5f * fmaf(acc_lin[jt][i], lin_scale, acc_abs[jt][i]);
+          sblk[(4 * g + i) * stride + key] = v;
           rmin[i] = fminf(rmin[i], v);
           rmax[i] = fmaxf(rmax[i], v);
         }
       }
+    } else {
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) {
+        const int key = kb + 16 * jt + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 4 * g + i;
+          const float v = 0.5f * fmaf(acc_lin[jt][i], lin_scale, acc_abs[jt][i]);
+          if (row < rows && key <= i0 + row) {
+            sblk[row * stride + key] = v;
+            rmin[i] = fminf(rmin[i], v);
+            rmax[i] = fmaxf(rmax[i], v);
+          }
+        }
+      }
     }
-#pragma unroll
-    for (int jt = 0; jt < NT; ++jt)
-#pragma unroll
-      for (int c = 0; c < CHU; ++c) bfr[jt][c] = bnx[jt][c];
+  };
+  i32x4 bA[NT][CHU], bB[NT][CHU];
+  const int kb0 = wave * NT * 16;
+  if (kb0 < kend) load_b(bA, kb0);
+  for (int kb = kb0; kb < kend; kb += 2 * STEP) {
+    kb_body(bA, bB, kb);
+    if (kb + STEP < kend) kb_body(bB, bA, kb + STEP);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

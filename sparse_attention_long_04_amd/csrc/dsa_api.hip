@@ -194,7 +194,8 @@ DecodeWs decode_layout(const dsa_decode_shape* s) {
   w.nchunk = topk_decode_nchunk(s->max_cache_len);
   const size_t lst = B * size_t(w.nchunk) * 4096;
   w.ghist = off; off = align_up(off + B * 2048 * sizeof(int), 256);
-  w.keyrange = off; off = align_up(off + B * size_t((s->max_cache_len + 255) / 256) * sizeof(uint2), 256);
+  w.keyrange = off;
+  off = align_up(off + B * size_t((s->max_cache_len + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock) * sizeof(uint2), 256);
   w.lkeys = off; off = align_up(off + lst * sizeof(uint32_t), 256);
   w.lids = off; off = align_up(off + lst * sizeof(int), 256);
   w.counts = off; off = align_up(off + B * size_t(w.nchunk) * sizeof(int), 256);

@@ -374,16 +374,20 @@ template <int HMAX, int NT>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_cache, const int32_t* __restrict__ cache_lens, int cap, int H,
-    int64_t score_ld, float* __restrict__ scores, uint2* __restrict__ blkrange, int blk_stride) {
+    int64_t score_ld, float* __restrict__ scores, uint2* __restrict__ blkrange, int blk_stride,
+    int* __restrict__ ghist) {
   constexpr int ROWB = 128, UNITS = 8, CH = 32;
+  constexpr int WKEYS = kDecodeKeysPerBlock / 4;  // contiguous keys per wave
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[HMAX * ROWB];
   __shared__ float w_lds[HMAX];
   __shared__ uint2 red_lds[4];
   const int b = blockIdx.y;
   const int n = cache_lens[b];
-  const int key0 = blockIdx.x * (4 * NT * 16);
+  const int key0 = blockIdx.x * kDecodeKeysPerBlock;
   const int tid = threadIdx.x;
-  // the top-k that follows merges chunk histograms into ghist[b] with atomics: clear it here
+  // the top-k after this kernel merges chunk histograms into ghist[b] with atomics: clear it
+  if (blockIdx.x == 0)
+    for (int i = tid; i < 2048; i += 256) ghist[b * 2048 + i] = 0;
   if (key0 >= n) return;
   for (int u = tid; u < H * UNITS; u += 256) {
     const int h = u / UNITS, c = u - h * UNITS;
@@ -393,48 +397,59 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
   for (int h = tid; h < H; h += 256) w_lds[h] = w_idx[(int64_t)b * H + h];
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
-  const int kb = key0 + wave * NT * 16;
+  const int kw0 = key0 + wave * WKEYS;
+  const int kw1 = min(n, kw0 + WKEYS);
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  if (kb < n) {
-  i32x8 bfr[NT];
-#pragma unroll
-  for (int jt = 0; jt < NT; ++jt) {
-    const int key = min(kb + 16 * jt + r, n - 1);
-    const uint8_t* p = k_cache + ((int64_t)b * cap + key) * ROWB + g * CH;
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
-    bfr[jt] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-  float acc[NT];
-#pragma unroll
-  for (int jt = 0; jt < NT; ++jt) acc[jt] = 0.f;
-  for (int hb = 0; hb < H; hb += 16) {
-    const uint8_t* qa = q_lds + (hb + r) * ROWB;
-    const int hr = (hb + r) & 7;
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(qa + (((2 * g) ^ hr) * 16));
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(qa + (((2 * g + 1) ^ hr) * 16));
-    const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    const f32x4 wv = *reinterpret_cast<const f32x4*>(w_lds + hb + 4 * g);
+  auto load = [&](i32x8 (&dst)[NT], int kb) {
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
-      f32x4 c = mfma_fp8_16x16x128(a8, bfr[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[jt] = fmaf(wv[i], fmaxf(c[i], 0.f), acc[jt]);
+      const int key = min(kb + 16 * jt + r, n - 1);
+      const uint8_t* p = k_cache + ((int64_t)b * cap + key) * ROWB + g * CH;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
+      dst[jt] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-  }
+  };
+  auto step = [&](const i32x8 (&bfr)[NT], i32x8 (&nxt)[NT], int kb) {
+    load(nxt, kb + NT * 16);  // unconditional (clamped) prefetch of the next step
+    float acc[NT];
 #pragma unroll
-  for (int jt = 0; jt < NT; ++jt) {
-    float v = acc[jt];
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    const int key = kb + 16 * jt + r;
-    if (g == 0 && key < n) {
-      scores[(int64_t)b * score_ld + key] = v;
-      const uint32_t kk = score_key(v);
-      kmin = min(kmin, kk);
-      kmax = max(kmax, kk);
+    for (int jt = 0; jt < NT; ++jt) acc[jt] = 0.f;
+    for (int hb = 0; hb < H; hb += 16) {
+      const uint8_t* qa = q_lds + (hb + r) * ROWB;
+      const int hr = (hb + r) & 7;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(qa + (((2 * g) ^ hr) * 16));
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(qa + (((2 * g + 1) ^ hr) * 16));
+      const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(w_lds + hb + 4 * g);
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) {
+        f32x4 c = mfma_fp8_16x16x128(a8, bfr[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[jt] = fmaf(wv[i], fmaxf(c[i], 0.f), acc[jt]);
+      }
     }
-  }
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+      float v = acc[jt];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      const int key = kb + 16 * jt + r;
+      if (g == 0 && key < kw1) {
+        scores[(int64_t)b * score_ld + key] = v;
+        const uint32_t kk = score_key(v);
+        kmin = min(kmin, kk);
+        kmax = max(kmax, kk);
+      }
+    }
+  };
+  if (kw0 < kw1) {
+    i32x8 bA[NT], bB[NT];
+    load(bA, kw0);
+    for (int kb = kw0; kb < kw1; kb += 2 * NT * 16) {
+      step(bA, bB, kb);
+      if (kb + NT * 16 < kw1) step(bB, bA, kb + NT * 16);
+    }
   }
   // this block's score range (order keys) for the top-k's value binning: one slot per block,
   // reduced by the top-k kernels (no atomics)
@@ -453,12 +468,6 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     }
     blkrange[(int64_t)b * blk_stride + blockIdx.x] = a;
   }
-}
-
-// Clear the decode top-k's merged histograms.
-__global__ void decode_topk_reset_kernel(int* __restrict__ ghist) {
-  const int b = blockIdx.x;
-  for (int i = threadIdx.x; i < 2048; i += blockDim.x) ghist[b * 2048 + i] = 0;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -501,13 +510,10 @@ hipError_t launch_indexer_decode(const void* q_idx, const float* w, const void* 
                                  const int32_t* cache_lens, int B, int cap, int max_len, int H,
                                  int64_t score_ld, float* scores, int* ghist, uint2* blkrange,
                                  hipStream_t st) {
-  constexpr int NT = 4;
-  const int per_block = 4 * NT * 16;
-  dim3 grid((max_len + per_block - 1) / per_block, B);
-  decode_topk_reset_kernel<<<B, 256, 0, st>>>(ghist);
-  indexer_decode_kernel<64, NT><<<grid, 256, 0, st>>>(static_cast<const uint8_t*>(q_idx), w,
-                                                      static_cast<const uint8_t*>(k_cache), cache_lens,
-                                                      cap, H, score_ld, scores, blkrange, (int)grid.x);
+  dim3 grid((max_len + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock, B);
+  indexer_decode_kernel<64, 4><<<grid, 256, 0, st>>>(static_cast<const uint8_t*>(q_idx), w,
+                                                     static_cast<const uint8_t*>(k_cache), cache_lens,
+                                                     cap, H, score_ld, scores, blkrange, (int)grid.x, ghist);
   return hipGetLastError();
 }
 

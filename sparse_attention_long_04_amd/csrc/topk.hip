@@ -32,7 +32,7 @@ namespace dsa {
 
 constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kListCap = 4096;     // LDS candidate list capacity (prefill)
+constexpr int kListCap = 3072;     // LDS candidate list capacity (prefill)
 constexpr int kBins = 2048;        // value bins / radix digit size
 constexpr int kChunk = 4096;       // decode chunk
 constexpr int kFinalCap = 12288;   // LDS list capacity of the decode finalize step
@@ -95,8 +95,8 @@ __device__ __forceinline__ void clear_hist(TopkSmem& sm, int nb) {
 }
 
 // Monotone value bin of score x in a row with range [lo, lo + 1/sc].
-__device__ __forceinline__ int value_bin(float x, float lo, float sc) {
-  return min(kBins - 1, int((x - lo) * sc));
+__device__ __forceinline__ int value_bin(float x, float lo, float sc, int nbins = kBins) {
+  return min(nbins - 1, int((x - lo) * sc));
 }
 
 __device__ __forceinline__ float key_to_score(uint32_t k) {
@@ -264,14 +264,117 @@ __device__ int ordered_emit_bin_ge(const RowSrc& src, int n, float lo, float sc,
   return base;
 }
 
+// ---- finishing a candidate list ------------------------------------------------------------
+// The list (keys, ids) holds, in index order, every element whose value bin is >= b1.  All of
+// bin > b1 is kept; of the m elements in bin b1 the krem best under (key desc, id asc) are kept.
+// They are ranked directly (m^2/256 comparisons per thread) and the dropped ones get key 0,
+// which no score maps to; the output is then an ordered compaction of the non-zero keys.
+template <int CAP>
+struct FinishSmem {
+  uint32_t sk[CAP];
+  int sid[CAP];
+  int spos[CAP];
+  int sub_n;
+};
+
+// Returns false (list untouched) when bin b1 holds more than CAP elements.
+template <int CAP, class BinOf>
+__device__ bool rank_threshold_bin(uint32_t* keys, const int* ids, int total, int b1, int krem, BinOf bin_of,
+                                   FinishSmem<CAP>& fs) {
+  constexpr int kSubCap = CAP;
+  if (threadIdx.x == 0) fs.sub_n = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < total; i += kTopkThreads) {
+    const uint32_t k = keys[i];
+    if (bin_of(k) == b1) {
+      const int j = atomicAdd(&fs.sub_n, 1);
+      if (j < kSubCap) {
+        fs.sk[j] = k;
+        fs.sid[j] = ids[i];
+        fs.spos[j] = i;
+      }
+    }
+  }
+  __syncthreads();
+  const int m = fs.sub_n;
+  if (m > kSubCap) return false;
+  for (int j = threadIdx.x; j < m; j += kTopkThreads) {
+    const uint32_t k = fs.sk[j];
+    const int id = fs.sid[j];
+    int rank = 0;
+    for (int x = 0; x < m; ++x) {
+      const uint32_t kx = fs.sk[x];
+      rank += (kx > k) | ((kx == k) & (fs.sid[x] < id));
+    }
+    if (rank >= krem) keys[fs.spos[j]] = 0u;
+  }
+  __syncthreads();
+  return true;
+}
+
+// Ordered compaction of the list entries with a non-zero key.
+__device__ void emit_nonzero(const uint32_t* keys, const int* ids, int total, int32_t* __restrict__ out,
+                             TopkSmem& sm) {
+  int base = 0;
+  for (int c0 = 0; c0 < total; c0 += 4 * kTopkThreads) {
+    const int s0 = c0 + 4 * threadIdx.x;
+    bool keep[4];
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      keep[e] = (s0 + e < total) && keys[s0 + e] != 0u;
+      c += keep[e];
+    }
+    int tot;
+    const int incl = block_incl_scan(c, sm.wave_tot, &tot);
+    int pos = base + incl - c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (keep[e]) out[pos++] = ids[s0 + e];
+    base += tot;
+  }
+  __syncthreads();
+}
+
+// ---- prefill row select: per-wave segments, no block barriers inside the two HBM passes ----
+constexpr int kQ = 8;  // float4 loads in flight per lane per wave step (2048 elements)
+constexpr int kVBins = 1024;  // value bins of the prefill pass 1 (per wave)
+
 struct TopkRowSmem {
   TopkSmem s;
-  uint32_t lkeys[kListCap];
-  int lids[kListCap];
+  union {
+    int whist[kTopkWaves][kVBins];  // pass 1: per-wave value histograms
+    struct {
+      uint32_t lkeys[kListCap];    // pass 2 on: candidate list (index order)
+      int lids[kListCap];
+    } l;
+  } u;
+  int wcnt[kTopkWaves];
+  int woff[kTopkWaves];
+  FinishSmem<512> f;
 };
 
 __device__ __forceinline__ void first_k(int n, int K, int32_t* __restrict__ out) {
   for (int s = threadIdx.x; s < K; s += kTopkThreads) out[s] = (s < n) ? s : -1;
+}
+
+// Load the wave step [base, base + 1024) of a segment ending at hi: lane gets elements
+// base + 4(lane + 64e) + j; slots past hi read as NaN-free zeros and are flagged invalid.
+__device__ __forceinline__ void load_step(const float* __restrict__ row, int base, int hi, int lane, f32x4 (&v)[kQ]) {
+#pragma unroll
+  for (int e = 0; e < kQ; ++e) {
+    const int i = base + 4 * (lane + 64 * e);
+    if (i + 3 < hi) {
+      v[e] = *reinterpret_cast<const f32x4*>(row + i);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[e][j] = (i + j < hi) ? row[i + j] : 0.f;
+    }
+  }
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));
 }
 
 __device__ void select_row(const float* __restrict__ row, int n, int K, float lo, float hi,
@@ -280,25 +383,104 @@ __device__ void select_row(const float* __restrict__ row, int n, int K, float lo
     first_k(n, K, out);
     return;
   }
-  const RowSrc src{row, (reinterpret_cast<uintptr_t>(row) & 15) == 0};
-  const float sc = float(kBins) / (hi - lo);
-  clear_hist(sm.s, kBins);
-  value_hist_pass(src, n, lo, sc, sm.s.hist);
-  find_digit(sm.s, kBins, K);
-  const int b1 = sm.s.sel_digit;
-  const int cand = sm.s.sel_above + sm.s.hist[b1];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const float sc = float(kVBins) / (hi - lo);
+  // wave w owns the contiguous segment [seg_lo, seg_hi) (starts are multiples of 4 elements)
+  const int seg = (((n + kTopkWaves - 1) / kTopkWaves) + 3) & ~3;
+  const int seg_lo = min(n, w * seg), seg_hi = min(n, seg_lo + seg);
+  constexpr int STEPW = 256 * kQ;  // elements per wave step
+
+  // pass 1: per-wave histograms of the value bins
+  for (int i = tid; i < kTopkWaves * kVBins; i += kTopkThreads) (&sm.u.whist[0][0])[i] = 0;
+  if (tid < kTopkWaves) sm.wcnt[tid] = 0;
   __syncthreads();
+  for (int base = seg_lo; base < seg_hi; base += STEPW) {
+    f32x4 v[kQ];
+    load_step(row, base, seg_hi, lane, v);
+#pragma unroll
+    for (int e = 0; e < kQ; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (base + 4 * (lane + 64 * e) + j < seg_hi) atomicAdd(&sm.u.whist[w][value_bin(v[e][j], lo, sc, kVBins)], 1);
+  }
+  __syncthreads();
+  for (int b = tid; b < kVBins; b += kTopkThreads) {
+    int a = 0;
+#pragma unroll
+    for (int ww = 0; ww < kTopkWaves; ++ww) a += sm.u.whist[ww][b];
+    sm.s.hist[b] = a;
+  }
+  __syncthreads();
+  find_digit(sm.s, kVBins, K);
+  const int b1 = sm.s.sel_digit;
+  // candidates per wave: elements whose bin >= b1
+  {
+    int c[kTopkWaves];
+#pragma unroll
+    for (int ww = 0; ww < kTopkWaves; ++ww) c[ww] = 0;
+    for (int b = b1 + tid; b < kVBins; b += kTopkThreads)
+#pragma unroll
+      for (int ww = 0; ww < kTopkWaves; ++ww) c[ww] += sm.u.whist[ww][b];
+#pragma unroll
+    for (int ww = 0; ww < kTopkWaves; ++ww) c[ww] = wave_sum_i(c[ww]);
+    if (lane == 0)
+#pragma unroll
+      for (int ww = 0; ww < kTopkWaves; ++ww) atomicAdd(&sm.wcnt[ww], c[ww]);
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int ww = 0; ww < kTopkWaves; ++ww) {
+        sm.woff[ww] = acc;
+        acc += sm.wcnt[ww];
+      }
+      sm.s.list_n = acc;
+    }
+    __syncthreads();
+  }
+  const int cand = sm.s.list_n;
   uint32_t prefix = 0, hmask = 0;
   int krem = K;
   if (cand <= kListCap) {
-    ordered_emit_bin_ge(src, n, lo, sc, b1, [&](int slot, uint32_t key, int id) {
-      sm.lkeys[slot] = key;
-      sm.lids[slot] = id;
-    }, sm.s);
-    const ListSrc ls{sm.lkeys, sm.lids};
-    radix_rest(ls, cand, 0, prefix, hmask, krem, sm.s);
-    ordered_emit(ls, cand, prefix, krem, [&](int slot, uint32_t, int id) { out[slot] = id; }, sm.s);
+    // pass 2: each wave compacts its segment's candidates, in index order, at its offset
+    int pos = sm.woff[w];
+    for (int base = seg_lo; base < seg_hi; base += STEPW) {
+      f32x4 v[kQ];
+      load_step(row, base, seg_hi, lane, v);
+#pragma unroll
+      for (int e = 0; e < kQ; ++e) {
+        const int i0 = base + 4 * (lane + 64 * e);
+        bool keep[4];
+        int before = 0, total = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          keep[j] = (i0 + j < seg_hi) && value_bin(v[e][j], lo, sc, kVBins) >= b1;
+          const uint64_t bm = __ballot(keep[j]);
+          before += lanes_below(bm);
+          total += __popcll(bm);
+        }
+        int slot = pos + before;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (keep[j]) {
+            sm.u.l.lkeys[slot] = score_key(v[e][j]);
+            sm.u.l.lids[slot] = i0 + j;
+            ++slot;
+          }
+        pos += total;
+      }
+    }
+    __syncthreads();
+    const int above = sm.s.sel_above;
+    auto bin_of = [&](uint32_t k) { return value_bin(key_to_score(k), lo, sc, kVBins); };
+    if (rank_threshold_bin(sm.u.l.lkeys, sm.u.l.lids, cand, b1, K - above, bin_of, sm.f)) {
+      emit_nonzero(sm.u.l.lkeys, sm.u.l.lids, cand, out, sm.s);
+    } else {
+      const ListSrc ls{sm.u.l.lkeys, sm.u.l.lids};
+      radix_rest(ls, cand, 0, prefix, hmask, krem, sm.s);
+      ordered_emit(ls, cand, prefix, krem, [&](int slot, uint32_t, int id) { out[slot] = id; }, sm.s);
+    }
   } else {
+    const RowSrc src{row, true};
     radix_rest(src, n, 0, prefix, hmask, krem, sm.s);
     ordered_emit(src, n, prefix, krem, [&](int slot, uint32_t, int id) { out[slot] = id; }, sm.s);
   }
@@ -328,10 +510,10 @@ struct RowRange {
   bool flat;
 };
 
-// Row range from the decode indexer's per-block (min, max) key slots (256 keys per slot).
-// Every thread of the block must call it.
+// Row range from the decode indexer's per-block (min, max) key slots (kDecodeKeysPerBlock keys
+// per slot).  Every thread of the block must call it.
 __device__ RowRange decode_range(const uint2* __restrict__ blkrange, int stride, int b, int n, TopkSmem& sm) {
-  const int nblk = (n + 255) / 256;
+  const int nblk = (n + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int i = threadIdx.x; i < nblk; i += kTopkThreads) {
     const uint2 v = blkrange[(int64_t)b * stride + i];
@@ -406,15 +588,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_collect_kernel(
 
 struct TopkFinalSmem {
   TopkSmem s;
+  FinishSmem<1024> f;
   uint32_t lkeys[kFinalCap];
   int lids[kFinalCap];
-  int offs[256];
+  int offs[257];
 };
 
 __global__ __launch_bounds__(kTopkThreads) void topk_decode_final_kernel(
-    const int32_t* __restrict__ cache_lens, int K, const uint2* __restrict__ blkrange, int blk_stride, int nchunk,
-    const uint32_t* __restrict__ gkeys, const int* __restrict__ gids, const int* __restrict__ counts,
-    int32_t* __restrict__ out, int* __restrict__ spill_keys_ids) {
+    const int32_t* __restrict__ cache_lens, int K, const uint2* __restrict__ blkrange, int blk_stride,
+    const int* __restrict__ ghist, int nchunk, const uint32_t* __restrict__ gkeys, const int* __restrict__ gids,
+    const int* __restrict__ counts, int32_t* __restrict__ out, int* __restrict__ spill_keys_ids) {
   __shared__ TopkFinalSmem sm;
   const int b = blockIdx.x;
   const int n = cache_lens[b];
@@ -424,16 +607,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_final_kernel(
     first_k(n, K, orow);
     return;
   }
-  // concatenate the chunk lists (chunk order = index order)
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int c = 0; c < nchunk; ++c) {
-      sm.offs[c] = acc;
-      acc += counts[b * nchunk + c];
-    }
-    sm.s.list_n = acc;
-  }
+  // threshold bin again (same histogram as the collect step)
+  for (int i = threadIdx.x; i < kBins; i += kTopkThreads) sm.s.hist[i] = ghist[b * kBins + i];
   __syncthreads();
+  find_digit(sm.s, kBins, K);
+  const int b1 = sm.s.sel_digit, above = sm.s.sel_above;
+  // chunk offsets: one count per thread, block prefix sum
+  {
+    const int c = threadIdx.x < nchunk ? counts[b * nchunk + threadIdx.x] : 0;
+    int tot;
+    const int incl = block_incl_scan(c, sm.s.wave_tot, &tot);
+    if (threadIdx.x < nchunk) sm.offs[threadIdx.x] = incl - c;
+    if (threadIdx.x == 0) {
+      sm.offs[nchunk] = tot;
+      sm.s.list_n = tot;
+    }
+    __syncthreads();
+  }
   const int total = sm.s.list_n;
   uint32_t* keys = sm.lkeys;
   int* ids = sm.lids;
@@ -441,15 +631,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_final_kernel(
     keys = reinterpret_cast<uint32_t*>(spill_keys_ids) + (int64_t)b * 2 * nchunk * kChunk;
     ids = reinterpret_cast<int*>(keys + nchunk * kChunk);
   }
-  for (int c = 0; c < nchunk; ++c) {
-    const int cnt = counts[b * nchunk + c];
-    const int64_t src = ((int64_t)b * nchunk + c) * kChunk;
-    for (int i = threadIdx.x; i < cnt; i += kTopkThreads) {
-      keys[sm.offs[c] + i] = gkeys[src + i];
-      ids[sm.offs[c] + i] = gids[src + i];
+  // flattened gather of the concatenated chunk lists (chunk order = index order)
+  for (int i = threadIdx.x; i < total; i += kTopkThreads) {
+    int lo = 0, hi = nchunk - 1;  // last chunk c with offs[c] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sm.offs[mid] <= i) lo = mid; else hi = mid - 1;
     }
+    const int64_t src = ((int64_t)b * nchunk + lo) * kChunk + (i - sm.offs[lo]);
+    keys[i] = gkeys[src];
+    ids[i] = gids[src];
   }
   __syncthreads();
+  auto bin_of = [&](uint32_t k) { return value_bin(key_to_score(k), rr.lo, rr.sc); };
+  if (total <= kFinalCap && rank_threshold_bin(keys, ids, total, b1, K - above, bin_of, sm.f)) {
+    emit_nonzero(keys, ids, total, orow, sm.s);
+    return;
+  }
   const ListSrc ls{keys, ids};
   uint32_t prefix = 0, hmask = 0;
   int krem = K;
@@ -471,15 +669,15 @@ int topk_decode_nchunk(int max_len) { return (max_len + kChunk - 1) / kChunk; }
 hipError_t launch_topk_decode(const float* scores, int64_t ld, const int32_t* cache_lens, int B, int max_len,
                               int K, const uint2* blkrange, int* ghist, uint32_t* lkeys, int* lids, int* counts,
                               int* spill, int32_t* out, hipStream_t st) {
-  const int blk_stride = (max_len + 255) / 256;
+  const int blk_stride = (max_len + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock;
   const int nchunk = topk_decode_nchunk(max_len);
-  if (nchunk > 256) return hipErrorInvalidValue;
+  if (nchunk > kTopkThreads) return hipErrorInvalidValue;
   dim3 grid(nchunk, B);
   topk_decode_hist_kernel<<<grid, kTopkThreads, 0, st>>>(scores, ld, cache_lens, K, blkrange, blk_stride, ghist);
   topk_decode_collect_kernel<<<grid, kTopkThreads, 0, st>>>(scores, ld, cache_lens, K, blkrange, blk_stride, ghist, nchunk, lkeys,
                                                             lids, counts);
-  topk_decode_final_kernel<<<B, kTopkThreads, 0, st>>>(cache_lens, K, blkrange, blk_stride, nchunk, lkeys, lids, counts, out,
-                                                       spill);
+  topk_decode_final_kernel<<<B, kTopkThreads, 0, st>>>(cache_lens, K, blkrange, blk_stride, ghist, nchunk, lkeys,
+                                                       lids, counts, out, spill);
   return hipGetLastError();
 }
 

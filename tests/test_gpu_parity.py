@@ -242,3 +242,46 @@ def test_other_gqa_shapes(hq, hkv):
     assert_out_close(bf16_to_float(pb.out), ref, f"sparse {hq}/{hkv}")
     dense = bf16_to_float(pb.dense(out=torch.empty_like(pb.out)))
     assert_out_close(dense, o.dense_rows(range(p.total_tokens)), f"dense {hq}/{hkv}")
+
+
+def _two_valued(p, rng):
+    """Indexer inputs whose scores take two values: keys are all-ones or all-zero rows and
+    every query is all ones, so each row's threshold bin holds thousands of tied keys."""
+    one = 0x38 if p.idx_dtype == "fp8_e4m3" else 0x3F80
+    p.q_idx[:] = one
+    hot = rng.random(p.k_idx.shape[0]) < 0.5
+    p.k_idx[:] = 0
+    p.k_idx[hot] = one
+
+
+def test_topk_two_valued_scores_prefill():
+    p = gen.make_prefill([9000, 2500], idx_heads=16, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=2048,
+                         seed=41)
+    _two_valued(p, np.random.default_rng(0))
+    pb = PrefillBatch(p)
+    pb.index_topk()
+    idx = pb.topk_idx.cpu().numpy()
+    o = oracle_of(p)
+    for t in [2047, 2048, 4100, 8999, 9000 + 2047, 9000 + 2048, 11499]:
+        assert np.array_equal(idx[t], O.select_topk_row(o.scores(t), p.topk)), t
+
+
+def test_topk_two_valued_scores_decode():
+    d = gen.make_decode(2, 20000, 20064, 1, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", topk=2048, seed=42)
+    rng = np.random.default_rng(1)
+    hot = rng.random(d.k_idx_cache.shape[:2]) < 0.5
+    d.k_idx_cache[:] = 0
+    d.k_idx_cache[hot] = 0x38
+    st = DecodeState(d)
+    s = st.load_step(0)
+    s["q_idx"][:] = 0x38
+    st.step_dev["q_idx"].fill_(0x38)
+    st.append()
+    st.decode()
+    torch.cuda.synchronize()
+    kc, kk, vv = d.k_idx_cache.copy(), d.k_cache.copy(), d.v_cache.copy()
+    kc[:, 20000], kk[:, 20000], vv[:, 20000] = s["k_idx_new"], s["k_new"], s["v_new"]
+    sel, ref = O.decode_step(kc, kk, vv, st.len_host, s["q_idx"], s["w_idx"], s["q"], d.idx_dtype, d.topk,
+                             d.softmax_scale)
+    assert np.array_equal(st.topk_idx.cpu().numpy(), sel)
+    assert_out_close(bf16_to_float(st.out), ref, "decode two-valued")

@@ -205,6 +205,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="prefill only (no dense/decode/varlen/cpu)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--only", choices=["decode"], default=None,
+                    help="profiling aid: run only the decode measurement and print its figures")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -225,6 +227,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": 1 << 30, "copies": 3}), flush=True)
+        return
+    if args.only == "decode":
+        print(json.dumps(bench_decode()), flush=True)
         return
     name = args.workload or workloads.P128K
     w = workloads.WORKLOADS[name]

@@ -25,6 +25,8 @@
  *   - `stream` is a hipStream_t (NULL = the default stream); every call only enqueues work on
  *     it and returns without synchronising; nothing is copied between host and device;
  *   - bf16 tensors are uint16 bit patterns; fp8 tensors are OCP E4M3 ("e4m3fn") codes;
+ *   - a prefill batch with total_tokens == 0 is valid and does nothing (tensor pointers may
+ *     then be NULL);
  *   - return DSA_OK (0) or a positive dsa_status.  Argument checks happen on the host
  *     before anything is enqueued; on error nothing is enqueued.  Contents of device arrays
  *     (cu_seqlens, cache_lens) are the caller's contract and are not checked;

@@ -225,6 +225,7 @@ int dsa_prefill_workspace_size(const dsa_prefill_shape* s, const int32_t* cu_seq
   if (!bytes) return DSA_ERR_INVALID_ARGUMENT;
   int rc = check_prefill(s, false);
   if (rc) return rc;
+  if (s->total_tokens == 0) return DSA_OK;  // empty batch: nothing to do, pointers may be null
   *bytes = prefill_layout(s, cu_seqlens_host).total;
   // the library only checks the host bound, so never report less than it
   const size_t bound = prefill_layout(s, nullptr).total;
@@ -236,6 +237,7 @@ int dsa_index_scores(const dsa_prefill_shape* s, const void* q_idx, const void* 
                      float* scores, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_prefill(s, true);
   if (rc) return rc;
+  if (s->total_tokens == 0) return DSA_OK;  // empty batch: nothing to do, pointers may be null
   if (!q_idx || !k_idx || !w_idx || !scores) return DSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx)) return DSA_ERR_INVALID_ARGUMENT;
   PrefillWs L;
@@ -250,6 +252,7 @@ int dsa_index_topk(const dsa_prefill_shape* s, const void* q_idx, const void* k_
                    int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_prefill(s, true);
   if (rc) return rc;
+  if (s->total_tokens == 0) return DSA_OK;  // empty batch: nothing to do, pointers may be null
   if (!q_idx || !k_idx || !w_idx || !topk_idx) return DSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx)) return DSA_ERR_INVALID_ARGUMENT;
   PrefillWs L;
@@ -264,6 +267,7 @@ int dsa_sparse_attention(const dsa_prefill_shape* s, const uint16_t* q, const ui
                          const int32_t* topk_idx, uint16_t* out, void* stream) {
   int rc = check_prefill(s, false);
   if (rc) return rc;
+  if (s->total_tokens == 0) return DSA_OK;  // empty batch: nothing to do, pointers may be null
   if (!q || !k || !v || !topk_idx || !out) return DSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return DSA_ERR_INVALID_ARGUMENT;
   return hip_status(launch_gather_attention(q, k, v, topk_idx, s->topk, 0, s->cu_seqlens, s->num_seqs, nullptr, 0,
@@ -282,6 +286,11 @@ int prefill_impl(const dsa_prefill_shape* s, const void* q_idx, const void* k_id
                  void* ws, size_t ws_bytes, void* stream, void* const* ev) {
   int rc = check_prefill(s, true);
   if (rc) return rc;
+  if (s->total_tokens == 0) {  // empty batch: nothing to compute, pointers may be null
+    for (int i = 0; i < 4 && ev; ++i)
+      if ((rc = record(ev, i, static_cast<hipStream_t>(stream)))) return rc;
+    return DSA_OK;
+  }
   if (!q_idx || !k_idx || !w_idx || !q || !k || !v || !out) return DSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx) || !aligned16(q) || !aligned16(k) ||
       !aligned16(v) || !aligned16(out))
@@ -363,6 +372,7 @@ int dense_causal_attention(const dsa_prefill_shape* s, const uint16_t* q, const 
                            uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_prefill(s, false);
   if (rc) return rc;
+  if (s->total_tokens == 0) return DSA_OK;  // empty batch: nothing to do, pointers may be null
   if (!q || !k || !v || !out) return DSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return DSA_ERR_INVALID_ARGUMENT;
   PrefillWs L;

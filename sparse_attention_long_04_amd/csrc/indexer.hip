@@ -268,26 +268,49 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
       acc_abs[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
       acc_lin[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
-    for (int h = 0; h < H; h += 2) {  // H is a multiple of 16: heads in pairs for more ILP
-      i32x4 afr0[CHU], afr1[CHU];
-      load_a(afr0, q_lds + h * 16 * ROWB);
-      load_a(afr1, q_lds + (h + 1) * 16 * ROWB);
-      const f32x4 wv0 = *reinterpret_cast<const f32x4*>(w_lds + h * 16 + 4 * g);
-      const f32x4 wv1 = *reinterpret_cast<const f32x4*>(w_lds + (h + 1) * 16 + 4 * g);
-      f32x4 c0[NT], c1[NT];
-#pragma unroll
-      for (int jt = 0; jt < NT; ++jt) c0[jt] = mma(afr0, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
+    // software pipeline over head pairs (H is a multiple of 16): the MFMAs of pair p+1 are
+    // issued while the VALU folds pair p's results, so no FMA waits on a fresh MFMA
+    f32x4 c0[NT], c1[NT];
+    f32x4 wv0, wv1;
+    {
+      i32x4 a0[CHU], a1[CHU];
+      load_a(a0, q_lds);
+      load_a(a1, q_lds + 16 * ROWB);
+      wv0 = *reinterpret_cast<const f32x4*>(w_lds + 4 * g);
+      wv1 = *reinterpret_cast<const f32x4*>(w_lds + 16 + 4 * g);
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) {
-        c1[jt] = mma(afr1, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
+        c0[jt] = mma(a0, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
+        c1[jt] = mma(a1, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
+      }
+    }
+    for (int h = 2; h < H; h += 2) {
+      i32x4 a0[CHU], a1[CHU];
+      load_a(a0, q_lds + h * 16 * ROWB);
+      load_a(a1, q_lds + (h + 1) * 16 * ROWB);
+      const f32x4 nw0 = *reinterpret_cast<const f32x4*>(w_lds + h * 16 + 4 * g);
+      const f32x4 nw1 = *reinterpret_cast<const f32x4*>(w_lds + (h + 1) * 16 + 4 * g);
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) {
+        const f32x4 n0 = mma(a0, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc_abs[jt][i] = fmaf(wv0[i], fabsf(c0[jt][i]), acc_abs[jt][i]);
-      }
-#pragma unroll
-      for (int jt = 0; jt < NT; ++jt)
+        const f32x4 n1 = mma(a1, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc_abs[jt][i] = fmaf(wv1[i], fabsf(c1[jt][i]), acc_abs[jt][i]);
+        c0[jt] = n0;
+        c1[jt] = n1;
+      }
+      wv0 = nw0;
+      wv1 = nw1;
     }
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc_abs[jt][i] = fmaf(wv0[i], fabsf(c0[jt][i]), acc_abs[jt][i]);
+        acc_abs[jt][i] = fmaf(wv1[i], fabsf(c1[jt][i]), acc_abs[jt][i]);
+      }
 #pragma unroll
     for (int pc = 0; pc < NP; ++pc) {
       i32x4 afr[CHU];

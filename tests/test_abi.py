@@ -140,3 +140,12 @@ def test_schedule_rank_is_a_longest_first_permutation():
         assert sorted(ranks) == list(range(len(pairs)))
         order = [p for _, p in sorted(zip(ranks, pairs))]
         assert order == sorted(pairs, key=lambda p: (-p[1], p[0]))
+
+
+def test_empty_prefill_batch_is_a_noop_with_null_pointers():
+    s = shape(T=0, max_seqlen=0)
+    for fn in (lambda: dsa.dsa_prefill(s, None, None, None, None, None, None, None, None, None, stream=0),
+               lambda: dsa.dsa_index_topk(s, None, None, None, None, None, stream=0),
+               lambda: dsa.dsa_sparse_attention(s, None, None, None, None, None, stream=0),
+               lambda: dsa.dense_causal_attention(s, None, None, None, None, None, stream=0)):
+        fn()

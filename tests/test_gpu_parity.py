@@ -285,3 +285,68 @@ def test_topk_two_valued_scores_decode():
                              d.softmax_scale)
     assert np.array_equal(st.topk_idx.cpu().numpy(), sel)
     assert_out_close(bf16_to_float(st.out), ref, "decode two-valued")
+
+
+def test_decode_unequal_cache_lengths():
+    """Sequences of one batch at different lengths: 1 token, fewer than k, about k, many chunks."""
+    lens = [1, 700, 2048, 2049, 13000]
+    cap = 13100
+    d = gen.make_decode(len(lens), max(lens), cap, 1, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", topk=2048,
+                        seed=51)
+    st = DecodeState(d)
+    st.lens.copy_(torch.tensor([L - 1 for L in lens], dtype=torch.int32))
+    st.len_host[:] = [L - 1 for L in lens]
+    s = st.load_step(0)
+    st.append()
+    st.decode()
+    torch.cuda.synchronize()
+    kc, kk, vv = d.k_idx_cache.copy(), d.k_cache.copy(), d.v_cache.copy()
+    for b, L in enumerate(lens):
+        kc[b, L - 1], kk[b, L - 1], vv[b, L - 1] = s["k_idx_new"][b], s["k_new"][b], s["v_new"][b]
+    assert list(st.len_host) == lens
+    sel, ref = O.decode_step(kc, kk, vv, st.len_host, s["q_idx"], s["w_idx"], s["q"], d.idx_dtype, d.topk,
+                             d.softmax_scale)
+    assert np.array_equal(st.topk_idx.cpu().numpy(), sel)
+    assert_out_close(bf16_to_float(st.out), ref, "decode unequal lengths")
+    dense = bf16_to_float(st.dense(out=torch.empty_like(st.out)))
+    assert_out_close(dense, O.dense_decode(kk, vv, st.len_host, s["q"], d.softmax_scale), "dense unequal lengths")
+
+
+def test_empty_prefill_batch():
+    p = gen.make_prefill([0, 0], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=16, seed=52)
+    pb = PrefillBatch(p)
+    pb.prefill()
+    pb.dense(out=torch.empty_like(pb.out))
+    torch.cuda.synchronize()
+    assert pb.out.numel() == 0
+
+
+@pytest.mark.parametrize("k", [1, 4096])
+def test_topk_extreme_k(k):
+    p = gen.make_prefill([5000, 33], idx_heads=16, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=k,
+                         seed=53, video=True)
+    pb = PrefillBatch(p)
+    pb.prefill()
+    idx = pb.topk_idx.cpu().numpy()
+    o = oracle_of(p)
+    rows = np.array([0, 1, 17, 4094, 4095, 4096, 4999, 5000, 5032])
+    sel, ref = o.rows(rows)
+    assert np.array_equal(idx[rows], sel)
+    assert_out_close(bf16_to_float(pb.out)[rows], ref, f"k={k}")
+
+
+@pytest.mark.parametrize("H,dt,dI", [(16, "fp8_e4m3", 128), (32, "fp8_e4m3", 128), (32, "bf16", 128), (64, "bf16", 64)])
+def test_indexer_head_shapes(H, dt, dI):
+    p = gen.make_prefill([1200, 250], idx_heads=H, idx_dim=dI, idx_dtype=dt, idx_range=4 if dt == "fp8_e4m3" else 8,
+                         topk=300, seed=54)
+    pb = PrefillBatch(p)
+    got = pb.index_scores().cpu().numpy().astype(np.float64)
+    ref = O.index_score_matrix(p.cu_seqlens, p.q_idx, p.k_idx, p.w_idx, p.idx_dtype)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    pb.index_topk()
+    idx = pb.topk_idx.cpu().numpy()
+    o = oracle_of(p)
+    for t in [0, 299, 300, 1199, 1200, 1449]:
+        assert np.array_equal(idx[t], O.select_topk_row(o.scores(t), p.topk)), t

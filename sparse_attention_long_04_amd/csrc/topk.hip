@@ -602,19 +602,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_final_kernel(
   const int b = blockIdx.x;
   const int n = cache_lens[b];
   int32_t* orow = out + (int64_t)b * K;
+  // issue the independent global reads together (histogram, chunk count) before the range
+  // reduction, which has its own read: one round trip instead of three
+  int hreg[kBins / kTopkThreads];
+#pragma unroll
+  for (int j = 0; j < kBins / kTopkThreads; ++j) hreg[j] = ghist[b * kBins + threadIdx.x + j * kTopkThreads];
+  const int c = threadIdx.x < nchunk ? counts[b * nchunk + threadIdx.x] : 0;
   const RowRange rr = decode_range(blkrange, blk_stride, b, n, sm.s);
   if (n <= K || rr.flat) {
     first_k(n, K, orow);
     return;
   }
   // threshold bin again (same histogram as the collect step)
-  for (int i = threadIdx.x; i < kBins; i += kTopkThreads) sm.s.hist[i] = ghist[b * kBins + i];
+#pragma unroll
+  for (int j = 0; j < kBins / kTopkThreads; ++j) sm.s.hist[threadIdx.x + j * kTopkThreads] = hreg[j];
   __syncthreads();
   find_digit(sm.s, kBins, K);
   const int b1 = sm.s.sel_digit, above = sm.s.sel_above;
-  // chunk offsets: one count per thread, block prefix sum
+  // chunk offsets: block prefix sum of the per-chunk counts
   {
-    const int c = threadIdx.x < nchunk ? counts[b * nchunk + threadIdx.x] : 0;
     int tot;
     const int incl = block_incl_scan(c, sm.s.wave_tot, &tot);
     if (threadIdx.x < nchunk) sm.offs[threadIdx.x] = incl - c;
@@ -631,16 +637,36 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_final_kernel(
     keys = reinterpret_cast<uint32_t*>(spill_keys_ids) + (int64_t)b * 2 * nchunk * kChunk;
     ids = reinterpret_cast<int*>(keys + nchunk * kChunk);
   }
-  // flattened gather of the concatenated chunk lists (chunk order = index order)
-  for (int i = threadIdx.x; i < total; i += kTopkThreads) {
-    int lo = 0, hi = nchunk - 1;  // last chunk c with offs[c] <= i
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sm.offs[mid] <= i) lo = mid; else hi = mid - 1;
+  // flattened gather of the concatenated chunk lists (chunk order = index order); a batch of
+  // loads is issued into registers before any store, so the round trips overlap
+  constexpr int PER = 16;
+  for (int base = 0; base < total; base += PER * kTopkThreads) {
+    uint32_t kv[PER];
+    int iv[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = base + u * kTopkThreads + threadIdx.x;
+      kv[u] = 0u;
+      iv[u] = -1;
+      if (i < total) {
+        int lo = 0, hi = nchunk - 1;  // last chunk c with offs[c] <= i
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sm.offs[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        const int64_t src = ((int64_t)b * nchunk + lo) * kChunk + (i - sm.offs[lo]);
+        kv[u] = gkeys[src];
+        iv[u] = gids[src];
+      }
     }
-    const int64_t src = ((int64_t)b * nchunk + lo) * kChunk + (i - sm.offs[lo]);
-    keys[i] = gkeys[src];
-    ids[i] = gids[src];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = base + u * kTopkThreads + threadIdx.x;
+      if (i < total) {
+        keys[i] = kv[u];
+        ids[i] = iv[u];
+      }
+    }
   }
   __syncthreads();
   auto bin_of = [&](uint32_t k) { return value_bin(key_to_score(k), rr.lo, rr.sc); };

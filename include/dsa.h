@@ -146,11 +146,15 @@ int dense_causal_attention(const dsa_prefill_shape* shape, const uint16_t* q, co
 /* Workspace bytes for dsa_decode / dense_decode_attention. */
 int dsa_decode_workspace_size(const dsa_decode_shape* shape, size_t* bytes);
 
-/* Append one token per sequence to the caches at row positions[b] (DEVICE int32 [B],
- * 0 <= positions[b] < cache_capacity): k_idx_new [B, d_I] -> k_idx_cache [B, cap, d_I],
- * k_new/v_new bf16 [B, Hkv, d] -> k_cache/v_cache bf16 [B, cap, Hkv, d]. */
+/* Append one token per sequence to the caches and count it: with n = cache_lens[b] (DEVICE
+ * int32 [B], in/out), row n of each cache receives the token and cache_lens[b] becomes n + 1.
+ * k_idx_new [B, d_I] -> k_idx_cache [B, cap, d_I]; k_new/v_new bf16 [B, Hkv, d] ->
+ * k_cache/v_cache bf16 [B, cap, Hkv, d].  A sequence whose cache is full (n >= cap) is left
+ * unchanged, lengths included, so the caller detects it by reading cache_lens back.
+ * cache_lens is normally the same buffer as shape->cache_lens; the shape's max_cache_len is
+ * not read here, so the caller raises it for the following dsa_decode. */
 int dsa_kv_append(const dsa_decode_shape* shape, const void* k_idx_new, const uint16_t* k_new,
-                  const uint16_t* v_new, const int32_t* positions, void* k_idx_cache,
+                  const uint16_t* v_new, int32_t* cache_lens, void* k_idx_cache,
                   uint16_t* k_cache, uint16_t* v_cache, void* stream);
 
 /* One DSA decode step (summary page sections 一 and 八): for each sequence b the newest token

@@ -236,23 +236,53 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
   }
 }
 
-// Merge split partials: out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-__global__ void combine_kernel(const float* __restrict__ o_part, const float2* __restrict__ ml_part,
-                               int nsplit, int Hq, int D, uint16_t* __restrict__ out) {
+// Merge split partials: out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  Splits are read
+// in batches of kCombineBatch whose loads are all issued before any is used, with a running
+// maximum carried across batches; empty splits (l_s == 0) contribute nothing.
+constexpr int kCombineBatch = 16;
+
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ o_part,
+                                                      const float2* __restrict__ ml_part, int nsplit, int Hq,
+                                                      int D, uint16_t* __restrict__ out) {
   const int64_t r = blockIdx.x;
   const int h = blockIdx.y;
   const int d = threadIdx.x;
-  float M = -__builtin_inff();
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml_part[(r * nsplit + s) * Hq + h].x);
-  float L = 0.f, acc = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 ml = ml_part[(r * nsplit + s) * Hq + h];
-    if (ml.y == 0.f) continue;
-    const float wgt = exp2f(ml.x - M);
-    L += ml.y * wgt;
-    acc += o_part[((r * nsplit + s) * Hq + h) * (int64_t)D + d] * wgt;
+  float M = -__builtin_inff(), L = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += kCombineBatch) {
+    float m[kCombineBatch], l[kCombineBatch], o[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const int s = s0 + u;
+      m[u] = -__builtin_inff();
+      l[u] = 0.f;
+      o[u] = 0.f;
+      if (s < nsplit) {
+        const int64_t slot = (r * nsplit + s) * Hq + h;
+        const float2 ml = ml_part[slot];
+        m[u] = ml.x;
+        l[u] = ml.y;
+        o[u] = o_part[slot * D + d];
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u)
+      if (l[u] != 0.f) Mb = fmaxf(Mb, m[u]);
+    if (Mb == -__builtin_inff()) continue;  // nothing non-empty so far
+    const float rescale = exp2f(M - Mb);    // 0 while M is still -inf
+    L *= rescale;
+    acc *= rescale;
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      if (l[u] != 0.f) {
+        const float wgt = exp2f(m[u] - Mb);
+        L += l[u] * wgt;
+        acc += o[u] * wgt;
+      }
+    }
+    M = Mb;
   }
-  if (d < D) out[(r * Hq + h) * D + d] = f32_to_bf16(L > 0.f ? acc / L : 0.f);
+  out[(r * Hq + h) * D + d] = f32_to_bf16(L > 0.f ? acc / L : 0.f);
 }
 
 // ------------------------------------------------------------------------------------------

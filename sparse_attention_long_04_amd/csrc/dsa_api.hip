@@ -31,18 +31,40 @@ hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint
                                 int Hkv, float scale, const int2* sched, const int* count, int nb_bound,
                                 uint16_t* out, hipStream_t st);
 
-// Copy one new token per sequence into the caches at row positions[b].
-__global__ void kv_append_kernel(const uint8_t* __restrict__ kin, const uint16_t* __restrict__ knew,
-                                 const uint16_t* __restrict__ vnew, const int32_t* __restrict__ pos,
-                                 int cap, int idx_row_bytes, int kv_row_elems, uint8_t* __restrict__ kic,
-                                 uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
+// Copy one new token per sequence into the caches at row lens[b] and count it (lens[b] += 1);
+// a full cache (lens[b] >= cap) is left untouched.  Rows are moved in 16-byte units (VEC) when
+// every row size and base pointer allows it, else byte by byte.
+template <bool VEC>
+__global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restrict__ kin,
+                                                        const uint8_t* __restrict__ knew,
+                                                        const uint8_t* __restrict__ vnew, int32_t* __restrict__ lens,
+                                                        int cap, int idx_row_bytes, int kv_row_bytes,
+                                                        uint8_t* __restrict__ kic, uint8_t* __restrict__ kc,
+                                                        uint8_t* __restrict__ vc) {
   const int b = blockIdx.x;
-  const int64_t row = (int64_t)b * cap + pos[b];
-  for (int i = threadIdx.x; i < idx_row_bytes; i += blockDim.x) kic[row * idx_row_bytes + i] = kin[(int64_t)b * idx_row_bytes + i];
-  for (int i = threadIdx.x; i < kv_row_elems; i += blockDim.x) {
-    kc[row * kv_row_elems + i] = knew[(int64_t)b * kv_row_elems + i];
-    vc[row * kv_row_elems + i] = vnew[(int64_t)b * kv_row_elems + i];
+  const int pos = lens[b];
+  if (pos < 0 || pos >= cap) return;
+  const int64_t row = (int64_t)b * cap + pos;
+  const int U = VEC ? 16 : 1;
+  const int ni = idx_row_bytes / U, nk = kv_row_bytes / U;
+  for (int i = threadIdx.x; i < ni + 2 * nk; i += blockDim.x) {
+    const uint8_t* src;
+    uint8_t* dst;
+    if (i < ni) {
+      src = kin + ((int64_t)b * ni + i) * U;
+      dst = kic + (row * ni + i) * U;
+    } else if (i < ni + nk) {
+      src = knew + ((int64_t)b * nk + i - ni) * U;
+      dst = kc + (row * nk + i - ni) * U;
+    } else {
+      src = vnew + ((int64_t)b * nk + i - ni - nk) * U;
+      dst = vc + (row * nk + i - ni - nk) * U;
+    }
+    if (VEC) *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    else *dst = *src;
   }
+  __syncthreads();  // every thread has read lens[b] before it changes
+  if (threadIdx.x == 0) lens[b] = pos + 1;
 }
 }  // namespace dsa
 
@@ -394,16 +416,29 @@ int dsa_decode_workspace_size(const dsa_decode_shape* s, size_t* bytes) {
 }
 
 int dsa_kv_append(const dsa_decode_shape* s, const void* k_idx_new, const uint16_t* k_new, const uint16_t* v_new,
-                  const int32_t* positions, void* k_idx_cache, uint16_t* k_cache, uint16_t* v_cache, void* stream) {
+                  int32_t* cache_lens, void* k_idx_cache, uint16_t* k_cache, uint16_t* v_cache, void* stream) {
   if (!s || s->batch < 1 || s->cache_capacity < 1 || s->idx_dim < 1 || s->kv_heads < 1 || s->head_dim < 1)
     return DSA_ERR_INVALID_ARGUMENT;
   if (s->idx_dtype != DSA_IDX_BF16 && s->idx_dtype != DSA_IDX_FP8_E4M3) return DSA_ERR_INVALID_ARGUMENT;
-  if (!k_idx_new || !k_new || !v_new || !positions || !k_idx_cache || !k_cache || !v_cache)
+  if (!k_idx_new || !k_new || !v_new || !cache_lens || !k_idx_cache || !k_cache || !v_cache)
     return DSA_ERR_INVALID_ARGUMENT;
   const int idx_row_bytes = s->idx_dim * (s->idx_dtype == DSA_IDX_BF16 ? 2 : 1);
-  kv_append_kernel<<<s->batch, 256, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint8_t*>(k_idx_new), k_new, v_new, positions, s->cache_capacity, idx_row_bytes,
-      s->kv_heads * s->head_dim, static_cast<uint8_t*>(k_idx_cache), k_cache, v_cache);
+  const int kv_row_bytes = s->kv_heads * s->head_dim * 2;
+  const bool vec = idx_row_bytes % 16 == 0 && kv_row_bytes % 16 == 0 && aligned16(k_idx_new) && aligned16(k_new) &&
+                   aligned16(v_new) && aligned16(k_idx_cache) && aligned16(k_cache) && aligned16(v_cache);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint8_t* ki = static_cast<const uint8_t*>(k_idx_new);
+  const uint8_t* kn = reinterpret_cast<const uint8_t*>(k_new);
+  const uint8_t* vn = reinterpret_cast<const uint8_t*>(v_new);
+  uint8_t* kic = static_cast<uint8_t*>(k_idx_cache);
+  uint8_t* kc = reinterpret_cast<uint8_t*>(k_cache);
+  uint8_t* vc = reinterpret_cast<uint8_t*>(v_cache);
+  if (vec)
+    kv_append_kernel<true><<<s->batch, 256, 0, st>>>(ki, kn, vn, cache_lens, s->cache_capacity, idx_row_bytes,
+                                                     kv_row_bytes, kic, kc, vc);
+  else
+    kv_append_kernel<false><<<s->batch, 256, 0, st>>>(ki, kn, vn, cache_lens, s->cache_capacity, idx_row_bytes,
+                                                      kv_row_bytes, kic, kc, vc);
   return hip_status(hipGetLastError());
 }
 

@@ -187,8 +187,8 @@ def dsa_decode_workspace_size(shape: DecodeShape) -> int:
     return n.value
 
 
-def dsa_kv_append(shape, k_idx_new, k_new, v_new, positions, k_idx_cache, k_cache, v_cache, stream=None):
-    _check(lib().dsa_kv_append(ctypes.byref(shape), _ptr(k_idx_new), _ptr(k_new), _ptr(v_new), _ptr(positions),
+def dsa_kv_append(shape, k_idx_new, k_new, v_new, cache_lens, k_idx_cache, k_cache, v_cache, stream=None):
+    _check(lib().dsa_kv_append(ctypes.byref(shape), _ptr(k_idx_new), _ptr(k_new), _ptr(v_new), _ptr(cache_lens),
                                _ptr(k_idx_cache), _ptr(k_cache), _ptr(v_cache), _stream(stream)), "dsa_kv_append")
 
 

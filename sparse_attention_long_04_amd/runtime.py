@@ -106,11 +106,12 @@ class DecodeState:
         return s
 
     def append(self, stream=None):
-        """Append the loaded step's token at row cache_len, then count it in cache_lens."""
+        """Append the loaded step's token at row cache_lens[b]; the kernel also counts it."""
+        if int(self.len_host.max()) >= self.d.capacity:
+            raise ValueError("decode cache is full")
         sd = self.step_dev
         dsa.dsa_kv_append(self.shape, sd["k_idx_new"], sd["k_new"], sd["v_new"], self.lens, self.k_idx_cache,
                           self.k_cache, self.v_cache, stream)
-        self.lens += 1
         self.len_host += 1
 
     def decode(self, stream=None):

@@ -104,36 +104,16 @@ __device__ __forceinline__ void load_tile(GatherTile& t, const int* __restrict__
     t.vf[m] = *reinterpret_cast<const i32x4*>(vg_base + (int64_t)max(t.sv[m], 0) * kvs + 8 * lr);
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ idx, int K, int mode, const int32_t* __restrict__ cu, int nseq,
-    const int32_t* __restrict__ cache_lens, int cap, int Hq, int Hkv, float scale_log2,
-    int keys_per_split, int nsplit, uint16_t* __restrict__ out, float* __restrict__ o_part,
-    float2* __restrict__ ml_part) {
-  static_assert(D == 128, "head_dim 128 only");
-  __shared__ __attribute__((aligned(16))) int il[kMaxSplitKeys + 32];
-  const int64_t r = blockIdx.x;
-  const int split = blockIdx.y;
-  const int g = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int G = Hq / Hkv;
-  const RowInfo ri = row_info(mode, r, cu, nseq, cache_lens, cap);
-  const int m_all = idx ? min(K, ri.n) : ri.n;
-  const int p_begin = split * keys_per_split;
-  const int p_end = min(m_all, p_begin + keys_per_split);
-  const int cnt = max(0, p_end - p_begin);
-  const int cnt32 = (cnt + 31) & ~31;
-
-  // stage this split's key indices in LDS; slots past the end hold -1
-  for (int j = threadIdx.x; j < cnt32; j += 64 * NW) {
-    int s = -1;
-    if (j < cnt) s = idx ? __builtin_nontemporal_load(idx + r * K + p_begin + j) : p_begin + j;
-    il[j] = s;
-  }
-  __syncthreads();
-
-  // Q^T operand: lane holds head lr, dims 32c + 8lg .. +7
+// Attention of one wave's row r over cnt32 staged key slots (il, -1 = masked) of KV head g:
+// the Q^T operand holds head lr of the group, dims 32c + 8lg .. +7; on return o[dt][i] is the
+// unnormalised O[head lr][dim 32lg + 8i + dt], m_run the running max (log2 units) and l_tot the
+// softmax denominator summed over the wave.
+template <int D>
+__device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, const int* __restrict__ il, int cnt32,
+                                              int64_t r, int g, int G, int Hq, int64_t kvs,
+                                              const uint16_t* __restrict__ kg_base,
+                                              const uint16_t* __restrict__ vg_base, float scale_log2, int lr, int lg,
+                                              f32x4 (&o)[8], float& m_run, float& l_tot) {
   i32x4 qf[4];
   {
     const bool hv = lr < G;
@@ -144,14 +124,10 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
       if (!hv) qf[c] = (i32x4){0, 0, 0, 0};
     }
   }
-  // O accumulator: o[dt][i] = O[head lr][dim 32lg + 8i + dt]
-  f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff(), l_run = 0.f;
-  const int64_t kvs = (int64_t)Hkv * D;
-  const uint16_t* __restrict__ kg_base = k + ri.kv_row0 * kvs + g * D;
-  const uint16_t* __restrict__ vg_base = v + ri.kv_row0 * kvs + g * D;
+  m_run = -__builtin_inff();
+  float l_run = 0.f;
 
   GatherTile cur, nxt;
   if (cnt32 > 0) load_tile(cur, il, 0, kg_base, vg_base, kvs, lr, lg);
@@ -205,23 +181,65 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
     }
     cur = nxt;
   }
-
-  float l_tot = l_run;
+  l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16);
   l_tot += __shfl_xor(l_tot, 32);
+}
+
+// Normalised bf16 output of head `head` (lane column) from the attend_staged accumulators.
+template <int D>
+__device__ __forceinline__ void store_out_bf16(uint16_t* __restrict__ out, int64_t r, int Hq, int head, int lg,
+                                               const f32x4 (&o)[8], float l_tot) {
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  uint16_t* op = out + (r * Hq + head) * D + 32 * lg;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    i32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = int(uint32_t(f32_to_bf16(o[2 * e][i] * inv)) | (uint32_t(f32_to_bf16(o[2 * e + 1][i] * inv)) << 16));
+    __builtin_nontemporal_store(w, reinterpret_cast<i32x4*>(op + 8 * i));
+  }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ idx, int K, int mode, const int32_t* __restrict__ cu, int nseq,
+    const int32_t* __restrict__ cache_lens, int cap, int Hq, int Hkv, float scale_log2,
+    int keys_per_split, int nsplit, uint16_t* __restrict__ out, float* __restrict__ o_part,
+    float2* __restrict__ ml_part) {
+  static_assert(D == 128, "head_dim 128 only");
+  __shared__ __attribute__((aligned(16))) int il[kMaxSplitKeys + 32];
+  const int64_t r = blockIdx.x;
+  const int split = blockIdx.y;
+  const int g = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int G = Hq / Hkv;
+  const RowInfo ri = row_info(mode, r, cu, nseq, cache_lens, cap);
+  const int m_all = idx ? min(K, ri.n) : ri.n;
+  const int p_begin = split * keys_per_split;
+  const int p_end = min(m_all, p_begin + keys_per_split);
+  const int cnt = max(0, p_end - p_begin);
+  const int cnt32 = (cnt + 31) & ~31;
+
+  // stage this split's key indices in LDS; slots past the end hold -1
+  for (int j = threadIdx.x; j < cnt32; j += 64 * NW) {
+    int s = -1;
+    if (j < cnt) s = idx ? __builtin_nontemporal_load(idx + r * K + p_begin + j) : p_begin + j;
+    il[j] = s;
+  }
+  __syncthreads();
+
+  const int64_t kvs = (int64_t)Hkv * D;
+  f32x4 o[8];
+  float m_run, l_tot;
+  attend_staged<D>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D, v + ri.kv_row0 * kvs + g * D,
+                   scale_log2, lr, lg, o, m_run, l_tot);
   if (lr >= G) return;
   const int head = g * G + lr;
   if (nsplit == 1) {
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    uint16_t* op = out + (r * Hq + head) * D + 32 * lg;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      i32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = int(uint32_t(f32_to_bf16(o[2 * e][i] * inv)) | (uint32_t(f32_to_bf16(o[2 * e + 1][i] * inv)) << 16));
-      __builtin_nontemporal_store(w, reinterpret_cast<i32x4*>(op + 8 * i));
-    }
+    store_out_bf16<D>(out, r, Hq, head, lg, o, l_tot);
   } else {
     const int64_t slot = (r * nsplit + split) * Hq + head;
     float* pp = o_part + slot * D + 32 * lg;
@@ -234,6 +252,45 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
     }
     if (lg == 0) ml_part[slot] = make_float2(m_run, l_tot);
   }
+}
+
+// Prefill variant with an XCD-aware mapping: workgroup b runs on XCD b % 8 (the dispatcher
+// deals workgroups round-robin over the 8 XCDs), serves KV head (b % 8) % Hkv, and its NW waves
+// take NW consecutive rows, each staging its own indices.  Every XCD then gathers the K/V rows
+// of a single head (Hkv * 256 B less per key than a workgroup spanning all heads), so its L2
+// holds that many more of the keys that neighbouring rows share.  Needs 8 % Hkv == 0 and
+// K <= kRowKeys.
+constexpr int kRowKeys = 2048;
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ idx, int K, const int32_t* __restrict__ cu, int nseq, int64_t rows, int Hq,
+    int Hkv, float scale_log2, uint16_t* __restrict__ out) {
+  static_assert(D == 128, "head_dim 128 only");
+  __shared__ __attribute__((aligned(16))) int il_all[NW][kRowKeys + 32];
+  const int xcd = blockIdx.x & 7;
+  const int g = xcd % Hkv;
+  const int64_t group = (int64_t)(blockIdx.x >> 3) * (8 / Hkv) + xcd / Hkv;
+  const int wave = threadIdx.x >> 6;
+  const int64_t r = group * NW + wave;
+  if (r >= rows) return;  // waves are independent: no workgroup barrier below
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int G = Hq / Hkv;
+  const RowInfo ri = row_info(0, r, cu, nseq, nullptr, 0);
+  const int cnt = min(K, ri.n);
+  const int cnt32 = (cnt + 31) & ~31;
+  int* il = il_all[wave];
+  for (int j = lane; j < cnt32; j += 64) il[j] = (j < cnt) ? __builtin_nontemporal_load(idx + r * K + j) : -1;
+  __builtin_amdgcn_wave_barrier();  // the wave's own LDS writes precede its reads (in-order LDS)
+
+  const int64_t kvs = (int64_t)Hkv * D;
+  f32x4 o[8];
+  float m_run, l_tot;
+  attend_staged<D>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D, v + ri.kv_row0 * kvs + g * D,
+                   scale_log2, lr, lg, o, m_run, l_tot);
+  if (lr >= G) return;
+  store_out_bf16<D>(out, r, Hq, g * G + lr, lg, o, l_tot);
 }
 
 // Merge split partials: out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  Splits are read
@@ -480,6 +537,15 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
                                    float* o_part, float2* ml_part, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const float scale_log2 = scale * 1.4426950408889634f;
+  if (mode == 0 && nsplit == 1 && idx && K <= kRowKeys && 8 % Hkv == 0) {
+    constexpr int NWR = 4;
+    const int64_t groups = (rows + NWR - 1) / NWR;
+    const int per = 8 / Hkv;  // XCDs per head
+    const int64_t blocks = 8 * ((groups + per - 1) / per);
+    gather_rows_kernel<128, NWR><<<(unsigned)blocks, 64 * NWR, 0, st>>>(q, k, v, idx, K, cu, nseq, rows, Hq, Hkv,
+                                                                        scale_log2, out);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)rows, nsplit);
 #define DSA_GATHER(NW)                                                                                   \
   gather_attention_kernel<128, NW><<<grid, 64 * NW, 0, st>>>(q, k, v, idx, K, mode, cu, nseq, cache_lens, \

@@ -412,13 +412,6 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
   if (blockIdx.x == 0)
     for (int i = tid; i < 2048; i += 256) ghist[b * 2048 + i] = 0;
   if (key0 >= n) return;
-  for (int u = tid; u < H * UNITS; u += 256) {
-    const int h = u / UNITS, c = u - h * UNITS;
-    *reinterpret_cast<i32x4*>(q_lds + h * ROWB + ((c ^ (h & 7)) * 16)) =
-        *reinterpret_cast<const i32x4*>(q_idx + ((int64_t)b * H + h) * ROWB + c * 16);
-  }
-  for (int h = tid; h < H; h += 256) w_lds[h] = w_idx[(int64_t)b * H + h];
-  __syncthreads();
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int kw0 = key0 + wave * WKEYS;
   const int kw1 = min(n, kw0 + WKEYS);
@@ -466,9 +459,17 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
       }
     }
   };
+  // the first keys are requested before the queries are staged, so the two latencies overlap
+  i32x8 bA[NT], bB[NT];
+  load(bA, min(kw0, n - 1));
+  for (int u = tid; u < H * UNITS; u += 256) {
+    const int h = u / UNITS, c = u - h * UNITS;
+    *reinterpret_cast<i32x4*>(q_lds + h * ROWB + ((c ^ (h & 7)) * 16)) =
+        *reinterpret_cast<const i32x4*>(q_idx + ((int64_t)b * H + h) * ROWB + c * 16);
+  }
+  for (int h = tid; h < H; h += 256) w_lds[h] = w_idx[(int64_t)b * H + h];
+  __syncthreads();
   if (kw0 < kw1) {
-    i32x8 bA[NT], bB[NT];
-    load(bA, kw0);
     for (int kb = kw0; kb < kw1; kb += 2 * NT * 16) {
       step(bA, bB, kb);
       if (kb + NT * 16 < kw1) step(bB, bA, kb + NT * 16);

@@ -155,6 +155,26 @@ def test_decode_parity(ctx, cap, k, steps):
         assert_out_close(dense, O.dense_decode(kk, vv, st.len_host, s["q"], d.softmax_scale), f"dense decode {i}")
 
 
+@pytest.mark.parametrize("hq,hkv,k", [(32, 4, 3000), (12, 4, 300), (16, 1, 512), (8, 8, 64), (32, 2, 2048)])
+def test_decode_gqa_shapes_and_k(hq, hkv, k):
+    """Decode attention for other head layouts, and a selection larger than one workgroup's
+    slices (k = 3000 takes the split path with a separate combine)."""
+    d = gen.make_decode(2, 3500, 3600, 1, idx_heads=16, idx_dim=128, idx_dtype="fp8_e4m3", topk=k, seed=57,
+                        q_heads=hq, kv_heads=hkv)
+    st = DecodeState(d)
+    kc, kk, vv = d.k_idx_cache.copy(), d.k_cache.copy(), d.v_cache.copy()
+    s = st.load_step(0)
+    st.append()
+    st.decode()
+    torch.cuda.synchronize()
+    n = int(st.len_host[0])
+    kc[:, n - 1], kk[:, n - 1], vv[:, n - 1] = s["k_idx_new"], s["k_new"], s["v_new"]
+    sel, ref = O.decode_step(kc, kk, vv, st.len_host, s["q_idx"], s["w_idx"], s["q"], d.idx_dtype, d.topk,
+                             d.softmax_scale)
+    assert np.array_equal(st.topk_idx.cpu().numpy(), sel)
+    assert_out_close(bf16_to_float(st.out), ref, f"decode {hq}/{hkv} k={k}")
+
+
 def test_topk_all_ties_prefill():
     """Degenerate case: every score equal (zero indexer queries) -> each row keeps its first
     min(k, i+1) keys; rows longer than the LDS candidate list take the multi-pass path."""

@@ -270,11 +270,11 @@ def main():
                                        traffic.get("indexer_prefill_kernel"), idx_flops, "flop"),
         "topk_prefill_kernel": roof("hbm", topk_bytes / (pre["topk_ms"] * 1e-3), PEAK_HBM, "GB/s",
                                     traffic.get("topk_prefill_kernel"), topk_bytes, "byte"),
-        "gather_attention_kernel": roof("hbm", attn_bytes / (pre["attn_ms"] * 1e-3), PEAK_HBM, "GB/s",
-                                        traffic.get("gather_attention_kernel"), attn_bytes, "byte"),
+        "gather_rows_kernel": roof("hbm", attn_bytes / (pre["attn_ms"] * 1e-3), PEAK_HBM, "GB/s",
+                                        traffic.get("gather_rows_kernel"), attn_bytes, "byte"),
     }
     stage_ms = {"indexer_prefill_kernel": pre["indexer_ms"], "topk_prefill_kernel": pre["topk_ms"],
-                "gather_attention_kernel": pre["attn_ms"]}
+                "gather_rows_kernel": pre["attn_ms"]}
     dominant = max(stage_ms, key=stage_ms.get)
     line = {
         "metric": METRIC,

@@ -2,9 +2,9 @@
 // (Keye-VL-2.0 summary page, gsyq.cn, section 一: attention only among the selected positions;
 // the base LLM uses GQA; costs are quoted against standard full attention).
 //
-// gather_attention_kernel -- one workgroup per query row (a prefill token or a decode
-//   sequence) and optional key split; one wave per KV head.  The wave's query heads (Hq/Hkv,
-//   padded to 16) share the row's index set.  Per 32-key tile:
+// attend_staged (the per-wave body shared by both gather kernels) -- one wave attends one row
+//   for one KV head; the head's query heads (Hq/Hkv, padded to 16) share the row's index set.
+//   Per 32-key tile:
 //     S^T = K Q^T   bf16 MFMA 16x16x32, K rows gathered from HBM straight into A registers;
 //     online softmax in fp32 (exp2, running max/sum per head);
 //     O^T += V^T P^T  bf16 MFMA 16x16x32 with P split as hi + lo bf16 (two MFMAs, relative
@@ -13,14 +13,22 @@
 //                     (dim tile dt holds dims 8*row + dt), so the transpose happens inside the
 //                     lane's registers -- no LDS round trip for V.
 //   The next tile's K/V rows are loaded while the current one is computed; the row's key
-//   indices are staged in LDS once per workgroup.
-//   With several splits the wave writes (unnormalised O, running max, sum) partials that
-//   combine_kernel merges by log-sum-exp; with one split it writes bf16 output directly.
-//   idx == nullptr means "keys 0..n-1" (dense decode).
+//   indices are staged in LDS first.
 //
-// dense_prefill_kernel -- FlashAttention-style causal attention: a workgroup owns 128 query
-//   tokens of one query head (4 waves x 32 queries); 64-key K and V^T tiles are staged in LDS
-//   and shared by the 4 waves; S^T and O^T use 32x32x16 MFMAs (bf16 for QK, fp16 for PV).
+// gather_rows_kernel (prefill) -- XCD-aware: workgroup b runs on XCD b % 8 and serves KV head
+//   (b % 8) % Hkv, its 4 waves taking 4 consecutive rows, so each XCD's L2 only ever holds one
+//   head's K/V rows (512 B per key instead of 2 KiB) and catches more of the keys that
+//   neighbouring rows share.
+//
+// gather_attention_kernel (decode, dense decode, and prefill shapes the row kernel does not
+//   take) -- one workgroup per row and key split, one wave per KV head.  With several splits
+//   the wave writes (unnormalised O, running max, sum) partials that combine_kernel merges by
+//   log-sum-exp; with one split it writes bf16 output directly.  idx == nullptr means
+//   "keys 0..n-1" (dense decode).
+//
+// dense_prefill_kernel -- FlashAttention-style causal attention: a workgroup of 8 waves owns
+//   128 query tokens x 2 query heads of one KV group; 64-key K/V tiles are double-buffered in
+//   LDS and shared by both heads; S^T and O^T use 32x32x16 MFMAs (bf16 for QK, fp16 for PV).
 #include "common.h"
 
 namespace dsa {

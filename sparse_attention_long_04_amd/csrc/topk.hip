@@ -5,27 +5,27 @@
 // Rule: the first min(k, n) keys in the order (score descending, index ascending), written in
 // ascending index order and padded with -1.
 //
-// Scores map to order-preserving uint32 keys.  The k-th largest key T is found by a most-
-// significant-digit radix select (digits of 11, 11 and 10 bits; histograms in LDS); then an
-// ordered stream compaction keeps every key > T and the lowest-index keys == T until k are
-// kept.  A block-wide prefix sum gives every kept key its output slot, so the output is
-// sorted without a sort pass.  No float atomics anywhere; integer histogram atomics commute.
+// Scores map to order-preserving uint32 keys.  Scores of one row crowd into a few float
+// exponents, so selection first bins them by VALUE: bin(x) = floor((x - lo) * nbins / (hi - lo))
+// with the row's min lo and max hi (written by the indexer).  The map is monotone, so the
+// threshold bin (the bin holding the k-th largest key) splits the row into elements that are
+// surely kept (higher bins), surely dropped (lower bins) and the threshold bin's own elements,
+// which are ranked exactly by (key descending, index ascending).  An ordered, block-wide prefix
+// sum over the kept elements gives every one its output slot, so the output is sorted without
+// a sort pass.  No float atomics anywhere; integer histogram atomics commute.
 //
-// Scores of one row crowd into a few float exponents, so the first pass bins by VALUE:
-// bin(x) = floor((x - lo) * 2048 / (hi - lo)) with the row's min lo and max hi (written by the
-// indexer).  The map is monotone, so every element of a bin above the threshold bin is kept and
-// only the threshold bin needs a closer look.
-//
-// Prefill (one workgroup per row): pass 1 histograms the value bins over the row in HBM;
-// pass 2 compacts every element whose bin is >= the threshold bin into LDS (in index order);
-// the exact radix select and the output compaction then run on that short LDS list.  Rows whose
-// list would not fit (heavy ties) fall back to radix passes over HBM; rows whose scores are all
-// equal keep their first k keys directly.
+// Prefill (one workgroup per row, each of the 4 waves owning a contiguous quarter of the row):
+// pass 1 builds per-wave histograms of 1024 value bins straight from HBM; pass 2 compacts every
+// element whose bin is >= the threshold bin into an LDS list in index order (ballot + mbcnt
+// inside the wave, per-wave offsets).  The threshold bin is then ranked pairwise when it holds
+// at most 512 elements, else an exact most-significant-digit radix select (digits of 11, 11 and
+// 10 bits) runs on the list.  Rows whose list would not fit in LDS (heavy ties) run the radix
+// select over HBM; rows whose scores are all equal keep their first k keys directly.
 //
 // Decode (few rows of ~10^5 keys): the row is split into 4096-key chunks handled by separate
-// workgroups -- chunk histograms are merged with integer atomics, every chunk compacts its
-// candidates into its own list, and one workgroup per row finishes the select over the
-// concatenated lists.
+// workgroups -- chunk histograms of 2048 value bins are merged with integer atomics, every chunk
+// compacts its candidates into its own list, and one workgroup per row finishes the select over
+// the concatenated lists (pairwise rank of the threshold bin, radix select as the fallback).
 #include "common.h"
 
 namespace dsa {
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_prefill_kernel(
 
 // ------------------------------------------------------------------------------------------
 // Decode: chunked top-k over rows of n = cache_lens[b] scores.
-//   blkrange [B][ceil(n/256)] (min, max order keys per decode-indexer block), ghist [B][kBins] int
+//   blkrange [B][ceil(n/1024)] (min, max order keys per decode-indexer block), ghist [B][kBins] int
 //   (cleared before the indexer), lists [B][nchunk][kChunk] (key, id), counts [B][nchunk].
 // ------------------------------------------------------------------------------------------
 struct RowRange {

@@ -187,6 +187,46 @@ def bench_decode(steps_total=64, stage_reps=16):
     return res
 
 
+def bench_topk_general(reps=5):
+    """The standalone top-k (dsa_topk) on its workload: 2048 rows x 131072 fp32 scores, k = 2048,
+    timed over ``reps`` back-to-back launches with HIP events.  torch.topk on the same scores is
+    timed alongside as context only (it returns value-sorted positions with no tie rule)."""
+    import torch
+    from sparse_attention_long_04_amd import dsa, workloads
+    from sparse_attention_long_04_amd.runtime import timing_events
+
+    w = workloads.WORKLOADS[workloads.TOPK]
+    rows, n, k = w["rows"], w["n"], w["topk"]
+    t0 = time.time()
+    dev = torch.from_numpy(workloads.make(workloads.TOPK)).cuda()
+    log(f"topk: {rows} x {n} scores generated and uploaded in {time.time() - t0:.1f}s")
+    out = torch.empty((rows, k), dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    dsa.dsa_topk(dev, rows, n, n, None, k, out)
+    torch.cuda.synchronize()
+    a, b = timing_events(2)
+    a.record(stream)
+    for _ in range(reps):
+        dsa.dsa_topk(dev, rows, n, n, None, k, out)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = ms_between(a, b) / reps
+    torch.topk(dev, k, dim=1)
+    torch.cuda.synchronize()
+    a, b = timing_events(2)
+    a.record(stream)
+    for _ in range(reps):
+        torch.topk(dev, k, dim=1)
+    b.record(stream)
+    torch.cuda.synchronize()
+    tms = ms_between(a, b) / reps
+    work = rows * n * 4 + rows * k * 4
+    log(f"topk: {ms:.3f} ms per launch ({work / (ms * 1e-3) / 1e9:.0f} GB/s algorithmic); torch.topk {tms:.3f} ms")
+    del dev, out
+    torch.cuda.empty_cache()
+    return dict(ms=ms, torch_topk_ms=tms, work=work, rows=rows, n=n, k=k)
+
+
 def cpu_baseline(p, seconds=15.0, max_rows=4000, seed=0):
     """The oracle (as is) on a uniform random sample of the workload's rows, for a bounded time."""
     from oracle import dsa_oracle as O
@@ -220,8 +260,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="prefill only (no dense/decode/varlen/cpu)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--only", choices=["decode"], default=None,
-                    help="profiling aid: run only the decode measurement and print its figures")
+    ap.add_argument("--only", choices=["decode", "topk"], default=None,
+                    help="profiling aid: run only the decode (or standalone top-k) measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -245,6 +285,9 @@ def main():
         return
     if args.only == "decode":
         print(json.dumps(bench_decode()), flush=True)
+        return
+    if args.only == "topk":
+        print(json.dumps(bench_topk_general()), flush=True)
         return
     name = args.workload or workloads.P128K
     w = workloads.WORKLOADS[name]
@@ -314,6 +357,11 @@ def main():
                           "dense_us": round(dec["dense_us"], 2),
                           "ratio_dsa_over_dense": round(dec["us_mean"] / dec["dense_us"], 4),
                           "workload": workloads.DECODE}
+        tk = bench_topk_general()
+        line["topk_general"] = {"workload": workloads.TOPK, "ms": round(tk["ms"], 3),
+                                "roofline": roof("hbm", tk["work"] / (tk["ms"] * 1e-3), PEAK_HBM, "GB/s", None,
+                                                 tk["work"], "byte"),
+                                "torch_topk_ms_context": round(tk["torch_topk_ms"], 3)}
         vl = bench_prefill(workloads.VARLEN, max(1, args.steps - 1), 1, with_dense=False)
         line["varlen"] = {"workload": workloads.VARLEN, "tokens_per_s": round(vl["T"] / (vl["ms"] * 1e-3), 1),
                           "ms": round(vl["ms"], 3), "lengths": vl["lengths"]}

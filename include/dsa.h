@@ -178,6 +178,21 @@ int dense_decode_attention(const dsa_decode_shape* shape, const uint16_t* q,
                            const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Standalone deterministic top-k
+ * ------------------------------------------------------------------------------------- */
+
+/* The deterministic replacement of torch.topk in the DSA selection (summary page section 八),
+ * as an op over arbitrary float32 rows.  Row r of scores (DEVICE fp32) starts at
+ * scores + r*ld and holds n candidates, or its first row_lens[r] (DEVICE int32 [rows],
+ * nullable; clamped to [0, n]).  NaN (any payload) and -inf are never selected; +0 and -0 are
+ * equal.  out (DEVICE int32 [rows, k]) receives the first min(k, #selectable) positions in
+ * the order (score descending, index ascending), written in ascending position order and
+ * padded with -1.  Deterministic (no float atomics), no workspace, enqueued on `stream`.
+ * rows == 0 is a no-op; n == 0 writes all -1.  Requires 1 <= k <= 2^24 and ld >= n. */
+int dsa_topk(const float* scores, int64_t rows, int32_t n, int64_t ld, const int32_t* row_lens,
+             int32_t k, int32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

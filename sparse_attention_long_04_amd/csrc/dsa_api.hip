@@ -27,6 +27,8 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
                                    int mode, const int32_t* cu, int nseq, const int32_t* cache_lens, int cap,
                                    int64_t rows, int Hq, int Hkv, float scale, int keys_per_split, int nsplit,
                                    uint16_t* out, float* o_part, float2* ml_part, hipStream_t st);
+hipError_t launch_topk_general(const float* scores, int64_t rows, int n, int64_t ld, const int32_t* lens, int K,
+                               int32_t* out, hipStream_t st);
 hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu, int Hq,
                                 int Hkv, float scale, const int2* sched, const int* count, int nb_bound,
                                 uint16_t* out, hipStream_t st);
@@ -468,6 +470,16 @@ int dense_decode_attention(const dsa_decode_shape* s, const uint16_t* q, const u
                                             s->cache_capacity, s->batch, s->q_heads, s->kv_heads, s->softmax_scale,
                                             kDecodeDenseSplit, L.nsplit_dense, out, at<float>(ws, L.opart),
                                             at<float2>(ws, L.mlpart), static_cast<hipStream_t>(stream)));
+}
+
+int dsa_topk(const float* scores, int64_t rows, int32_t n, int64_t ld, const int32_t* row_lens, int32_t k,
+             int32_t* out, void* stream) {
+  if (rows < 0 || rows > 0x7FFFFFFF || n < 0 || k < 1 || k > (1 << 24)) return DSA_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return DSA_OK;
+  if (!out || (n > 0 && (!scores || ld < n))) return DSA_ERR_INVALID_ARGUMENT;
+  if (rows * (int64_t)k > (int64_t(1) << 40)) return DSA_ERR_UNSUPPORTED;
+  return hip_status(launch_topk_general(scores, rows, n, n > 0 ? ld : 0, row_lens, k, out,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -681,6 +681,243 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_final_kernel(
   ordered_emit(ls, total, prefix, krem, [&](int slot, uint32_t, int id) { orow[slot] = id; }, sm.s);
 }
 
+// ------------------------------------------------------------------------------------------
+// Standalone top-k over general float32 rows (the deterministic stand-in for torch.topk).
+// NaN (any payload) and -inf are masked: key 0.  Every other value keeps its order-preserving
+// key, which is >= 0x00800000 (the key of -FLT_MAX), so the top 11-bit digit of a selectable
+// key is >= 4 and digit 0 counts masked elements only.
+// One workgroup per row, each wave owning a contiguous quarter of it:
+//   pass 1   per-wave histograms of the top digit -> #selectable, threshold digit d1;
+//   pass 1b  only when digit d1 would leave too many candidates for LDS: per-wave histograms of
+//            the second digit among elements whose top digit is d1 (threshold now 22 bits);
+//   pass 2   ordered compaction of every key >= the threshold prefix into an LDS list;
+//   finish   radix select of the remaining digits on the list, ordered emit to the output.
+// Rows with more candidates than the list holds even after pass 1b (massive ties) run the
+// remaining digits and the emit over HBM.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t general_key(float x) {
+  return (x != x || x == -__builtin_inff()) ? 0u : score_key(x);
+}
+
+struct GenRowSrc {
+  const float* __restrict__ row;
+  bool vec;  // 16-byte aligned
+  __device__ __forceinline__ void quad(int n, int s0, uint32_t* keys, int* ids) const {
+    if (vec && s0 + 3 < n) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(row + s0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) keys[e] = general_key(v[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) keys[e] = (s0 + e < n) ? general_key(row[s0 + e]) : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ids[e] = s0 + e;
+  }
+};
+
+constexpr int kGenListCap = 4096;
+
+struct TopkGenSmem {
+  TopkSmem s;
+  union {
+    int whist[kTopkWaves][kBins];  // per-wave digit histograms
+    struct {
+      uint32_t lkeys[kGenListCap];  // candidate list (index order)
+      int lids[kGenListCap];
+    } l;
+  } u;
+  int wcnt[kTopkWaves];
+  int woff[kTopkWaves];
+};
+
+// One wave step of kQ float4 per lane over [base, base + 256 kQ); slots at or past hi are 0.
+template <bool VEC>
+__device__ __forceinline__ void gen_load_step(const float* __restrict__ row, int base, int hi, int lane,
+                                              f32x4 (&v)[kQ]) {
+#pragma unroll
+  for (int e = 0; e < kQ; ++e) {
+    const int i = base + 4 * (lane + 64 * e);
+    if (VEC && i + 3 < hi) {
+      v[e] = *reinterpret_cast<const f32x4*>(row + i);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[e][j] = (i + j < hi) ? row[i + j] : 0.f;
+    }
+  }
+}
+
+// Per-wave histogram over [lo, hi): bin = dig(key), skipped when negative.
+template <bool VEC, class Dig>
+__device__ __forceinline__ void gen_wave_hist(const float* __restrict__ row, int lo, int hi, int lane, int* wh,
+                                              Dig dig) {
+  for (int base = lo; base < hi; base += 256 * kQ) {
+    f32x4 v[kQ];
+    gen_load_step<VEC>(row, base, hi, lane, v);
+#pragma unroll
+    for (int e = 0; e < kQ; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (base + 4 * (lane + 64 * e) + j < hi) {
+          const int d = dig(general_key(v[e][j]));
+          if (d >= 0) atomicAdd(&wh[d], 1);
+        }
+  }
+}
+
+// Per-wave ordered compaction over [lo, hi) of the elements with keep(key): put(slot, key, id)
+// with slots counting up from pos in index order.
+template <bool VEC, class Keep, class Put>
+__device__ __forceinline__ void gen_wave_compact(const float* __restrict__ row, int lo, int hi, int lane, int pos,
+                                                 Keep keep_fn, Put put) {
+  for (int base = lo; base < hi; base += 256 * kQ) {
+    f32x4 v[kQ];
+    gen_load_step<VEC>(row, base, hi, lane, v);
+#pragma unroll
+    for (int e = 0; e < kQ; ++e) {
+      const int i0 = base + 4 * (lane + 64 * e);
+      bool keep[4];
+      uint32_t key[4];
+      int before = 0, total = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        key[j] = general_key(v[e][j]);
+        keep[j] = (i0 + j < hi) && keep_fn(key[j]);
+        const uint64_t bm = __ballot(keep[j]);
+        before += lanes_below(bm);
+        total += __popcll(bm);
+      }
+      int slot = pos + before;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (keep[j]) put(slot++, key[j], i0 + j);
+      pos += total;
+    }
+  }
+}
+
+// Sum the per-wave histograms into sm.s.hist.
+__device__ __forceinline__ void gen_merge_hist(TopkGenSmem& sm) {
+  for (int b = threadIdx.x; b < kBins; b += kTopkThreads) {
+    int a = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) a += sm.u.whist[w][b];
+    sm.s.hist[b] = a;
+  }
+  __syncthreads();
+}
+
+// Per-wave counts of the bins [from, kBins) into sm.wcnt (added), then exclusive offsets in
+// sm.woff and the total in sm.s.list_n.
+__device__ __forceinline__ void gen_wave_counts(TopkGenSmem& sm, int from, bool add) {
+  const int lane = threadIdx.x & 63;
+  int c[kTopkWaves];
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) c[w] = 0;
+  for (int b = from + threadIdx.x; b < kBins; b += kTopkThreads)
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) c[w] += sm.u.whist[w][b];
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) c[w] = wave_sum_i(c[w]);
+  if (!add && threadIdx.x < kTopkWaves) sm.wcnt[threadIdx.x] = 0;
+  __syncthreads();
+  if (lane == 0)
+#pragma unroll
+    for (int w = 0; w < kTopkWaves; ++w) atomicAdd(&sm.wcnt[w], c[w]);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int acc = 0;
+    for (int w = 0; w < kTopkWaves; ++w) {
+      sm.woff[w] = acc;
+      acc += sm.wcnt[w];
+    }
+    sm.s.list_n = acc;
+  }
+  __syncthreads();
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kTopkThreads) void topk_general_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                    int n_all, const int32_t* __restrict__ lens,
+                                                                    int K, int32_t* __restrict__ out) {
+  __shared__ TopkGenSmem sm;
+  const int64_t r = blockIdx.x;
+  const float* __restrict__ row = scores + r * ld;
+  const int n = lens ? max(0, min(n_all, lens[r])) : n_all;
+  int32_t* __restrict__ orow = out + r * K;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int seg = (((n + kTopkWaves - 1) / kTopkWaves) + 3) & ~3;
+  const int seg_lo = min(n, w * seg), seg_hi = min(n, seg_lo + seg);
+
+  // pass 1: top digit
+  for (int i = tid; i < kTopkWaves * kBins; i += kTopkThreads) (&sm.u.whist[0][0])[i] = 0;
+  __syncthreads();
+  gen_wave_hist<VEC>(row, seg_lo, seg_hi, lane, sm.u.whist[w], [](uint32_t k) { return int(k >> 21); });
+  __syncthreads();
+  gen_merge_hist(sm);
+  const int nvalid = n - sm.s.hist[0];
+  const int kp = min(K, nvalid);
+  if (kp == nvalid) {
+    // every selectable element is kept: compact them straight into the output
+    gen_wave_counts(sm, 1, false);
+    gen_wave_compact<VEC>(row, seg_lo, seg_hi, lane, sm.woff[w], [](uint32_t k) { return k != 0u; },
+                          [&](int slot, uint32_t, int id) { orow[slot] = id; });
+  } else {
+    find_digit(sm.s, kBins, kp);
+    const int d1 = sm.s.sel_digit;
+    int krem = kp - sm.s.sel_above;
+    uint32_t prefix = uint32_t(d1) << 21, hmask = 0x7FFu << 21;
+    int d0 = 1;
+    gen_wave_counts(sm, d1, false);  // candidates per wave: top digit >= d1
+    if (sm.s.list_n > kGenListCap) {
+      // pass 1b: refine inside digit d1 with the second digit
+      gen_wave_counts(sm, d1 + 1, false);  // keep only the surely-kept part (top digit > d1)
+      for (int i = tid; i < kTopkWaves * kBins; i += kTopkThreads) (&sm.u.whist[0][0])[i] = 0;
+      __syncthreads();
+      gen_wave_hist<VEC>(row, seg_lo, seg_hi, lane, sm.u.whist[w],
+                         [d1](uint32_t k) { return int(k >> 21) == d1 ? int((k >> 10) & 0x7FFu) : -1; });
+      __syncthreads();
+      gen_merge_hist(sm);
+      find_digit(sm.s, kBins, krem);
+      const int d2 = sm.s.sel_digit;
+      krem -= sm.s.sel_above;
+      prefix |= uint32_t(d2) << 10;
+      hmask |= 0x7FFu << 10;
+      d0 = 2;
+      gen_wave_counts(sm, d2, true);  // + elements of digit d1 whose second digit >= d2
+    }
+    const int cand = sm.s.list_n;
+    if (cand <= kGenListCap) {
+      // pass 2: every key >= prefix (higher bits above the threshold, or equal so far)
+      gen_wave_compact<VEC>(row, seg_lo, seg_hi, lane, sm.woff[w], [prefix](uint32_t k) { return k >= prefix; },
+                            [&](int slot, uint32_t key, int id) {
+                              sm.u.l.lkeys[slot] = key;
+                              sm.u.l.lids[slot] = id;
+                            });
+      __syncthreads();
+      const ListSrc ls{sm.u.l.lkeys, sm.u.l.lids};
+      radix_rest(ls, cand, d0, prefix, hmask, krem, sm.s);
+      ordered_emit(ls, cand, prefix, krem, [&](int slot, uint32_t, int id) { orow[slot] = id; }, sm.s);
+    } else {
+      const GenRowSrc src{row, VEC};
+      radix_rest(src, n, d0, prefix, hmask, krem, sm.s);
+      ordered_emit(src, n, prefix, krem, [&](int slot, uint32_t, int id) { orow[slot] = id; }, sm.s);
+    }
+  }
+  for (int s2 = kp + tid; s2 < K; s2 += kTopkThreads) orow[s2] = -1;
+}
+
+hipError_t launch_topk_general(const float* scores, int64_t rows, int n, int64_t ld, const int32_t* lens, int K,
+                               int32_t* out, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const bool vec = (reinterpret_cast<uintptr_t>(scores) & 15) == 0 && ld % 4 == 0;
+  if (vec)
+    topk_general_kernel<true><<<(unsigned)rows, kTopkThreads, 0, st>>>(scores, ld, n, lens, K, out);
+  else
+    topk_general_kernel<false><<<(unsigned)rows, kTopkThreads, 0, st>>>(scores, ld, n, lens, K, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_prefill(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq,
                                int64_t T, int K, const float2* rowrange, int32_t* out, hipStream_t st) {
   if (T == 0) return hipSuccess;

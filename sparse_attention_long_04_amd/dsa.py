@@ -60,6 +60,8 @@ EXPORTS = {
     "dense_decode_attention": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "dsa_prefill_timed": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "dsa_decode_timed": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "dsa_topk": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
 }
 
 
@@ -223,3 +225,9 @@ def dsa_decode_timed(shape, q_idx, w_idx, q, k_idx_cache, k_cache, v_cache, out,
     _check(lib().dsa_decode_timed(ctypes.byref(shape), _ptr(q_idx), _ptr(w_idx), _ptr(q), _ptr(k_idx_cache),
                                   _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(topk_idx), _ptr(workspace),
                                   _nbytes(workspace), _stream(stream), ev), "dsa_decode_timed")
+
+
+def dsa_topk(scores, rows, n, ld, row_lens, k, out, stream=None):
+    """Standalone deterministic top-k: scores fp32 rows (row r at scores + r*ld), out int32 [rows, k]."""
+    _check(lib().dsa_topk(_ptr(scores), int(rows), int(n), int(ld), _ptr(row_lens), int(k), _ptr(out),
+                          _stream(stream)), "dsa_topk")

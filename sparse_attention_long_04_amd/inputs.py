@@ -288,3 +288,47 @@ def make_decode(batch, ctx_len, capacity, steps, *, idx_heads, idx_dim, idx_dtyp
     return DecodeInputs(batch, capacity, ctx_len, idx_heads, idx_dim, idx_dtype, int(topk),
                         1.0 / math.sqrt(head_dim), kc, kk, vv, q_heads, kv_heads, head_dim,
                         idx_range, seed, list(s_steps.spawn(steps)))
+
+
+def make_topk_scores(rows: int, n: int, *, seed: int, kind: str = "normal", masked: float = 0.0,
+                     nans: float = 0.0, infs: float = 0.0, zeros: float = 0.0) -> np.ndarray:
+    """float32 score rows [rows, n] for the standalone top-k.
+
+    kind: "normal" (N(0,1)), "ties" (integers in {-3..3} / 2: few distinct values),
+    "narrow" (1 + U[0, 0.25): one exponent, distinct low bits), "const" (all 1.5).
+    Then, independently per element: a fraction ``masked`` becomes -inf, ``nans`` NaN (random
+    sign and payload), ``infs`` +inf and ``zeros`` a signed zero."""
+    out = np.empty((rows, n), dtype=np.float32)
+    parts = _chunks(rows, max(n, 1))
+    kids = np.random.SeedSequence(seed).spawn(len(parts))
+
+    def work(i, r0, r1):
+        g = np.random.Generator(np.random.PCG64(kids[i]))
+        shape = (r1 - r0, n)
+        if kind == "normal":
+            x = g.standard_normal(size=shape, dtype=np.float32)
+        elif kind == "ties":
+            x = g.integers(-3, 4, size=shape).astype(np.float32) / np.float32(2)
+        elif kind == "narrow":
+            x = np.float32(1) + g.random(size=shape, dtype=np.float32) * np.float32(0.25)
+        elif kind == "const":
+            x = np.full(shape, 1.5, dtype=np.float32)
+        else:
+            raise ValueError(kind)
+        if masked:
+            x[g.random(size=shape) < masked] = -np.inf
+        if nans:
+            m = g.random(size=shape) < nans
+            bits = (g.integers(0, 1 << 22, size=int(m.sum()), dtype=np.uint32) | np.uint32(0x7FC00000)
+                    | (g.integers(0, 2, size=int(m.sum()), dtype=np.uint32) << np.uint32(31)))
+            x[m] = bits.view(np.float32)
+        if infs:
+            x[g.random(size=shape) < infs] = np.inf
+        if zeros:
+            m = g.random(size=shape) < zeros
+            x[m] = np.where(g.random(size=int(m.sum())) < 0.5, np.float32(-0.0), np.float32(0.0))
+        out[r0:r1] = x
+
+    if n > 0:
+        _par(work, [(i, a, b) for i, (a, b) in enumerate(parts)])
+    return out

@@ -15,6 +15,7 @@ P32K = "prefill_32k"
 P128K = "prefill_128k_video"
 DECODE = "decode_16x128k_video"
 VARLEN = "varlen_256k_video"
+TOPK = "topk_2048x131072"
 
 WORKLOADS = {
     TINY: dict(kind="prefill", lengths=[2048], idx_heads=16, idx_dim=64, idx_dtype="bf16",
@@ -27,6 +28,8 @@ WORKLOADS = {
                  idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=2048, video=True, seed=1003),
     VARLEN: dict(kind="prefill", lengths=None, n_seqs=6, total=262144, idx_heads=64, idx_dim=128,
                  idx_dtype="fp8_e4m3", idx_range=4, topk=2048, video=True, seed=1004),
+    # standalone top-k: 2048 rows x 131072 N(0,1) fp32 scores, 1% masked with -inf, k = 2048
+    TOPK: dict(kind="topk", rows=2048, n=131072, topk=2048, masked=0.01, seed=1005),
 }
 
 
@@ -40,6 +43,8 @@ def lengths_of(name: str):
 def make(name: str, lengths=None):
     """Build the inputs of a named workload (``lengths`` overrides the sequence lengths)."""
     w = WORKLOADS[name]
+    if w["kind"] == "topk":
+        return inputs.make_topk_scores(w["rows"], w["n"], seed=w["seed"], masked=w["masked"])
     if w["kind"] == "decode":
         return inputs.make_decode(w["batch"], w["ctx_len"], w["capacity"], w["steps"],
                                   idx_heads=w["idx_heads"], idx_dim=w["idx_dim"],

@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["dsa_index_topk", "dsa_prefill", "dsa_decode", "dense_causal_attention", "dsa_sparse_attention",
               "dense_decode_attention", "dsa_kv_append", "dsa_index_scores", "dsa_prefill_workspace_size",
-              "dsa_decode_workspace_size", "dsa_status_string", "dsa_last_hip_error"]:
+              "dsa_decode_workspace_size", "dsa_status_string", "dsa_last_hip_error", "dsa_topk"]:
         assert n in names
 
 
@@ -149,3 +149,24 @@ def test_empty_prefill_batch_is_a_noop_with_null_pointers():
                lambda: dsa.dsa_sparse_attention(s, None, None, None, None, None, stream=0),
                lambda: dsa.dense_causal_attention(s, None, None, None, None, None, stream=0)):
         fn()
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(rows=4, n=100, ld=100, k=0), 1),          # k < 1
+    (dict(rows=-1, n=100, ld=100, k=8), 1),         # negative rows
+    (dict(rows=4, n=-3, ld=100, k=8), 1),           # negative n
+    (dict(rows=4, n=100, ld=99, k=8), 1),           # row stride shorter than the row
+    (dict(rows=4, n=100, ld=100, k=8, scores=None), 1),
+    (dict(rows=4, n=100, ld=100, k=8, out=None), 1),
+    (dict(rows=1 << 31, n=100, ld=100, k=8), 1),    # more rows than one launch takes
+])
+def test_topk_rejects_bad_arguments_before_launch(args, code):
+    a = dict(scores=FAKE, row_lens=None, out=FAKE)
+    a.update(args)
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_topk(a["scores"], a["rows"], a["n"], a["ld"], a["row_lens"], a["k"], a["out"], stream=0)
+    assert ei.value.status == code
+
+
+def test_topk_zero_rows_is_a_noop_with_null_pointers():
+    dsa.dsa_topk(None, 0, 100, 100, None, 16, None, stream=0)

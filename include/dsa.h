@@ -133,6 +133,31 @@ int dsa_prefill_timed(const dsa_prefill_shape* shape, const void* q_idx, const v
                       uint16_t* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
                       void* stream, void* const* events);
 
+/* ---------------------------------------------------------------------------------------
+ * Adjacent-query dedup (summary page section 八: the top-k sets of adjacent queries overlap,
+ * so each block of 16 adjacent rows attends over the union of its rows' sets once, with a
+ * per-(row, key) mask).  Same results as dsa_sparse_attention / dsa_prefill up to the order of
+ * fp32 sums; fastest when adjacent rows' selections overlap.  Needs Hq/Hkv in {2, 4, 8, 16}
+ * (DSA_ERR_UNSUPPORTED otherwise).  A separate "dedup workspace" (DEVICE, 16-byte aligned)
+ * holds the block schedule and the unions (about T * k * 6 bytes).
+ * ------------------------------------------------------------------------------------- */
+
+/* Dedup workspace bytes for this shape (host only). */
+int dsa_dedup_workspace_size(const dsa_prefill_shape* shape, size_t* bytes);
+
+/* dsa_sparse_attention through the union of each 16-row block's index sets. */
+int dsa_sparse_attention_dedup(const dsa_prefill_shape* shape, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const int32_t* topk_idx, uint16_t* out,
+                               void* dedup_workspace, size_t dedup_workspace_bytes, void* stream);
+
+/* dsa_prefill whose attention stage runs through the unions.  events (nullable): as
+ * dsa_prefill_timed, 4 caller-created hipEvent_t recorded after each stage. */
+int dsa_prefill_dedup(const dsa_prefill_shape* shape, const void* q_idx, const void* k_idx,
+                      const float* w_idx, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      uint16_t* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
+                      void* dedup_workspace, size_t dedup_workspace_bytes, void* stream,
+                      void* const* events);
+
 /* Standard full causal GQA attention (the cost reference of summary page section 一), same
  * tensors as dsa_sparse_attention without indices.  Uses the prefill workspace. */
 int dense_causal_attention(const dsa_prefill_shape* shape, const uint16_t* q, const uint16_t* k,

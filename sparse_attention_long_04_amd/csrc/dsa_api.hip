@@ -27,6 +27,12 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
                                    int mode, const int32_t* cu, int nseq, const int32_t* cache_lens, int cap,
                                    int64_t rows, int Hq, int Hkv, float scale, int keys_per_split, int nsplit,
                                    uint16_t* out, float* o_part, float2* ml_part, hipStream_t st);
+hipError_t launch_union(const int32_t* idx, int K, const int32_t* cu, const int2* sched, const int* count,
+                        int nb_bound, int64_t ustride, int32_t* ukeys, uint16_t* umask, int* ucount, hipStream_t st);
+hipError_t launch_dedup_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu, int Hq,
+                                  int Hkv, float scale, const int2* sched, const int* count, int nb_bound,
+                                  int64_t ustride, const int32_t* ukeys, const uint16_t* umask, const int* ucount,
+                                  uint16_t* out, hipStream_t st);
 hipError_t launch_topk_general(const float* scores, int64_t rows, int n, int64_t ld, const int32_t* lens, int K,
                                int32_t* out, hipStream_t st);
 hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu, int Hq,
@@ -175,6 +181,33 @@ int run_index_scores_tri(const dsa_prefill_shape* s, const void* q_idx, const vo
   return hip_status(e);
 }
 
+// Dedup workspace layout (adjacent-query union per 16-row block; 256-byte aligned):
+//   counts int[64] | sched16 int2[nb16] | ucount int[nb16] | ukeys int32[nb16][16k] | umask uint16[nb16][16k]
+struct DedupWs {
+  size_t counts, sched16, ucount, ukeys, umask, total;
+  int nb16;
+  int64_t ustride;
+};
+
+DedupWs dedup_layout(const dsa_prefill_shape* s) {
+  DedupWs w{};
+  w.nb16 = int((s->total_tokens + 15) / 16 + s->num_seqs);
+  w.ustride = 16 * int64_t(s->topk);
+  size_t off = 0;
+  w.counts = off; off = align_up(off + 64 * sizeof(int), 256);
+  w.sched16 = off; off = align_up(off + size_t(w.nb16) * sizeof(int2), 256);
+  w.ucount = off; off = align_up(off + size_t(w.nb16) * sizeof(int), 256);
+  w.ukeys = off; off = align_up(off + size_t(w.nb16) * size_t(w.ustride) * sizeof(int32_t), 256);
+  w.umask = off; off = align_up(off + size_t(w.nb16) * size_t(w.ustride) * sizeof(uint16_t), 256);
+  w.total = off;
+  return w;
+}
+
+bool dedup_supported(const dsa_prefill_shape* s) {
+  const int G = s->q_heads / s->kv_heads;
+  return G == 2 || G == 4 || G == 8 || G == 16;
+}
+
 int check_prefill_ws(const dsa_prefill_shape* s, void* ws, size_t ws_bytes, PrefillWs* L) {
   *L = prefill_layout(s, nullptr);
   if (!ws || !aligned16(ws)) return DSA_ERR_INVALID_ARGUMENT;
@@ -305,11 +338,36 @@ int record(void* const* ev, int i, hipStream_t st) {
   return hip_status(hipEventRecord(static_cast<hipEvent_t>(ev[i]), st));
 }
 
+// Union + masked attention over given indices, with a 16-row block schedule already built.
+int dedup_attention(const dsa_prefill_shape* s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const int32_t* idx, uint16_t* out, const int2* sched16, const int* count, int nb16,
+                    void* dws, const DedupWs& D, hipStream_t st) {
+  int rc;
+  if ((rc = hip_status(launch_union(idx, s->topk, s->cu_seqlens, sched16, count, nb16, D.ustride,
+                                    at<int32_t>(dws, D.ukeys), at<uint16_t>(dws, D.umask), at<int>(dws, D.ucount),
+                                    st))))
+    return rc;
+  return hip_status(launch_dedup_attention(q, k, v, s->cu_seqlens, s->q_heads, s->kv_heads, s->softmax_scale,
+                                           sched16, count, nb16, D.ustride, at<int32_t>(dws, D.ukeys),
+                                           at<uint16_t>(dws, D.umask), at<int>(dws, D.ucount), out, st));
+}
+
+int check_dedup_ws(const dsa_prefill_shape* s, void* dws, size_t dws_bytes, DedupWs* D) {
+  if (!dedup_supported(s)) return DSA_ERR_UNSUPPORTED;
+  *D = dedup_layout(s);
+  if (!dws || !aligned16(dws)) return DSA_ERR_INVALID_ARGUMENT;
+  if (dws_bytes < D->total) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  return DSA_OK;
+}
+
 int prefill_impl(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
                  const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int32_t* topk_idx,
-                 void* ws, size_t ws_bytes, void* stream, void* const* ev) {
+                 void* ws, size_t ws_bytes, void* stream, void* const* ev, void* dws = nullptr,
+                 size_t dws_bytes = 0, bool dedup = false) {
   int rc = check_prefill(s, true);
   if (rc) return rc;
+  DedupWs D{};
+  if (dedup && s->total_tokens > 0 && (rc = check_dedup_ws(s, dws, dws_bytes, &D))) return rc;
   if (s->total_tokens == 0) {  // empty batch: nothing to compute, pointers may be null
     for (int i = 0; i < 4 && ev; ++i)
       if ((rc = record(ev, i, static_cast<hipStream_t>(stream)))) return rc;
@@ -338,10 +396,15 @@ int prefill_impl(const dsa_prefill_shape* s, const void* q_idx, const void* k_id
                                            s->num_seqs, s->total_tokens, s->topk, at<float2>(ws, L.rowrange), idx, st))))
     return rc;
   if ((rc = record(ev, 2, st))) return rc;
-  if ((rc = hip_status(launch_gather_attention(q, k, v, idx, s->topk, 0, s->cu_seqlens, s->num_seqs, nullptr, 0,
-                                               s->total_tokens, s->q_heads, s->kv_heads, s->softmax_scale, 1 << 30,
-                                               1, out, nullptr, nullptr, st))))
+  if (dedup) {
+    if ((rc = dedup_attention(s, q, k, v, idx, out, at<int2>(ws, L.sched16), at<int>(ws, L.counts), L.nb16, dws, D,
+                              st)))
+      return rc;
+  } else if ((rc = hip_status(launch_gather_attention(q, k, v, idx, s->topk, 0, s->cu_seqlens, s->num_seqs, nullptr,
+                                                      0, s->total_tokens, s->q_heads, s->kv_heads, s->softmax_scale,
+                                                      1 << 30, 1, out, nullptr, nullptr, st)))) {
     return rc;
+  }
   return record(ev, 3, st);
 }
 
@@ -390,6 +453,39 @@ int dsa_prefill_timed(const dsa_prefill_shape* s, const void* q_idx, const void*
                       void* ws, size_t ws_bytes, void* stream, void* const* events) {
   if (!events) return DSA_ERR_INVALID_ARGUMENT;
   return prefill_impl(s, q_idx, k_idx, w_idx, q, k, v, out, topk_idx, ws, ws_bytes, stream, events);
+}
+
+int dsa_dedup_workspace_size(const dsa_prefill_shape* s, size_t* bytes) {
+  if (!bytes) return DSA_ERR_INVALID_ARGUMENT;
+  int rc = check_prefill(s, false);
+  if (rc) return rc;
+  if (!dedup_supported(s)) return DSA_ERR_UNSUPPORTED;
+  *bytes = dedup_layout(s).total;
+  return DSA_OK;
+}
+
+int dsa_sparse_attention_dedup(const dsa_prefill_shape* s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const int32_t* topk_idx, uint16_t* out, void* dws, size_t dws_bytes, void* stream) {
+  int rc = check_prefill(s, false);
+  if (rc) return rc;
+  if (s->total_tokens == 0) return DSA_OK;
+  if (!q || !k || !v || !topk_idx || !out) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return DSA_ERR_INVALID_ARGUMENT;
+  DedupWs D;
+  if ((rc = check_dedup_ws(s, dws, dws_bytes, &D))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_build_schedule(s->cu_seqlens, s->num_seqs, 16, D.nb16, at<int2>(dws, D.sched16),
+                                       at<int>(dws, D.counts), nullptr, st);
+  if (e != hipSuccess) return hip_status(e);
+  return dedup_attention(s, q, k, v, topk_idx, out, at<int2>(dws, D.sched16), at<int>(dws, D.counts), D.nb16, dws, D,
+                         st);
+}
+
+int dsa_prefill_dedup(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
+                      const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out, int32_t* topk_idx,
+                      void* ws, size_t ws_bytes, void* dws, size_t dws_bytes, void* stream, void* const* events) {
+  return prefill_impl(s, q_idx, k_idx, w_idx, q, k, v, out, topk_idx, ws, ws_bytes, stream, events, dws, dws_bytes,
+                      true);
 }
 
 int dense_causal_attention(const dsa_prefill_shape* s, const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -60,6 +60,9 @@ EXPORTS = {
     "dense_decode_attention": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "dsa_prefill_timed": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "dsa_decode_timed": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "dsa_dedup_workspace_size": ([ctypes.POINTER(PrefillShape), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "dsa_sparse_attention_dedup": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "dsa_prefill_dedup": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "dsa_topk": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
                   ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
 }
@@ -231,3 +234,25 @@ def dsa_topk(scores, rows, n, ld, row_lens, k, out, stream=None):
     """Standalone deterministic top-k: scores fp32 rows (row r at scores + r*ld), out int32 [rows, k]."""
     _check(lib().dsa_topk(_ptr(scores), int(rows), int(n), int(ld), _ptr(row_lens), int(k), _ptr(out),
                           _stream(stream)), "dsa_topk")
+
+
+def dsa_dedup_workspace_size(shape: PrefillShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().dsa_dedup_workspace_size(ctypes.byref(shape), ctypes.byref(n)), "dsa_dedup_workspace_size")
+    return n.value
+
+
+def dsa_sparse_attention_dedup(shape, q, k, v, topk_idx, out, dedup_workspace, stream=None):
+    _check(lib().dsa_sparse_attention_dedup(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(topk_idx), _ptr(out),
+                                            _ptr(dedup_workspace), _nbytes(dedup_workspace), _stream(stream)),
+           "dsa_sparse_attention_dedup")
+
+
+def dsa_prefill_dedup(shape, q_idx, k_idx, w_idx, q, k, v, out, topk_idx, workspace, dedup_workspace, events=None,
+                      stream=None):
+    """``events``: None, or 4 recorded-once timing events (as dsa_prefill_timed)."""
+    ev = None if events is None else _events(events)
+    _check(lib().dsa_prefill_dedup(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(k),
+                                   _ptr(v), _ptr(out), _ptr(topk_idx), _ptr(workspace), _nbytes(workspace),
+                                   _ptr(dedup_workspace), _nbytes(dedup_workspace), _stream(stream), ev),
+           "dsa_prefill_dedup")

@@ -192,23 +192,71 @@ class PrefillInputs:
         return int(self.lengths.max()) if len(self.lengths) else 0
 
 
+def _drifting_query_codes(ss: np.random.SeedSequence, lengths, idx_heads, idx_dim, idx_fmt, rho,
+                          rank=16) -> np.ndarray:
+    """Indexer queries that drift slowly along each sequence: a rank-``rank`` latent AR(1)
+    process z_t = rho z_{t-1} + sqrt(1 - rho^2) e_t (z_0 = e_0, e ~ N(0, I)) mapped through a
+    fixed Gaussian matrix M [rank, H_I d_I] / sqrt(rank), so every coordinate is N(0, 1) with
+    lag-1 correlation rho; codes = clamp(rint(2x), -4, 4), as for the keys."""
+    from scipy.signal import lfilter
+    T = int(sum(lengths))
+    D = idx_heads * idx_dim
+    kids = ss.spawn(len(lengths) + 1)
+    gm = np.random.Generator(np.random.PCG64(kids[-1]))
+    M = gm.standard_normal(size=(rank, D), dtype=np.float32) / np.float32(math.sqrt(rank))
+    z = np.empty((T, rank), dtype=np.float32)
+    off = 0
+    for s, L in enumerate(lengths):
+        if L:
+            g = np.random.Generator(np.random.PCG64(kids[s]))
+            e = g.standard_normal(size=(L, rank))
+            zz = np.empty_like(e)
+            zz[0] = e[0]
+            if L > 1:
+                zz[1:] = lfilter([math.sqrt(1.0 - rho * rho)], [1.0, -rho], e[1:], axis=0,
+                                 zi=(rho * e[0])[None, :])[0]
+            z[off:off + L] = zz
+        off += L
+    table = _int_code_table(idx_fmt, 4)
+    out = np.empty((T, D), dtype=_fmt_np_dtype(idx_fmt))
+
+    def work(a, b):
+        x = z[a:b] @ M
+        out[a:b] = table[np.clip(np.rint(np.float32(2.0) * x), -4, 4).astype(np.int64) + 4]
+
+    step = 4096
+    _par(work, [(a, min(T, a + step)) for a in range(0, T, step)])
+    return out.reshape(T, idx_heads, idx_dim)
+
+
 def make_prefill(lengths, *, idx_heads, idx_dim, idx_dtype, idx_range, topk, seed,
                  video=False, q_heads=32, kv_heads=4, head_dim=128,
-                 softmax_scale=None) -> PrefillInputs:
-    """Draw a packed prefill batch.  Draw order: q_idx, k_idx, w, q, k, v."""
+                 softmax_scale=None, query_corr=None) -> PrefillInputs:
+    """Draw a packed prefill batch.  Draw order: q_idx, k_idx, w, q, k, v.
+
+    ``query_corr`` (rho in (0, 1)): indexer queries drift along each sequence
+    (_drifting_query_codes) and the head weights are one 2^-j per head and sequence, so
+    adjacent tokens' selections overlap -- the correlated-query workload."""
     lengths = [int(x) for x in lengths]
     T = sum(lengths)
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
     root = np.random.SeedSequence(seed)
     s_qi, s_ki, s_w, s_q, s_k, s_v = root.spawn(6)
-    q_idx = _fill_int_codes(s_qi, (T, idx_heads, idx_dim), idx_dtype, idx_range)
+    if query_corr is None:
+        q_idx = _fill_int_codes(s_qi, (T, idx_heads, idx_dim), idx_dtype, idx_range)
+    else:
+        q_idx = _drifting_query_codes(s_qi, lengths, idx_heads, idx_dim, idx_dtype, float(query_corr))
     if video:
         k_idx, k = _video_keys(s_ki, lengths, idx_dim, kv_heads, head_dim, idx_dtype)
     else:
         k_idx = _fill_int_codes(s_ki, (T, idx_dim), idx_dtype, idx_range)
         k = None
-    w = _pow2_weights(s_w, (T, idx_heads))
+    if query_corr is None:
+        w = _pow2_weights(s_w, (T, idx_heads))
+    else:
+        per_seq = _pow2_weights(s_w, (len(lengths), idx_heads))
+        w = np.repeat(per_seq, lengths, axis=0).astype(np.float32)
     q = _fill_normal_bf16(s_q, (T, q_heads, head_dim))
     if k is None:
         k = _fill_normal_bf16(s_k, (T, kv_heads, head_dim))

@@ -64,6 +64,22 @@ class PrefillBatch:
         dsa.dense_causal_attention(self.shape, self.q, self.k, self.v, out, self.ws, stream)
         return out
 
+    # --- adjacent-query dedup ----------------------------------------------------------
+    def _dedup_ws(self):
+        if getattr(self, "dws", None) is None:
+            self.dws = torch.empty(max(dsa.dsa_dedup_workspace_size(self.shape), 256), dtype=torch.uint8,
+                                   device=self.device)
+        return self.dws
+
+    def prefill_dedup(self, events=None, stream=None):
+        dsa.dsa_prefill_dedup(self.shape, self.q_idx, self.k_idx, self.w_idx, self.q, self.k, self.v, self.out,
+                              self.topk_idx, self.ws, self._dedup_ws(), events, stream)
+
+    def sparse_attention_dedup(self, out=None, stream=None):
+        out = self.out if out is None else out
+        dsa.dsa_sparse_attention_dedup(self.shape, self.q, self.k, self.v, self.topk_idx, out, self._dedup_ws(), stream)
+        return out
+
     def index_scores(self, stream=None):
         T = self.p.total_tokens
         scores = torch.empty((T, max(1, self.p.max_seqlen)), dtype=torch.float32, device=self.device)

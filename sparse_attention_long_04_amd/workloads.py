@@ -16,6 +16,7 @@ P128K = "prefill_128k_video"
 DECODE = "decode_16x128k_video"
 VARLEN = "varlen_256k_video"
 TOPK = "topk_2048x131072"
+P128K_CORR = "prefill_128k_video_corr"
 
 WORKLOADS = {
     TINY: dict(kind="prefill", lengths=[2048], idx_heads=16, idx_dim=64, idx_dtype="bf16",
@@ -28,6 +29,9 @@ WORKLOADS = {
                  idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=2048, video=True, seed=1003),
     VARLEN: dict(kind="prefill", lengths=None, n_seqs=6, total=262144, idx_heads=64, idx_dim=128,
                  idx_dtype="fp8_e4m3", idx_range=4, topk=2048, video=True, seed=1004),
+    # the 128K video prefill with slowly drifting indexer queries (adjacent-query dedup)
+    P128K_CORR: dict(kind="prefill", lengths=[131072], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3",
+                     idx_range=4, topk=2048, video=True, seed=1006, query_corr=0.95),
     # standalone top-k: 2048 rows x 131072 N(0,1) fp32 scores, 1% masked with -inf, k = 2048
     TOPK: dict(kind="topk", rows=2048, n=131072, topk=2048, masked=0.01, seed=1005),
 }
@@ -53,4 +57,5 @@ def make(name: str, lengths=None):
     return inputs.make_prefill(lengths if lengths is not None else lengths_of(name),
                                idx_heads=w["idx_heads"], idx_dim=w["idx_dim"],
                                idx_dtype=w["idx_dtype"], idx_range=w["idx_range"],
-                               topk=w["topk"], seed=w["seed"], video=w["video"])
+                               topk=w["topk"], seed=w["seed"], video=w["video"],
+                               query_corr=w.get("query_corr"))

@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["dsa_index_topk", "dsa_prefill", "dsa_decode", "dense_causal_attention", "dsa_sparse_attention",
               "dense_decode_attention", "dsa_kv_append", "dsa_index_scores", "dsa_prefill_workspace_size",
-              "dsa_decode_workspace_size", "dsa_status_string", "dsa_last_hip_error", "dsa_topk"]:
+              "dsa_decode_workspace_size", "dsa_status_string", "dsa_last_hip_error", "dsa_topk",
+              "dsa_prefill_dedup", "dsa_sparse_attention_dedup", "dsa_dedup_workspace_size"]:
         assert n in names
 
 
@@ -170,3 +171,20 @@ def test_topk_rejects_bad_arguments_before_launch(args, code):
 
 def test_topk_zero_rows_is_a_noop_with_null_pointers():
     dsa.dsa_topk(None, 0, 100, 100, None, 16, None, stream=0)
+
+
+def test_dedup_workspace_layout_and_unsupported_groups():
+    s = shape(T=4096, max_seqlen=4096, topk=2048)
+    n = dsa.dsa_dedup_workspace_size(s)
+    nb16 = 4096 // 16 + 1
+    assert n >= nb16 * 16 * 2048 * 6
+    assert n < nb16 * 16 * 2048 * 6 + (1 << 20)
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_dedup_workspace_size(shape(q_heads=24, kv_heads=4))   # G = 6
+    assert ei.value.status == 2
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_sparse_attention_dedup(s, FAKE, FAKE, FAKE, FAKE, FAKE, (FAKE, n - 1), stream=0)
+    assert ei.value.status == 3
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_sparse_attention_dedup(s, FAKE, FAKE, FAKE, None, FAKE, (FAKE, n), stream=0)
+    assert ei.value.status == 1

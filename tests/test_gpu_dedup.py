@@ -1,0 +1,103 @@
+"""GPU parity of the adjacent-query dedup path (dsa_prefill_dedup / dsa_sparse_attention_dedup,
+through the C ABI) against the float64 oracle.  The dedup path computes the same sparse
+attention as the gather path -- each row over its own top-k set -- so the oracle is the sparse
+attention oracle, and the bars are the same: selected indices bit-exact, outputs within max-abs
+1e-2 and mean-rel 2e-3."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+from sparse_attention_long_04_amd import inputs as gen
+from sparse_attention_long_04_amd import workloads
+from sparse_attention_long_04_amd.runtime import PrefillBatch, bf16_to_float
+
+from gpu_util import assert_out_close, gpu_available, sample_rows
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _oracle(p):
+    return O.Prefill(p.cu_seqlens, p.q_idx, p.k_idx, p.w_idx, p.q, p.k, p.v, p.idx_dtype, p.topk, p.softmax_scale)
+
+
+CASES = {
+    # name: (lengths, k, query_corr, q_heads, kv_heads)
+    "corr_3k": ([3100], 2048, 0.95, 32, 4),
+    "corr_varlen": ([129, 0, 17, 300, 1000, 1, 2600], 100, 0.95, 32, 4),
+    "iid_2k": ([2200], 256, None, 32, 4),
+    "corr_g16": ([1500, 77], 300, 0.9, 16, 1),
+    "corr_g4": ([1500], 300, 0.9, 16, 4),
+    "corr_g2": ([900], 200, 0.9, 8, 4),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_dedup_prefill_parity(name):
+    lens, k, rho, hq, hkv = CASES[name]
+    p = gen.make_prefill(lens, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=k, seed=71,
+                         video=True, q_heads=hq, kv_heads=hkv, query_corr=rho)
+    print(f"[dedup] {name}: T={p.total_tokens}", flush=True)
+    pb = PrefillBatch(p)
+    pb.prefill_dedup()
+    torch.cuda.synchronize()
+    o = _oracle(p)
+    sel, ref = o.rows(range(p.total_tokens))
+    assert np.array_equal(pb.topk_idx.cpu().numpy(), sel)
+    assert_out_close(bf16_to_float(pb.out), ref, f"dedup {name}")
+
+
+def test_dedup_given_indices_matches_gather_path():
+    """Same indices through both attention paths: both within the bar of the oracle, and close
+    to each other (they differ only in fp32 summation order and the P.V operand precision)."""
+    p = gen.make_prefill([4000], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=2048, seed=72,
+                         video=True, query_corr=0.95)
+    pb = PrefillBatch(p)
+    pb.index_topk()
+    pb.sparse_attention()
+    a = bf16_to_float(pb.out)
+    b = bf16_to_float(pb.sparse_attention_dedup(out=torch.empty_like(pb.out)))
+    rows = np.array([0, 1, 15, 16, 2047, 2048, 2049, 3999])
+    _, ref = _oracle(p).rows(rows)
+    assert_out_close(b[rows], ref, "dedup given indices")
+    assert np.abs(a - b).max() < 1e-2
+
+
+def test_dedup_k_ge_L_equals_dense():
+    p = gen.make_prefill([700, 333], idx_heads=16, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=1024, seed=73,
+                         video=True, query_corr=0.9)
+    pb = PrefillBatch(p)
+    pb.prefill_dedup()
+    out = bf16_to_float(pb.out)
+    dense = bf16_to_float(pb.dense(out=torch.empty_like(pb.out)))
+    assert np.abs(out - dense).max() < 1e-2
+    assert_out_close(out, _oracle(p).dense_rows(range(p.total_tokens)), "dedup k>=L")
+
+
+def test_dedup_is_deterministic():
+    p = gen.make_prefill([3000], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=2048, seed=74,
+                         video=True, query_corr=0.95)
+    pb = PrefillBatch(p)
+    pb.prefill_dedup()
+    a = pb.out.clone()
+    pb.out.zero_()
+    pb.prefill_dedup()
+    assert torch.equal(a, pb.out)
+
+
+@pytest.mark.timeout(900)
+def test_dedup_full_128k_correlated_sampled():
+    """The correlated 128K workload through dsa_prefill_dedup (the launch the benchmark times),
+    checked on sampled rows."""
+    p = workloads.make(workloads.P128K_CORR)
+    pb = PrefillBatch(p)
+    pb.prefill_dedup()
+    rows = sample_rows(p.cu_seqlens, p.topk, seed=5)
+    idx = pb.topk_idx[torch.from_numpy(rows).cuda()].cpu().numpy()
+    out = bf16_to_float(pb.out[torch.from_numpy(rows).cuda()])
+    del pb
+    torch.cuda.empty_cache()
+    sel, ref = _oracle(p).rows(rows)
+    bad = [int(r) for r, a, b in zip(rows, idx, sel) if not np.array_equal(a, b)]
+    assert not bad, f"index mismatch on rows {bad[:10]}"
+    assert_out_close(out, ref, "dedup 128K correlated")

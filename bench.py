@@ -187,6 +187,52 @@ def bench_decode(steps_total=64, stage_reps=16):
     return res
 
 
+def bench_dedup(steps=3):
+    """Adjacent-query dedup on the correlated 128K workload (indexer queries drifting along the
+    sequence): dsa_prefill (gather path) and dsa_prefill_dedup on the same inputs, per-stage
+    HIP-event times, and the masked MFMA work the dedup kernel executes."""
+    import torch
+    from sparse_attention_long_04_amd import workloads
+    from sparse_attention_long_04_amd.runtime import PrefillBatch, timing_events
+
+    name = workloads.P128K_CORR
+    p = workloads.make(name)
+    pb = PrefillBatch(p)
+    st = torch.cuda.current_stream()
+    res = {}
+    for mode in ("gather", "dedup"):
+        runs = []
+        for it in range(steps + 1):
+            ev = timing_events(4)
+            a, = timing_events(1)
+            a.record(st)
+            if mode == "gather":
+                pb.prefill_timed(ev)
+            else:
+                pb.prefill_dedup(events=ev)
+            torch.cuda.synchronize()
+            runs.append([ms_between(a, ev[3]), ms_between(ev[2], ev[3])])
+        r = np.array(runs[1:]).mean(0)
+        res[mode] = dict(ms=float(r[0]), attention_ms=float(r[1]))
+    pb.sparse_attention_dedup(out=torch.empty_like(pb.out))
+    torch.cuda.synchronize()
+    _, cnt, _, _ = pb.dedup_unions()
+    u = cnt.double()
+    Hq, Hkv, d = p.q.shape[1], p.k.shape[1], p.q.shape[2]
+    # executed: every 64-key tile of a union against the block's 16 rows x Hq heads
+    executed = float((torch.ceil(u / 64) * 64).sum()) * 16 * Hq * d * 4
+    useful = selected_of(p.lengths, p.topk) * Hq * d * 4
+    out = dict(workload=name, T=int(p.total_tokens), gather=res["gather"], dedup=res["dedup"],
+               union_mean=float(u.mean()), union_per_row=float(u.sum()) / p.total_tokens,
+               executed_flop=float(executed), useful_flop=float(useful))
+    log(f"dedup {name}: gather {res['gather']['ms']:.2f} ms (attention {res['gather']['attention_ms']:.2f}); "
+        f"dedup {res['dedup']['ms']:.2f} ms (attention {res['dedup']['attention_ms']:.2f}); mean union of 16 rows "
+        f"{out['union_mean']:.0f}")
+    del pb
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_topk_general(reps=5):
     """The standalone top-k (dsa_topk) on its workload: 2048 rows x 131072 fp32 scores, k = 2048,
     timed over ``reps`` back-to-back launches with HIP events.  torch.topk on the same scores is
@@ -260,7 +306,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="prefill only (no dense/decode/varlen/cpu)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--only", choices=["decode", "topk"], default=None,
+    ap.add_argument("--only", choices=["decode", "topk", "dedup"], default=None,
                     help="profiling aid: run only the decode (or standalone top-k) measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (scales the HBM byte counters)")
@@ -288,6 +334,9 @@ def main():
         return
     if args.only == "topk":
         print(json.dumps(bench_topk_general()), flush=True)
+        return
+    if args.only == "dedup":
+        print(json.dumps(bench_dedup()), flush=True)
         return
     name = args.workload or workloads.P128K
     w = workloads.WORKLOADS[name]
@@ -362,6 +411,16 @@ def main():
                                 "roofline": roof("hbm", tk["work"] / (tk["ms"] * 1e-3), PEAK_HBM, "GB/s", None,
                                                  tk["work"], "byte"),
                                 "torch_topk_ms_context": round(tk["torch_topk_ms"], 3)}
+        dd = bench_dedup(max(1, args.steps - 1))
+        line["dedup"] = {"workload": dd["workload"], "gather_ms": round(dd["gather"]["ms"], 3),
+                         "dedup_ms": round(dd["dedup"]["ms"], 3),
+                         "tokens_per_s_dedup": round(dd["T"] / (dd["dedup"]["ms"] * 1e-3), 1),
+                         "attention_ms": {"gather": round(dd["gather"]["attention_ms"], 3),
+                                          "dedup": round(dd["dedup"]["attention_ms"], 3)},
+                         "union_mean_16_rows": round(dd["union_mean"], 1),
+                         "roofline": roof("mfma", dd["executed_flop"] / (dd["dedup"]["attention_ms"] * 1e-3),
+                                          PEAK_BF16, "TFLOP/s", None, dd["executed_flop"], "flop (masked MFMA)"),
+                         "useful_tflops": round(dd["useful_flop"] / (dd["dedup"]["attention_ms"] * 1e-3) / 1e12, 1)}
         vl = bench_prefill(workloads.VARLEN, max(1, args.steps - 1), 1, with_dense=False)
         line["varlen"] = {"workload": workloads.VARLEN, "tokens_per_s": round(vl["T"] / (vl["ms"] * 1e-3), 1),
                           "ms": round(vl["ms"], 3), "lengths": vl["lengths"]}

@@ -75,6 +75,27 @@ class PrefillBatch:
         dsa.dsa_prefill_dedup(self.shape, self.q_idx, self.k_idx, self.w_idx, self.q, self.k, self.v, self.out,
                               self.topk_idx, self.ws, self._dedup_ws(), events, stream)
 
+    def dedup_unions(self):
+        """After sparse_attention_dedup: (sched [n, 2] = (sequence, 16-row block), union sizes [n],
+        union positions and row masks per block) read back from the dedup workspace, whose layout
+        is counts int[64] | sched int2[nb] | ucount int[nb] | ukeys int32[nb][16k] |
+        umask uint16[nb][16k], each part 256-byte aligned, nb = ceil(T/16) + #sequences."""
+        def up(x):
+            return (x + 255) // 256 * 256
+        T, B, k = self.p.total_tokens, len(self.p.lengths), self.p.topk
+        nb, us = (T + 15) // 16 + B, 16 * k
+        o_sched = 256
+        o_cnt = up(o_sched + nb * 8)
+        o_keys = up(o_cnt + nb * 4)
+        o_mask = up(o_keys + nb * us * 4)
+        w = self.dws
+        n = int(w[0:4].view(torch.int32).item())
+        sched = w[o_sched:o_sched + n * 8].view(torch.int32).view(n, 2)
+        cnt = w[o_cnt:o_cnt + n * 4].view(torch.int32)
+        keys = w[o_keys:o_keys + n * us * 4].view(torch.int32).view(n, us)
+        mask = w[o_mask:o_mask + n * us * 2].view(torch.int16).view(n, us)
+        return sched, cnt, keys, mask
+
     def sparse_attention_dedup(self, out=None, stream=None):
         out = self.out if out is None else out
         dsa.dsa_sparse_attention_dedup(self.shape, self.q, self.k, self.v, self.topk_idx, out, self._dedup_ws(), stream)

@@ -101,3 +101,33 @@ def test_dedup_full_128k_correlated_sampled():
     bad = [int(r) for r, a, b in zip(rows, idx, sel) if not np.array_equal(a, b)]
     assert not bad, f"index mismatch on rows {bad[:10]}"
     assert_out_close(out, ref, "dedup 128K correlated")
+
+
+def test_union_kernel_contents():
+    """The union of every 16-row block, read back from the dedup workspace: ascending positions,
+    equal to the set union of the block rows' selections, and bit r of a key's mask set exactly
+    when row r selected it."""
+    p = gen.make_prefill([129, 0, 17, 300, 40, 1000], idx_heads=16, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4,
+                         topk=64, seed=75, video=True, query_corr=0.9)
+    pb = PrefillBatch(p)
+    pb.index_topk()
+    pb.sparse_attention_dedup(out=torch.empty_like(pb.out))
+    torch.cuda.synchronize()
+    sched, cnt, keys, mask = (t.cpu().numpy() for t in pb.dedup_unions())
+    idx = pb.topk_idx.cpu().numpy()
+    cu = p.cu_seqlens
+    seen = set()
+    for n in range(len(cnt)):
+        b, j = int(sched[n, 0]), int(sched[n, 1])
+        seen.add((b, j))
+        t0 = cu[b] + 16 * j
+        nr = min(16, cu[b + 1] - t0)
+        sets = [idx[t0 + r][idx[t0 + r] >= 0] for r in range(nr)]
+        ref = np.unique(np.concatenate(sets))
+        got = keys[n, :cnt[n]]
+        assert np.array_equal(got, ref), (b, j)
+        m = mask[n, :cnt[n]].astype(np.uint16)
+        for r in range(16):
+            want = np.isin(ref, sets[r]) if r < nr else np.zeros(ref.size, bool)
+            assert np.array_equal(((m >> r) & 1).astype(bool), want), (b, j, r)
+    assert seen == {(b, j) for b in range(len(cu) - 1) for j in range((cu[b + 1] - cu[b] + 15) // 16)}

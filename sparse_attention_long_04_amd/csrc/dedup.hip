@@ -233,27 +233,34 @@ __global__ __launch_bounds__(32 * G) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const uint32_t bit = 1u << (16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3));
-        const float zz = ((rb ? mhi : mlo) & bit) ? sacc[rb][i] * scale_log2 : -__builtin_inff();
+        const float zz = ((rb ? mhi : mlo) & bit) ? sacc[rb][i] : -__builtin_inff();
         z[rb][i] = zz;
         mt = fmaxf(mt, zz);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;  // unscaled max, then scaled (scale > 0)
+    // lazy rescale: the reference max moves only when a lane's max passes it by more than
+    // kLazy (log2 units), so p = 2^(s - ref) <= 2^kLazy and the O / sum rescale is rare
+    constexpr float kLazy = 8.f;
+    const bool upd = mt > m_run + kLazy;
+    if (__any(upd)) {
+      const float m_new = upd ? mt : m_run;
+      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
     float ps = 0.f;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(z[rb][i] - m_use);
+        const float pv = __builtin_amdgcn_exp2f(fmaf(z[rb][i], scale_log2, -m_use));
         z[rb][i] = pv;
         ps += pv;
       }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    l_run += ps;
     const int grp = lane >> 4, jj = lane & 15;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)

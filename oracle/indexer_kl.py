@@ -50,8 +50,11 @@ def kl_row(q_t, k_ctx, qi_t, ki_ctx, w_t, scale):
     c = qi_t @ ki_ctx.T                                                             # [H, n]
     scores = (w_t[:, None] * np.maximum(c, 0.0)).sum(axis=0)
     r = _softmax(scores)
+    # log r as a log-softmax: r itself underflows to 0 when scores differ by more than ~745
+    m = scores.max()
+    log_r = scores - m - np.log(np.exp(scores - m).sum())
     pos = p > 0
-    kl = float(np.sum(p[pos] * (np.log(p[pos]) - np.log(r[pos]))))
+    kl = float(np.sum(p[pos] * (np.log(p[pos]) - log_r[pos])))
     return kl, p, r, r - p, c
 
 

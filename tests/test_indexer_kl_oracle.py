@@ -169,3 +169,16 @@ def test_planted_backward_mistakes_are_caught(mistake):
             flat[j] = old
             bad |= abs((lp - lm) / (2 * eps) - grad.reshape(-1)[j]) > 1e-5
     assert bad
+
+
+def test_kl_finite_when_indexer_softmax_underflows():
+    """Indexer scores 0 and 1000: r = [e^-1000 / (1 + e^-1000), ~1] underflows in float64, but
+    KL(p || r) is finite: with p = [1/2, 1/2] it equals 1/2 ln(1/2 / r0) + 1/2 ln(1/2 / r1)
+    = 1/2 (1000 + ln(1 + e^-1000)) + ln(1/2) + 1/2 ln(1 + e^-1000) = 500 - ln 2 (to double precision)."""
+    q = np.zeros((1, 1, 2))                                  # equal main logits -> p = [1/2, 1/2]
+    k = np.array([[[1.0, 0.0]], [[0.0, 1.0]]])
+    qi = np.array([[0.0, 1000.0]])                           # scores c = q_I . k_I = [0, 1000]
+    ki = np.array([[1.0, 0.0], [0.0, 1.0]])
+    kl, p, r, _, _ = kl_row(q[0], k, qi, ki, np.ones(1), 1.0)
+    assert np.allclose(p, [0.5, 0.5]) and r[0] == 0.0
+    assert abs(kl - (500.0 - math.log(2.0))) < 1e-9

@@ -158,6 +158,27 @@ int dsa_prefill_dedup(const dsa_prefill_shape* shape, const void* q_idx, const v
                       void* dedup_workspace, size_t dedup_workspace_bytes, void* stream,
                       void* const* events);
 
+/* ---------------------------------------------------------------------------------------
+ * Indexer dense warm-up objective (summary page section 一: with the full attention frozen, the
+ * indexer is trained so that its distribution follows the full attention's, minimising a KL
+ * divergence).  Per query token t over its keys s <= t:
+ *   p_t = mean over the Hq heads of softmax_s(scale q[t,h] . k[s, g(h)])  (target, constant)
+ *   r_t = softmax_s(I[t, :]) with I the Lightning Indexer scores (as dsa_index_scores)
+ *   kl[t] = sum_s p log(p / r)
+ * and the gradients of sum_t kl[t] with respect to the indexer inputs, with g = r - p and
+ * c = q_I[t,h] . k_I[s]:  dw[t,h] = sum_s g max(0, c);  dq_I[t,h] = w[t,h] sum_s g [c>0] k_I[s];
+ * dk_I[s] = sum_{t>=s} sum_h g w[t,h] [c>0] q_I[t,h].
+ * Inputs as dsa_prefill (q, k bf16; V is not used); indexer e4m3 with d_I = 128 and
+ * H_I in {16, 32, 64}; Hkv in {1, 2, 4}; Hq even (DSA_ERR_UNSUPPORTED otherwise).
+ * Outputs (DEVICE fp32): kl [T], dq_idx [T, H_I, d_I], dk_idx [T, d_I], dw_idx [T, H_I].
+ * Deterministic (no float atomics).  Workspace: dsa_indexer_kl_workspace_size.
+ * ------------------------------------------------------------------------------------- */
+int dsa_indexer_kl_workspace_size(const dsa_prefill_shape* shape, size_t* bytes);
+int dsa_indexer_kl(const dsa_prefill_shape* shape, const void* q_idx, const void* k_idx,
+                   const float* w_idx, const uint16_t* q, const uint16_t* k, float* kl,
+                   float* dq_idx, float* dk_idx, float* dw_idx, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* Standard full causal GQA attention (the cost reference of summary page section 一), same
  * tensors as dsa_sparse_attention without indices.  Uses the prefill workspace. */
 int dense_causal_attention(const dsa_prefill_shape* shape, const uint16_t* q, const uint16_t* k,

@@ -31,6 +31,14 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Exact value of an OCP e4m3 ("fn") code (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+// exponent 0 is subnormal).  The NaN code is never produced by the inputs here.
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float mag = (e == 0) ? float(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -mag : mag;
+}
+
 // Reinterpret 4 dwords as 8 bf16 for the MFMA builtins.
 __device__ __forceinline__ bf16x8 as_bf16x8(i32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 

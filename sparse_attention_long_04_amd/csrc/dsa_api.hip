@@ -33,6 +33,22 @@ hipError_t launch_dedup_attention(const uint16_t* q, const uint16_t* k, const ui
                                   int Hkv, float scale, const int2* sched, const int* count, int nb_bound,
                                   int64_t ustride, const int32_t* ukeys, const uint16_t* umask, const int* ucount,
                                   uint16_t* out, hipStream_t st);
+hipError_t launch_kl_lse(const uint16_t* q, const uint16_t* k, const int32_t* cu, int Hq, int Hkv, float scale,
+                         const int2* sched128, const int* count128, int nb128, float* lse, hipStream_t st);
+hipError_t launch_kl_target(const uint16_t* q, const uint16_t* k, const int32_t* cu, int Hq, int Hkv, float scale,
+                            const int2* sched128, const int* count128, int nb128, const float* lse,
+                            const int64_t* seqoff, float* P, hipStream_t st);
+hipError_t launch_kl_rows(const float* I, float* P, const int64_t* seqoff, const int32_t* cu, int nseq, int64_t T,
+                          const float2* rowrange, float* kl, hipStream_t st);
+hipError_t launch_kl_gscale(const float* w, int64_t n, float* gsc, hipStream_t st);
+hipError_t launch_kl_dq(int H, const uint8_t* q_idx, const uint8_t* k_idx, const float* w, const float* G,
+                        const int64_t* seqoff, const int32_t* cu, const int2* schedR, const int* countR, int nbR,
+                        const float* gsc, float* dq, float* dw, hipStream_t st);
+int kl_dk_slices(int max_len);
+hipError_t launch_kl_dk(int H, const uint8_t* q_idx, const uint8_t* k_idx, const float* w, const float* G,
+                        const int64_t* seqoff, const int32_t* cu, int nseq, const int2* sched256,
+                        const int* count256, int nb256, int max_len, int64_t T, const float* gsc, float* dk_part,
+                        float* dk, hipStream_t st);
 hipError_t launch_topk_general(const float* scores, int64_t rows, int n, int64_t ld, const int32_t* lens, int K,
                                int32_t* out, hipStream_t st);
 hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu, int Hq,
@@ -201,6 +217,44 @@ DedupWs dedup_layout(const dsa_prefill_shape* s) {
   w.umask = off; off = align_up(off + size_t(w.nb16) * size_t(w.ustride) * sizeof(uint16_t), 256);
   w.total = off;
   return w;
+}
+
+// Warm-up KL workspace: the prefill layout (schedules, row ranges, indexer score triangle) then
+//   P triangle float[score_floats] | lse float[T][Hq] | schedR int2[nbR] | sched256 int2[nb256] |
+//   dk partials float[slices][T][128].  counts[2] / counts[3] hold the R-row / 256-row schedule sizes;
+//   counts[8..9] (as floats) the fp16 pre-scale of the gradient weights and its inverse.
+struct KlWs {
+  PrefillWs base;
+  size_t P, lse, schedR, sched256, dkpart, total;
+  int R, nbR, nb256, slices;
+};
+
+KlWs kl_layout(const dsa_prefill_shape* s) {
+  KlWs w{};
+  w.base = prefill_layout(s, nullptr);
+  const int64_t T = s->total_tokens;
+  w.R = 256 / (s->idx_heads > 0 ? s->idx_heads : 1);
+  w.nbR = int((T + w.R - 1) / w.R + s->num_seqs);
+  w.nb256 = int((T + 255) / 256 + s->num_seqs);
+  w.slices = kl_dk_slices(s->max_seqlen);
+  size_t off = w.base.total;
+  w.P = off; off = align_up(off + size_t(w.base.score_floats) * sizeof(float), 256);
+  w.lse = off; off = align_up(off + size_t(T) * size_t(s->q_heads) * sizeof(float), 256);
+  w.schedR = off; off = align_up(off + size_t(w.nbR) * sizeof(int2), 256);
+  w.sched256 = off; off = align_up(off + size_t(w.nb256) * sizeof(int2), 256);
+  w.dkpart = off; off = align_up(off + size_t(w.slices) * size_t(T) * 128 * sizeof(float), 256);
+  w.total = off;
+  return w;
+}
+
+int check_kl(const dsa_prefill_shape* s) {
+  int rc = check_prefill(s, true);
+  if (rc) return rc;
+  if (s->idx_dtype != DSA_IDX_FP8_E4M3 || s->idx_dim != 128) return DSA_ERR_UNSUPPORTED;
+  if (s->idx_heads != 16 && s->idx_heads != 32 && s->idx_heads != 64) return DSA_ERR_UNSUPPORTED;
+  if (s->kv_heads != 1 && s->kv_heads != 2 && s->kv_heads != 4) return DSA_ERR_UNSUPPORTED;
+  if (s->q_heads % 2 != 0) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
 }
 
 bool dedup_supported(const dsa_prefill_shape* s) {
@@ -453,6 +507,66 @@ int dsa_prefill_timed(const dsa_prefill_shape* s, const void* q_idx, const void*
                       void* ws, size_t ws_bytes, void* stream, void* const* events) {
   if (!events) return DSA_ERR_INVALID_ARGUMENT;
   return prefill_impl(s, q_idx, k_idx, w_idx, q, k, v, out, topk_idx, ws, ws_bytes, stream, events);
+}
+
+int dsa_indexer_kl_workspace_size(const dsa_prefill_shape* s, size_t* bytes) {
+  if (!bytes) return DSA_ERR_INVALID_ARGUMENT;
+  int rc = check_kl(s);
+  if (rc) return rc;
+  *bytes = kl_layout(s).total;
+  return DSA_OK;
+}
+
+int dsa_indexer_kl(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
+                   const uint16_t* q, const uint16_t* k, float* kl, float* dq_idx, float* dk_idx, float* dw_idx,
+                   void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_kl(s);
+  if (rc) return rc;
+  if (s->total_tokens == 0) return DSA_OK;
+  if (!q_idx || !k_idx || !w_idx || !q || !k || !kl || !dq_idx || !dk_idx || !dw_idx || !ws)
+    return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(w_idx) || !aligned16(q) || !aligned16(k) ||
+      !aligned16(dq_idx) || !aligned16(dk_idx) || !aligned16(ws))
+    return DSA_ERR_INVALID_ARGUMENT;
+  const KlWs K = kl_layout(s);
+  if (ws_bytes < K.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  const PrefillWs& L = K.base;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int* counts = at<int>(ws, L.counts);
+  hipError_t e;
+  if ((e = launch_build_schedule(s->cu_seqlens, s->num_seqs, 16, L.nb16, at<int2>(ws, L.sched16), counts,
+                                 at<int64_t>(ws, L.seqoff), st)) != hipSuccess ||
+      (e = launch_build_schedule(s->cu_seqlens, s->num_seqs, 128, L.nb128, at<int2>(ws, L.sched128), counts + 1,
+                                 nullptr, st)) != hipSuccess ||
+      (e = launch_build_schedule(s->cu_seqlens, s->num_seqs, K.R, K.nbR, at<int2>(ws, K.schedR), counts + 2, nullptr,
+                                 st)) != hipSuccess ||
+      (e = launch_build_schedule(s->cu_seqlens, s->num_seqs, 256, K.nb256, at<int2>(ws, K.sched256), counts + 3,
+                                 nullptr, st)) != hipSuccess)
+    return hip_status(e);
+  const int64_t* seqoff = at<int64_t>(ws, L.seqoff);
+  float* scores = at<float>(ws, L.scores);
+  float* P = at<float>(ws, K.P);
+  if ((e = launch_indexer_prefill(true, 128, q_idx, k_idx, w_idx, s->cu_seqlens, s->idx_heads,
+                                  at<int2>(ws, L.sched16), counts, L.nb16, seqoff, scores,
+                                  at<float2>(ws, L.rowrange), st)) != hipSuccess ||
+      (e = launch_kl_lse(q, k, s->cu_seqlens, s->q_heads, s->kv_heads, s->softmax_scale, at<int2>(ws, L.sched128),
+                         counts + 1, L.nb128, at<float>(ws, K.lse), st)) != hipSuccess ||
+      (e = launch_kl_target(q, k, s->cu_seqlens, s->q_heads, s->kv_heads, s->softmax_scale,
+                            at<int2>(ws, L.sched128), counts + 1, L.nb128, at<float>(ws, K.lse), seqoff, P,
+                            st)) != hipSuccess ||
+      (e = launch_kl_rows(scores, P, seqoff, s->cu_seqlens, s->num_seqs, s->total_tokens,
+                          at<float2>(ws, L.rowrange), kl, st)) != hipSuccess ||
+      (e = launch_kl_gscale(w_idx, s->total_tokens * s->idx_heads, reinterpret_cast<float*>(counts + 8), st)) !=
+          hipSuccess ||
+      (e = launch_kl_dq(s->idx_heads, static_cast<const uint8_t*>(q_idx), static_cast<const uint8_t*>(k_idx), w_idx,
+                        P, seqoff, s->cu_seqlens, at<int2>(ws, K.schedR), counts + 2, K.nbR,
+                        reinterpret_cast<const float*>(counts + 8), dq_idx, dw_idx, st)) != hipSuccess ||
+      (e = launch_kl_dk(s->idx_heads, static_cast<const uint8_t*>(q_idx), static_cast<const uint8_t*>(k_idx), w_idx,
+                        P, seqoff, s->cu_seqlens, s->num_seqs, at<int2>(ws, K.sched256), counts + 3, K.nb256,
+                        s->max_seqlen, s->total_tokens, reinterpret_cast<const float*>(counts + 8),
+                        at<float>(ws, K.dkpart), dk_idx, st)) != hipSuccess)
+    return hip_status(e);
+  return DSA_OK;
 }
 
 int dsa_dedup_workspace_size(const dsa_prefill_shape* s, size_t* bytes) {

@@ -54,11 +54,6 @@ __global__ void build_schedule_kernel(const int32_t* __restrict__ cu, int nseq, 
 // ------------------------------------------------------------------------------------------
 // Exact helpers for OCP e4m3 ("fn") values.
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ float e4m3_decode(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  const float mag = (e == 0) ? float(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (b & 0x80u) ? -mag : mag;
-}
 
 // Round to the e4m3 grid (nearest even), |result| <= 448.
 __device__ __forceinline__ float e4m3_round(float v) {

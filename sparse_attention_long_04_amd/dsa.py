@@ -63,6 +63,8 @@ EXPORTS = {
     "dsa_dedup_workspace_size": ([ctypes.POINTER(PrefillShape), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "dsa_sparse_attention_dedup": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "dsa_prefill_dedup": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
+    "dsa_indexer_kl_workspace_size": ([ctypes.POINTER(PrefillShape), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "dsa_indexer_kl": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "dsa_topk": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
                   ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
 }
@@ -256,3 +258,15 @@ def dsa_prefill_dedup(shape, q_idx, k_idx, w_idx, q, k, v, out, topk_idx, worksp
                                    _ptr(v), _ptr(out), _ptr(topk_idx), _ptr(workspace), _nbytes(workspace),
                                    _ptr(dedup_workspace), _nbytes(dedup_workspace), _stream(stream), ev),
            "dsa_prefill_dedup")
+
+
+def dsa_indexer_kl_workspace_size(shape: PrefillShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().dsa_indexer_kl_workspace_size(ctypes.byref(shape), ctypes.byref(n)), "dsa_indexer_kl_workspace_size")
+    return n.value
+
+
+def dsa_indexer_kl(shape, q_idx, k_idx, w_idx, q, k, kl, dq_idx, dk_idx, dw_idx, workspace, stream=None):
+    _check(lib().dsa_indexer_kl(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(k), _ptr(kl),
+                                _ptr(dq_idx), _ptr(dk_idx), _ptr(dw_idx), _ptr(workspace), _nbytes(workspace),
+                                _stream(stream)), "dsa_indexer_kl")

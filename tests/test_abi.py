@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     for n in ["dsa_index_topk", "dsa_prefill", "dsa_decode", "dense_causal_attention", "dsa_sparse_attention",
               "dense_decode_attention", "dsa_kv_append", "dsa_index_scores", "dsa_prefill_workspace_size",
               "dsa_decode_workspace_size", "dsa_status_string", "dsa_last_hip_error", "dsa_topk",
-              "dsa_prefill_dedup", "dsa_sparse_attention_dedup", "dsa_dedup_workspace_size"]:
+              "dsa_prefill_dedup", "dsa_sparse_attention_dedup", "dsa_dedup_workspace_size",
+              "dsa_indexer_kl", "dsa_indexer_kl_workspace_size"]:
         assert n in names
 
 
@@ -188,3 +189,16 @@ def test_dedup_workspace_layout_and_unsupported_groups():
     with pytest.raises(dsa.DSAError) as ei:
         dsa.dsa_sparse_attention_dedup(s, FAKE, FAKE, FAKE, None, FAKE, (FAKE, n), stream=0)
     assert ei.value.status == 1
+
+
+def test_indexer_kl_rejects_unsupported_shapes():
+    ok = shape(T=4096, max_seqlen=4096)
+    n = dsa.dsa_indexer_kl_workspace_size(ok)
+    assert n > 4096 * 32 * 4
+    for kw in (dict(idx_dtype="bf16", idx_dim=64), dict(idx_heads=48), dict(kv_heads=8, q_heads=32)):
+        with pytest.raises(dsa.DSAError) as ei:
+            dsa.dsa_indexer_kl_workspace_size(shape(T=4096, max_seqlen=4096, **kw))
+        assert ei.value.status == 2, kw
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_indexer_kl(ok, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, (FAKE, n - 1), stream=0)
+    assert ei.value.status == 3

@@ -233,6 +233,48 @@ def bench_dedup(steps=3):
     return out
 
 
+def bench_indexer_kl(reps=3):
+    """The indexer's dense warm-up objective (dsa_indexer_kl: KL value per token and gradients for
+    q_I, k_I, w) on one 32768-token sequence with the 32K prefill shapes (indexer 64 x 128 e4m3,
+    GQA 32q/4kv d128), timed with HIP events over ``reps`` calls."""
+    import torch
+    from sparse_attention_long_04_amd import dsa
+    from sparse_attention_long_04_amd import inputs as gen
+    from sparse_attention_long_04_amd.runtime import PrefillBatch, timing_events
+
+    L = 32768
+    p = gen.make_prefill([L], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=2048, seed=1007,
+                         video=True)
+    pb = PrefillBatch(p, workspace=False)
+    H = 64
+    ws = torch.empty(dsa.dsa_indexer_kl_workspace_size(pb.shape), dtype=torch.uint8, device="cuda")
+    kl = torch.empty(L, dtype=torch.float32, device="cuda")
+    dq = torch.empty((L, H, 128), dtype=torch.float32, device="cuda")
+    dk = torch.empty((L, 128), dtype=torch.float32, device="cuda")
+    dw = torch.empty((L, H), dtype=torch.float32, device="cuda")
+    args = (pb.shape, pb.q_idx, pb.k_idx, pb.w_idx, pb.q, pb.k, kl, dq, dk, dw, ws)
+    dsa.dsa_indexer_kl(*args)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    a, b = timing_events(2)
+    a.record(st)
+    for _ in range(reps):
+        dsa.dsa_indexer_kl(*args)
+    b.record(st)
+    torch.cuda.synchronize()
+    ms = ms_between(a, b) / reps
+    pairs = pairs_of([L])
+    # MFMA work executed per call: two passes of QK^T over all query heads (log-sum-exp, target),
+    # the fp8 indexer scores, and per gradient kernel one S recompute plus the contraction twice
+    # (fp16 hi + lo)
+    bf16_flop = 2 * 32 * 128 * 2 * pairs + 2 * (H * 128 * 2 * pairs * 3)
+    fp8_flop = H * 128 * 2 * pairs
+    log(f"indexer KL 32K: {ms:.2f} ms per call (forward + gradients)")
+    del pb, ws, dq
+    torch.cuda.empty_cache()
+    return dict(ms=ms, tokens=L, bf16_flop=float(bf16_flop), fp8_flop=float(fp8_flop))
+
+
 def bench_topk_general(reps=5):
     """The standalone top-k (dsa_topk) on its workload: 2048 rows x 131072 fp32 scores, k = 2048,
     timed over ``reps`` back-to-back launches with HIP events.  torch.topk on the same scores is
@@ -306,7 +348,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="prefill only (no dense/decode/varlen/cpu)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--only", choices=["decode", "topk", "dedup"], default=None,
+    ap.add_argument("--only", choices=["decode", "topk", "dedup", "kl"], default=None,
                     help="profiling aid: run only the decode (or standalone top-k) measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (scales the HBM byte counters)")
@@ -337,6 +379,9 @@ def main():
         return
     if args.only == "dedup":
         print(json.dumps(bench_dedup()), flush=True)
+        return
+    if args.only == "kl":
+        print(json.dumps(bench_indexer_kl()), flush=True)
         return
     name = args.workload or workloads.P128K
     w = workloads.WORKLOADS[name]
@@ -421,6 +466,13 @@ def main():
                          "roofline": roof("mfma", dd["executed_flop"] / (dd["dedup"]["attention_ms"] * 1e-3),
                                           PEAK_BF16, "TFLOP/s", None, dd["executed_flop"], "flop (masked MFMA)"),
                          "useful_tflops": round(dd["useful_flop"] / (dd["dedup"]["attention_ms"] * 1e-3) / 1e12, 1)}
+        kr = bench_indexer_kl()
+        kl_equiv = kr["bf16_flop"] + kr["fp8_flop"] / 2  # fp8 work counted at half a bf16 flop (twice the rate)
+        line["indexer_kl"] = {"workload": "indexer dense warm-up KL, 32768 tokens, indexer 64x128 e4m3, GQA 32q/4kv",
+                              "ms": round(kr["ms"], 3),
+                              "tokens_per_s": round(kr["tokens"] / (kr["ms"] * 1e-3), 1),
+                              "roofline": roof("mfma", kl_equiv / (kr["ms"] * 1e-3), PEAK_BF16, "TFLOP/s", None,
+                                               kl_equiv, "bf16-equivalent flop (executed MFMA work)")}
         vl = bench_prefill(workloads.VARLEN, max(1, args.steps - 1), 1, with_dense=False)
         line["varlen"] = {"workload": workloads.VARLEN, "tokens_per_s": round(vl["T"] / (vl["ms"] * 1e-3), 1),
                           "ms": round(vl["ms"], 3), "lengths": vl["lengths"]}

@@ -36,11 +36,11 @@ hipError_t launch_dedup_attention(const uint16_t* q, const uint16_t* k, const ui
 hipError_t launch_kl_lse(const uint16_t* q, const uint16_t* k, const int32_t* cu, int Hq, int Hkv, float scale,
                          const int2* sched128, const int* count128, int nb128, float* lse, hipStream_t st);
 hipError_t launch_kl_target(const uint16_t* q, const uint16_t* k, const int32_t* cu, int Hq, int Hkv, float scale,
-                            const int2* sched128, const int* count128, int nb128, const float* lse,
+                            const int2* sched128, const int* count128, int nb128, int max_len, const float* lse,
                             const int64_t* seqoff, float* P, hipStream_t st);
 hipError_t launch_kl_rows(const float* I, float* P, const int64_t* seqoff, const int32_t* cu, int nseq, int64_t T,
                           const float2* rowrange, float* kl, hipStream_t st);
-hipError_t launch_kl_gscale(const float* w, int64_t n, float* gsc, hipStream_t st);
+hipError_t launch_kl_gscale(const float* w, int64_t n, float* part, float* gsc, hipStream_t st);
 hipError_t launch_kl_dq(int H, const uint8_t* q_idx, const uint8_t* k_idx, const float* w, const float* G,
                         const int64_t* seqoff, const int32_t* cu, const int2* schedR, const int* countR, int nbR,
                         const float* gsc, float* dq, float* dw, hipStream_t st);
@@ -221,11 +221,12 @@ DedupWs dedup_layout(const dsa_prefill_shape* s) {
 
 // Warm-up KL workspace: the prefill layout (schedules, row ranges, indexer score triangle) then
 //   P triangle float[score_floats] | lse float[T][Hq] | schedR int2[nbR] | sched256 int2[nb256] |
-//   dk partials float[slices][T][128].  counts[2] / counts[3] hold the R-row / 256-row schedule sizes;
+//   dk partials float[slices][T][128] | w max partials float[256].  counts[2] / counts[3] hold the
+//   R-row / 256-row schedule sizes;
 //   counts[8..9] (as floats) the fp16 pre-scale of the gradient weights and its inverse.
 struct KlWs {
   PrefillWs base;
-  size_t P, lse, schedR, sched256, dkpart, total;
+  size_t P, lse, schedR, sched256, dkpart, wpart, total;
   int R, nbR, nb256, slices;
 };
 
@@ -243,6 +244,7 @@ KlWs kl_layout(const dsa_prefill_shape* s) {
   w.schedR = off; off = align_up(off + size_t(w.nbR) * sizeof(int2), 256);
   w.sched256 = off; off = align_up(off + size_t(w.nb256) * sizeof(int2), 256);
   w.dkpart = off; off = align_up(off + size_t(w.slices) * size_t(T) * 128 * sizeof(float), 256);
+  w.wpart = off; off = align_up(off + 256 * sizeof(float), 256);
   w.total = off;
   return w;
 }
@@ -552,12 +554,12 @@ int dsa_indexer_kl(const dsa_prefill_shape* s, const void* q_idx, const void* k_
       (e = launch_kl_lse(q, k, s->cu_seqlens, s->q_heads, s->kv_heads, s->softmax_scale, at<int2>(ws, L.sched128),
                          counts + 1, L.nb128, at<float>(ws, K.lse), st)) != hipSuccess ||
       (e = launch_kl_target(q, k, s->cu_seqlens, s->q_heads, s->kv_heads, s->softmax_scale,
-                            at<int2>(ws, L.sched128), counts + 1, L.nb128, at<float>(ws, K.lse), seqoff, P,
-                            st)) != hipSuccess ||
+                            at<int2>(ws, L.sched128), counts + 1, L.nb128, s->max_seqlen, at<float>(ws, K.lse), seqoff,
+                            P, st)) != hipSuccess ||
       (e = launch_kl_rows(scores, P, seqoff, s->cu_seqlens, s->num_seqs, s->total_tokens,
                           at<float2>(ws, L.rowrange), kl, st)) != hipSuccess ||
-      (e = launch_kl_gscale(w_idx, s->total_tokens * s->idx_heads, reinterpret_cast<float*>(counts + 8), st)) !=
-          hipSuccess ||
+      (e = launch_kl_gscale(w_idx, s->total_tokens * s->idx_heads, at<float>(ws, K.wpart),
+                            reinterpret_cast<float*>(counts + 8), st)) != hipSuccess ||
       (e = launch_kl_dq(s->idx_heads, static_cast<const uint8_t*>(q_idx), static_cast<const uint8_t*>(k_idx), w_idx,
                         P, seqoff, s->cu_seqlens, at<int2>(ws, K.schedR), counts + 2, K.nbR,
                         reinterpret_cast<const float*>(counts + 8), dq_idx, dw_idx, st)) != hipSuccess ||

@@ -156,9 +156,11 @@ __global__ __launch_bounds__(256) void kl_lse_kernel(const uint16_t* __restrict_
 }
 
 // ------------------------------------------------------------------------------------------
-// kl_target_kernel: grid (128-row blocks), 4 waves x 32 query rows, all heads; 32-key tiles of
-// the HKV KV heads double-buffered in LDS.
+// kl_target_kernel: grid (128-row blocks, key chunks of kKlTargetChunk), 4 waves x 32 query
+// rows, all heads; 32-key tiles of the HKV KV heads double-buffered in LDS.
 // ------------------------------------------------------------------------------------------
+constexpr int kKlTargetChunk = 2048;
+
 template <int HKV>
 __global__ __launch_bounds__(256) void kl_target_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                         const int32_t* __restrict__ cu, int Hq, float scale_log2,
@@ -175,6 +177,10 @@ __global__ __launch_bounds__(256) void kl_target_kernel(const uint16_t* __restri
   const int64_t seq0 = cu[b];
   const int L = cu[b + 1] - cu[b];
   const int q0 = 128 * e.y, kend = min(L, q0 + 128);
+  // this workgroup's key chunk (the rows' outputs are independent across key ranges)
+  const int kbeg = kKlTargetChunk * blockIdx.y;
+  if (kbeg >= kend) return;
+  const int kstop = min(kend, kbeg + kKlTargetChunk);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 31, hf = lane >> 5;
   const int my_q = q0 + 32 * w + qc;
   const int qrow = min(my_q, kend - 1);
@@ -199,12 +205,12 @@ __global__ __launch_bounds__(256) void kl_target_kernel(const uint16_t* __restri
   };
   const float* lse_row = lse + (seq0 + qrow) * Hq;
   float* prow = const_cast<float*>(tri_row(P, seqoff[b], qrow));
-  gload(0);
+  gload(kbeg);
   lstore(0);
   __syncthreads();
   int buf = 0;
-  for (int kt = 0; kt < kend; kt += BN) {
-    const bool more = kt + BN < kend;
+  for (int kt = kbeg; kt < kstop; kt += BN) {
+    const bool more = kt + BN < kstop;
     if (more) gload(kt + BN);
     if (kt <= wave_qmax) {
       float pacc[16];
@@ -317,17 +323,28 @@ __device__ __forceinline__ void fp8_tile_store(uint8_t* lds0, uint8_t* lds1, uin
 
 // Power-of-two pre-scale for the fp16 hi + lo split of G = g w [c > 0] (|g| <= 1): 2^(14 - e)
 // with 2^e >= max |w|, so |G| scale <= 2^14 stays below fp16's maximum and small values stay
-// normal.  gsc[0] = scale, gsc[1] = 1 / scale (both exact).
-__global__ __launch_bounds__(1024) void kl_gscale_kernel(const float* __restrict__ w, int64_t n, float* __restrict__ gsc) {
-  __shared__ float red[16];
+// normal.  gsc[0] = scale, gsc[1] = 1 / scale (both exact).  Two stages: kGscaleBlocks partial
+// maxima, then one workgroup.
+constexpr int kGscaleBlocks = 256;
+
+__global__ __launch_bounds__(256) void kl_wmax_kernel(const float* __restrict__ w, int64_t n, float* __restrict__ part) {
+  __shared__ float red[4];
   float m = 0.f;
-  for (int64_t i = threadIdx.x; i < n; i += 1024) m = fmaxf(m, fabsf(w[i]));
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += 256 * kGscaleBlocks) m = fmaxf(m, fabsf(w[i]));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(256) void kl_gscale_kernel(const float* __restrict__ part, float* __restrict__ gsc) {
+  __shared__ float red[4];
+  float m = part[threadIdx.x];
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int i = 1; i < 16; ++i) m = fmaxf(m, red[i]);
-    red[0] = m;
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     int e = 0;
     if (m > 0.f && m < __builtin_inff()) frexpf(m, &e);  // m = f 2^e, f in [1/2, 1): 2^e >= m
     e = max(-100, min(100, e));
@@ -596,14 +613,15 @@ hipError_t launch_kl_lse(const uint16_t* q, const uint16_t* k, const int32_t* cu
 }
 
 hipError_t launch_kl_target(const uint16_t* q, const uint16_t* k, const int32_t* cu, int Hq, int Hkv, float scale,
-                            const int2* sched128, const int* count128, int nb128, const float* lse,
+                            const int2* sched128, const int* count128, int nb128, int max_len, const float* lse,
                             const int64_t* seqoff, float* P, hipStream_t st) {
   if (nb128 == 0) return hipSuccess;
   const float sl2 = scale * 1.4426950408889634f;
+  const dim3 grid(nb128, (max_len + kKlTargetChunk - 1) / kKlTargetChunk);
   switch (Hkv) {
-    case 1: kl_target_kernel<1><<<nb128, 256, 0, st>>>(q, k, cu, Hq, sl2, sched128, count128, lse, seqoff, P); break;
-    case 2: kl_target_kernel<2><<<nb128, 256, 0, st>>>(q, k, cu, Hq, sl2, sched128, count128, lse, seqoff, P); break;
-    case 4: kl_target_kernel<4><<<nb128, 256, 0, st>>>(q, k, cu, Hq, sl2, sched128, count128, lse, seqoff, P); break;
+    case 1: kl_target_kernel<1><<<grid, 256, 0, st>>>(q, k, cu, Hq, sl2, sched128, count128, lse, seqoff, P); break;
+    case 2: kl_target_kernel<2><<<grid, 256, 0, st>>>(q, k, cu, Hq, sl2, sched128, count128, lse, seqoff, P); break;
+    case 4: kl_target_kernel<4><<<grid, 256, 0, st>>>(q, k, cu, Hq, sl2, sched128, count128, lse, seqoff, P); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -616,8 +634,9 @@ hipError_t launch_kl_rows(const float* I, float* P, const int64_t* seqoff, const
   return hipGetLastError();
 }
 
-hipError_t launch_kl_gscale(const float* w, int64_t n, float* gsc, hipStream_t st) {
-  kl_gscale_kernel<<<1, 1024, 0, st>>>(w, n, gsc);
+hipError_t launch_kl_gscale(const float* w, int64_t n, float* part, float* gsc, hipStream_t st) {
+  kl_wmax_kernel<<<kGscaleBlocks, 256, 0, st>>>(w, n, part);
+  kl_gscale_kernel<<<1, 256, 0, st>>>(part, gsc);
   return hipGetLastError();
 }
 

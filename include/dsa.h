@@ -179,6 +179,33 @@ int dsa_indexer_kl(const dsa_prefill_shape* shape, const void* q_idx, const void
                    float* dq_idx, float* dk_idx, float* dw_idx, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Sparse attention backward (summary page section 一: the "sparse adaptation" stage trains the
+ * whole model in sparse mode, which needs this attention's gradients).  With P = softmax over
+ * the selected keys of scale q.k, O = P V, upstream gradient dO and D = rowsum(dO * O):
+ *   dS = P (dO . v - D);  dq = scale sum_s dS k[s];  dk[s] = scale sum_{(t,h) selecting s} dS q;
+ *   dv[s] = sum_{(t,h) selecting s} P dO.
+ * Deterministic: no float atomics; every key's sums run over its rows in a fixed order.
+ * Needs Hq/Hkv in {2, 4, 8, 16} (DSA_ERR_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------------------- */
+
+/* dsa_sparse_attention that also writes lse (DEVICE fp32 [T, Hq]): the natural-log
+ * log-sum-exp of each row's scaled scores over its selected keys (the backward's statistics). */
+int dsa_sparse_attention_fwd_lse(const dsa_prefill_shape* shape, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, const int32_t* topk_idx, uint16_t* out,
+                                 float* lse, void* stream);
+
+/* Workspace bytes for dsa_sparse_attention_bwd (host only). */
+int dsa_sparse_attention_bwd_workspace_size(const dsa_prefill_shape* shape, size_t* bytes);
+
+/* Gradients of sum <d_out, O> with respect to q, k and v.  q, k, v, topk_idx as given to the
+ * forward; out and lse from dsa_sparse_attention_fwd_lse; d_out bf16 [T, Hq, d].  Outputs
+ * (DEVICE fp32): dq [T, Hq, d], dk [T, Hkv, d], dv [T, Hkv, d]. */
+int dsa_sparse_attention_bwd(const dsa_prefill_shape* shape, const uint16_t* q, const uint16_t* k,
+                             const uint16_t* v, const int32_t* topk_idx, const uint16_t* out,
+                             const float* lse, const uint16_t* d_out, float* dq, float* dk,
+                             float* dv, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Standard full causal GQA attention (the cost reference of summary page section 一), same
  * tensors as dsa_sparse_attention without indices.  Uses the prefill workspace. */
 int dense_causal_attention(const dsa_prefill_shape* shape, const uint16_t* q, const uint16_t* k,

@@ -193,7 +193,7 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
     const int32_t* __restrict__ idx, int K, int mode, const int32_t* __restrict__ cu, int nseq,
     const int32_t* __restrict__ cache_lens, int cap, int Hq, int Hkv, float scale_log2,
     int keys_per_split, int nsplit, uint16_t* __restrict__ out, float* __restrict__ o_part,
-    float2* __restrict__ ml_part) {
+    float2* __restrict__ ml_part, float* __restrict__ lse_out) {
   static_assert(D == 128, "head_dim 128 only");
   __shared__ __attribute__((aligned(16))) int il[kMaxSplitKeys + 32];
   const int64_t r = blockIdx.x;
@@ -225,6 +225,7 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
   const int head = g * G + lr;
   if (nsplit == 1) {
     store_out_bf16<D>(out, r, Hq, head, lg, o, l_tot);
+    if (lse_out && lg == 0) lse_out[r * Hq + head] = (m_run + __log2f(l_tot)) * 0.6931471805599453f;
   } else {
     const int64_t slot = (r * nsplit + split) * Hq + head;
     float* pp = o_part + slot * D + 32 * lg;
@@ -251,7 +252,7 @@ template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, int K, const int32_t* __restrict__ cu, int nseq, int64_t rows, int Hq,
-    int Hkv, float scale_log2, uint16_t* __restrict__ out) {
+    int Hkv, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse_out) {
   static_assert(D == 128, "head_dim 128 only");
   __shared__ __attribute__((aligned(16))) int il_all[NW][kRowKeys + 32];
   const int xcd = blockIdx.x & 7;
@@ -276,6 +277,8 @@ __global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
                    scale_log2, lr, lg, o, m_run, l_tot);
   if (lr >= G) return;
   store_out_bf16<D>(out, r, Hq, g * G + lr, lg, o, l_tot);
+  // natural-log log-sum-exp of the row's scaled scores (the backward's softmax statistics)
+  if (lse_out && lg == 0) lse_out[r * Hq + g * G + lr] = (m_run + __log2f(l_tot)) * 0.6931471805599453f;
 }
 
 // Merge split partials: out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  Splits are read
@@ -494,7 +497,7 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
                                    const int32_t* idx, int K, int mode, const int32_t* cu, int nseq,
                                    const int32_t* cache_lens, int cap, int64_t rows, int Hq, int Hkv,
                                    float scale, int keys_per_split, int nsplit, uint16_t* out,
-                                   float* o_part, float2* ml_part, hipStream_t st) {
+                                   float* o_part, float2* ml_part, hipStream_t st, float* lse_out) {
   if (rows == 0) return hipSuccess;
   const float scale_log2 = scale * 1.4426950408889634f;
   if (mode == 0 && nsplit == 1 && idx && K <= kRowKeys && 8 % Hkv == 0) {
@@ -503,14 +506,14 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
     const int per = 8 / Hkv;  // XCDs per head
     const int64_t blocks = 8 * ((groups + per - 1) / per);
     gather_rows_kernel<128, NWR><<<(unsigned)blocks, 64 * NWR, 0, st>>>(q, k, v, idx, K, cu, nseq, rows, Hq, Hkv,
-                                                                        scale_log2, out);
+                                                                        scale_log2, out, lse_out);
     return hipGetLastError();
   }
   dim3 grid((unsigned)rows, nsplit);
 #define DSA_GATHER(NW)                                                                                   \
   gather_attention_kernel<128, NW><<<grid, 64 * NW, 0, st>>>(q, k, v, idx, K, mode, cu, nseq, cache_lens, \
                                                             cap, Hq, Hkv, scale_log2, keys_per_split,    \
-                                                            nsplit, out, o_part, ml_part)
+                                                            nsplit, out, o_part, ml_part, lse_out)
   switch (Hkv) {
     case 1: DSA_GATHER(1); break;
     case 2: DSA_GATHER(2); break;

@@ -26,7 +26,8 @@ hipError_t launch_topk_decode(const float* scores, int64_t ld, const int32_t* ca
 hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx, int K,
                                    int mode, const int32_t* cu, int nseq, const int32_t* cache_lens, int cap,
                                    int64_t rows, int Hq, int Hkv, float scale, int keys_per_split, int nsplit,
-                                   uint16_t* out, float* o_part, float2* ml_part, hipStream_t st);
+                                   uint16_t* out, float* o_part, float2* ml_part, hipStream_t st,
+                                   float* lse_out = nullptr);
 hipError_t launch_union(const int32_t* idx, int K, const int32_t* cu, const int2* sched, const int* count,
                         int nb_bound, int64_t ustride, int32_t* ukeys, uint16_t* umask, int* ucount, hipStream_t st);
 hipError_t launch_dedup_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu, int Hq,
@@ -49,6 +50,19 @@ hipError_t launch_kl_dk(int H, const uint8_t* q_idx, const uint8_t* k_idx, const
                         const int64_t* seqoff, const int32_t* cu, int nseq, const int2* sched256,
                         const int* count256, int nb256, int max_len, int64_t T, const float* gsc, float* dk_part,
                         float* dk, hipStream_t st);
+int bwd_slices(int max_len);
+hipError_t launch_bwd_delta(const uint16_t* dout, const uint16_t* out, int64_t pairs, float* D, hipStream_t st);
+hipError_t launch_sel_bitmap(const int32_t* idx, int K, const int32_t* cu, const int2* sched32, const int* count32,
+                             int nb32, uint32_t* W, hipStream_t st);
+hipError_t launch_dedup_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                           const float* lse, const float* Dlt, const int32_t* cu, int Hq, int Hkv, float scale,
+                           const int2* sched16, const int* count16, int nb16, int64_t ustride, const int32_t* ukeys,
+                           const uint16_t* umask, const int* ucount, float* dq, hipStream_t st);
+hipError_t launch_sparse_dkv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                             const float* lse, const float* Dlt, const int32_t* cu, int nseq, int Hq, int Hkv,
+                             float scale, const int2* sched128, const int* count128, int nb128, const uint32_t* W,
+                             int max_len, int64_t T, float* dk_part, float* dv_part, float* dk, float* dv,
+                             hipStream_t st);
 hipError_t launch_topk_general(const float* scores, int64_t rows, int n, int64_t ld, const int32_t* lens, int K,
                                int32_t* out, hipStream_t st);
 hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu, int Hq,
@@ -257,6 +271,41 @@ int check_kl(const dsa_prefill_shape* s) {
   if (s->kv_heads != 1 && s->kv_heads != 2 && s->kv_heads != 4) return DSA_ERR_UNSUPPORTED;
   if (s->q_heads % 2 != 0) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
+}
+
+// Sparse attention backward workspace: counts int[64] (0: 16-row, 1: 32-row, 2: 128-key
+// schedule sizes) | D float[T][Hq] | sched16 | sched32 | sched128 | ucount int[nb16] |
+// ukeys int32[nb16][16k] | umask uint16[nb16][16k] | bitmap uint32[(max_len/32 + 1) T] |
+// dk, dv partials float[slices][T][Hkv][128] each.
+struct BwdWs {
+  size_t counts, delta, sched16, sched32, sched128, ucount, ukeys, umask, bitmap, dkpart, dvpart, total;
+  int nb16, nb32, nb128;
+  int64_t ustride;
+};
+
+BwdWs bwd_layout(const dsa_prefill_shape* s) {
+  BwdWs w{};
+  const int64_t T = s->total_tokens;
+  const int B = s->num_seqs;
+  w.nb16 = int((T + 15) / 16 + B);
+  w.nb32 = int((T + 31) / 32 + B);
+  w.nb128 = int((T + 127) / 128 + B);
+  w.ustride = 16 * int64_t(s->topk);
+  const size_t parts = size_t(bwd_slices(s->max_seqlen)) * size_t(T) * size_t(s->kv_heads) * 128 * sizeof(float);
+  size_t off = 0;
+  w.counts = off; off = align_up(off + 64 * sizeof(int), 256);
+  w.delta = off; off = align_up(off + size_t(T) * size_t(s->q_heads) * sizeof(float), 256);
+  w.sched16 = off; off = align_up(off + size_t(w.nb16) * sizeof(int2), 256);
+  w.sched32 = off; off = align_up(off + size_t(w.nb32) * sizeof(int2), 256);
+  w.sched128 = off; off = align_up(off + size_t(w.nb128) * sizeof(int2), 256);
+  w.ucount = off; off = align_up(off + size_t(w.nb16) * sizeof(int), 256);
+  w.ukeys = off; off = align_up(off + size_t(w.nb16) * size_t(w.ustride) * sizeof(int32_t), 256);
+  w.umask = off; off = align_up(off + size_t(w.nb16) * size_t(w.ustride) * sizeof(uint16_t), 256);
+  w.bitmap = off; off = align_up(off + size_t(s->max_seqlen / 32 + 1) * size_t(T) * sizeof(uint32_t), 256);
+  w.dkpart = off; off = align_up(off + parts, 256);
+  w.dvpart = off; off = align_up(off + parts, 256);
+  w.total = off;
+  return w;
 }
 
 bool dedup_supported(const dsa_prefill_shape* s) {
@@ -567,6 +616,69 @@ int dsa_indexer_kl(const dsa_prefill_shape* s, const void* q_idx, const void* k_
                         P, seqoff, s->cu_seqlens, s->num_seqs, at<int2>(ws, K.sched256), counts + 3, K.nb256,
                         s->max_seqlen, s->total_tokens, reinterpret_cast<const float*>(counts + 8),
                         at<float>(ws, K.dkpart), dk_idx, st)) != hipSuccess)
+    return hip_status(e);
+  return DSA_OK;
+}
+
+int dsa_sparse_attention_fwd_lse(const dsa_prefill_shape* s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* topk_idx, uint16_t* out, float* lse, void* stream) {
+  int rc = check_prefill(s, false);
+  if (rc) return rc;
+  if (s->total_tokens == 0) return DSA_OK;
+  if (!q || !k || !v || !topk_idx || !out || !lse) return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return DSA_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_gather_attention(q, k, v, topk_idx, s->topk, 0, s->cu_seqlens, s->num_seqs, nullptr, 0,
+                                            s->total_tokens, s->q_heads, s->kv_heads, s->softmax_scale, 1 << 30, 1,
+                                            out, nullptr, nullptr, static_cast<hipStream_t>(stream), lse));
+}
+
+int dsa_sparse_attention_bwd_workspace_size(const dsa_prefill_shape* s, size_t* bytes) {
+  if (!bytes) return DSA_ERR_INVALID_ARGUMENT;
+  int rc = check_prefill(s, false);
+  if (rc) return rc;
+  if (!dedup_supported(s)) return DSA_ERR_UNSUPPORTED;
+  *bytes = bwd_layout(s).total;
+  return DSA_OK;
+}
+
+int dsa_sparse_attention_bwd(const dsa_prefill_shape* s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const int32_t* topk_idx, const uint16_t* out, const float* lse, const uint16_t* d_out,
+                             float* dq, float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_prefill(s, false);
+  if (rc) return rc;
+  if (!dedup_supported(s)) return DSA_ERR_UNSUPPORTED;
+  if (s->total_tokens == 0) return DSA_OK;
+  if (!q || !k || !v || !topk_idx || !out || !lse || !d_out || !dq || !dk || !dv || !ws)
+    return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(d_out) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(ws))
+    return DSA_ERR_INVALID_ARGUMENT;
+  const BwdWs W = bwd_layout(s);
+  if (ws_bytes < W.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int* counts = at<int>(ws, W.counts);
+  const int32_t* cu = s->cu_seqlens;
+  float* Dl = at<float>(ws, W.delta);
+  hipError_t e;
+  if ((e = launch_build_schedule(cu, s->num_seqs, 16, W.nb16, at<int2>(ws, W.sched16), counts, nullptr, st)) !=
+          hipSuccess ||
+      (e = launch_build_schedule(cu, s->num_seqs, 32, W.nb32, at<int2>(ws, W.sched32), counts + 1, nullptr, st)) !=
+          hipSuccess ||
+      (e = launch_build_schedule(cu, s->num_seqs, 128, W.nb128, at<int2>(ws, W.sched128), counts + 2, nullptr, st)) !=
+          hipSuccess ||
+      (e = launch_bwd_delta(d_out, out, s->total_tokens * s->q_heads, Dl, st)) != hipSuccess ||
+      (e = launch_union(topk_idx, s->topk, cu, at<int2>(ws, W.sched16), counts, W.nb16, W.ustride,
+                        at<int32_t>(ws, W.ukeys), at<uint16_t>(ws, W.umask), at<int>(ws, W.ucount), st)) !=
+          hipSuccess ||
+      (e = launch_dedup_dq(q, k, v, d_out, lse, Dl, cu, s->q_heads, s->kv_heads, s->softmax_scale,
+                           at<int2>(ws, W.sched16), counts, W.nb16, W.ustride, at<int32_t>(ws, W.ukeys),
+                           at<uint16_t>(ws, W.umask), at<int>(ws, W.ucount), dq, st)) != hipSuccess ||
+      (e = launch_sel_bitmap(topk_idx, s->topk, cu, at<int2>(ws, W.sched32), counts + 1, W.nb32,
+                             at<uint32_t>(ws, W.bitmap), st)) != hipSuccess ||
+      (e = launch_sparse_dkv(q, k, v, d_out, lse, Dl, cu, s->num_seqs, s->q_heads, s->kv_heads, s->softmax_scale,
+                             at<int2>(ws, W.sched128), counts + 2, W.nb128, at<uint32_t>(ws, W.bitmap), s->max_seqlen,
+                             s->total_tokens, at<float>(ws, W.dkpart), at<float>(ws, W.dvpart), dk, dv, st)) !=
+          hipSuccess)
     return hip_status(e);
   return DSA_OK;
 }

@@ -65,6 +65,9 @@ EXPORTS = {
     "dsa_prefill_dedup": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "dsa_indexer_kl_workspace_size": ([ctypes.POINTER(PrefillShape), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "dsa_indexer_kl": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "dsa_sparse_attention_fwd_lse": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 7, ctypes.c_int),
+    "dsa_sparse_attention_bwd_workspace_size": ([ctypes.POINTER(PrefillShape), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "dsa_sparse_attention_bwd": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 11 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "dsa_topk": ([ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
                   ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
 }
@@ -270,3 +273,21 @@ def dsa_indexer_kl(shape, q_idx, k_idx, w_idx, q, k, kl, dq_idx, dk_idx, dw_idx,
     _check(lib().dsa_indexer_kl(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(k), _ptr(kl),
                                 _ptr(dq_idx), _ptr(dk_idx), _ptr(dw_idx), _ptr(workspace), _nbytes(workspace),
                                 _stream(stream)), "dsa_indexer_kl")
+
+
+def dsa_sparse_attention_fwd_lse(shape, q, k, v, topk_idx, out, lse, stream=None):
+    _check(lib().dsa_sparse_attention_fwd_lse(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(topk_idx), _ptr(out),
+                                              _ptr(lse), _stream(stream)), "dsa_sparse_attention_fwd_lse")
+
+
+def dsa_sparse_attention_bwd_workspace_size(shape: PrefillShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().dsa_sparse_attention_bwd_workspace_size(ctypes.byref(shape), ctypes.byref(n)),
+           "dsa_sparse_attention_bwd_workspace_size")
+    return n.value
+
+
+def dsa_sparse_attention_bwd(shape, q, k, v, topk_idx, out, lse, d_out, dq, dk, dv, workspace, stream=None):
+    _check(lib().dsa_sparse_attention_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(topk_idx), _ptr(out),
+                                          _ptr(lse), _ptr(d_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                          _nbytes(workspace), _stream(stream)), "dsa_sparse_attention_bwd")

@@ -380,3 +380,8 @@ def make_topk_scores(rows: int, n: int, *, seed: int, kind: str = "normal", mask
     if n > 0:
         _par(work, [(i, a, b) for i, (a, b) in enumerate(parts)])
     return out
+
+
+def make_grad_bf16(shape, seed: int) -> np.ndarray:
+    """An upstream gradient (e.g. dO [T, Hq, d]): N(0,1) rounded to bf16 (bit patterns)."""
+    return _fill_normal_bf16(np.random.SeedSequence(seed), tuple(shape))

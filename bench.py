@@ -275,6 +275,48 @@ def bench_indexer_kl(reps=3):
     return dict(ms=ms, tokens=L, bf16_flop=float(bf16_flop), fp8_flop=float(fp8_flop))
 
 
+def bench_sparse_bwd(reps=3):
+    """Sparse attention backward on one 32768-token sequence with k = 2048 (the 32K prefill
+    shapes): dsa_sparse_attention_bwd given the forward's out and lse, timed with HIP events."""
+    import torch
+    from sparse_attention_long_04_amd import dsa, workloads
+    from sparse_attention_long_04_amd import inputs as gen
+    from sparse_attention_long_04_amd.runtime import PrefillBatch, timing_events
+
+    p = workloads.make(workloads.P32K)
+    pb = PrefillBatch(p)
+    pb.index_topk()
+    T, Hq, d = p.q.shape
+    Hkv = p.k.shape[1]
+    out = torch.empty_like(pb.out)
+    lse = torch.empty((T, Hq), dtype=torch.float32, device="cuda")
+    dsa.dsa_sparse_attention_fwd_lse(pb.shape, pb.q, pb.k, pb.v, pb.topk_idx, out, lse)
+    dout = torch.from_numpy(gen.make_grad_bf16((T, Hq, d), 1008).view(np.int16)).cuda()
+    pb.ws = None
+    torch.cuda.empty_cache()
+    ws = torch.empty(dsa.dsa_sparse_attention_bwd_workspace_size(pb.shape), dtype=torch.uint8, device="cuda")
+    dq = torch.empty((T, Hq, d), dtype=torch.float32, device="cuda")
+    dk = torch.empty((T, Hkv, d), dtype=torch.float32, device="cuda")
+    dv = torch.empty((T, Hkv, d), dtype=torch.float32, device="cuda")
+    args = (pb.shape, pb.q, pb.k, pb.v, pb.topk_idx, out, lse, dout, dq, dk, dv, ws)
+    dsa.dsa_sparse_attention_bwd(*args)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    a, b = timing_events(2)
+    a.record(st)
+    for _ in range(reps):
+        dsa.dsa_sparse_attention_bwd(*args)
+    b.record(st)
+    torch.cuda.synchronize()
+    ms = ms_between(a, b) / reps
+    sel = selected_of([T], p.topk)
+    useful = sel * Hq * d * 2 * 4  # dS (via dP), and the dq, dk, dv products: 4 x 2 flop per (pair, head, dim)
+    log(f"sparse attention backward 32K: {ms:.2f} ms per call")
+    del pb, ws, dq, dk, dv
+    torch.cuda.empty_cache()
+    return dict(ms=ms, tokens=T, useful_flop=float(useful))
+
+
 def bench_topk_general(reps=5):
     """The standalone top-k (dsa_topk) on its workload: 2048 rows x 131072 fp32 scores, k = 2048,
     timed over ``reps`` back-to-back launches with HIP events.  torch.topk on the same scores is
@@ -348,7 +390,7 @@ def main():
     ap.add_argument("--quick", action="store_true", help="prefill only (no dense/decode/varlen/cpu)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--only", choices=["decode", "topk", "dedup", "kl"], default=None,
+    ap.add_argument("--only", choices=["decode", "topk", "dedup", "kl", "bwd"], default=None,
                     help="profiling aid: run only the decode (or standalone top-k) measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (scales the HBM byte counters)")
@@ -382,6 +424,9 @@ def main():
         return
     if args.only == "kl":
         print(json.dumps(bench_indexer_kl()), flush=True)
+        return
+    if args.only == "bwd":
+        print(json.dumps(bench_sparse_bwd()), flush=True)
         return
     name = args.workload or workloads.P128K
     w = workloads.WORKLOADS[name]
@@ -473,6 +518,11 @@ def main():
                               "tokens_per_s": round(kr["tokens"] / (kr["ms"] * 1e-3), 1),
                               "roofline": roof("mfma", kl_equiv / (kr["ms"] * 1e-3), PEAK_BF16, "TFLOP/s", None,
                                                kl_equiv, "bf16-equivalent flop (executed MFMA work)")}
+        sb = bench_sparse_bwd()
+        line["sparse_attention_bwd"] = {"workload": "prefill_32k (32768 tokens, k = 2048, GQA 32q/4kv d128)",
+                                        "ms": round(sb["ms"], 3),
+                                        "tokens_per_s": round(sb["tokens"] / (sb["ms"] * 1e-3), 1),
+                                        "useful_tflops": round(sb["useful_flop"] / (sb["ms"] * 1e-3) / 1e12, 1)}
         vl = bench_prefill(workloads.VARLEN, max(1, args.steps - 1), 1, with_dense=False)
         line["varlen"] = {"workload": workloads.VARLEN, "tokens_per_s": round(vl["T"] / (vl["ms"] * 1e-3), 1),
                           "ms": round(vl["ms"], 3), "lengths": vl["lengths"]}

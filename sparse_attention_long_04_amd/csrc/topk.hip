@@ -377,12 +377,139 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));
 }
 
+// ---- prefill fast path for long rows: a sampled threshold and one pass over HBM ------------
+// A histogram of every kSampleStride-th 64-byte line of the row places a value bin b_est below
+// the k-th largest score with a margin of a few standard deviations; one pass then gathers every
+// element of bin >= b_est into the LDS list (slots reserved with one LDS atomic per wave and
+// load group, so the list is in no particular order).  The exact threshold bin is found on the
+// list and its elements ranked pairwise by (key desc, index asc); the kept positions are marked
+// in an LDS bitmap and written in index order.  Any miss (too few or too many candidates, a
+// crowded threshold bin) returns false before anything is written, and the exact two-pass path
+// runs instead, so the result never depends on the sample.
+constexpr int kSampleStride = 8;                          // sample one 16-float line in 8
+constexpr int kFastMinN = 65536;                          // shorter rows: the exact path
+constexpr int kFastMaxN = kTopkWaves * kVBins * 32;       // bitmap bits that fit in the union
+
+__device__ bool select_row_fast(const float* __restrict__ row, int n, int K, float lo, float sc,
+                                int32_t* __restrict__ out, TopkRowSmem& sm) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // 1. sampled histogram (rows are 64-byte aligned, so every sample is one whole line)
+  for (int i = tid; i < kVBins; i += kTopkThreads) sm.s.hist[i] = 0;
+  if (tid == 0) sm.s.list_n = 0;
+  __syncthreads();
+  const int nlines = n >> 4;
+  const int nsl = (nlines + kSampleStride - 1) / kSampleStride;
+  for (int m = tid; m < nsl; m += kTopkThreads) {
+    const float* p = row + (int64_t)m * kSampleStride * 16;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) atomicAdd(&sm.s.hist[value_bin(x[e], lo, sc, kVBins)], 1);
+    }
+  }
+  __syncthreads();
+  const int ns = 16 * nsl;
+  const float expect = float(K) * float(ns) / float(n);
+  const int need = int(expect * 1.1f + 3.f * sqrtf(expect) + 4.f);
+  if (need > ns) return false;
+  find_digit(sm.s, kVBins, need);
+  const int b_est = sm.s.sel_digit;
+  // 2. one pass: every element of bin >= b_est into the list
+  const int seg = (((n + kTopkWaves - 1) / kTopkWaves) + 3) & ~3;
+  const int seg_lo = min(n, w * seg), seg_hi = min(n, seg_lo + seg);
+  constexpr int STEPW = 256 * kQ;
+  for (int base = seg_lo; base < seg_hi; base += STEPW) {
+    f32x4 v[kQ];
+    load_step(row, base, seg_hi, lane, v);
+#pragma unroll
+    for (int e = 0; e < kQ; ++e) {
+      const int i0 = base + 4 * (lane + 64 * e);
+      bool keep[4];
+      int before = 0, total = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        keep[j] = (i0 + j < seg_hi) && value_bin(v[e][j], lo, sc, kVBins) >= b_est;
+        const uint64_t bm = __ballot(keep[j]);
+        before += lanes_below(bm);
+        total += __popcll(bm);
+      }
+      if (total == 0) continue;
+      int bpos = 0;
+      if (lane == 0) bpos = atomicAdd(&sm.s.list_n, total);
+      int slot = __shfl(bpos, 0) + before;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (keep[j]) {
+          if (slot < kListCap) {
+            sm.u.l.lkeys[slot] = score_key(v[e][j]);
+            sm.u.l.lids[slot] = i0 + j;
+          }
+          ++slot;
+        }
+    }
+  }
+  __syncthreads();
+  const int total = sm.s.list_n;
+  if (total < K || total > kListCap) return false;
+  // 3. the exact threshold bin among the candidates (they contain every element of bin >= b_est)
+  for (int i = tid; i < kVBins; i += kTopkThreads) sm.s.hist[i] = 0;
+  __syncthreads();
+  auto bin_of = [&](uint32_t k) { return value_bin(key_to_score(k), lo, sc, kVBins); };
+  for (int i = tid; i < total; i += kTopkThreads) atomicAdd(&sm.s.hist[bin_of(sm.u.l.lkeys[i])], 1);
+  __syncthreads();
+  find_digit(sm.s, kVBins, K);
+  const int b1 = sm.s.sel_digit, above = sm.s.sel_above;
+  if (!rank_threshold_bin(sm.u.l.lkeys, sm.u.l.lids, total, b1, K - above, bin_of, sm.f)) return false;
+  // 4. kept = bin > b1, or bin == b1 and not rejected; their positions into registers, then a
+  // bitmap over [0, n) (in the union, now free) and an ordered emit
+  constexpr int PER = kListCap / kTopkThreads;
+  int kept[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) {
+    const int i = tid + kTopkThreads * c;
+    kept[c] = -1;
+    if (i < total) {
+      const uint32_t k = sm.u.l.lkeys[i];
+      if (k != 0u && bin_of(k) >= b1) kept[c] = sm.u.l.lids[i];
+    }
+  }
+  __syncthreads();
+  uint32_t* bits = reinterpret_cast<uint32_t*>(&sm.u);
+  const int nwords = (n + 31) >> 5;
+  for (int i = tid; i < nwords; i += kTopkThreads) bits[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < PER; ++c)
+    if (kept[c] >= 0) atomicOr(&bits[kept[c] >> 5], 1u << (kept[c] & 31));
+  __syncthreads();
+  const int wpt = (nwords + kTopkThreads - 1) / kTopkThreads;  // words per thread, in order
+  const int w0 = min(nwords, tid * wpt), w1 = min(nwords, w0 + wpt);
+  int cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __popc(bits[i]);
+  int tot;
+  const int incl = block_incl_scan(cnt, sm.s.wave_tot, &tot);
+  int pos = incl - cnt;
+  for (int i = w0; i < w1; ++i) {
+    uint32_t x = bits[i];
+    while (x) {
+      const int bpos = __ffs(x) - 1;
+      out[pos++] = 32 * i + bpos;
+      x &= x - 1u;
+    }
+  }
+  return true;
+}
+
 __device__ void select_row(const float* __restrict__ row, int n, int K, float lo, float hi,
                            int32_t* __restrict__ out, TopkRowSmem& sm) {
   if (n <= K || !(hi > lo)) {  // everything kept, or every score equal: the first k keys win
     first_k(n, K, out);
     return;
   }
+  if (n >= kFastMinN && n <= kFastMaxN && select_row_fast(row, n, K, lo, float(kVBins) / (hi - lo), out, sm))
+    return;
+  __syncthreads();  // the fast path's LDS is reused below
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const float sc = float(kVBins) / (hi - lo);
   // wave w owns the contiguous segment [seg_lo, seg_hi) (starts are multiples of 4 elements)

@@ -377,7 +377,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));
 }
 
-// ---- prefill fast path for long rows: a sampled threshold and one pass over HBM ------------
+// ---- prefill fast path for rows of 8K+ keys: a sampled threshold and one pass over HBM ----
 // A histogram of every kSampleStride-th 64-byte line of the row places a value bin b_est below
 // the k-th largest score with a margin of a few standard deviations; one pass then gathers every
 // element of bin >= b_est into the LDS list (slots reserved with one LDS atomic per wave and
@@ -387,7 +387,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // crowded threshold bin) returns false before anything is written, and the exact two-pass path
 // runs instead, so the result never depends on the sample.
 constexpr int kSampleStride = 8;                          // sample one 16-float line in 8
-constexpr int kFastMinN = 65536;                          // shorter rows: the exact path
+constexpr int kFastMinN = 8192;                           // shorter rows: the exact path
 constexpr int kFastMaxN = kTopkWaves * kVBins * 32;       // bitmap bits that fit in the union
 
 __device__ bool select_row_fast(const float* __restrict__ row, int n, int K, float lo, float sc,
@@ -411,7 +411,7 @@ __device__ bool select_row_fast(const float* __restrict__ row, int n, int K, flo
   __syncthreads();
   const int ns = 16 * nsl;
   const float expect = float(K) * float(ns) / float(n);
-  const int need = int(expect * 1.1f + 3.f * sqrtf(expect) + 4.f);
+  const int need = int(expect + 3.f * sqrtf(expect) + 4.f);
   if (need > ns) return false;
   find_digit(sm.s, kVBins, need);
   const int b_est = sm.s.sel_digit;

@@ -395,3 +395,36 @@ def test_indexer_head_shapes(H, dt, dI):
     o = oracle_of(p)
     for t in [0, 299, 300, 1199, 1200, 1449]:
         assert np.array_equal(idx[t], O.select_topk_row(o.scores(t), p.topk)), t
+
+
+def test_topk_long_rows_sampled_threshold():
+    """Rows of 8K..20K keys take the sampled-threshold single pass; every one of a spread of
+    rows must match the oracle's select exactly."""
+    p = gen.make_prefill([20000], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=2048,
+                         seed=43, video=True)
+    pb = PrefillBatch(p)
+    pb.index_topk()
+    idx = pb.topk_idx.cpu().numpy()
+    o = oracle_of(p)
+    rng = np.random.default_rng(3)
+    rows = np.concatenate([[8190, 8191, 8192, 8193, 12345, 19999], rng.integers(8192, 20000, 14)])
+    for t in rows:
+        assert np.array_equal(idx[t], O.select_topk_row(o.scores(int(t)), p.topk)), int(t)
+
+
+@pytest.mark.parametrize("hot_on_sampled", [False, True])
+def test_topk_sample_misleads(hot_on_sampled):
+    """Keys are zeroed (score exactly 0) on one class of 16-key lines: either the lines a 1-in-8
+    sample reads or the others.  The sample then over- or under-estimates the threshold (too
+    many candidates, or fewer than k); the select must still match the oracle exactly."""
+    n = 20000
+    p = gen.make_prefill([n], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=2048, seed=44)
+    sampled = (np.arange(n) // 16) % 8 == 0
+    cold = ~sampled if hot_on_sampled else sampled
+    p.k_idx[cold] = 0
+    pb = PrefillBatch(p)
+    pb.index_topk()
+    idx = pb.topk_idx.cpu().numpy()
+    o = oracle_of(p)
+    for t in [8191, 8192, 9000, 15000, 19999]:
+        assert np.array_equal(idx[t], O.select_topk_row(o.scores(t), p.topk)), t

@@ -65,7 +65,7 @@ __device__ __forceinline__ int block_incl_scan(int v, int* wave_tot, int* total)
 
 // Given sm.hist[0..nb) filled, find the digit d with  above(d) < krem <= above(d) + hist[d],
 // above(d) = sum of hist over digits > d.  Results in sm.sel_digit / sm.sel_above.
-__device__ void find_digit(TopkSmem& sm, int nb, int krem) {
+__device__ __forceinline__ void find_digit(TopkSmem& sm, int nb, int krem) {
   const int tid = threadIdx.x;
   const int bpt = nb / kTopkThreads;
   const int top = nb - bpt * tid;
@@ -279,7 +279,7 @@ struct FinishSmem {
 
 // Returns false (list untouched) when bin b1 holds more than CAP elements.
 template <int CAP, class BinOf>
-__device__ bool rank_threshold_bin(uint32_t* keys, const int* ids, int total, int b1, int krem, BinOf bin_of,
+__device__ __forceinline__ bool rank_threshold_bin(uint32_t* keys, const int* ids, int total, int b1, int krem, BinOf bin_of,
                                    FinishSmem<CAP>& fs) {
   constexpr int kSubCap = CAP;
   if (threadIdx.x == 0) fs.sub_n = 0;
@@ -302,6 +302,7 @@ __device__ bool rank_threshold_bin(uint32_t* keys, const int* ids, int total, in
     const uint32_t k = fs.sk[j];
     const int id = fs.sid[j];
     int rank = 0;
+#pragma unroll 8
     for (int x = 0; x < m; ++x) {
       const uint32_t kx = fs.sk[x];
       rank += (kx > k) | ((kx == k) & (fs.sid[x] < id));
@@ -377,7 +378,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));
 }
 
-// ---- prefill fast path for rows of 8K+ keys: a sampled threshold and one pass over HBM ----
+// ---- fast path for rows of 8K+ keys: a sampled threshold and one pass over HBM -------------
 // A histogram of every kSampleStride-th 64-byte line of the row places a value bin b_est below
 // the k-th largest score with a margin of a few standard deviations; one pass then gathers every
 // element of bin >= b_est into the LDS list (slots reserved with one LDS atomic per wave and
@@ -388,34 +389,133 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // runs instead, so the result never depends on the sample.
 constexpr int kSampleStride = 8;                          // sample one 16-float line in 8
 constexpr int kFastMinN = 8192;                           // shorter rows: the exact path
-constexpr int kFastMaxN = kTopkWaves * kVBins * 32;       // bitmap bits that fit in the union
+constexpr int kFastMaxN = int(sizeof(decltype(TopkRowSmem::u))) * 8;  // bitmap bits in the union
 
-__device__ bool select_row_fast(const float* __restrict__ row, int n, int K, float lo, float sc,
-                                int32_t* __restrict__ out, TopkRowSmem& sm) {
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  // 1. sampled histogram (rows are 64-byte aligned, so every sample is one whole line)
-  for (int i = tid; i < kVBins; i += kTopkThreads) sm.s.hist[i] = 0;
-  if (tid == 0) sm.s.list_n = 0;
+// Sampled threshold bin of a row whose scores lie in [lo, lo + kVBins/sc] (rows start 64-byte
+// aligned, so every sampled line is whole).  The bin leaves z standard deviations of the sampled
+// count (plus 4) as margin above k.  Returns 0 (every element a candidate) when the sample is too
+// small to place the margin.  BATCH line loads per thread are issued before their histogram
+// atomics.  Every thread of the block must call it; all get the same result.
+template <int BATCH>
+__device__ __forceinline__ int sample_threshold(const float* __restrict__ row, int n, int K, float lo, float sc,
+                                                float z, TopkSmem& s) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kVBins; i += kTopkThreads) s.hist[i] = 0;
   __syncthreads();
   const int nlines = n >> 4;
   const int nsl = (nlines + kSampleStride - 1) / kSampleStride;
-  for (int m = tid; m < nsl; m += kTopkThreads) {
-    const float* p = row + (int64_t)m * kSampleStride * 16;
+  for (int m0 = 0; m0 < nsl; m0 += BATCH * kTopkThreads) {
+    f32x4 x[BATCH][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * c);
+    for (int u = 0; u < BATCH; ++u) {
+      const int m = m0 + u * kTopkThreads + tid;
+      if (m < nsl) {
+        const float* p = row + (int64_t)m * kSampleStride * 16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(&sm.s.hist[value_bin(x[e], lo, sc, kVBins)], 1);
+        for (int c = 0; c < 4; ++c) x[u][c] = *reinterpret_cast<const f32x4*>(p + 4 * c);
+      }
     }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u)
+      if (m0 + u * kTopkThreads + tid < nsl)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) atomicAdd(&s.hist[value_bin(x[u][c][e], lo, sc, kVBins)], 1);
   }
   __syncthreads();
   const int ns = 16 * nsl;
   const float expect = float(K) * float(ns) / float(n);
-  const int need = int(expect + 3.f * sqrtf(expect) + 4.f);
-  if (need > ns) return false;
-  find_digit(sm.s, kVBins, need);
-  const int b_est = sm.s.sel_digit;
-  // 2. one pass: every element of bin >= b_est into the list
+  const int need = int(expect + z * sqrtf(expect) + 4.f);
+  if (need > ns) return 0;
+  find_digit(s, kVBins, need);
+  return s.sel_digit;
+}
+
+// keys/ids (LDS) hold `total` (K <= total <= CAP) candidates of a row of n <= kFastMaxN scores,
+// in any order, among them every element whose value bin is >= some bin b_est.  Finds the exact
+// threshold bin b1 (>= b_est), ranks its elements, and writes the k selected positions in index
+// order.  `bits` (kFastMaxN / 32 words of LDS) may alias keys/ids: the kept positions are moved
+// to registers first.  Each kept position then finds its output slot directly: the exclusive
+// count of 4-word bitmap groups before it (a block scan, stored in s.hist) plus at most four
+// popcounts -- balanced however the selection clusters.  Returns false, with nothing written,
+// when bin b1 is too crowded to rank in LDS.
+static_assert(kFastMaxN / 128 <= kBins, "bitmap group counts must fit the histogram array");
+
+template <int CAP>
+__device__ __forceinline__ bool finish_unordered(int n, int K, float lo, float sc, int total, uint32_t* keys,
+                                                 int* ids, uint32_t* bits, int32_t* __restrict__ out, TopkSmem& s,
+                                                 FinishSmem<512>& f) {
+  static_assert(CAP % kTopkThreads == 0, "list capacity must be a multiple of the block size");
+  const int tid = threadIdx.x;
+  auto bin_of = [&](uint32_t k) { return value_bin(key_to_score(k), lo, sc, kVBins); };
+  for (int i = tid; i < kVBins; i += kTopkThreads) s.hist[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < total; i += kTopkThreads) atomicAdd(&s.hist[bin_of(keys[i])], 1);
+  __syncthreads();
+  find_digit(s, kVBins, K);
+  const int b1 = s.sel_digit, above = s.sel_above;
+  if (!rank_threshold_bin(keys, ids, total, b1, K - above, bin_of, f)) return false;
+  // kept = bin > b1, or bin == b1 and not rejected (rejected keys were set to 0)
+  constexpr int PER = CAP / kTopkThreads;
+  int kept[PER];
+#pragma unroll
+  for (int c = 0; c < PER; ++c) {
+    const int i = tid + kTopkThreads * c;
+    kept[c] = -1;
+    if (i < total) {
+      const uint32_t k = keys[i];
+      if (k != 0u && bin_of(k) >= b1) kept[c] = ids[i];
+    }
+  }
+  __syncthreads();
+  const int nwords = (n + 31) >> 5;
+  for (int i = tid; i < nwords; i += kTopkThreads) bits[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < PER; ++c)
+    if (kept[c] >= 0) atomicOr(&bits[kept[c] >> 5], 1u << (kept[c] & 31));
+  __syncthreads();
+  // exclusive counts of 4-word groups: thread t scans groups [t*gpt, t*gpt + gpt)
+  const int ngroups = (nwords + 3) >> 2;
+  const int gpt = (ngroups + kTopkThreads - 1) / kTopkThreads;
+  const int g0 = min(ngroups, tid * gpt), g1 = min(ngroups, g0 + gpt);
+  auto group_count = [&](int g) {
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (4 * g + q < nwords) c += __popc(bits[4 * g + q]);
+    return c;
+  };
+  int cnt = 0;
+  for (int g = g0; g < g1; ++g) cnt += group_count(g);
+  int tot;
+  const int incl = block_incl_scan(cnt, s.wave_tot, &tot);
+  int run = incl - cnt;
+  for (int g = g0; g < g1; ++g) {
+    s.hist[g] = run;  // the histogram is no longer needed; ngroups <= kBins
+    run += group_count(g);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < PER; ++c) {
+    const int id = kept[c];
+    if (id >= 0) {
+      const int w = id >> 5, g = w >> 2;
+      int pos = s.hist[g] + __popc(bits[w] & ((1u << (id & 31)) - 1u));
+      for (int q = 4 * g; q < w; ++q) pos += __popc(bits[q]);
+      out[pos] = id;
+    }
+  }
+  return true;
+}
+
+__device__ bool select_row_fast(const float* __restrict__ row, int n, int K, float lo, float sc,
+                                int32_t* __restrict__ out, TopkRowSmem& sm) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  if (tid == 0) sm.s.list_n = 0;
+  const int b_est = sample_threshold<2>(row, n, K, lo, sc, 3.f, sm.s);
+  // one pass: every element of bin >= b_est into the list
   const int seg = (((n + kTopkWaves - 1) / kTopkWaves) + 3) & ~3;
   const int seg_lo = min(n, w * seg), seg_hi = min(n, seg_lo + seg);
   constexpr int STEPW = 256 * kQ;
@@ -452,64 +552,15 @@ __device__ bool select_row_fast(const float* __restrict__ row, int n, int K, flo
   __syncthreads();
   const int total = sm.s.list_n;
   if (total < K || total > kListCap) return false;
-  // 3. the exact threshold bin among the candidates (they contain every element of bin >= b_est)
-  for (int i = tid; i < kVBins; i += kTopkThreads) sm.s.hist[i] = 0;
-  __syncthreads();
-  auto bin_of = [&](uint32_t k) { return value_bin(key_to_score(k), lo, sc, kVBins); };
-  for (int i = tid; i < total; i += kTopkThreads) atomicAdd(&sm.s.hist[bin_of(sm.u.l.lkeys[i])], 1);
-  __syncthreads();
-  find_digit(sm.s, kVBins, K);
-  const int b1 = sm.s.sel_digit, above = sm.s.sel_above;
-  if (!rank_threshold_bin(sm.u.l.lkeys, sm.u.l.lids, total, b1, K - above, bin_of, sm.f)) return false;
-  // 4. kept = bin > b1, or bin == b1 and not rejected; their positions into registers, then a
-  // bitmap over [0, n) (in the union, now free) and an ordered emit
-  constexpr int PER = kListCap / kTopkThreads;
-  int kept[PER];
-#pragma unroll
-  for (int c = 0; c < PER; ++c) {
-    const int i = tid + kTopkThreads * c;
-    kept[c] = -1;
-    if (i < total) {
-      const uint32_t k = sm.u.l.lkeys[i];
-      if (k != 0u && bin_of(k) >= b1) kept[c] = sm.u.l.lids[i];
-    }
-  }
-  __syncthreads();
-  uint32_t* bits = reinterpret_cast<uint32_t*>(&sm.u);
-  const int nwords = (n + 31) >> 5;
-  for (int i = tid; i < nwords; i += kTopkThreads) bits[i] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int c = 0; c < PER; ++c)
-    if (kept[c] >= 0) atomicOr(&bits[kept[c] >> 5], 1u << (kept[c] & 31));
-  __syncthreads();
-  const int wpt = (nwords + kTopkThreads - 1) / kTopkThreads;  // words per thread, in order
-  const int w0 = min(nwords, tid * wpt), w1 = min(nwords, w0 + wpt);
-  int cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(bits[i]);
-  int tot;
-  const int incl = block_incl_scan(cnt, sm.s.wave_tot, &tot);
-  int pos = incl - cnt;
-  for (int i = w0; i < w1; ++i) {
-    uint32_t x = bits[i];
-    while (x) {
-      const int bpos = __ffs(x) - 1;
-      out[pos++] = 32 * i + bpos;
-      x &= x - 1u;
-    }
-  }
-  return true;
+  return finish_unordered<kListCap>(n, K, lo, sc, total, sm.u.l.lkeys, sm.u.l.lids,
+                                    reinterpret_cast<uint32_t*>(&sm.u), out, sm.s, sm.f);
 }
 
-__device__ void select_row(const float* __restrict__ row, int n, int K, float lo, float hi,
-                           int32_t* __restrict__ out, TopkRowSmem& sm) {
-  if (n <= K || !(hi > lo)) {  // everything kept, or every score equal: the first k keys win
-    first_k(n, K, out);
-    return;
-  }
-  if (n >= kFastMinN && n <= kFastMaxN && select_row_fast(row, n, K, lo, float(kVBins) / (hi - lo), out, sm))
-    return;
-  __syncthreads();  // the fast path's LDS is reused below
+// Exact select of a row with n > K and hi > lo: two passes over the row (per-wave value
+// histograms, then an ordered compaction of the threshold bin and above), with radix passes over
+// HBM for rows whose candidates overflow the LDS list.
+__device__ __forceinline__ void select_row_exact(const float* __restrict__ row, int n, int K, float lo, float hi,
+                                 int32_t* __restrict__ out, TopkRowSmem& sm) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const float sc = float(kVBins) / (hi - lo);
   // wave w owns the contiguous segment [seg_lo, seg_hi) (starts are multiples of 4 elements)
@@ -613,6 +664,18 @@ __device__ void select_row(const float* __restrict__ row, int n, int K, float lo
   }
 }
 
+__device__ void select_row(const float* __restrict__ row, int n, int K, float lo, float hi,
+                           int32_t* __restrict__ out, TopkRowSmem& sm) {
+  if (n <= K || !(hi > lo)) {  // everything kept, or every score equal: the first k keys win
+    first_k(n, K, out);
+    return;
+  }
+  if (n >= kFastMinN && n <= kFastMaxN && select_row_fast(row, n, K, lo, float(kVBins) / (hi - lo), out, sm))
+    return;
+  __syncthreads();  // the fast path's LDS is reused below
+  select_row_exact(row, n, K, lo, hi, out, sm);
+}
+
 // Prefill rows: one workgroup per token, longest rows first (row t = T-1-blockIdx.x).
 __global__ __launch_bounds__(kTopkThreads) void topk_prefill_kernel(
     const float* __restrict__ tri, const int64_t* __restrict__ seqoff, const int32_t* __restrict__ cu,
@@ -633,13 +696,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_prefill_kernel(
 //   (cleared before the indexer), lists [B][nchunk][kChunk] (key, id), counts [B][nchunk].
 // ------------------------------------------------------------------------------------------
 struct RowRange {
-  float lo, sc;
+  float lo, hi, sc;  // sc: kBins value bins over [lo, hi]
   bool flat;
 };
 
 // Row range from the decode indexer's per-block (min, max) key slots (kDecodeKeysPerBlock keys
 // per slot).  Every thread of the block must call it.
-__device__ RowRange decode_range(const uint2* __restrict__ blkrange, int stride, int b, int n, TopkSmem& sm) {
+__device__ __forceinline__ RowRange decode_range(const uint2* __restrict__ blkrange, int stride, int b, int n, TopkSmem& sm) {
   const int nblk = (n + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int i = threadIdx.x; i < nblk; i += kTopkThreads) {
@@ -661,9 +724,9 @@ __device__ RowRange decode_range(const uint2* __restrict__ blkrange, int stride,
   __syncthreads();
   RowRange rr;
   rr.lo = key_to_score(mn);
-  const float hi = key_to_score(mx);
-  rr.flat = !(hi > rr.lo);
-  rr.sc = rr.flat ? 0.f : float(kBins) / (hi - rr.lo);
+  rr.hi = key_to_score(mx);
+  rr.flat = !(rr.hi > rr.lo);
+  rr.sc = rr.flat ? 0.f : float(kBins) / (rr.hi - rr.lo);
   return rr;
 }
 

@@ -12,7 +12,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
-constexpr int kDecodeKeysPerBlock = 1024;  // cached keys per decode-indexer workgroup (one range slot each)
+constexpr int kDecodeKeysPerBlock = 256;   // cached keys per decode-indexer workgroup (one range slot each)
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 

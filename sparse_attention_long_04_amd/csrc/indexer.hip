@@ -411,10 +411,13 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
   const int kw0 = key0 + wave * WKEYS;
   const int kw1 = min(n, kw0 + WKEYS);
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  // loads are clamped to the wave's own last key: the prefetch issued by its last step then
+  // re-reads cached lines instead of fetching the next wave's keys
+  const int klast = kw1 - 1;  // >= 0: n >= 1 here
   auto load = [&](i32x8 (&dst)[NT], int kb) {
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
-      const int key = min(kb + 16 * jt + r, n - 1);
+      const int key = min(kb + 16 * jt + r, klast);
       const uint8_t* p = k_cache + ((int64_t)b * cap + key) * ROWB + g * CH;
       const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
       const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
@@ -454,15 +457,24 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
       }
     }
   };
-  // the first keys are requested before the queries are staged, so the two latencies overlap
+  // the first keys, the queries and the head weights are all requested before any is used:
+  // one round trip (a load-then-store loop would wait for each of its loads in turn)
   i32x8 bA[NT], bB[NT];
-  load(bA, min(kw0, n - 1));
-  for (int u = tid; u < H * UNITS; u += 256) {
-    const int h = u / UNITS, c = u - h * UNITS;
-    *reinterpret_cast<i32x4*>(q_lds + h * ROWB + ((c ^ (h & 7)) * 16)) =
-        *reinterpret_cast<const i32x4*>(q_idx + ((int64_t)b * H + h) * ROWB + c * 16);
+  load(bA, kw0);
+  constexpr int QPT = HMAX * UNITS / 256;  // 16-byte query pieces per thread
+  i32x4 qv[QPT];
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int u = tid + 256 * j, h = u / UNITS, c = u - h * UNITS;
+    if (h < H) qv[j] = *reinterpret_cast<const i32x4*>(q_idx + ((int64_t)b * H + h) * ROWB + c * 16);
   }
-  for (int h = tid; h < H; h += 256) w_lds[h] = w_idx[(int64_t)b * H + h];
+  const float wv_in = tid < H ? w_idx[(int64_t)b * H + tid] : 0.f;
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int u = tid + 256 * j, h = u / UNITS, c = u - h * UNITS;
+    if (h < H) *reinterpret_cast<i32x4*>(q_lds + h * ROWB + ((c ^ (h & 7)) * 16)) = qv[j];
+  }
+  if (tid < H) w_lds[tid] = wv_in;
   __syncthreads();
   if (kw0 < kw1) {
     for (int kb = kw0; kb < kw1; kb += 2 * NT * 16) {
@@ -530,7 +542,7 @@ hipError_t launch_indexer_decode(const void* q_idx, const float* w, const void* 
                                  int64_t score_ld, float* scores, int* ghist, uint2* blkrange,
                                  hipStream_t st) {
   dim3 grid((max_len + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock, B);
-  indexer_decode_kernel<64, 4><<<grid, 256, 0, st>>>(static_cast<const uint8_t*>(q_idx), w,
+  indexer_decode_kernel<64, 2><<<grid, 256, 0, st>>>(static_cast<const uint8_t*>(q_idx), w,
                                                      static_cast<const uint8_t*>(k_cache), cache_lens,
                                                      cap, H, score_ld, scores, blkrange, (int)grid.x, ghist);
   return hipGetLastError();

@@ -524,7 +524,7 @@ hipError_t launch_indexer_prefill(bool fp8, int di, const void* q_idx, const voi
   else if (!fp8 && di == 64)
     indexer_prefill_kernel<false, 64, 64, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores, rowrange);
   else if (!fp8 && di == 128)
-    indexer_prefill_kernel<false, 128, 32, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores, rowrange);
+    indexer_prefill_kernel<false, 128, 32, 8, 1><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores, rowrange);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -137,12 +137,14 @@ __device__ __forceinline__ void accumulate_xt_gt_bf16(const uint8_t* xl, const f
 }
 
 // ------------------------------------------------------------------------------------------
-// dedup_dq_kernel<G>: one workgroup per (16-row block, KV head g), G/2 waves, as the dedup
-// attention kernel (same union, masks and mapping).
+// dedup_dq_kernel<G, SUB>: one workgroup per (16-row block, group of G query heads), G/2 waves,
+// as the dedup attention kernel (same union, masks and mapping).  SUB groups share one KV head:
+// 16 query heads per KV head run as two 8-head workgroups (one 8-wave workgroup would be
+// limited to 256 registers per wave and spill).
 // ------------------------------------------------------------------------------------------
 constexpr int kDqRows = 16;
 
-template <int G>
+template <int G, int SUB>
 __global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dlt,
@@ -153,8 +155,9 @@ __global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
   static_assert(G == 2 || G == 4 || G == 8 || G == 16, "a wave's 32 query vectors must span whole rows");
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2][2][kKvTileB];  // [buffer][K=0/V=1], bf16
   __shared__ int upos[2][BN];
-  const int n = blockIdx.x / Hkv;
-  const int g = blockIdx.x % Hkv;
+  const int n = blockIdx.x / (Hkv * SUB);
+  const int gv = blockIdx.x % (Hkv * SUB);  // query-head group
+  const int g = gv / SUB;                    // its KV head
   if (n >= *sched_count) return;
   const int2 e = sched[n];
   const int b = e.x, j = e.y;
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
   const int qc = lane & 31, hf = lane >> 5;
   const int qv = 32 * w + qc;
   const int my_r = qv / G;
-  const int head = g * G + qv % G;
+  const int head = gv * G + qv % G;
   const int rbase = (32 * w) / G;
   const int64_t kvs = (int64_t)Hkv * D;
   const int64_t trow = seq0 + i0 + min(my_r, nr - 1);
@@ -474,15 +477,13 @@ hipError_t launch_dedup_dq(const uint16_t* q, const uint16_t* k, const uint16_t*
   const float sl2 = scale * 1.4426950408889634f;
   const unsigned grid = (unsigned)(nb16 * Hkv);
   switch (Hq / Hkv) {
-#define DSA_DQ(GG)                                                                                                 \
-  case GG:                                                                                                         \
-    dedup_dq_kernel<GG><<<grid, 32 * GG, 0, st>>>(q, k, v, dout, lse, Dlt, cu, Hq, Hkv, sl2, scale, sched16, count16, \
-                                                  ustride, ukeys, umask, ucount, dq);                              \
-    break;
-    DSA_DQ(2)
-    DSA_DQ(4)
-    DSA_DQ(8)
-    DSA_DQ(16)
+#define DSA_DQ(GG, SUB)                                                                                             \
+  dedup_dq_kernel<GG, SUB><<<grid * SUB, 32 * GG, 0, st>>>(q, k, v, dout, lse, Dlt, cu, Hq, Hkv, sl2, scale, sched16, \
+                                                          count16, ustride, ukeys, umask, ucount, dq);
+    case 2: DSA_DQ(2, 1) break;
+    case 4: DSA_DQ(4, 1) break;
+    case 8: DSA_DQ(8, 1) break;
+    case 16: DSA_DQ(8, 2) break;
 #undef DSA_DQ
     default:
       return hipErrorInvalidValue;

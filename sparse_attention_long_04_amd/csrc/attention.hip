@@ -17,10 +17,10 @@
 //
 // gather_rows_kernel (prefill) -- XCD- and cache-aware: the launch runs the KV heads one after
 //   another (phases in launch order); within a phase workgroup b runs on XCD b % 8 and its 4
-//   waves take 4 consecutive rows, row groups dealt round-robin over the XCDs.  Each XCD's L2
-//   then holds one head's K/V rows (512 B per key instead of 2 KiB), and all XCDs work on the
-//   same stretch of rows of the same head, whose K/V rows (67 MB at 128K) fit the memory-side
-//   Infinity Cache that they share.
+//   waves take 4 consecutive rows, chunks of consecutive row groups dealt round-robin over the
+//   XCDs.  Each XCD's L2 then holds one head's K/V rows (512 B per key instead of 2 KiB) of
+//   neighbouring rows, and all XCDs work on the same stretch of rows of the same head, whose K/V
+//   rows (67 MB at 128K) fit the memory-side Infinity Cache that they share.
 //
 // gather_attention_kernel (decode, dense decode, and prefill shapes the row kernel does not
 //   take) -- one workgroup per row and key split, one wave per KV head.  With several splits
@@ -246,10 +246,18 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
 // workgroups (a multiple of 8); phase p serves heads p*hp .. p*hp + hp - 1 over all rows.  Within
 // a phase, workgroup b runs on XCD b % 8 (the dispatcher deals workgroups round-robin over the 8
 // XCDs), serves head p*hp + (b % 8) % hp, and its NW waves take NW consecutive rows, each staging
-// its own indices; consecutive row groups go to consecutive XCDs.  Every XCD gathers the K/V
+// its own indices; chunks of kGatherChunk consecutive row groups go to consecutive XCDs.  Every XCD gathers the K/V
 // rows of a single head (Hkv * 256 B less per key than a workgroup spanning all heads), and the
 // heads in flight at once are only hp.  Needs 8 % Hkv == 0 and K <= kRowKeys.
 constexpr int kRowKeys = 2048;
+// KV heads gathered at once.  One head at a time (in head order) keeps the working set of K/V
+// rows to one head's (67 MB at 128K tokens): measured at 128K, 4 heads at once 59.8 ms, 2 heads
+// 56.0, 1 head 55.4.
+constexpr int kGatherHeadsPerPhase = 1;
+// Row groups per chunk dealt to one XCD: consecutive rows on one XCD keep the keys that
+// neighbouring rows share in its L2.  Measured (attention ms, 128K i.i.d. / drifting queries):
+// 1 group 55.8 / 46.1, 4: 55.8 / 41.6, 16: 55.4 / 39.8, 32: 55.4 / 39.7, 64: 55.3 / 39.7.
+constexpr int kGatherChunk = 32;
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
@@ -263,7 +271,9 @@ __global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
   const unsigned phase = blockIdx.x / blocks_per_phase, bid = blockIdx.x % blocks_per_phase;
   const int xcd = bid & 7;  // blocks_per_phase is a multiple of 8: the XCD of the workgroup
   const int g = int(phase) * hp + xcd % hp;
-  const int64_t group = (int64_t)(bid >> 3) * (8 / hp) + xcd / hp;
+  // row groups are dealt to the 8 / hp XCDs of a head in chunks of kGatherChunk consecutive groups
+  const int64_t slot = bid >> 3;
+  const int64_t group = (slot / kGatherChunk) * (8 / hp) * kGatherChunk + (xcd / hp) * kGatherChunk + slot % kGatherChunk;
   const int wave = threadIdx.x >> 6;
   const int64_t r = group * NW + wave;
   if (r >= rows) return;  // waves are independent: no workgroup barrier below
@@ -499,10 +509,6 @@ __global__ __launch_bounds__(512) void dense_prefill_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// KV heads gathered at once.  One head at a time (in head order) keeps the working set of K/V
-// rows to one head's (67 MB at 128K tokens): measured at 128K, 4 heads at once 59.8 ms, 2 heads
-// 56.0, 1 head 55.4.
-constexpr int kGatherHeadsPerPhase = 1;
 
 hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    const int32_t* idx, int K, int mode, const int32_t* cu, int nseq,
@@ -516,7 +522,8 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
     const int64_t groups = (rows + NWR - 1) / NWR;
     const int hp = kGatherHeadsPerPhase < Hkv ? kGatherHeadsPerPhase : Hkv;  // heads gathered at once
     const int per = 8 / hp;  // XCDs per head
-    const int64_t bpp = 8 * ((groups + per - 1) / per);
+    const int64_t chunks = (groups + per * kGatherChunk - 1) / (per * kGatherChunk);
+    const int64_t bpp = 8 * chunks * kGatherChunk;
     gather_rows_kernel<128, NWR><<<(unsigned)(bpp * (Hkv / hp)), 64 * NWR, 0, st>>>(
         q, k, v, idx, K, cu, nseq, rows, Hq, Hkv, scale_log2, out, lse_out, hp, (unsigned)bpp);
     return hipGetLastError();

@@ -113,6 +113,10 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   __shared__ uint32_t qmax_lds;
   __shared__ float scale_lds;
   uint8_t* const lin_lds = q_lds + HMAX * 16 * ROWB;
+  // 16-byte unit swizzle of row t (0..15) of a head's 16-row tile: an A-operand read (16 lanes =
+  // 16 rows per 256-byte LDS pass) then touches 16 distinct bank groups.  128-byte rows pair up
+  // in a pass, so rows t and t + 8 (same parity, same t & 7) need different units.
+  auto swz = [](int t) { return UNITS == 8 ? ((t & 7) ^ ((t >> 3) & 1)) : (t & 15); };
 
   const int n = blockIdx.x;
   if (n >= *sched_count) return;
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   const int kend = i0 + rows;  // keys [0, kend) are needed by this block
   const int tid = threadIdx.x;
 
-  // stage queries: lds[(h*16 + t)*ROWB + ((u ^ (t&7)) * 16)] <- q_idx[seq0+i0+t][h][u*16..]
+  // stage queries: lds[(h*16 + t)*ROWB + ((u ^ swz(t)) * 16)] <- q_idx[seq0+i0+t][h][u*16..]
   {
     const int per_tok = H * UNITS;
     const int total = 16 * per_tok;
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
       i32x4 val = {0, 0, 0, 0};
       if (t < rows)
         val = *reinterpret_cast<const i32x4*>(q_idx + ((seq0 + i0 + t) * H + h) * (int64_t)ROWB + c * 16);
-      *reinterpret_cast<i32x4*>(q_lds + (h * 16 + t) * ROWB + ((c ^ (t & 7)) * 16)) = val;
+      *reinterpret_cast<i32x4*>(q_lds + (h * 16 + t) * ROWB + ((c ^ swz(t)) * 16)) = val;
     }
     for (int u = tid; u < 16 * H; u += NWAVES * 64) {
       const int h = u >> 4, t = u & 15;
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
     for (int x = 0; x < EPU; ++x) lin[x] = 0.f;
     if (act) {
       for (int h = 0; h < H; ++h) {
-        const i32x4 val = *reinterpret_cast<const i32x4*>(q_lds + (h * 16 + t) * ROWB + ((u ^ (t & 7)) * 16));
+        const i32x4 val = *reinterpret_cast<const i32x4*>(q_lds + (h * 16 + t) * ROWB + ((u ^ swz(t)) * 16));
         const float wv = w_lds[h * 16 + t];
 #pragma unroll
         for (int x = 0; x < EPU; ++x) {
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
           lin[x] -= piece;
           codes[x / (EPU / 4)] |= int(c);
         }
-        *reinterpret_cast<i32x4*>(lin_lds + (pc * 16 + t) * ROWB + ((u ^ (t & 7)) * 16)) = codes;
+        *reinterpret_cast<i32x4*>(lin_lds + (pc * 16 + t) * ROWB + ((u ^ swz(t)) * 16)) = codes;
       }
     }
     if (tid == 0) scale_lds = scale;
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   auto load_a = [&](i32x4 (&dst)[CHU], const uint8_t* base) {
     const uint8_t* qa = base + r * ROWB;
 #pragma unroll
-    for (int c = 0; c < CHU; ++c) dst[c] = *reinterpret_cast<const i32x4*>(qa + (((g * CHU + c) ^ (r & 7)) * 16));
+    for (int c = 0; c < CHU; ++c) dst[c] = *reinterpret_cast<const i32x4*>(qa + (((g * CHU + c) ^ swz(r)) * 16));
   };
 
   constexpr int STEP = NWAVES * NT * 16;
@@ -408,6 +412,9 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     for (int i = tid; i < 2048; i += 256) ghist[b * 2048 + i] = 0;
   if (key0 >= n) return;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  // 16-byte unit swizzle of head row h: the 16 heads an A-operand read touches (one 256-byte LDS
+  // pass) land on 16 distinct bank groups
+  auto dswz = [](int h) { return (h & 7) ^ ((h >> 3) & 1); };
   const int kw0 = key0 + wave * WKEYS;
   const int kw1 = min(n, kw0 + WKEYS);
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
@@ -431,7 +438,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     for (int jt = 0; jt < NT; ++jt) acc[jt] = 0.f;
     for (int hb = 0; hb < H; hb += 16) {
       const uint8_t* qa = q_lds + (hb + r) * ROWB;
-      const int hr = (hb + r) & 7;
+      const int hr = dswz(hb + r);
       const i32x4 lo = *reinterpret_cast<const i32x4*>(qa + (((2 * g) ^ hr) * 16));
       const i32x4 hi = *reinterpret_cast<const i32x4*>(qa + (((2 * g + 1) ^ hr) * 16));
       const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -472,7 +479,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
 #pragma unroll
   for (int j = 0; j < QPT; ++j) {
     const int u = tid + 256 * j, h = u / UNITS, c = u - h * UNITS;
-    if (h < H) *reinterpret_cast<i32x4*>(q_lds + h * ROWB + ((c ^ (h & 7)) * 16)) = qv[j];
+    if (h < H) *reinterpret_cast<i32x4*>(q_lds + h * ROWB + ((c ^ dswz(h)) * 16)) = qv[j];
   }
   if (tid < H) w_lds[tid] = wv_in;
   __syncthreads();

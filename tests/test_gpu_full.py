@@ -86,3 +86,25 @@ def test_decode_16x128k_full():
     assert np.array_equal(st.k_idx_cache[:, lo:hi].cpu().numpy(), kc[:, lo:hi])
     assert np.array_equal(st.k_cache[:, lo:hi].cpu().numpy().view(np.uint16), kk[:, lo:hi])
     assert np.array_equal(st.v_cache[:, lo:hi].cpu().numpy().view(np.uint16), vv[:, lo:hi])
+
+
+@pytest.mark.timeout(900)
+def test_topk_rows_past_single_pass_limit():
+    """One 200000-token video sequence: rows of up to 196608 keys take the top-k's single-pass
+    path, longer rows its exact two-pass select.  Rows on both sides of that boundary, and the
+    sequence end, must match the oracle exactly."""
+    from sparse_attention_long_04_amd import inputs as gen
+    n = 200000
+    p = gen.make_prefill([n], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=2048, seed=51,
+                         video=True)
+    print(f"[full] topk past the single-pass limit: T={n}", flush=True)
+    pb = PrefillBatch(p)
+    pb.index_topk()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(196600, 196616), [n - 1], rng.integers(150000, n, 4)]))
+    idx = pb.topk_idx[torch.from_numpy(rows).to(pb.topk_idx.device)].cpu().numpy()
+    del pb
+    torch.cuda.empty_cache()
+    o = O.Prefill(p.cu_seqlens, p.q_idx, p.k_idx, p.w_idx, p.q, p.k, p.v, p.idx_dtype, p.topk, p.softmax_scale)
+    bad = [int(t) for t, got in zip(rows, idx) if not np.array_equal(got, O.select_topk_row(o.scores(int(t)), p.topk))]
+    assert not bad, f"index mismatch on rows {bad}"

@@ -428,3 +428,37 @@ def test_topk_sample_misleads(hot_on_sampled):
     o = oracle_of(p)
     for t in [8191, 8192, 9000, 15000, 19999]:
         assert np.array_equal(idx[t], O.select_topk_row(o.scores(t), p.topk)), t
+
+
+_IDX_CFGS = [("fp8_e4m3", 128, 16), ("fp8_e4m3", 128, 48), ("fp8_e4m3", 128, 64), ("bf16", 64, 32),
+             ("bf16", 64, 64), ("bf16", 128, 16), ("bf16", 128, 32)]
+_GQA = [(32, 4), (16, 1), (8, 8), (12, 4), (24, 3), (40, 8), (64, 4), (7, 7), (10, 5), (6, 1)]
+_TOPKS = [1, 5, 64, 333, 1024, 2048, 3000]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes(seed):
+    """Seeded random combinations of indexer format and heads, GQA grouping (including head
+    counts that do not divide the 8 XCDs, which take the general gather kernel), k and packed
+    lengths (empty, one token, k - 1, k, k + 1, random): every row's selection bit-exact and
+    every output within the bar."""
+    rng = np.random.default_rng(1000 + seed)
+    dt, dI, H = _IDX_CFGS[(5 * seed) % len(_IDX_CFGS)]  # every format, grouping and k is drawn
+    hq, hkv = _GQA[seed % len(_GQA)]
+    k = _TOPKS[(3 * seed) % len(_TOPKS)]
+    pool = [0, 1, max(1, k - 1), k, k + 1] + [int(x) for x in rng.integers(2, 1500, 3)]
+    lens = [min(int(pool[i]), 2000) for i in rng.integers(len(pool), size=int(rng.integers(1, 4)))]
+    if sum(lens) == 0:
+        lens.append(7)
+    print(f"[random {seed}] idx {dt}/{dI}/{H} gqa {hq}/{hkv} k={k} lengths={lens}", flush=True)
+    p = gen.make_prefill(lens, idx_heads=H, idx_dim=dI, idx_dtype=dt, idx_range=4 if dt == "fp8_e4m3" else 8,
+                         topk=k, seed=2000 + seed, video=bool(seed % 2), q_heads=hq, kv_heads=hkv)
+    pb = PrefillBatch(p)
+    pb.prefill()
+    idx = pb.topk_idx.cpu().numpy()
+    out = bf16_to_float(pb.out)
+    o = oracle_of(p)
+    sel, ref = o.rows(range(p.total_tokens))
+    bad = [t for t in range(p.total_tokens) if not np.array_equal(idx[t], sel[t])]
+    assert not bad, f"index mismatch on rows {bad[:10]}"
+    assert_out_close(out, ref, f"random {seed}")

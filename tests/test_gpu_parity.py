@@ -462,3 +462,37 @@ def test_random_shapes(seed):
     bad = [t for t in range(p.total_tokens) if not np.array_equal(idx[t], sel[t])]
     assert not bad, f"index mismatch on rows {bad[:10]}"
     assert_out_close(out, ref, f"random {seed}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_decode(seed):
+    """Seeded random decode steps: batch 1..6, unequal cache lengths (1 .. ~9000, some below k),
+    capacity slack, GQA grouping and k drawn per seed, two consecutive steps (append + decode);
+    selections bit-exact and outputs within the bar after each step."""
+    rng = np.random.default_rng(3000 + seed)
+    hq, hkv = _GQA[(seed + 3) % len(_GQA)]
+    k = _TOPKS[(2 * seed + 1) % len(_TOPKS)]
+    B = int(rng.integers(1, 7))
+    lens = [int(x) for x in rng.integers(1, 9000, B)]
+    lens[0] = max(1, min(lens[0], k - 1))  # one sequence with fewer than k cached keys
+    cap = max(lens) + 2 + int(rng.integers(0, 40))
+    print(f"[random decode {seed}] B={B} gqa {hq}/{hkv} k={k} lens={lens} cap={cap}", flush=True)
+    d = gen.make_decode(B, max(lens), cap, 2, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", topk=k,
+                        seed=4000 + seed, q_heads=hq, kv_heads=hkv)
+    st = DecodeState(d)
+    st.lens.copy_(torch.tensor(lens, dtype=torch.int32))
+    st.len_host[:] = lens
+    kc, kk, vv = d.k_idx_cache.copy(), d.k_cache.copy(), d.v_cache.copy()
+    for step in range(2):
+        s = st.load_step(step)
+        st.append()
+        st.decode()
+        torch.cuda.synchronize()
+        for b in range(B):
+            n = int(st.len_host[b])
+            kc[b, n - 1], kk[b, n - 1], vv[b, n - 1] = s["k_idx_new"][b], s["k_new"][b], s["v_new"][b]
+        assert st.lens.cpu().tolist() == list(st.len_host)
+        sel, ref = O.decode_step(kc, kk, vv, st.len_host, s["q_idx"], s["w_idx"], s["q"], d.idx_dtype, d.topk,
+                                 d.softmax_scale)
+        assert np.array_equal(st.topk_idx.cpu().numpy(), sel), f"step {step}"
+        assert_out_close(bf16_to_float(st.out), ref, f"random decode {seed} step {step}")

@@ -248,7 +248,8 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
 // XCDs), serves head p*hp + (b % 8) % hp, and its NW waves take NW consecutive rows, each staging
 // its own indices; chunks of kGatherChunk consecutive row groups go to consecutive XCDs.  Every XCD gathers the K/V
 // rows of a single head (Hkv * 256 B less per key than a workgroup spanning all heads), and the
-// heads in flight at once are only hp.  Needs 8 % Hkv == 0 and K <= kRowKeys.
+// heads in flight at once are only hp.  `order` (optional) maps slots to rows: rows whose
+// selections share a key block are then gathered together.  Needs 8 % Hkv == 0 and K <= kRowKeys.
 constexpr int kRowKeys = 2048;
 // KV heads gathered at once.  One head at a time (in head order) keeps the working set of K/V
 // rows to one head's (67 MB at 128K tokens): measured at 128K, 4 heads at once 59.8 ms, 2 heads
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, int K, const int32_t* __restrict__ cu, int nseq, int64_t rows, int Hq,
     int Hkv, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse_out, int hp,
-    unsigned blocks_per_phase) {
+    unsigned blocks_per_phase, const int32_t* __restrict__ order) {
   static_assert(D == 128, "head_dim 128 only");
   __shared__ __attribute__((aligned(16))) int il_all[NW][kRowKeys + 32];
   // phase p (in launch order) serves heads p*hp .. p*hp+hp-1 over all rows
@@ -275,8 +276,9 @@ __global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
   const int64_t slot = bid >> 3;
   const int64_t group = (slot / kGatherChunk) * (8 / hp) * kGatherChunk + (xcd / hp) * kGatherChunk + slot % kGatherChunk;
   const int wave = threadIdx.x >> 6;
-  const int64_t r = group * NW + wave;
-  if (r >= rows) return;  // waves are independent: no workgroup barrier below
+  const int64_t rslot = group * NW + wave;
+  if (rslot >= rows) return;  // waves are independent: no workgroup barrier below
+  const int64_t r = order ? (int64_t)order[rslot] : rslot;  // the row this slot serves
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int G = Hq / Hkv;
   const RowInfo ri = row_info(0, r, cu, nseq, nullptr, 0);
@@ -514,7 +516,8 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
                                    const int32_t* idx, int K, int mode, const int32_t* cu, int nseq,
                                    const int32_t* cache_lens, int cap, int64_t rows, int Hq, int Hkv,
                                    float scale, int keys_per_split, int nsplit, uint16_t* out,
-                                   float* o_part, float2* ml_part, hipStream_t st, float* lse_out) {
+                                   float* o_part, float2* ml_part, hipStream_t st, float* lse_out,
+                                   const int32_t* order) {
   if (rows == 0) return hipSuccess;
   const float scale_log2 = scale * 1.4426950408889634f;
   if (mode == 0 && nsplit == 1 && idx && K <= kRowKeys && 8 % Hkv == 0) {
@@ -525,7 +528,7 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
     const int64_t chunks = (groups + per * kGatherChunk - 1) / (per * kGatherChunk);
     const int64_t bpp = 8 * chunks * kGatherChunk;
     gather_rows_kernel<128, NWR><<<(unsigned)(bpp * (Hkv / hp)), 64 * NWR, 0, st>>>(
-        q, k, v, idx, K, cu, nseq, rows, Hq, Hkv, scale_log2, out, lse_out, hp, (unsigned)bpp);
+        q, k, v, idx, K, cu, nseq, rows, Hq, Hkv, scale_log2, out, lse_out, hp, (unsigned)bpp, order);
     return hipGetLastError();
   }
   dim3 grid((unsigned)rows, nsplit);

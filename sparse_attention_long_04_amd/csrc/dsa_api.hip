@@ -27,7 +27,10 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
                                    int mode, const int32_t* cu, int nseq, const int32_t* cache_lens, int cap,
                                    int64_t rows, int Hq, int Hkv, float scale, int keys_per_split, int nsplit,
                                    uint16_t* out, float* o_part, float2* ml_part, hipStream_t st,
-                                   float* lse_out = nullptr);
+                                   float* lse_out = nullptr, const int32_t* order = nullptr);
+int row_order_keys(int64_t T, int max_seqlen, int nseq, int* shift_out);
+hipError_t launch_row_order(const int32_t* idx, int K, const int32_t* cu, int nseq, int64_t T, int max_seqlen,
+                            int* sig, int* cnt, int32_t* order, hipStream_t st);
 hipError_t launch_union(const int32_t* idx, int K, const int32_t* cu, const int2* sched, const int* count,
                         int nb_bound, int64_t ustride, int32_t* ukeys, uint16_t* umask, int* ucount, hipStream_t st);
 hipError_t launch_dedup_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu, int Hq,
@@ -154,7 +157,7 @@ int check_prefill(const dsa_prefill_shape* s, bool need_indexer) {
 //   counts int[64] | seqoff int64[B+1] | sched16 int2[nb16] | sched128 int2[nb128] |
 //   rowrange float2[T] | scores float[score_floats] | topk int32[T*k]
 struct PrefillWs {
-  size_t counts, seqoff, sched16, sched128, rowrange, scores, topk, total;
+  size_t counts, seqoff, sched16, sched128, rowrange, scores, topk, osig, ocnt, order, total;
   int nb16, nb128;
   int64_t score_floats;
 };
@@ -192,6 +195,10 @@ PrefillWs prefill_layout(const dsa_prefill_shape* s, const int32_t* cu_host) {
   w.rowrange = off; off = align_up(off + size_t(T) * sizeof(float2), 256);
   w.scores = off; off = align_up(off + size_t(w.score_floats) * sizeof(float), 256);
   w.topk = off; off = align_up(off + size_t(T) * size_t(s->topk) * sizeof(int32_t), 256);
+  // gather row order: per-row key, per-key counts / offsets, the order itself
+  w.osig = off; off = align_up(off + size_t(T) * sizeof(int), 256);
+  w.ocnt = off; off = align_up(off + size_t(row_order_keys(T, s->max_seqlen, B, nullptr)) * sizeof(int), 256);
+  w.order = off; off = align_up(off + size_t(T) * sizeof(int32_t), 256);
   w.total = off;
   return w;
 }
@@ -505,10 +512,20 @@ int prefill_impl(const dsa_prefill_shape* s, const void* q_idx, const void* k_id
     if ((rc = dedup_attention(s, q, k, v, idx, out, at<int2>(ws, L.sched16), at<int>(ws, L.counts), L.nb16, dws, D,
                               st)))
       return rc;
-  } else if ((rc = hip_status(launch_gather_attention(q, k, v, idx, s->topk, 0, s->cu_seqlens, s->num_seqs, nullptr,
-                                                      0, s->total_tokens, s->q_heads, s->kv_heads, s->softmax_scale,
-                                                      1 << 30, 1, out, nullptr, nullptr, st)))) {
-    return rc;
+  } else {
+    // rows gathered in the order of their dominant key block (identity when the key space is
+    // too large to sort)
+    const int32_t* order = nullptr;
+    if (row_order_keys(s->total_tokens, s->max_seqlen, s->num_seqs, nullptr) > 0) {
+      if ((rc = hip_status(launch_row_order(idx, s->topk, s->cu_seqlens, s->num_seqs, s->total_tokens, s->max_seqlen,
+                                            at<int>(ws, L.osig), at<int>(ws, L.ocnt), at<int32_t>(ws, L.order), st))))
+        return rc;
+      order = at<int32_t>(ws, L.order);
+    }
+    if ((rc = hip_status(launch_gather_attention(q, k, v, idx, s->topk, 0, s->cu_seqlens, s->num_seqs, nullptr, 0,
+                                                 s->total_tokens, s->q_heads, s->kv_heads, s->softmax_scale, 1 << 30,
+                                                 1, out, nullptr, nullptr, st, nullptr, order))))
+      return rc;
   }
   return record(ev, 3, st);
 }

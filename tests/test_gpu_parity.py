@@ -496,3 +496,18 @@ def test_random_decode(seed):
                                  d.softmax_scale)
         assert np.array_equal(st.topk_idx.cpu().numpy(), sel), f"step {step}"
         assert_out_close(bf16_to_float(st.out), ref, f"random decode {seed} step {step}")
+
+
+def test_ordered_gather_matches_natural_order():
+    """dsa_prefill gathers rows in the order of their dominant key block; dsa_sparse_attention
+    on the same index sets takes them in natural order.  Rows are independent, so the outputs
+    must be bit-identical."""
+    p = gen.make_prefill([5000, 3000, 1, 2100], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4,
+                         topk=2048, seed=61, video=True)
+    pb = PrefillBatch(p)
+    pb.prefill()
+    ordered = pb.out.clone()
+    pb.out.zero_()
+    pb.sparse_attention()
+    torch.cuda.synchronize()
+    assert torch.equal(pb.out, ordered)

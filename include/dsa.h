@@ -120,14 +120,17 @@ int dsa_sparse_attention(const dsa_prefill_shape* shape, const uint16_t* q, cons
                          const uint16_t* v, const int32_t* topk_idx, uint16_t* out, void* stream);
 
 /* The whole prefill hot path: dsa_index_topk then dsa_sparse_attention.  topk_idx may be
- * NULL (the workspace then holds the indices). */
+ * NULL (the workspace then holds the indices).  Between the two, the rows are ordered by the
+ * key block most of their selection falls in, and the attention takes them in that order
+ * (better cache reuse; the results are those of the natural order, bit for bit). */
 int dsa_prefill(const dsa_prefill_shape* shape, const void* q_idx, const void* k_idx,
                 const float* w_idx, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                 uint16_t* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
                 void* stream);
 
 /* dsa_prefill that also records caller-created hipEvent_t events[0..3] on `stream` after the
- * work schedule, the indexer, the top-k and the attention kernels (per-stage timing). */
+ * work schedule, the indexer, the top-k (with the row ordering) and the attention kernels
+ * (per-stage timing). */
 int dsa_prefill_timed(const dsa_prefill_shape* shape, const void* q_idx, const void* k_idx,
                       const float* w_idx, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       uint16_t* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,

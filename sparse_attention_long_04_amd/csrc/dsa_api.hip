@@ -507,21 +507,21 @@ int prefill_impl(const dsa_prefill_shape* s, const void* q_idx, const void* k_id
   if ((rc = hip_status(launch_topk_prefill(at<float>(ws, L.scores), at<int64_t>(ws, L.seqoff), s->cu_seqlens,
                                            s->num_seqs, s->total_tokens, s->topk, at<float2>(ws, L.rowrange), idx, st))))
     return rc;
+  // the gather takes rows in the order of their dominant key block (identity when the key
+  // space is too large to sort); this post-processing of the selection counts to the top-k stage
+  const int32_t* order = nullptr;
+  if (!dedup && row_order_keys(s->total_tokens, s->max_seqlen, s->num_seqs, nullptr) > 0) {
+    if ((rc = hip_status(launch_row_order(idx, s->topk, s->cu_seqlens, s->num_seqs, s->total_tokens, s->max_seqlen,
+                                          at<int>(ws, L.osig), at<int>(ws, L.ocnt), at<int32_t>(ws, L.order), st))))
+      return rc;
+    order = at<int32_t>(ws, L.order);
+  }
   if ((rc = record(ev, 2, st))) return rc;
   if (dedup) {
     if ((rc = dedup_attention(s, q, k, v, idx, out, at<int2>(ws, L.sched16), at<int>(ws, L.counts), L.nb16, dws, D,
                               st)))
       return rc;
   } else {
-    // rows gathered in the order of their dominant key block (identity when the key space is
-    // too large to sort)
-    const int32_t* order = nullptr;
-    if (row_order_keys(s->total_tokens, s->max_seqlen, s->num_seqs, nullptr) > 0) {
-      if ((rc = hip_status(launch_row_order(idx, s->topk, s->cu_seqlens, s->num_seqs, s->total_tokens, s->max_seqlen,
-                                            at<int>(ws, L.osig), at<int>(ws, L.ocnt), at<int32_t>(ws, L.order), st))))
-        return rc;
-      order = at<int32_t>(ws, L.order);
-    }
     if ((rc = hip_status(launch_gather_attention(q, k, v, idx, s->topk, 0, s->cu_seqlens, s->num_seqs, nullptr, 0,
                                                  s->total_tokens, s->q_heads, s->kv_heads, s->softmax_scale, 1 << 30,
                                                  1, out, nullptr, nullptr, st, nullptr, order))))

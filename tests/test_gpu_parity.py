@@ -501,10 +501,12 @@ def test_random_decode(seed):
 def test_ordered_gather_matches_natural_order():
     """dsa_prefill gathers rows in the order of their dominant key block; dsa_sparse_attention
     on the same index sets takes them in natural order.  Rows are independent, so the outputs
-    must be bit-identical."""
+    must be bit-identical.  The output starts as a NaN pattern, so a row the order skipped (a
+    hole or a repeat in the permutation) cannot match."""
     p = gen.make_prefill([5000, 3000, 1, 2100], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4,
                          topk=2048, seed=61, video=True)
     pb = PrefillBatch(p)
+    pb.out.fill_(-1)  # 0xffff: a bf16 NaN
     pb.prefill()
     ordered = pb.out.clone()
     pb.out.zero_()

@@ -28,7 +28,7 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
                                    int64_t rows, int Hq, int Hkv, float scale, int keys_per_split, int nsplit,
                                    uint16_t* out, float* o_part, float2* ml_part, hipStream_t st,
                                    float* lse_out = nullptr, const int32_t* order = nullptr);
-int row_order_keys(int64_t T, int max_seqlen, int nseq, int* shift_out);
+int64_t row_order_count_ints(int64_t T, int max_seqlen, int nseq);
 hipError_t launch_row_order(const int32_t* idx, int K, const int32_t* cu, int nseq, int64_t T, int max_seqlen,
                             int* sig, int* cnt, int32_t* order, hipStream_t st);
 hipError_t launch_union(const int32_t* idx, int K, const int32_t* cu, const int2* sched, const int* count,
@@ -197,7 +197,7 @@ PrefillWs prefill_layout(const dsa_prefill_shape* s, const int32_t* cu_host) {
   w.topk = off; off = align_up(off + size_t(T) * size_t(s->topk) * sizeof(int32_t), 256);
   // gather row order: per-row key, per-key counts / offsets, the order itself
   w.osig = off; off = align_up(off + size_t(T) * sizeof(int), 256);
-  w.ocnt = off; off = align_up(off + size_t(row_order_keys(T, s->max_seqlen, B, nullptr)) * sizeof(int), 256);
+  w.ocnt = off; off = align_up(off + size_t(row_order_count_ints(T, s->max_seqlen, B)) * sizeof(int), 256);
   w.order = off; off = align_up(off + size_t(T) * sizeof(int32_t), 256);
   w.total = off;
   return w;
@@ -510,7 +510,7 @@ int prefill_impl(const dsa_prefill_shape* s, const void* q_idx, const void* k_id
   // the gather takes rows in the order of their dominant key block (identity when the key
   // space is too large to sort); this post-processing of the selection counts to the top-k stage
   const int32_t* order = nullptr;
-  if (!dedup && row_order_keys(s->total_tokens, s->max_seqlen, s->num_seqs, nullptr) > 0) {
+  if (!dedup && row_order_count_ints(s->total_tokens, s->max_seqlen, s->num_seqs) > 0) {
     if ((rc = hip_status(launch_row_order(idx, s->topk, s->cu_seqlens, s->num_seqs, s->total_tokens, s->max_seqlen,
                                           at<int>(ws, L.osig), at<int>(ws, L.ocnt), at<int32_t>(ws, L.order), st))))
       return rc;

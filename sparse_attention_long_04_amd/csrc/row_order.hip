@@ -8,48 +8,66 @@
 // context run together and share those keys' lines.  The order changes nothing else -- every
 // row is computed on its own and written to its own output row.
 //
+// A counting sort of the rows by that key, with no global atomics (neighbouring rows rarely
+// share a key, and device-wide atomics on a few hundred counters serialise):
 //   row_signature_kernel  one wave per row (four consecutive rows per wave): LDS histogram of
 //                         its selected positions >> shift, the fullest bin (lowest on ties),
-//                         key = global block of that bin; integer atomics count the rows per
-//                         key, one per run of equal keys
-//   row_order_scan_kernel one workgroup: exclusive prefix over the key counts
-//   row_order_scatter     each row takes the next slot of its key (one atomic per run of equal
-//                         keys in a wave; the order inside a key is unspecified, which the
-//                         results do not depend on)
+//                         key = global block of that bin
+//   row_order_count       one workgroup per chunk of rows: LDS count per key, written out as
+//                         the chunk's row of a [chunk][key] matrix
+//   row_order_scan        one workgroup: the matrix becomes each (chunk, key)'s first slot,
+//                         key-major (keys ascending, chunks ascending inside a key)
+//   row_order_scatter     one workgroup per chunk: each row takes the next slot of its
+//                         (chunk, key) through an LDS atomic (the order inside a chunk and key
+//                         is unspecified, which the results do not depend on)
 #include "common.h"
 
 namespace dsa {
 
-constexpr int kSigBins = 1024;       // histogram bins per row (4 KiB of LDS per wave)
-constexpr int kOrderMaxKeys = 65536; // beyond this (very many sequences) the identity order is kept
+constexpr int kSigBins = 1024;          // histogram bins per row (4 KiB of LDS per wave)
+constexpr int kSigRowsPerWave = 4;      // consecutive rows per wave of the signature kernel
+constexpr int kOrderMaxKeys = 16384;    // LDS counters per chunk (64 KiB); beyond: identity order
+constexpr int kOrderCountMax = 1 << 20; // [chunk][key] matrix entries (4 MiB of workspace)
+constexpr int kOrderMaxChunks = 1024;
+constexpr int kOrderMinRows = 4096;     // rows per chunk at least
+constexpr int kOrderThreads = 1024;
 
-// shift of the block size (1024 keys or coarser, so that every row fits kSigBins bins and the
-// key space stays below kOrderMaxKeys); returns the number of keys, 0 = no reordering.
-int row_order_keys(int64_t T, int max_seqlen, int nseq, int* shift_out) {
+struct OrderPlan {
+  int shift = 0, nkeys = 0, chunks = 0;
+  int64_t rows = 0;  // rows per chunk
+};
+
+// Block size 2^shift (1024 keys or coarser, so that every row fits kSigBins bins and the key
+// space stays below kOrderMaxKeys) and the chunking of the rows; nkeys = 0: no reordering.
+static OrderPlan order_plan(int64_t T, int max_seqlen, int nseq) {
+  OrderPlan p;
   int shift = 10;
   while ((int64_t(max_seqlen) >> shift) >= kSigBins) ++shift;
   while ((T >> shift) >= kOrderMaxKeys / 2) ++shift;
   const int64_t nkeys = (T >> shift) + nseq + 2;
-  if (shift_out) *shift_out = shift;
-  return nkeys <= kOrderMaxKeys ? int(nkeys) : 0;
+  if (T <= 0 || nkeys > kOrderMaxKeys) return p;
+  const int64_t gmax = std::min<int64_t>(kOrderMaxChunks, kOrderCountMax / nkeys);
+  p.shift = shift;
+  p.nkeys = int(nkeys);
+  p.rows = std::max<int64_t>(kOrderMinRows, (T + gmax - 1) / gmax);
+  p.chunks = int((T + p.rows - 1) / p.rows);
+  return p;
 }
 
-__global__ __launch_bounds__(256) void row_order_clear_kernel(int* __restrict__ cnt, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) cnt[i] = 0;
+// Entries of the [chunk][key] matrix the ordering needs in the workspace; 0 = no reordering.
+int64_t row_order_count_ints(int64_t T, int max_seqlen, int nseq) {
+  const OrderPlan p = order_plan(T, max_seqlen, nseq);
+  return int64_t(p.chunks) * p.nkeys;
 }
-
-constexpr int kSigRowsPerWave = 4;  // consecutive rows per wave: neighbours mostly share a key
 
 __global__ __launch_bounds__(256) void row_signature_kernel(const int32_t* __restrict__ idx, int K,
                                                             const int32_t* __restrict__ cu, int nseq, int64_t T,
-                                                            int shift, int* __restrict__ sig, int* __restrict__ cnt) {
+                                                            int shift, int* __restrict__ sig) {
   __shared__ int hist[4][kSigBins];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t0 = ((int64_t)blockIdx.x * 4 + w) * kSigRowsPerWave;
   if (t0 >= T) return;  // waves are independent: no workgroup barrier below
   int* h = hist[w];
-  int run_key = -1, run_n = 0;  // lane 0: rows counted but not yet added to cnt
   for (int r = 0; r < kSigRowsPerWave && t0 + r < T; ++r) {
     const int64_t t = t0 + r;
     const int b = find_seq(cu, nseq, t);
@@ -114,75 +132,77 @@ __global__ __launch_bounds__(256) void row_signature_kernel(const int32_t* __res
       }
     }
     __builtin_amdgcn_wave_barrier();  // every lane has read h before the next row clears it
-    if (lane == 0) {
-      const int key = int((int64_t(cu[b]) + (int64_t(best_b) << shift)) >> shift) + b;
-      sig[t] = key;
-      if (key != run_key) {
-        if (run_n > 0) atomicAdd(&cnt[run_key], run_n);
-        run_key = key;
-        run_n = 0;
-      }
-      ++run_n;
-    }
+    if (lane == 0) sig[t] = int((int64_t(cu[b]) + (int64_t(best_b) << shift)) >> shift) + b;
   }
-  if (lane == 0 && run_n > 0) atomicAdd(&cnt[run_key], run_n);
 }
 
-// Exclusive prefix over n counts in place (one workgroup of 1024 threads, n <= kOrderMaxKeys).
-__global__ __launch_bounds__(1024) void row_order_scan_kernel(int* __restrict__ cnt, int n) {
-  __shared__ int part[1024];
+// cnt[chunk * nkeys + key] = rows of the chunk with that key (every entry written).
+__global__ __launch_bounds__(kOrderThreads) void row_order_count_kernel(const int* __restrict__ sig, int64_t T,
+                                                                         int64_t rows, int nkeys,
+                                                                         int* __restrict__ cnt) {
+  __shared__ int h[kOrderMaxKeys];
+  for (int x = threadIdx.x; x < nkeys; x += kOrderThreads) h[x] = 0;
+  __syncthreads();
+  const int64_t a = int64_t(blockIdx.x) * rows, e = std::min<int64_t>(T, a + rows);
+  for (int64_t t = a + threadIdx.x; t < e; t += kOrderThreads) atomicAdd(&h[sig[t]], 1);
+  __syncthreads();
+  int* out = cnt + int64_t(blockIdx.x) * nkeys;
+  for (int x = threadIdx.x; x < nkeys; x += kOrderThreads) out[x] = h[x];
+}
+
+// In place: cnt[g * nkeys + key] becomes the first slot of (chunk g, key) in the order.
+__global__ __launch_bounds__(kOrderThreads) void row_order_scan_kernel(int* __restrict__ cnt, int nkeys,
+                                                                        int chunks) {
+  __shared__ int part[kOrderThreads];
   const int tid = threadIdx.x;
-  const int per = (n + 1023) / 1024;
-  const int a = min(n, tid * per), e = min(n, a + per);
-  int s = 0;
-  for (int x = a; x < e; ++x) s += cnt[x];
+  const int per = (nkeys + kOrderThreads - 1) / kOrderThreads;
+  const int a = min(nkeys, tid * per), e = min(nkeys, a + per);
+  int s = 0;  // rows of this thread's keys, over all chunks
+  for (int x = a; x < e; ++x)
+    for (int g = 0; g < chunks; ++g) s += cnt[int64_t(g) * nkeys + x];
   part[tid] = s;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan of the 1024 partial sums
+  for (int o = 1; o < kOrderThreads; o <<= 1) {  // inclusive scan of the per-thread sums
     const int v = tid >= o ? part[tid - o] : 0;
     __syncthreads();
     part[tid] += v;
     __syncthreads();
   }
   int run = part[tid] - s;
-  for (int x = a; x < e; ++x) {
-    const int c = cnt[x];
-    cnt[x] = run;
-    run += c;
-  }
+  for (int x = a; x < e; ++x)
+    for (int g = 0; g < chunks; ++g) {
+      int* p = cnt + int64_t(g) * nkeys + x;
+      const int c = *p;
+      *p = run;
+      run += c;
+    }
 }
 
-// Lanes of a wave whose keys equal their left neighbour's join its run: the run's first lane
-// takes the run's slots with one atomic and each lane writes at its offset inside the run.
-__global__ __launch_bounds__(256) void row_order_scatter_kernel(const int* __restrict__ sig, int64_t T,
-                                                                int* __restrict__ off, int32_t* __restrict__ order) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int lane = threadIdx.x & 63;
-  const bool live = t < T;
-  const int key = live ? sig[t] : -1;
-  const int left = __shfl_up(key, 1);
-  const uint64_t starts = __ballot(lane == 0 || key != left);
-  const int lead = 63 - __builtin_clzll(starts & (~0ull >> (63 - lane)));  // this lane's run start
-  const uint64_t after = lane < 63 ? starts & (~0ull << (lane + 1)) : 0ull;
-  const int next = after ? __builtin_ctzll(after) : 64;  // first lane of the following run
-  int base = 0;
-  // rows past T hold key -1 and so start runs of their own: a live run holds live rows only
-  if (lead == lane && live) base = atomicAdd(&off[key], next - lane);
-  base = __shfl(base, lead);
-  if (live) order[base + (lane - lead)] = int32_t(t);
+__global__ __launch_bounds__(kOrderThreads) void row_order_scatter_kernel(const int* __restrict__ sig, int64_t T,
+                                                                           int64_t rows, int nkeys,
+                                                                           const int* __restrict__ first,
+                                                                           int32_t* __restrict__ order) {
+  __shared__ int next[kOrderMaxKeys];
+  const int* f = first + int64_t(blockIdx.x) * nkeys;
+  for (int x = threadIdx.x; x < nkeys; x += kOrderThreads) next[x] = f[x];
+  __syncthreads();
+  const int64_t a = int64_t(blockIdx.x) * rows, e = std::min<int64_t>(T, a + rows);
+  for (int64_t t = a + threadIdx.x; t < e; t += kOrderThreads) order[atomicAdd(&next[sig[t]], 1)] = int32_t(t);
 }
 
-// Writes order[0..T) (a permutation of the rows).  Returns hipErrorInvalidValue (nothing
-// launched) when the key space is too large; the caller then keeps the identity order.
+// Writes order[0..T) (a permutation of the rows).  cnt holds row_order_count_ints(...) ints.
+// Returns hipErrorInvalidValue (nothing launched) when the key space is too large; the caller
+// then keeps the identity order.
 hipError_t launch_row_order(const int32_t* idx, int K, const int32_t* cu, int nseq, int64_t T, int max_seqlen,
                             int* sig, int* cnt, int32_t* order, hipStream_t st) {
-  int shift = 0;
-  const int nkeys = row_order_keys(T, max_seqlen, nseq, &shift);
-  if (nkeys == 0 || T == 0) return hipErrorInvalidValue;
-  row_order_clear_kernel<<<(nkeys + 255) / 256, 256, 0, st>>>(cnt, nkeys);
-  row_signature_kernel<<<(unsigned)((T + 4 * kSigRowsPerWave - 1) / (4 * kSigRowsPerWave)), 256, 0, st>>>(idx, K, cu, nseq, T, shift, sig, cnt);
-  row_order_scan_kernel<<<1, 1024, 0, st>>>(cnt, nkeys);
-  row_order_scatter_kernel<<<(unsigned)((T + 255) / 256), 256, 0, st>>>(sig, T, cnt, order);
+  const OrderPlan p = order_plan(T, max_seqlen, nseq);
+  if (p.nkeys == 0) return hipErrorInvalidValue;
+  const int64_t per_block = 4 * kSigRowsPerWave;
+  row_signature_kernel<<<(unsigned)((T + per_block - 1) / per_block), 256, 0, st>>>(idx, K, cu, nseq, T, p.shift,
+                                                                                    sig);
+  row_order_count_kernel<<<p.chunks, kOrderThreads, 0, st>>>(sig, T, p.rows, p.nkeys, cnt);
+  row_order_scan_kernel<<<1, kOrderThreads, 0, st>>>(cnt, p.nkeys, p.chunks);
+  row_order_scatter_kernel<<<p.chunks, kOrderThreads, 0, st>>>(sig, T, p.rows, p.nkeys, cnt, order);
   return hipGetLastError();
 }
 

@@ -108,11 +108,14 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   constexpr int EPU = FP8 ? 16 : 8;          // elements per 16-byte unit
   static_assert(UNITS >= 8, "swizzle needs >= 8 units per row");
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[(HMAX + NP) * 16 * ROWB];
-  __shared__ __attribute__((aligned(16))) float w_lds[HMAX * 16];
+  // two heads of padding: the head loop's last reloads read (unused) heads H and H+1
+  __shared__ __attribute__((aligned(16))) float w_lds[(HMAX + 2) * 16];
   __shared__ float2 range_lds[NWAVES][16];
   __shared__ uint32_t qmax_lds;
   __shared__ float scale_lds;
-  uint8_t* const lin_lds = q_lds + HMAX * 16 * ROWB;
+  // q_lin pieces follow head H-1 directly: the head loop's last reloads (heads H, H+1) then
+  // fetch pieces 0 and 1
+  uint8_t* const lin_lds = q_lds + H * 16 * ROWB;
   // 16-byte unit swizzle of row t (0..15) of a head's 16-row tile: an A-operand read (16 lanes =
   // 16 rows per 256-byte LDS pass) then touches 16 distinct bank groups.  128-byte rows pair up
   // in a pass, so rows t and t + 8 (same parity, same t & 7) need different units.
@@ -267,55 +270,83 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
       acc_abs[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
       acc_lin[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
-    // software pipeline over head pairs (H is a multiple of 16): the MFMAs of pair p+1 are
-    // issued while the VALU folds pair p's results, so no FMA waits on a fresh MFMA
+    // Software pipeline over head pairs (H is a multiple of 16, so the pair count P = H/2 is
+    // even).  c0/c1 hold the previous pair's products while this pair's MFMAs run: each MFMA is
+    // preceded by the four FMAs that fold the product it will overwrite, so the VALU work
+    // co-issues with the matrix pipe.  A head's A registers are reloaded (for the head two
+    // further on) as soon as its last MFMA has issued, so the LDS read has four MFMAs of time to
+    // land.  Head weights sit in two slots, even pairs in wx, odd pairs in wy: a step folds
+    // with one slot and then reloads it for the pair two ahead, so no register copies (which
+    // would wait on the fresh loads) are needed.  The scheduling barriers keep the compiler
+    // from hoisting the FMAs or the reloads out of this order.
     f32x4 c0[NT], c1[NT];
-    f32x4 wv0, wv1;
-    {
-      i32x4 a0[CHU], a1[CHU];
-      load_a(a0, q_lds);
-      load_a(a1, q_lds + 16 * ROWB);
-      wv0 = *reinterpret_cast<const f32x4*>(w_lds + 4 * g);
-      wv1 = *reinterpret_cast<const f32x4*>(w_lds + 16 + 4 * g);
+    i32x4 a0[CHU], a1[CHU];
+    auto w4 = [&](int h) { return *reinterpret_cast<const f32x4*>(w_lds + h * 16 + 4 * g); };
+    load_a(a0, q_lds);
+    load_a(a1, q_lds + 16 * ROWB);
+    f32x4 wx0 = w4(0), wx1 = w4(1);
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) c0[jt] = mma(a0, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(a0, q_lds + 2 * 16 * ROWB);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) c1[jt] = mma(a1, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(a1, q_lds + 3 * 16 * ROWB);
+    f32x4 wy0 = w4(2), wy1 = w4(3);
+    __builtin_amdgcn_sched_barrier(0);
+    // step for the pair of heads h, h+1 (a0/a1 in flight); folds pair h-2 with (wf0, wf1)
+    auto step = [&](f32x4& wf0, f32x4& wf1, int h) {
+      // the last step reloads "heads" H, H+1 = q_lin pieces 0 and 1 (their weights, read from
+      // w_lds's padding, are never used)
+      const int hq = h + 2;
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_abs[jt][i] = fmaf(wf0[i], fabsf(c0[jt][i]), acc_abs[jt][i]);
         c0[jt] = mma(a0, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
-        c1[jt] = mma(a1, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    for (int h = 2; h < H; h += 2) {
-      i32x4 a0[CHU], a1[CHU];
-      load_a(a0, q_lds + h * 16 * ROWB);
-      load_a(a1, q_lds + (h + 1) * 16 * ROWB);
-      const f32x4 nw0 = *reinterpret_cast<const f32x4*>(w_lds + h * 16 + 4 * g);
-      const f32x4 nw1 = *reinterpret_cast<const f32x4*>(w_lds + (h + 1) * 16 + 4 * g);
+      load_a(a0, q_lds + hq * 16 * ROWB);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) {
-        const f32x4 n0 = mma(a0, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc_abs[jt][i] = fmaf(wv0[i], fabsf(c0[jt][i]), acc_abs[jt][i]);
-        const f32x4 n1 = mma(a1, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc_abs[jt][i] = fmaf(wv1[i], fabsf(c1[jt][i]), acc_abs[jt][i]);
-        c0[jt] = n0;
-        c1[jt] = n1;
+        for (int i = 0; i < 4; ++i) acc_abs[jt][i] = fmaf(wf1[i], fabsf(c1[jt][i]), acc_abs[jt][i]);
+        c1[jt] = mma(a1, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
+        __builtin_amdgcn_sched_barrier(0);
       }
-      wv0 = nw0;
-      wv1 = nw1;
+      load_a(a1, q_lds + (hq + 1) * 16 * ROWB);
+      wf0 = w4(hq);
+      wf1 = w4(hq + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    int h = 2;
+    for (; h + 2 < H - 2; h += 4) {  // pairs 1 .. P-2, two per iteration
+      step(wx0, wx1, h);
+      step(wy0, wy1, h + 2);
     }
-#pragma unroll
-    for (int jt = 0; jt < NT; ++jt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc_abs[jt][i] = fmaf(wv0[i], fabsf(c0[jt][i]), acc_abs[jt][i]);
-        acc_abs[jt][i] = fmaf(wv1[i], fabsf(c1[jt][i]), acc_abs[jt][i]);
-      }
+    step(wx0, wx1, h);  // pair P-1 (odd): folds pair P-2 (even) with wx
+    // q_lin . k: NP pieces (0 and 1 already in a0/a1, in flight), each reloaded register set
+    // fetching the piece two further on; the last pair's fold co-issues with piece 0
 #pragma unroll
     for (int pc = 0; pc < NP; ++pc) {
-      i32x4 afr[CHU];
-      load_a(afr, lin_lds + pc * 16 * ROWB);
+      i32x4(&a)[CHU] = (pc & 1) ? a1 : a0;
 #pragma unroll
-      for (int jt = 0; jt < NT; ++jt) acc_lin[jt] = mma(afr, cur[jt], acc_lin[jt]);
+      for (int jt = 0; jt < NT; ++jt) {
+        if (pc == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc_abs[jt][i] = fmaf(wy0[i], fabsf(c0[jt][i]), acc_abs[jt][i]);
+            acc_abs[jt][i] = fmaf(wy1[i], fabsf(c1[jt][i]), acc_abs[jt][i]);
+          }
+        }
+        acc_lin[jt] = mma(a, cur[jt], acc_lin[jt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (pc + 2 < NP) load_a(a, lin_lds + (pc + 2) * 16 * ROWB);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (rows == 16 && kb + NT * 16 <= i0 + 1) {
       // every (row, key) of this step is causal: no masking

@@ -90,9 +90,11 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
 // the |c_h| sum is one FMA per element (|.| is a free source modifier), and the linear sum is
 // (sum_h w_h q_h) . k -- a per-token vector q_lin, split into NP pieces on the input grid
 // (e4m3 pieces scaled by a power of two per block, or bf16 pieces) and contracted by NP extra
-// MFMAs accumulating in place.  For integer-valued inputs and power-of-two weights every
-// quantity is a multiple of 1/8 below 2^18, so the result is exact in any summation order;
-// otherwise the linear term carries about 20 (fp8) or 24 (bf16) significant bits.
+// MFMAs accumulating in place.  The halving is folded into the staged weights (w/2 is exact,
+// and q_lin and its pieces then halve exactly).  For integer-valued inputs and power-of-two
+// weights every quantity is a multiple of 1/16 below 2^17, so the result is exact in any
+// summation order; otherwise the linear term carries about 20 (fp8) or 24 (bf16) significant
+// bits.
 // ------------------------------------------------------------------------------------------
 template <bool FP8, int DI, int HMAX, int NWAVES, int NT>
 __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
     }
     for (int u = tid; u < 16 * H; u += NWAVES * 64) {
       const int h = u >> 4, t = u & 15;
-      w_lds[u] = (t < rows) ? w_idx[(seq0 + i0 + t) * H + h] : 0.f;
+      w_lds[u] = (t < rows) ? 0.5f * w_idx[(seq0 + i0 + t) * H + h] : 0.f;  // the ReLU identity's 1/2
     }
     if (tid == 0) qmax_lds = 0u;
   }
@@ -264,12 +266,9 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
     // unconditional (addresses are clamped): a fixed number of loads in flight lets the
     // compiler wait only for the current buffer
     load_b(nxt, kb + STEP);
-    f32x4 acc_abs[NT], acc_lin[NT];
+    f32x4 acc_abs[NT], acc_lin[NT];  // acc_abs: first written by the first step's fold
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt) {
-      acc_abs[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      acc_lin[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    }
+    for (int jt = 0; jt < NT; ++jt) acc_lin[jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     // Software pipeline over head pairs (H is a multiple of 16, so the pair count P = H/2 is
     // even).  c0/c1 hold the previous pair's products while this pair's MFMAs run: each MFMA is
     // preceded by the four FMAs that fold the product it will overwrite, so the VALU work
@@ -297,14 +296,15 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
     f32x4 wy0 = w4(2), wy1 = w4(3);
     __builtin_amdgcn_sched_barrier(0);
     // step for the pair of heads h, h+1 (a0/a1 in flight); folds pair h-2 with (wf0, wf1)
-    auto step = [&](f32x4& wf0, f32x4& wf1, int h) {
+    auto step = [&](f32x4& wf0, f32x4& wf1, int h, bool first) {
       // the last step reloads "heads" H, H+1 = q_lin pieces 0 and 1 (their weights, read from
       // w_lds's padding, are never used)
       const int hq = h + 2;
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc_abs[jt][i] = fmaf(wf0[i], fabsf(c0[jt][i]), acc_abs[jt][i]);
+        for (int i = 0; i < 4; ++i)
+          acc_abs[jt][i] = first ? wf0[i] * fabsf(c0[jt][i]) : fmaf(wf0[i], fabsf(c0[jt][i]), acc_abs[jt][i]);
         c0[jt] = mma(a0, cur[jt], (f32x4){0.f, 0.f, 0.f, 0.f});
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -322,12 +322,12 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
       wf1 = w4(hq + 1);
       __builtin_amdgcn_sched_barrier(0);
     };
-    int h = 2;
-    for (; h + 2 < H - 2; h += 4) {  // pairs 1 .. P-2, two per iteration
-      step(wx0, wx1, h);
-      step(wy0, wy1, h + 2);
+    // step p folds pair p-1: odd p with wx (even pairs' weights), even p with wy
+    step(wx0, wx1, 2, true);
+    for (int h = 4; h < H; h += 4) {  // pairs 2 .. P-1, two per iteration
+      step(wy0, wy1, h, false);
+      step(wx0, wx1, h + 2, false);
     }
-    step(wx0, wx1, h);  // pair P-1 (odd): folds pair P-2 (even) with wx
     // q_lin . k: NP pieces (0 and 1 already in a0/a1, in flight), each reloaded register set
     // fetching the piece two further on; the last pair's fold co-issues with piece 0
 #pragma unroll
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
         const int key = kb + 16 * jt + r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = 0.5f * fmaf(acc_lin[jt][i], lin_scale, acc_abs[jt][i]);
+          const float v = fmaf(acc_lin[jt][i], lin_scale, acc_abs[jt][i]);
           sblk[(4 * g + i) * stride + key] = v;
           rmin[i] = fminf(rmin[i], v);
           rmax[i] = fmaxf(rmax[i], v);
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = 4 * g + i;
-          const float v = 0.5f * fmaf(acc_lin[jt][i], lin_scale, acc_abs[jt][i]);
+          const float v = fmaf(acc_lin[jt][i], lin_scale, acc_abs[jt][i]);
           if (row < rows && key <= i0 + row) {
             sblk[row * stride + key] = v;
             rmin[i] = fminf(rmin[i], v);

@@ -134,23 +134,43 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   const int kend = i0 + rows;  // keys [0, kend) are needed by this block
   const int tid = threadIdx.x;
 
-  // stage queries: lds[(h*16 + t)*ROWB + ((u ^ swz(t)) * 16)] <- q_idx[seq0+i0+t][h][u*16..]
+  // stage queries: lds[(h*16 + t)*ROWB + ((c ^ swz(t)) * 16)] <- q_idx[seq0+i0+t][h][c*16..].
+  // The block's H*ROWB-byte token rows are contiguous, so 16-byte unit u sits at base + 16u.
+  // Every load is issued before the first store (addresses clamped to the block's rows, rows
+  // past the end stored as zeros): one round trip instead of one per unit.
   {
+    constexpr int NT_ = NWAVES * 64;
+    constexpr int SPT = (16 * HMAX * UNITS + NT_ - 1) / NT_;  // units per thread
+    constexpr int WPT = (16 * HMAX + NT_ - 1) / NT_;          // weights per thread
     const int per_tok = H * UNITS;
-    const int total = 16 * per_tok;
-    for (int u = tid; u < total; u += NWAVES * 64) {
-      const int t = u / per_tok;
-      const int rem = u - t * per_tok;
-      const int h = rem / UNITS;
-      const int c = rem - h * UNITS;
-      i32x4 val = {0, 0, 0, 0};
-      if (t < rows)
-        val = *reinterpret_cast<const i32x4*>(q_idx + ((seq0 + i0 + t) * H + h) * (int64_t)ROWB + c * 16);
-      *reinterpret_cast<i32x4*>(q_lds + (h * 16 + t) * ROWB + ((c ^ swz(t)) * 16)) = val;
+    const int total = 16 * per_tok, valid = rows * per_tok;
+    const i32x4* qsrc = reinterpret_cast<const i32x4*>(q_idx + (seq0 + i0) * H * (int64_t)ROWB);
+    i32x4 sv[SPT];
+    float wsv[WPT];
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) sv[k] = __builtin_nontemporal_load(qsrc + min(tid + k * NT_, valid - 1));
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int u = tid + k * NT_;
+      const int h = min(u >> 4, H - 1), t = min(u & 15, rows - 1);
+      wsv[k] = w_idx[(seq0 + i0 + t) * H + h];
     }
-    for (int u = tid; u < 16 * H; u += NWAVES * 64) {
-      const int h = u >> 4, t = u & 15;
-      w_lds[u] = (t < rows) ? 0.5f * w_idx[(seq0 + i0 + t) * H + h] : 0.f;  // the ReLU identity's 1/2
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int u = tid + k * NT_;
+      if (u < total) {
+        const int t = u / per_tok;
+        const int rem = u - t * per_tok;
+        const int h = rem / UNITS;
+        const int c = rem - h * UNITS;
+        const i32x4 zero = {0, 0, 0, 0};
+        *reinterpret_cast<i32x4*>(q_lds + (h * 16 + t) * ROWB + ((c ^ swz(t)) * 16)) = u < valid ? sv[k] : zero;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int u = tid + k * NT_;
+      if (u < 16 * H) w_lds[u] = ((u & 15) < rows) ? 0.5f * wsv[k] : 0.f;  // the ReLU identity's 1/2
     }
     if (tid == 0) qmax_lds = 0u;
   }
@@ -164,7 +184,8 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
 #pragma unroll
     for (int x = 0; x < EPU; ++x) lin[x] = 0.f;
     if (act) {
-      for (int h = 0; h < H; ++h) {
+#pragma unroll 4
+      for (int h = 0; h < H; ++h) {  // H is a multiple of 16
         const i32x4 val = *reinterpret_cast<const i32x4*>(q_lds + (h * 16 + t) * ROWB + ((u ^ swz(t)) * 16));
         const float wv = w_lds[h * 16 + t];
 #pragma unroll

@@ -360,8 +360,10 @@ __device__ __forceinline__ void first_k(int n, int K, int32_t* __restrict__ out)
 }
 
 // Load the wave step [base, base + 1024) of a segment ending at hi: lane gets elements
-// base + 4(lane + 64e) + j; slots past hi read as NaN-free zeros and are flagged invalid.
-__device__ __forceinline__ void load_step(const float* __restrict__ row, int base, int hi, int lane, f32x4 (&v)[kQ]) {
+// base + 4(lane + 64e) + j; slots past hi read as `fill` (callers either flag them invalid or
+// fill -inf, which no threshold test passes).
+__device__ __forceinline__ void load_step(const float* __restrict__ row, int base, int hi, int lane, f32x4 (&v)[kQ],
+                                          float fill = 0.f) {
 #pragma unroll
   for (int e = 0; e < kQ; ++e) {
     const int i = base + 4 * (lane + 64 * e);
@@ -369,7 +371,7 @@ __device__ __forceinline__ void load_step(const float* __restrict__ row, int bas
       v[e] = *reinterpret_cast<const f32x4*>(row + i);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[e][j] = (i + j < hi) ? row[i + j] : 0.f;
+      for (int j = 0; j < 4; ++j) v[e][j] = (i + j < hi) ? row[i + j] : fill;
     }
   }
 }
@@ -388,6 +390,20 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // crowded threshold bin) returns false before anything is written, and the exact two-pass path
 // runs instead, so the result never depends on the sample.
 constexpr int kSampleStride = 8;                          // sample one 16-float line in 8
+// A score below every element of value bin >= b (value_bin is monotone, so any x with
+// value_bin(x) < b will do): lo + (b - 0.01)/sc, moved down by ulps until value_bin confirms it.
+// The pass then tests x > floor with one compare per element, gathering bins >= b and at most
+// a sliver of bin b-1 (the finish rejects the list unless its threshold bin is >= b).
+__device__ __forceinline__ float bin_floor_below(int b, float lo, float sc) {
+  if (b <= 0) return -__builtin_inff();
+  float x = lo + (float(b) - 0.01f) / sc;
+  for (int it = 0; it < 64; ++it) {
+    if (value_bin(x, lo, sc, kVBins) < b) return x;
+    x = key_to_score(score_key(x) - 1u);  // next float down
+  }
+  return -__builtin_inff();  // every element a candidate: the list overflows, the exact path runs
+}
+
 constexpr int kFastMinN = 8192;                           // shorter rows: the exact path
 constexpr int kFastMaxN = int(sizeof(decltype(TopkRowSmem::u))) * 8;  // bitmap bits in the union
 
@@ -433,9 +449,9 @@ __device__ __forceinline__ int sample_threshold(const float* __restrict__ row, i
 }
 
 // keys/ids (LDS) hold `total` (K <= total <= CAP) candidates of a row of n <= kFastMaxN scores,
-// in any order, among them every element whose value bin is >= some bin b_est.  Finds the exact
-// threshold bin b1 (>= b_est), ranks its elements, and writes the k selected positions in index
-// order.  `bits` (kFastMaxN / 32 words of LDS) may alias keys/ids: the kept positions are moved
+// in any order, among them every element whose value bin is >= b_est (and possibly some of
+// lower bins).  Finds the exact threshold bin b1, ranks its elements, and writes the k selected
+// positions in index order; b1 < b_est (the list's bins >= b_est hold fewer than k) fails.  `bits` (kFastMaxN / 32 words of LDS) may alias keys/ids: the kept positions are moved
 // to registers first.  Each kept position then finds its output slot directly: the exclusive
 // count of 4-word bitmap groups before it (a block scan, stored in s.hist) plus at most four
 // popcounts -- balanced however the selection clusters.  Returns false, with nothing written,
@@ -443,9 +459,9 @@ __device__ __forceinline__ int sample_threshold(const float* __restrict__ row, i
 static_assert(kFastMaxN / 128 <= kBins, "bitmap group counts must fit the histogram array");
 
 template <int CAP>
-__device__ __forceinline__ bool finish_unordered(int n, int K, float lo, float sc, int total, uint32_t* keys,
-                                                 int* ids, uint32_t* bits, int32_t* __restrict__ out, TopkSmem& s,
-                                                 FinishSmem<512>& f) {
+__device__ __forceinline__ bool finish_unordered(int n, int K, float lo, float sc, int b_est, int total,
+                                                 uint32_t* keys, int* ids, uint32_t* bits, int32_t* __restrict__ out,
+                                                 TopkSmem& s, FinishSmem<512>& f) {
   static_assert(CAP % kTopkThreads == 0, "list capacity must be a multiple of the block size");
   const int tid = threadIdx.x;
   auto bin_of = [&](uint32_t k) { return value_bin(key_to_score(k), lo, sc, kVBins); };
@@ -455,6 +471,7 @@ __device__ __forceinline__ bool finish_unordered(int n, int K, float lo, float s
   __syncthreads();
   find_digit(s, kVBins, K);
   const int b1 = s.sel_digit, above = s.sel_above;
+  if (b1 < b_est) return false;  // bins below b_est may be incomplete in the list
   if (!rank_threshold_bin(keys, ids, total, b1, K - above, bin_of, f)) return false;
   // kept = bin > b1, or bin == b1 and not rejected (rejected keys were set to 0)
   constexpr int PER = CAP / kTopkThreads;
@@ -515,13 +532,14 @@ __device__ bool select_row_fast(const float* __restrict__ row, int n, int K, flo
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   if (tid == 0) sm.s.list_n = 0;
   const int b_est = sample_threshold<2>(row, n, K, lo, sc, 3.f, sm.s);
-  // one pass: every element of bin >= b_est into the list
+  const float floor_est = bin_floor_below(b_est, lo, sc);
+  // one pass: every element above floor_est (all of bin >= b_est) into the list
   const int seg = (((n + kTopkWaves - 1) / kTopkWaves) + 3) & ~3;
   const int seg_lo = min(n, w * seg), seg_hi = min(n, seg_lo + seg);
   constexpr int STEPW = 256 * kQ;
   for (int base = seg_lo; base < seg_hi; base += STEPW) {
     f32x4 v[kQ];
-    load_step(row, base, seg_hi, lane, v);
+    load_step(row, base, seg_hi, lane, v, -__builtin_inff());
 #pragma unroll
     for (int e = 0; e < kQ; ++e) {
       const int i0 = base + 4 * (lane + 64 * e);
@@ -529,7 +547,7 @@ __device__ bool select_row_fast(const float* __restrict__ row, int n, int K, flo
       int before = 0, total = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        keep[j] = (i0 + j < seg_hi) && value_bin(v[e][j], lo, sc, kVBins) >= b_est;
+        keep[j] = v[e][j] > floor_est;  // slots past the segment hold -inf
         const uint64_t bm = __ballot(keep[j]);
         before += lanes_below(bm);
         total += __popcll(bm);
@@ -552,7 +570,7 @@ __device__ bool select_row_fast(const float* __restrict__ row, int n, int K, flo
   __syncthreads();
   const int total = sm.s.list_n;
   if (total < K || total > kListCap) return false;
-  return finish_unordered<kListCap>(n, K, lo, sc, total, sm.u.l.lkeys, sm.u.l.lids,
+  return finish_unordered<kListCap>(n, K, lo, sc, b_est, total, sm.u.l.lkeys, sm.u.l.lids,
                                     reinterpret_cast<uint32_t*>(&sm.u), out, sm.s, sm.f);
 }
 

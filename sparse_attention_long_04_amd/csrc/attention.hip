@@ -256,9 +256,11 @@ constexpr int kRowKeys = 2048;
 // 56.0, 1 head 55.4.
 constexpr int kGatherHeadsPerPhase = 1;
 // Row groups per chunk dealt to one XCD: consecutive rows on one XCD keep the keys that
-// neighbouring rows share in its L2.  Measured (attention ms, 128K i.i.d. / drifting queries):
-// 1 group 55.8 / 46.1, 4: 55.8 / 41.6, 16: 55.4 / 39.8, 32: 55.4 / 39.7, 64: 55.3 / 39.7.
-constexpr int kGatherChunk = 32;
+// neighbouring rows share in its L2.  Measured in natural row order (attention ms, 128K
+// i.i.d. / drifting queries): 1 group 55.8 / 46.1, 4: 55.8 / 41.6, 16: 55.4 / 39.8, 32: 55.4 /
+// 39.7, 64: 55.3 / 39.7; with the rows in dominant-block order (i.i.d.): 16: 41.6, 32: 41.5,
+// 64: 41.2, 128: 41.1, 256: 41.1, 512: 41.2.
+constexpr int kGatherChunk = 128;
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void gather_rows_kernel(

@@ -63,24 +63,57 @@ __device__ __forceinline__ uint32_t pair_bf16(const i32x4& a, const i32x4& b, in
 }
 
 // One tile of 32 gathered keys in registers.  Lane (lr, lg):
-//   kf[h][c]: K row of key slot 8(lr/4)+4h+(lr%4), dims 32c+8lg .. +7  (S^T A operand)
+//   kf[h][c]: K row of key slot 8(lr/4)+4h+(lr%4), dims 32lg+8c .. +7  (S^T A operand; the
+//             contraction runs over the dims in this order, and Q is loaded the same way)
 //   vf[m]   : V row of key slot 8lg+m, dims 8lr .. 8lr+7             (transposed in registers)
 //   sv[m]   : index of key slot 8lg+m (-1 = masked)
+// K arrives in a load-friendly order and is put into the layout above by quad_transpose: in
+// the MFMA layout the four lanes of a quad hold four different keys, so loading it directly
+// makes every 16-byte load touch four rows per quad, and the address unit pays per row.
 struct GatherTile {
   i32x4 kf[2][4];
   i32x4 vf[8];
   int sv[8];
 };
 
+// Within each quad: x[c] of lane i <- x[i] of lane c (a 4x4 transpose of lane-in-quad and
+// register index, per dword), as two 2x2 exchanges (bit 0, then bit 1) of DPP quad permutes.
+__device__ __forceinline__ void quad_transpose(i32x4 (&x)[4], int lane) {
+  const bool b0 = lane & 1, b1 = lane & 2;
+#pragma unroll
+  for (int p = 0; p < 4; p += 2)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int xv = x[p][e], yv = x[p + 1][e];
+      const int xs = __builtin_amdgcn_mov_dpp(xv, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+      const int ys = __builtin_amdgcn_mov_dpp(yv, 0xB1, 0xF, 0xF, false);
+      x[p][e] = b0 ? ys : xv;
+      x[p + 1][e] = b0 ? yv : xs;
+    }
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int xv = x[p][e], yv = x[p + 2][e];
+      const int xs = __builtin_amdgcn_mov_dpp(xv, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+      const int ys = __builtin_amdgcn_mov_dpp(yv, 0x4E, 0xF, 0xF, false);
+      x[p][e] = b1 ? ys : xv;
+      x[p + 2][e] = b1 ? yv : xs;
+    }
+}
+
+// K: load c of lane (4a+i, lg) reads key slot 8a+4h+c, dims 32lg+8i .. +7, so the quad reads 64
+// contiguous bytes of one key; quad_transpose (done by the consumer once the loads have landed)
+// turns that into the layout of GatherTile.
 __device__ __forceinline__ void load_tile(GatherTile& t, const int* __restrict__ il, int tl,
                                           const uint16_t* __restrict__ kg_base,
                                           const uint16_t* __restrict__ vg_base, int64_t kvs, int lr, int lg) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int s = max(il[tl + 8 * (lr >> 2) + 4 * h + (lr & 3)], 0);
-    const uint16_t* kp = kg_base + (int64_t)s * kvs + 8 * lg;
+    const i32x4 sk = *reinterpret_cast<const i32x4*>(il + tl + 8 * (lr >> 2) + 4 * h);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) t.kf[h][c] = *reinterpret_cast<const i32x4*>(kp + 32 * c);
+    for (int c = 0; c < 4; ++c)
+      t.kf[h][c] = *reinterpret_cast<const i32x4*>(kg_base + (int64_t)max(sk[c], 0) * kvs + 32 * lg + 8 * (lr & 3));
   }
   const i32x4 s0 = *reinterpret_cast<const i32x4*>(il + tl + 8 * lg);
   const i32x4 s1 = *reinterpret_cast<const i32x4*>(il + tl + 8 * lg + 4);
@@ -92,7 +125,7 @@ __device__ __forceinline__ void load_tile(GatherTile& t, const int* __restrict__
 }
 
 // Attention of one wave's row r over cnt32 staged key slots (il, -1 = masked) of KV head g:
-// the Q^T operand holds head lr of the group, dims 32c + 8lg .. +7; on return o[dt][i] is the
+// the Q^T operand holds head lr of the group, dims 32lg + 8c .. +7 in register c; on return o[dt][i] is the
 // unnormalised O[head lr][dim 32lg + 8i + dt], m_run the running max (log2 units) and l_tot the
 // softmax denominator summed over the wave.
 template <int D>
@@ -104,10 +137,10 @@ __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, co
   i32x4 qf[4];
   {
     const bool hv = lr < G;
-    const uint16_t* qp = q + (r * Hq + g * G + (hv ? lr : 0)) * D + 8 * lg;
+    const uint16_t* qp = q + (r * Hq + g * G + (hv ? lr : 0)) * D + 32 * lg;  // dims 32lg + 8c, as K
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      qf[c] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(qp + 32 * c));
+      qf[c] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(qp + 8 * c));
       if (!hv) qf[c] = (i32x4){0, 0, 0, 0};
     }
   }
@@ -124,6 +157,7 @@ __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, co
     float z[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      quad_transpose(cur.kf[h], lr);
       f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) c4 = mfma_bf16_16x16x32(cur.kf[h][c], qf[c], c4);

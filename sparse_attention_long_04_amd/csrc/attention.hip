@@ -128,7 +128,7 @@ __device__ __forceinline__ void load_tile(GatherTile& t, const int* __restrict__
 // the Q^T operand holds head lr of the group, dims 32lg + 8c .. +7 in register c; on return o[dt][i] is the
 // unnormalised O[head lr][dim 32lg + 8i + dt], m_run the running max (log2 units) and l_tot the
 // softmax denominator summed over the wave.
-template <int D>
+template <int D, bool LAZY>
 __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, const int* __restrict__ il, int cnt32,
                                               int64_t r, int g, int G, int Hq, int64_t kvs,
                                               const uint16_t* __restrict__ kg_base,
@@ -164,15 +164,34 @@ __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, co
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[4 * h + i] = (cur.sv[4 * h + i] >= 0) ? c4[i] * scale_log2 : -__builtin_inff();
     }
-    // ---- online softmax (per head = lane column; keys over registers and the 4 lane groups)
+    // ---- online softmax (per head = lane column; keys over registers and the 4 lane groups).
+    // LAZY: the reference max moves only when a head's tile max passes it by more than 8 (log2
+    // units), so p = 2^(z - m) <= 2^8 and the O rescale -- a round trip of the accumulators
+    // through VALU -- happens on few tiles (it costs registers: the decode kernel keeps the
+    // eager form to stay at two waves per SIMD).
     float mt = z[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mt = fmaxf(mt, z[i]);
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    if constexpr (LAZY) {
+      const bool move = mt > m_run + 8.f;  // false while every key so far is masked
+      if (__ballot(move)) {
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;  // m_run = -inf: 0
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+        m_run = move ? mt : m_run;
+      }
+    } else {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - ((m_new == -__builtin_inff()) ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
     float ps = 0.f;
     uint32_t phi[8], plo[8];
 #pragma unroll
@@ -184,10 +203,7 @@ __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, co
       phi[i] = hb;
       plo[i] = __float_as_uint(pv - __uint_as_float(hb)) & 0xFFFF0000u;
     }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    l_run += ps;
     const i32x4 bh = {int((phi[0] >> 16) | phi[1]), int((phi[2] >> 16) | phi[3]), int((phi[4] >> 16) | phi[5]),
                       int((phi[6] >> 16) | phi[7])};
     const i32x4 bl = {int((plo[0] >> 16) | plo[1]), int((plo[2] >> 16) | plo[3]), int((plo[4] >> 16) | plo[5]),
@@ -255,8 +271,8 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
   const int64_t kvs = (int64_t)Hkv * D;
   f32x4 o[8];
   float m_run, l_tot;
-  attend_staged<D>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D, v + ri.kv_row0 * kvs + g * D,
-                   scale_log2, lr, lg, o, m_run, l_tot);
+  attend_staged<D, false>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D, v + ri.kv_row0 * kvs + g * D,
+                          scale_log2, lr, lg, o, m_run, l_tot);
   if (lr >= G) return;
   const int head = g * G + lr;
   if (nsplit == 1) {
@@ -327,8 +343,8 @@ __global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
   const int64_t kvs = (int64_t)Hkv * D;
   f32x4 o[8];
   float m_run, l_tot;
-  attend_staged<D>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D, v + ri.kv_row0 * kvs + g * D,
-                   scale_log2, lr, lg, o, m_run, l_tot);
+  attend_staged<D, true>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D, v + ri.kv_row0 * kvs + g * D,
+                         scale_log2, lr, lg, o, m_run, l_tot);
   if (lr >= G) return;
   store_out_bf16<D>(out, r, Hq, g * G + lr, lg, o, l_tot);
   // natural-log log-sum-exp of the row's scaled scores (the backward's softmax statistics)

@@ -128,12 +128,22 @@ __device__ __forceinline__ void load_tile(GatherTile& t, const int* __restrict__
 // the Q^T operand holds head lr of the group, dims 32lg + 8c .. +7 in register c; on return o[dt][i] is the
 // unnormalised O[head lr][dim 32lg + 8i + dt], m_run the running max (log2 units) and l_tot the
 // softmax denominator summed over the wave.
-template <int D, bool LAZY>
+// K tile of the LDS path: load (h, c) of the wave lands in region 4h+c, each lane's 16 bytes at
+// lane*16; the 16-byte pad per region staggers the banks of the transposed read-back.
+constexpr int kKRegion = 64 * 16 + 16;
+constexpr int kKTileLds = 8 * kKRegion;  // per wave
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVm8 = 0x0F78;     // vmcnt(8), others not waited
+constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0), others not waited
+
+template <int D, bool LAZY, bool KLDS>
 __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, const int* __restrict__ il, int cnt32,
                                               int64_t r, int g, int G, int Hq, int64_t kvs,
                                               const uint16_t* __restrict__ kg_base,
                                               const uint16_t* __restrict__ vg_base, float scale_log2, int lr, int lg,
-                                              f32x4 (&o)[8], float& m_run, float& l_tot) {
+                                              f32x4 (&o)[8], float& m_run, float& l_tot,
+                                              __attribute__((address_space(3))) uint8_t* kb) {
   i32x4 qf[4];
   {
     const bool hv = lr < G;
@@ -149,20 +159,18 @@ __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, co
   m_run = -__builtin_inff();
   float l_run = 0.f;
 
-  GatherTile cur, nxt;
-  if (cnt32 > 0) load_tile(cur, il, 0, kg_base, vg_base, kvs, lr, lg);
-  for (int tl = 0; tl < cnt32; tl += 32) {
-    if (tl + 32 < cnt32) load_tile(nxt, il, tl + 32, kg_base, vg_base, kvs, lr, lg);
+  // One tile: kf in the MFMA layout of GatherTile (fix(h) puts sub-tile h there first).
+  auto compute = [&](i32x4 (&kf)[2][4], const i32x4 (&vf)[8], const int (&sv)[8], auto fix) {
     // ---- S^T = K Q^T for the two 16-key sub-tiles; lane slot 8lg + 4h + i
     float z[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      quad_transpose(cur.kf[h], lr);
+      fix(h);
       f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) c4 = mfma_bf16_16x16x32(cur.kf[h][c], qf[c], c4);
+      for (int c = 0; c < 4; ++c) c4 = mfma_bf16_16x16x32(kf[h][c], qf[c], c4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[4 * h + i] = (cur.sv[4 * h + i] >= 0) ? c4[i] * scale_log2 : -__builtin_inff();
+      for (int i = 0; i < 4; ++i) z[4 * h + i] = (sv[4 * h + i] >= 0) ? c4[i] * scale_log2 : -__builtin_inff();
     }
     // ---- online softmax (per head = lane column; keys over registers and the 4 lane groups).
     // LAZY: the reference max moves only when a head's tile max passes it by more than 8 (log2
@@ -211,12 +219,70 @@ __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, co
     // ---- O^T += V^T P^T; dim tile dt holds dims 8*row + dt, row = 0..15
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const i32x4 a = {int(pair_bf16(cur.vf[0], cur.vf[1], dt)), int(pair_bf16(cur.vf[2], cur.vf[3], dt)),
-                       int(pair_bf16(cur.vf[4], cur.vf[5], dt)), int(pair_bf16(cur.vf[6], cur.vf[7], dt))};
+      const i32x4 a = {int(pair_bf16(vf[0], vf[1], dt)), int(pair_bf16(vf[2], vf[3], dt)),
+                       int(pair_bf16(vf[4], vf[5], dt)), int(pair_bf16(vf[6], vf[7], dt))};
       o[dt] = mfma_bf16_16x16x32(a, bh, o[dt]);
       o[dt] = mfma_bf16_16x16x32(a, bl, o[dt]);
     }
-    cur = nxt;
+  };
+
+  if constexpr (KLDS) {
+    // K through LDS: the tile's 8 K loads go straight to the wave's LDS regions (load (h, c):
+    // lane (4a+i, lg) fetches key slot 8a+4h+c, dims 32lg+8i -- 64 contiguous bytes per quad)
+    // and are read back in the MFMA layout (lane (4a+i, lg), register c of sub-tile h = region
+    // (h, i), lane slot 4a+c+16lg), so no VALU transpose.  Per tile the K loads are issued
+    // before the V loads: at the top of the next iteration vmcnt(8) leaves only the V loads in
+    // flight.  The region is refilled only after its read-back has completed (lgkmcnt(0)).
+    struct VTile {
+      i32x4 vf[8];
+      int sv[8];
+    };
+    auto issue = [&](VTile& t, int tl) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const i32x4 sk = *reinterpret_cast<const i32x4*>(il + tl + 8 * (lr >> 2) + 4 * h);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          __builtin_amdgcn_global_load_lds(kg_base + (int64_t)max(sk[c], 0) * kvs + 32 * lg + 8 * (lr & 3),
+                                           kb + (4 * h + c) * kKRegion, 16, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the K loads ahead of the V loads (vmcnt order)
+      const i32x4 s0 = *reinterpret_cast<const i32x4*>(il + tl + 8 * lg);
+      const i32x4 s1 = *reinterpret_cast<const i32x4*>(il + tl + 8 * lg + 4);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) { t.sv[m] = s0[m]; t.sv[4 + m] = s1[m]; }
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        t.vf[m] = *reinterpret_cast<const i32x4*>(vg_base + (int64_t)max(t.sv[m], 0) * kvs + 8 * lr);
+    };
+    const __attribute__((address_space(3))) uint8_t* kr = kb + (lr & 3) * kKRegion + (4 * (lr >> 2) + 16 * lg) * 16;
+    VTile vc, vn;
+    if (cnt32 > 0) issue(vc, 0);
+    for (int tl = 0; tl < cnt32; tl += 32) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWaitVm8);  // this tile's K is in LDS
+      i32x4 kf[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          kf[h][c] = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(kr + 4 * h * kKRegion + 16 * c);
+      if (tl + 32 < cnt32) {
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the read-back has landed
+        __builtin_amdgcn_sched_barrier(0);
+        issue(vn, tl + 32);
+      }
+      compute(kf, vc.vf, vc.sv, [](int) {});
+      vc = vn;
+    }
+  } else {
+    GatherTile cur, nxt;
+    if (cnt32 > 0) load_tile(cur, il, 0, kg_base, vg_base, kvs, lr, lg);
+    for (int tl = 0; tl < cnt32; tl += 32) {
+      if (tl + 32 < cnt32) load_tile(nxt, il, tl + 32, kg_base, vg_base, kvs, lr, lg);
+      compute(cur.kf, cur.vf, cur.sv, [&](int h) { quad_transpose(cur.kf[h], lr); });
+      cur = nxt;
+    }
   }
   l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16);
@@ -271,8 +337,8 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
   const int64_t kvs = (int64_t)Hkv * D;
   f32x4 o[8];
   float m_run, l_tot;
-  attend_staged<D, false>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D, v + ri.kv_row0 * kvs + g * D,
-                          scale_log2, lr, lg, o, m_run, l_tot);
+  attend_staged<D, false, false>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D,
+                                 v + ri.kv_row0 * kvs + g * D, scale_log2, lr, lg, o, m_run, l_tot, nullptr);
   if (lr >= G) return;
   const int head = g * G + lr;
   if (nsplit == 1) {
@@ -320,6 +386,7 @@ __global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
     unsigned blocks_per_phase, const int32_t* __restrict__ order) {
   static_assert(D == 128, "head_dim 128 only");
   __shared__ __attribute__((aligned(16))) int il_all[NW][kRowKeys + 32];
+  __shared__ __attribute__((aligned(16))) uint8_t kb_all[NW][kKTileLds];  // K tiles (LDS path)
   // phase p (in launch order) serves heads p*hp .. p*hp+hp-1 over all rows
   const unsigned phase = blockIdx.x / blocks_per_phase, bid = blockIdx.x % blocks_per_phase;
   const int xcd = bid & 7;  // blocks_per_phase is a multiple of 8: the XCD of the workgroup
@@ -343,8 +410,9 @@ __global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
   const int64_t kvs = (int64_t)Hkv * D;
   f32x4 o[8];
   float m_run, l_tot;
-  attend_staged<D, true>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D, v + ri.kv_row0 * kvs + g * D,
-                         scale_log2, lr, lg, o, m_run, l_tot);
+  attend_staged<D, true, true>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D,
+                               v + ri.kv_row0 * kvs + g * D, scale_log2, lr, lg, o, m_run, l_tot,
+                               (__attribute__((address_space(3))) uint8_t*)kb_all[wave]);
   if (lr >= G) return;
   store_out_bf16<D>(out, r, Hq, g * G + lr, lg, o, l_tot);
   // natural-log log-sum-exp of the row's scaled scores (the backward's softmax statistics)

@@ -389,7 +389,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // in an LDS bitmap and written in index order.  Any miss (too few or too many candidates, a
 // crowded threshold bin) returns false before anything is written, and the exact two-pass path
 // runs instead, so the result never depends on the sample.
-constexpr int kSampleStride = 8;                          // sample one 16-float line in 8
+constexpr int kSampleStride = 8;                          // sample one 128-byte line in 8
 // A score below every element of value bin >= b (value_bin is monotone, so any x with
 // value_bin(x) < b will do): lo + (b - 0.01)/sc, moved down by ulps until value_bin confirms it.
 // The pass then tests x > floor with one compare per element, gathering bins >= b and at most
@@ -407,40 +407,44 @@ __device__ __forceinline__ float bin_floor_below(int b, float lo, float sc) {
 constexpr int kFastMinN = 8192;                           // shorter rows: the exact path
 constexpr int kFastMaxN = int(sizeof(decltype(TopkRowSmem::u))) * 8;  // bitmap bits in the union
 
-// Sampled threshold bin of a row whose scores lie in [lo, lo + kVBins/sc] (rows start 64-byte
-// aligned, so every sampled line is whole).  The bin leaves z standard deviations of the sampled
-// count (plus 4) as margin above k.  Returns 0 (every element a candidate) when the sample is too
-// small to place the margin.  BATCH line loads per thread are issued before their histogram
-// atomics.  Every thread of the block must call it; all get the same result.
+// Sampled threshold bin of a row whose scores lie in [lo, lo + kVBins/sc].  The sample is every
+// kSampleStride-th whole 128-byte line of the row (counted from the first 128-byte boundary in
+// it), so no sampled line drags in bytes that are not used.  The bin leaves z standard
+// deviations of the sampled count (plus 4) as margin above k.  Returns 0 (every element a
+// candidate) when the sample is too small to place the margin.  BATCH line loads per thread are
+// issued before their histogram atomics.  Every thread of the block must call it; all get the
+// same result.
 template <int BATCH>
 __device__ __forceinline__ int sample_threshold(const float* __restrict__ row, int n, int K, float lo, float sc,
                                                 float z, TopkSmem& s) {
   const int tid = threadIdx.x;
   for (int i = tid; i < kVBins; i += kTopkThreads) s.hist[i] = 0;
   __syncthreads();
-  const int nlines = n >> 4;
+  const int skip = int(((128u - (uint32_t(reinterpret_cast<uintptr_t>(row)) & 127u)) & 127u) >> 2);
+  const int nlines = n > skip ? (n - skip) >> 5 : 0;  // whole 32-float lines after the boundary
   const int nsl = (nlines + kSampleStride - 1) / kSampleStride;
+  const float* base = row + skip;
   for (int m0 = 0; m0 < nsl; m0 += BATCH * kTopkThreads) {
-    f32x4 x[BATCH][4];
+    f32x4 x[BATCH][8];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int m = m0 + u * kTopkThreads + tid;
       if (m < nsl) {
-        const float* p = row + (int64_t)m * kSampleStride * 16;
+        const float* p = base + (int64_t)m * kSampleStride * 32;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) x[u][c] = *reinterpret_cast<const f32x4*>(p + 4 * c);
+        for (int c = 0; c < 8; ++c) x[u][c] = *reinterpret_cast<const f32x4*>(p + 4 * c);
       }
     }
 #pragma unroll
     for (int u = 0; u < BATCH; ++u)
       if (m0 + u * kTopkThreads + tid < nsl)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
           for (int e = 0; e < 4; ++e) atomicAdd(&s.hist[value_bin(x[u][c][e], lo, sc, kVBins)], 1);
   }
   __syncthreads();
-  const int ns = 16 * nsl;
+  const int ns = 32 * nsl;
   const float expect = float(K) * float(ns) / float(n);
   const int need = int(expect + z * sqrtf(expect) + 4.f);
   if (need > ns) return 0;
@@ -531,7 +535,7 @@ __device__ bool select_row_fast(const float* __restrict__ row, int n, int K, flo
                                 int32_t* __restrict__ out, TopkRowSmem& sm) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   if (tid == 0) sm.s.list_n = 0;
-  const int b_est = sample_threshold<2>(row, n, K, lo, sc, 3.f, sm.s);
+  const int b_est = sample_threshold<1>(row, n, K, lo, sc, 3.f, sm.s);
   const float floor_est = bin_floor_below(b_est, lo, sc);
   // one pass: every element above floor_est (all of bin >= b_est) into the list
   const int seg = (((n + kTopkWaves - 1) / kTopkWaves) + 3) & ~3;

@@ -414,19 +414,22 @@ def test_topk_long_rows_sampled_threshold():
 
 @pytest.mark.parametrize("hot_on_sampled", [False, True])
 def test_topk_sample_misleads(hot_on_sampled):
-    """Keys are zeroed (score exactly 0) on one class of 16-key lines: either the lines a 1-in-8
-    sample reads or the others.  The sample then over- or under-estimates the threshold (too
-    many candidates, or fewer than k); the select must still match the oracle exactly."""
+    """Keys are zeroed (score exactly 0) on one class of 32-key lines: either the lines a 1-in-8
+    sample of 128-byte lines reads in a row that starts on a 128-byte boundary, or the others.
+    The sample then over- or under-estimates the threshold (too many candidates, or fewer than
+    k); the select must still match the oracle exactly.  Rows 8193 and 9001 start 64 bytes past
+    a boundary (row t of block j = t // 16 starts (t % 16)(j + 1) 64-byte units into the block),
+    so their sample straddles the planted lines."""
     n = 20000
     p = gen.make_prefill([n], idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=2048, seed=44)
-    sampled = (np.arange(n) // 16) % 8 == 0
+    sampled = (np.arange(n) // 32) % 8 == 0
     cold = ~sampled if hot_on_sampled else sampled
     p.k_idx[cold] = 0
     pb = PrefillBatch(p)
     pb.index_topk()
     idx = pb.topk_idx.cpu().numpy()
     o = oracle_of(p)
-    for t in [8191, 8192, 9000, 15000, 19999]:
+    for t in [8191, 8192, 8193, 9000, 9001, 15000, 19999]:
         assert np.array_equal(idx[t], O.select_topk_row(o.scores(t), p.topk)), t
 
 

@@ -462,13 +462,12 @@ __device__ __forceinline__ int sample_threshold(const float* __restrict__ row, i
 // when bin b1 is too crowded to rank in LDS.
 static_assert(kFastMaxN / 128 <= kBins, "bitmap group counts must fit the histogram array");
 
-template <int CAP>
-__device__ __forceinline__ bool finish_unordered(int n, int K, float lo, float sc, int b_est, int total,
+template <int CAP, class BinOf>
+__device__ __forceinline__ bool finish_unordered(int n, int K, BinOf bin_of, int b_est, int total,
                                                  uint32_t* keys, int* ids, uint32_t* bits, int32_t* __restrict__ out,
                                                  TopkSmem& s, FinishSmem<512>& f) {
   static_assert(CAP % kTopkThreads == 0, "list capacity must be a multiple of the block size");
   const int tid = threadIdx.x;
-  auto bin_of = [&](uint32_t k) { return value_bin(key_to_score(k), lo, sc, kVBins); };
   for (int i = tid; i < kVBins; i += kTopkThreads) s.hist[i] = 0;
   __syncthreads();
   for (int i = tid; i < total; i += kTopkThreads) atomicAdd(&s.hist[bin_of(keys[i])], 1);
@@ -574,7 +573,8 @@ __device__ bool select_row_fast(const float* __restrict__ row, int n, int K, flo
   __syncthreads();
   const int total = sm.s.list_n;
   if (total < K || total > kListCap) return false;
-  return finish_unordered<kListCap>(n, K, lo, sc, b_est, total, sm.u.l.lkeys, sm.u.l.lids,
+  auto bin_of = [&](uint32_t k) { return value_bin(key_to_score(k), lo, sc, kVBins); };
+  return finish_unordered<kListCap>(n, K, bin_of, b_est, total, sm.u.l.lkeys, sm.u.l.lids,
                                     reinterpret_cast<uint32_t*>(&sm.u), out, sm.s, sm.f);
 }
 
@@ -1048,15 +1048,129 @@ __device__ __forceinline__ void gen_wave_counts(TopkGenSmem& sm, int from, bool 
   __syncthreads();
 }
 
+// ---- fast path of the standalone top-k: a sampled key threshold and one pass over HBM -------
+// As the prefill fast path, but with no score range known: the sample (every kSampleStride-th
+// 128-byte line) is binned on the order-preserving key, top 11 bits and then the next 11 bits
+// inside the chosen digit, giving a threshold key T with a margin of three standard deviations
+// of the sampled count.  One pass gathers every element with key >= T (a float compare against
+// the score whose key is T: NaN and -inf never pass) into the unordered LDS list, which
+// finish_unordered settles exactly with key bins (k - T) >> sh.  Any miss returns false before
+// anything is written and the two-pass path runs.
+constexpr int kGenFastMaxK = 2048;  // the list (kListCap) must hold k plus the margin
+
+template <class Dig>
+__device__ __forceinline__ void gen_sample_hist(const float* __restrict__ base, int nsl, Dig dig, TopkSmem& s) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kBins; i += kTopkThreads) s.hist[i] = 0;
+  __syncthreads();
+  for (int m = tid; m < nsl; m += kTopkThreads) {
+    const float* p = base + (int64_t)m * kSampleStride * 32;
+    f32x4 x[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = *reinterpret_cast<const f32x4*>(p + 4 * c);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = dig(general_key(x[c][e]));
+        if (d >= 0) atomicAdd(&s.hist[d], 1);
+      }
+  }
+  __syncthreads();
+}
+
+__device__ bool select_general_fast(const float* __restrict__ row, int n, int K, int32_t* __restrict__ out,
+                                    TopkRowSmem& sm) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int skip = int(((128u - (uint32_t(reinterpret_cast<uintptr_t>(row)) & 127u)) & 127u) >> 2);
+  const int nlines = n > skip ? (n - skip) >> 5 : 0;
+  const int nsl = (nlines + kSampleStride - 1) / kSampleStride;
+  const int ns = 32 * nsl;
+  const float expect = float(K) * float(ns) / float(n);
+  const int need = int(expect + 3.f * sqrtf(expect) + 4.f);
+  if (need > ns) return false;
+  const float* base = row + skip;
+  gen_sample_hist(base, nsl, [](uint32_t k) { return int(k >> 21); }, sm.s);
+  find_digit(sm.s, kBins, need);
+  const int d1 = sm.s.sel_digit, above1 = sm.s.sel_above;
+  gen_sample_hist(base, nsl, [d1](uint32_t k) { return int(k >> 21) == d1 ? int((k >> 10) & 0x7FFu) : -1; }, sm.s);
+  find_digit(sm.s, kBins, need - above1);
+  const uint32_t T = (uint32_t(d1) << 21) | (uint32_t(sm.s.sel_digit) << 10);
+  if (T <= 0x007FFFFFu) return false;  // at or below the key of -inf: masked elements would pass
+  const float xT = key_to_score(T);    // the score whose key is T (NaN when T is a NaN key: nothing passes)
+  if (tid == 0) sm.s.list_n = 0;
+  __syncthreads();
+  const int seg = (((n + kTopkWaves - 1) / kTopkWaves) + 3) & ~3;
+  const int seg_lo = min(n, w * seg), seg_hi = min(n, seg_lo + seg);
+  constexpr int STEPW = 256 * kQ;
+  for (int b0 = seg_lo; b0 < seg_hi; b0 += STEPW) {
+    f32x4 v[kQ];
+    load_step(row, b0, seg_hi, lane, v, -__builtin_inff());
+#pragma unroll
+    for (int e = 0; e < kQ; ++e) {
+      const int i0 = b0 + 4 * (lane + 64 * e);
+      bool keep[4];
+      int before = 0, total = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        keep[j] = v[e][j] >= xT;  // slots past the segment hold -inf, which never passes
+        const uint64_t bm = __ballot(keep[j]);
+        before += lanes_below(bm);
+        total += __popcll(bm);
+      }
+      if (total == 0) continue;
+      int bpos = 0;
+      if (lane == 0) bpos = atomicAdd(&sm.s.list_n, total);
+      int slot = __shfl(bpos, 0) + before;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (keep[j]) {
+          if (slot < kListCap) {
+            sm.u.l.lkeys[slot] = score_key(v[e][j]);
+            sm.u.l.lids[slot] = i0 + j;
+          }
+          ++slot;
+        }
+    }
+  }
+  __syncthreads();
+  const int total = sm.s.list_n;
+  if (total < K || total > kListCap) return false;
+  // key bins relative to T, fine enough that the largest key lands in bin < kVBins
+  uint32_t kmax = 0u;
+  for (int i = tid; i < total; i += kTopkThreads) kmax = max(kmax, sm.u.l.lkeys[i]);
+  for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  if (lane == 0) sm.s.wave_tot[w] = int(kmax - T);
+  __syncthreads();
+  uint32_t span = 0u;
+#pragma unroll
+  for (int ww = 0; ww < kTopkWaves; ++ww) span = max(span, uint32_t(sm.s.wave_tot[ww]));
+  __syncthreads();
+  int sh = 0;
+  while ((span >> sh) >= uint32_t(kVBins)) ++sh;
+  auto bin_of = [T, sh](uint32_t k) { return min(kVBins - 1, int((k - T) >> sh)); };
+  return finish_unordered<kListCap>(n, K, bin_of, 0, total, sm.u.l.lkeys, sm.u.l.lids,
+                                    reinterpret_cast<uint32_t*>(&sm.u), out, sm.s, sm.f);
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kTopkThreads) void topk_general_kernel(const float* __restrict__ scores, int64_t ld,
                                                                     int n_all, const int32_t* __restrict__ lens,
                                                                     int K, int32_t* __restrict__ out) {
-  __shared__ TopkGenSmem sm;
+  __shared__ union {
+    TopkGenSmem g;  // two-pass path
+    TopkRowSmem f;  // sampled single pass
+  } smu;
+  TopkGenSmem& sm = smu.g;
   const int64_t r = blockIdx.x;
   const float* __restrict__ row = scores + r * ld;
   const int n = lens ? max(0, min(n_all, lens[r])) : n_all;
   int32_t* __restrict__ orow = out + r * K;
+  if constexpr (VEC) {
+    if (n >= kFastMinN && n <= kFastMaxN && K <= kGenFastMaxK && select_general_fast(row, n, K, orow, smu.f))
+      return;  // exactly k positions written
+    __syncthreads();  // the fast path's LDS is reused below
+  }
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int seg = (((n + kTopkWaves - 1) / kTopkWaves) + 3) & ~3;
   const int seg_lo = min(n, w * seg), seg_hi = min(n, seg_lo + seg);

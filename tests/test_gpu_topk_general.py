@@ -4,7 +4,11 @@ Bar: the selected positions are bit-exact (integer output).  Cases cover special
 (NaN of any sign and payload, +-inf, +-0), every path of the kernel (all selectable kept;
 candidates finished in LDS; a second-digit refinement when the threshold digit is crowded;
 the HBM fallback for massive ties), ragged row lengths, rows shorter than k, empty rows,
-unaligned rows, and the full-size workload on sampled rows."""
+unaligned rows, and the full-size workload on sampled rows.  Rows of 8192 keys or more take a
+sampled single pass first (falling back to the two-pass path on any miss); the long cases
+cover it with special values and with more than k ties at +inf."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -42,12 +46,15 @@ CASES = [
     ("const", 3, 20000, "const", dict(), (2048,)),
     ("all_masked", 2, 1000, "normal", dict(masked=0.6, nans=0.5), (16, 2048)),
     ("long_normal", 4, 131072, "normal", dict(masked=0.01), (2048,)),
+    # rows of 8192+ keys take the sampled single pass first
+    ("long_specials", 4, 50000, "normal", dict(masked=0.1, nans=0.1, infs=0.01, zeros=0.2), (1, 64, 2048)),
+    ("long_posinf_ties", 3, 40000, "normal", dict(infs=0.2), (2048,)),  # k among > k ties at +inf
 ]
 
 
 @pytest.mark.parametrize("name,rows,n,kind,sp,ks", CASES, ids=[c[0] for c in CASES])
 def test_topk_general_parity(name, rows, n, kind, sp, ks):
-    s = gen.make_topk_scores(rows, n, seed=hash(name) % 1000, kind=kind, **sp)
+    s = gen.make_topk_scores(rows, n, seed=zlib.crc32(name.encode()) % 1000, kind=kind, **sp)
     for k in ks:
         print(f"[topk] {name} rows={rows} n={n} k={k}", flush=True)
         got = _run(s, k)

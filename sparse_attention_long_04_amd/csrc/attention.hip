@@ -314,6 +314,7 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
     float2* __restrict__ ml_part, float* __restrict__ lse_out) {
   static_assert(D == 128, "head_dim 128 only");
   __shared__ __attribute__((aligned(16))) int il[kMaxSplitKeys + 32];
+  __shared__ __attribute__((aligned(16))) uint8_t kb_all[NW][kKTileLds];  // K tiles (LDS path)
   const int64_t r = blockIdx.x;
   const int split = blockIdx.y;
   const int g = threadIdx.x >> 6;
@@ -337,8 +338,9 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
   const int64_t kvs = (int64_t)Hkv * D;
   f32x4 o[8];
   float m_run, l_tot;
-  attend_staged<D, false, false>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D,
-                                 v + ri.kv_row0 * kvs + g * D, scale_log2, lr, lg, o, m_run, l_tot, nullptr);
+  attend_staged<D, false, true>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D,
+                                v + ri.kv_row0 * kvs + g * D, scale_log2, lr, lg, o, m_run, l_tot,
+                                (__attribute__((address_space(3))) uint8_t*)kb_all[g]);
   if (lr >= G) return;
   const int head = g * G + lr;
   if (nsplit == 1) {

@@ -5,7 +5,8 @@
 // attend_staged (the per-wave body shared by both gather kernels) -- one wave attends one row
 //   for one KV head; the head's query heads (Hq/Hkv, padded to 16) share the row's index set.
 //   Per 32-key tile:
-//     S^T = K Q^T   bf16 MFMA 16x16x32, K rows gathered from HBM straight into A registers;
+//     S^T = K Q^T   bf16 MFMA 16x16x32, K rows gathered from HBM into the wave's LDS (direct
+//                     loads, 64 contiguous bytes per quad) and read back as A operands;
 //     online softmax in fp32 (exp2, running max/sum per head);
 //     O^T += V^T P^T  bf16 MFMA 16x16x32 with P split as hi + lo bf16 (two MFMAs, relative
 //                     error ~2^-16).  V needs keys along the MFMA k dimension: each lane
@@ -62,72 +63,6 @@ __device__ __forceinline__ uint32_t pair_bf16(const i32x4& a, const i32x4& b, in
   return (e & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
 }
 
-// One tile of 32 gathered keys in registers.  Lane (lr, lg):
-//   kf[h][c]: K row of key slot 8(lr/4)+4h+(lr%4), dims 32lg+8c .. +7  (S^T A operand; the
-//             contraction runs over the dims in this order, and Q is loaded the same way)
-//   vf[m]   : V row of key slot 8lg+m, dims 8lr .. 8lr+7             (transposed in registers)
-//   sv[m]   : index of key slot 8lg+m (-1 = masked)
-// K arrives in a load-friendly order and is put into the layout above by quad_transpose: in
-// the MFMA layout the four lanes of a quad hold four different keys, so loading it directly
-// makes every 16-byte load touch four rows per quad, and the address unit pays per row.
-struct GatherTile {
-  i32x4 kf[2][4];
-  i32x4 vf[8];
-  int sv[8];
-};
-
-// Within each quad: x[c] of lane i <- x[i] of lane c (a 4x4 transpose of lane-in-quad and
-// register index, per dword), as two 2x2 exchanges (bit 0, then bit 1) of DPP quad permutes.
-__device__ __forceinline__ void quad_transpose(i32x4 (&x)[4], int lane) {
-  const bool b0 = lane & 1, b1 = lane & 2;
-#pragma unroll
-  for (int p = 0; p < 4; p += 2)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int xv = x[p][e], yv = x[p + 1][e];
-      const int xs = __builtin_amdgcn_mov_dpp(xv, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
-      const int ys = __builtin_amdgcn_mov_dpp(yv, 0xB1, 0xF, 0xF, false);
-      x[p][e] = b0 ? ys : xv;
-      x[p + 1][e] = b0 ? yv : xs;
-    }
-#pragma unroll
-  for (int p = 0; p < 2; ++p)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int xv = x[p][e], yv = x[p + 2][e];
-      const int xs = __builtin_amdgcn_mov_dpp(xv, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
-      const int ys = __builtin_amdgcn_mov_dpp(yv, 0x4E, 0xF, 0xF, false);
-      x[p][e] = b1 ? ys : xv;
-      x[p + 2][e] = b1 ? yv : xs;
-    }
-}
-
-// K: load c of lane (4a+i, lg) reads key slot 8a+4h+c, dims 32lg+8i .. +7, so the quad reads 64
-// contiguous bytes of one key; quad_transpose (done by the consumer once the loads have landed)
-// turns that into the layout of GatherTile.
-__device__ __forceinline__ void load_tile(GatherTile& t, const int* __restrict__ il, int tl,
-                                          const uint16_t* __restrict__ kg_base,
-                                          const uint16_t* __restrict__ vg_base, int64_t kvs, int lr, int lg) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const i32x4 sk = *reinterpret_cast<const i32x4*>(il + tl + 8 * (lr >> 2) + 4 * h);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      t.kf[h][c] = *reinterpret_cast<const i32x4*>(kg_base + (int64_t)max(sk[c], 0) * kvs + 32 * lg + 8 * (lr & 3));
-  }
-  const i32x4 s0 = *reinterpret_cast<const i32x4*>(il + tl + 8 * lg);
-  const i32x4 s1 = *reinterpret_cast<const i32x4*>(il + tl + 8 * lg + 4);
-#pragma unroll
-  for (int m = 0; m < 4; ++m) { t.sv[m] = s0[m]; t.sv[4 + m] = s1[m]; }
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-    t.vf[m] = *reinterpret_cast<const i32x4*>(vg_base + (int64_t)max(t.sv[m], 0) * kvs + 8 * lr);
-}
-
-// Attention of one wave's row r over cnt32 staged key slots (il, -1 = masked) of KV head g:
-// the Q^T operand holds head lr of the group, dims 32lg + 8c .. +7 in register c; on return o[dt][i] is the
-// unnormalised O[head lr][dim 32lg + 8i + dt], m_run the running max (log2 units) and l_tot the
-// softmax denominator summed over the wave.
 // K tile of the LDS path: load (h, c) of the wave lands in region 4h+c, each lane's 16 bytes at
 // lane*16; the 16-byte pad per region staggers the banks of the transposed read-back.
 constexpr int kKRegion = 64 * 16 + 16;
@@ -137,7 +72,7 @@ constexpr int kKTileLds = 8 * kKRegion;  // per wave
 constexpr int kWaitVm8 = 0x0F78;     // vmcnt(8), others not waited
 constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0), others not waited
 
-template <int D, bool LAZY, bool KLDS>
+template <int D, bool LAZY>
 __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, const int* __restrict__ il, int cnt32,
                                               int64_t r, int g, int G, int Hq, int64_t kvs,
                                               const uint16_t* __restrict__ kg_base,
@@ -159,13 +94,16 @@ __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, co
   m_run = -__builtin_inff();
   float l_run = 0.f;
 
-  // One tile: kf in the MFMA layout of GatherTile (fix(h) puts sub-tile h there first).
-  auto compute = [&](i32x4 (&kf)[2][4], const i32x4 (&vf)[8], const int (&sv)[8], auto fix) {
+  // One tile of 32 keys.  Lane (lr, lg):
+  //   kf[h][c]: K row of key slot 8(lr/4)+4h+(lr%4), dims 32lg+8c .. +7  (S^T A operand; the
+  //             contraction runs over the dims in this order, and Q is loaded the same way)
+  //   vf[m]   : V row of key slot 8lg+m, dims 8lr .. 8lr+7             (transposed in registers)
+  //   sv[m]   : index of key slot 8lg+m (-1 = masked)
+  auto compute = [&](const i32x4 (&kf)[2][4], const i32x4 (&vf)[8], const int (&sv)[8]) {
     // ---- S^T = K Q^T for the two 16-key sub-tiles; lane slot 8lg + 4h + i
     float z[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      fix(h);
       f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) c4 = mfma_bf16_16x16x32(kf[h][c], qf[c], c4);
@@ -226,13 +164,16 @@ __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, co
     }
   };
 
-  if constexpr (KLDS) {
-    // K through LDS: the tile's 8 K loads go straight to the wave's LDS regions (load (h, c):
-    // lane (4a+i, lg) fetches key slot 8a+4h+c, dims 32lg+8i -- 64 contiguous bytes per quad)
-    // and are read back in the MFMA layout (lane (4a+i, lg), register c of sub-tile h = region
-    // (h, i), lane slot 4a+c+16lg), so no VALU transpose.  Per tile the K loads are issued
-    // before the V loads: at the top of the next iteration vmcnt(8) leaves only the V loads in
-    // flight.  The region is refilled only after its read-back has completed (lgkmcnt(0)).
+  {
+    // K through LDS.  In the MFMA layout above the four lanes of a quad hold four different
+    // keys, so loading K straight into it would make every 16-byte load touch four rows per
+    // quad (the address unit pays per row).  Instead the tile's 8 K loads go straight to the
+    // wave's LDS regions (load (h, c): lane (4a+i, lg) fetches key slot 8a+4h+c, dims
+    // 32lg+8i -- 64 contiguous bytes per quad) and are read back in the MFMA layout (lane
+    // (4a+i, lg), register c of sub-tile h = region (h, i), lane slot 4a+c+16lg), with no VALU
+    // transpose.  Per tile the K loads are issued before the V loads: at the top of the next
+    // iteration vmcnt(8) leaves only the V loads in flight.  A region is refilled only after
+    // its read-back has completed (lgkmcnt(0)).
     struct VTile {
       i32x4 vf[8];
       int sv[8];
@@ -272,16 +213,8 @@ __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, co
         __builtin_amdgcn_sched_barrier(0);
         issue(vn, tl + 32);
       }
-      compute(kf, vc.vf, vc.sv, [](int) {});
+      compute(kf, vc.vf, vc.sv);
       vc = vn;
-    }
-  } else {
-    GatherTile cur, nxt;
-    if (cnt32 > 0) load_tile(cur, il, 0, kg_base, vg_base, kvs, lr, lg);
-    for (int tl = 0; tl < cnt32; tl += 32) {
-      if (tl + 32 < cnt32) load_tile(nxt, il, tl + 32, kg_base, vg_base, kvs, lr, lg);
-      compute(cur.kf, cur.vf, cur.sv, [&](int h) { quad_transpose(cur.kf[h], lr); });
-      cur = nxt;
     }
   }
   l_tot = l_run;
@@ -338,7 +271,7 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
   const int64_t kvs = (int64_t)Hkv * D;
   f32x4 o[8];
   float m_run, l_tot;
-  attend_staged<D, false, true>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D,
+  attend_staged<D, false>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D,
                                 v + ri.kv_row0 * kvs + g * D, scale_log2, lr, lg, o, m_run, l_tot,
                                 (__attribute__((address_space(3))) uint8_t*)kb_all[g]);
   if (lr >= G) return;
@@ -412,7 +345,7 @@ __global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
   const int64_t kvs = (int64_t)Hkv * D;
   f32x4 o[8];
   float m_run, l_tot;
-  attend_staged<D, true, true>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D,
+  attend_staged<D, true>(q, il, cnt32, r, g, G, Hq, kvs, k + ri.kv_row0 * kvs + g * D,
                                v + ri.kv_row0 * kvs + g * D, scale_log2, lr, lg, o, m_run, l_tot,
                                (__attribute__((address_space(3))) uint8_t*)kb_all[wave]);
   if (lr >= G) return;

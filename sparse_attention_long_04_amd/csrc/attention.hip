@@ -499,22 +499,42 @@ __global__ __launch_bounds__(512) void dense_prefill_kernel(
           sacc[rb] = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(kl + kv_off(key, 32 * s2 + 16 * hf)), qf[s2],
                                         sacc[rb]);
       }
-      // mask + scale; C row (reg i, half hf) of block rb <-> key kt + 32rb + kperm(8(i/4)+4hf+i%4)
+      // mask + scale; C row (reg i, half hf) of block rb <-> key kt + 32rb + kperm(8(i/4)+4hf+i%4).
+      // Tiles wholly before the wave's first query need no mask (all but the last one or two).
       float z[2][16];
       float mt = -__builtin_inff();
+      if (kt + BN - 1 <= q0 + 32 * (w & 3)) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kt + 32 * rb + kperm(8 * (i >> 2) + 4 * hf + (i & 3));
-          const float zz = (key <= my_q) ? sacc[rb][i] * scale_log2 : -__builtin_inff();
-          z[rb][i] = zz;
-          mt = fmaxf(mt, zz);
-        }
+          for (int i = 0; i < 16; ++i) {
+            z[rb][i] = sacc[rb][i] * scale_log2;
+            mt = fmaxf(mt, z[rb][i]);
+          }
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kt + 32 * rb + kperm(8 * (i >> 2) + 4 * hf + (i & 3));
+            const float zz = (key <= my_q) ? sacc[rb][i] * scale_log2 : -__builtin_inff();
+            z[rb][i] = zz;
+            mt = fmaxf(mt, zz);
+          }
+      }
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      // lazy reference max: it moves only when the query's tile max passes it by more than 8
+      // (log2 units), so P <= 2^8 (exact enough in fp16) and the O rescale -- a round trip of
+      // the accumulators through VALU -- happens on few tiles
+      const bool move = mt > m_run + 8.f;  // false while every key so far is masked
+      if (__ballot(move)) {
+        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;  // m_run = -inf: 0
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+        m_run = move ? mt : m_run;
+      }
+      const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
       float ps = 0.f;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
@@ -524,10 +544,7 @@ __global__ __launch_bounds__(512) void dense_prefill_kernel(
           z[rb][i] = pv;
           ps += pv;
         }
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      l_run += ps;
       // O^T += V^T P^T; k-step (rb, kk2) covers keys 32rb + 16kk2 + 0..15 = registers 8kk2..8kk2+7
       const int grp = lane >> 4, jj = lane & 15;
 #pragma unroll

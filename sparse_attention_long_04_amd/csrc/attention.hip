@@ -501,6 +501,8 @@ __global__ __launch_bounds__(512) void dense_prefill_kernel(
       }
       // mask + scale; C row (reg i, half hf) of block rb <-> key kt + 32rb + kperm(8(i/4)+4hf+i%4).
       // Tiles wholly before the wave's first query need no mask (all but the last one or two).
+      // The max is taken on the raw scores (the scale is positive) and the scale applied once
+      // per element inside the exponent's fma.
       float z[2][16];
       float mt = -__builtin_inff();
       if (kt + BN - 1 <= q0 + 32 * (w & 3)) {
@@ -508,7 +510,7 @@ __global__ __launch_bounds__(512) void dense_prefill_kernel(
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            z[rb][i] = sacc[rb][i] * scale_log2;
+            z[rb][i] = sacc[rb][i];
             mt = fmaxf(mt, z[rb][i]);
           }
       } else {
@@ -517,12 +519,12 @@ __global__ __launch_bounds__(512) void dense_prefill_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kt + 32 * rb + kperm(8 * (i >> 2) + 4 * hf + (i & 3));
-            const float zz = (key <= my_q) ? sacc[rb][i] * scale_log2 : -__builtin_inff();
+            const float zz = (key <= my_q) ? sacc[rb][i] : -__builtin_inff();
             z[rb][i] = zz;
             mt = fmaxf(mt, zz);
           }
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
       // lazy reference max: it moves only when the query's tile max passes it by more than 8
       // (log2 units), so P <= 2^8 (exact enough in fp16) and the O rescale -- a round trip of
       // the accumulators through VALU -- happens on few tiles
@@ -540,7 +542,7 @@ __global__ __launch_bounds__(512) void dense_prefill_kernel(
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(z[rb][i] - m_use);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(z[rb][i], scale_log2, -m_use));
           z[rb][i] = pv;
           ps += pv;
         }

@@ -93,7 +93,8 @@ int dsa_last_hip_error(void);
  * dense_causal_attention for `shape`.  cu_seqlens_host (HOST int32 [B+1], nullable) gives the
  * exact size; without it a bound from total_tokens, num_seqs and max_seqlen is returned.
  * The workspace holds the causal indexer score triangle (fp32, in 16-row blocks), a work
- * schedule and, for dsa_prefill with topk_idx == NULL, the index array. */
+ * schedule, for dsa_prefill with topk_idx == NULL the index array, the gather's row order,
+ * and for dense_causal_attention an fp16 copy of V (T * Hkv * 128 halves). */
 int dsa_prefill_workspace_size(const dsa_prefill_shape* shape, const int32_t* cu_seqlens_host,
                                size_t* bytes);
 

@@ -31,7 +31,8 @@
 //
 // dense_prefill_kernel -- FlashAttention-style causal attention: a workgroup of 8 waves owns
 //   128 query tokens x 2 query heads of one KV group; 64-key K/V tiles are double-buffered in
-//   LDS and shared by both heads; S^T and O^T use 32x32x16 MFMAs (bf16 for QK, fp16 for PV).
+//   LDS and shared by both heads; S^T and O^T use 32x32x16 MFMAs (bf16 for QK, fp16 for PV,
+//   with V converted to fp16 once beforehand).
 #include "attn_tiles.h"
 
 namespace dsa {
@@ -469,11 +470,7 @@ __global__ __launch_bounds__(512) void dense_prefill_kernel(
       const int u = tid + 512 * x;
       const int off = kv_off(u >> 4, 16 * (u & 15));
       *reinterpret_cast<i32x4*>(&kv_lds[buf][0][off]) = pre[x];
-      // V is kept as fp16 (exact for bf16 values in fp16's normal range) for the fp16 P.V MFMA
-      float vf[8];
-#pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) vf[e2] = bf16_to_f32(bf16_lane(pre[2 + x], e2));
-      *reinterpret_cast<i32x4*>(&kv_lds[buf][1][off]) = pack_f16x8(vf);
+      *reinterpret_cast<i32x4*>(&kv_lds[buf][1][off]) = pre[2 + x];  // V already fp16
     }
   };
 
@@ -628,13 +625,30 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
   return hipGetLastError();
 }
 
-hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu,
-                                int Hq, int Hkv, float scale, const int2* sched, const int* count,
+// V converted to fp16 once (exact for bf16 values in fp16's normal range) for the fp16 P.V MFMA
+// of the dense kernel, instead of once per staging workgroup (each key's V is staged by every
+// later 128-query block of its sequence).
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* __restrict__ in,
+                                                          uint16_t* __restrict__ out, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const i32x4 x = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(in) + i);
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = bf16_to_f32(bf16_lane(x, e));
+  reinterpret_cast<i32x4*>(out)[i] = pack_f16x8(f);
+}
+
+// v16: T * Hkv * 128 halves of scratch for V in fp16.
+hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* v16, int64_t T,
+                                const int32_t* cu, int Hq, int Hkv, float scale, const int2* sched, const int* count,
                                 int nb_bound, uint16_t* out, hipStream_t st) {
   if (nb_bound == 0) return hipSuccess;
+  const int64_t n8 = T * Hkv * 128 / 8;
+  bf16_to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(v, v16, n8);
   const int pair = ((Hq / Hkv) % 2 == 0) ? 1 : 0;
   dense_prefill_kernel<<<dim3(nb_bound, pair ? Hq / 2 : Hq), 512, 0, st>>>(
-      q, k, v, cu, Hq, Hkv, scale * 1.4426950408889634f, sched, count, pair, out);
+      q, k, v16, cu, Hq, Hkv, scale * 1.4426950408889634f, sched, count, pair, out);
   return hipGetLastError();
 }
 

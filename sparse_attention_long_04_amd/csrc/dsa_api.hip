@@ -68,7 +68,8 @@ hipError_t launch_sparse_dkv(const uint16_t* q, const uint16_t* k, const uint16_
                              hipStream_t st);
 hipError_t launch_topk_general(const float* scores, int64_t rows, int n, int64_t ld, const int32_t* lens, int K,
                                int32_t* out, hipStream_t st);
-hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu, int Hq,
+hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* v16, int64_t T,
+                                const int32_t* cu, int Hq,
                                 int Hkv, float scale, const int2* sched, const int* count, int nb_bound,
                                 uint16_t* out, hipStream_t st);
 
@@ -157,7 +158,7 @@ int check_prefill(const dsa_prefill_shape* s, bool need_indexer) {
 //   counts int[64] | seqoff int64[B+1] | sched16 int2[nb16] | sched128 int2[nb128] |
 //   rowrange float2[T] | scores float[score_floats] | topk int32[T*k]
 struct PrefillWs {
-  size_t counts, seqoff, sched16, sched128, rowrange, scores, topk, osig, ocnt, order, total;
+  size_t counts, seqoff, sched16, sched128, rowrange, scores, topk, osig, ocnt, order, v16, total;
   int nb16, nb128;
   int64_t score_floats;
 };
@@ -199,6 +200,8 @@ PrefillWs prefill_layout(const dsa_prefill_shape* s, const int32_t* cu_host) {
   w.osig = off; off = align_up(off + size_t(T) * sizeof(int), 256);
   w.ocnt = off; off = align_up(off + size_t(row_order_count_ints(T, s->max_seqlen, B)) * sizeof(int), 256);
   w.order = off; off = align_up(off + size_t(T) * sizeof(int32_t), 256);
+  // V in fp16 for the dense reference (dense_causal_attention only)
+  w.v16 = off; off = align_up(off + size_t(T) * size_t(s->kv_heads) * size_t(s->head_dim) * sizeof(uint16_t), 256);
   w.total = off;
   return w;
 }
@@ -746,7 +749,8 @@ int dense_causal_attention(const dsa_prefill_shape* s, const uint16_t* q, const 
   hipError_t e = launch_build_schedule(s->cu_seqlens, s->num_seqs, 128, L.nb128, at<int2>(ws, L.sched128),
                                        at<int>(ws, L.counts) + 1, nullptr, st);
   if (e != hipSuccess) return hip_status(e);
-  return hip_status(launch_dense_prefill(q, k, v, s->cu_seqlens, s->q_heads, s->kv_heads, s->softmax_scale,
+  return hip_status(launch_dense_prefill(q, k, v, at<uint16_t>(ws, L.v16), s->total_tokens, s->cu_seqlens,
+                                         s->q_heads, s->kv_heads, s->softmax_scale,
                                          at<int2>(ws, L.sched128), at<int>(ws, L.counts) + 1, L.nb128, out, st));
 }
 

@@ -516,3 +516,27 @@ def test_ordered_gather_matches_natural_order():
     pb.sparse_attention()
     torch.cuda.synchronize()
     assert torch.equal(pb.out, ordered)
+
+
+def test_many_sequences_keep_natural_order():
+    """17000 sequences of one or two tokens: the gather's row order would need a key per
+    sequence and 1024-key block, more than its 16384-key limit, so the rows keep their natural
+    order.  Every selection bit-exact and every output within the bar.  V is halved (exact in
+    bf16): an output here is a mean of at most two V rows, and at magnitudes of 4 and above the
+    bf16 output grid alone (half-ulp 2^-6) would exceed the bar's 1e-2."""
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.integers(1, 3, 17000)]
+    p = gen.make_prefill(lens, idx_heads=16, idx_dim=128, idx_dtype="fp8_e4m3", idx_range=4, topk=4, seed=78)
+    v = (p.v.astype(np.uint32) << 16).view(np.float32) * np.float32(0.5)
+    p.v = (v.view(np.uint32) >> 16).astype(np.uint16)
+    print(f"[many sequences] T={p.total_tokens}", flush=True)
+    pb = PrefillBatch(p)
+    pb.prefill()
+    idx = pb.topk_idx.cpu().numpy()
+    out = bf16_to_float(pb.out)
+    o = oracle_of(p)
+    sel, ref = o.rows(range(p.total_tokens))
+    bad = [t for t in range(p.total_tokens) if not np.array_equal(idx[t], sel[t])]
+    assert not bad, f"index mismatch on rows {bad[:10]}"
+    assert_out_close(out, ref, "many sequences")
+

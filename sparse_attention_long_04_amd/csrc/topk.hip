@@ -381,7 +381,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 }
 
 // ---- fast path for rows of 8K+ keys: a sampled threshold and one pass over HBM -------------
-// A histogram of every kSampleStride-th 64-byte line of the row places a value bin b_est below
+// A histogram of every kSampleStride-th 128-byte line of the row places a value bin b_est below
 // the k-th largest score with a margin of a few standard deviations; one pass then gathers every
 // element of bin >= b_est into the LDS list (slots reserved with one LDS atomic per wave and
 // load group, so the list is in no particular order).  The exact threshold bin is found on the

@@ -115,8 +115,10 @@ __global__ __launch_bounds__(256) void union_kernel(const int32_t* __restrict__ 
   if (tid == 0) ucount[n] = base;
 }
 
+// Two waves per SIMD for groups of 8 and 16 query heads; smaller groups give each wave 8 or 16
+// rows of softmax state, which only fits at one.
 template <int G>
-__global__ __launch_bounds__(32 * G) __attribute__((amdgpu_waves_per_eu(2, 2))) void dedup_attention_kernel(
+__global__ __launch_bounds__(32 * G) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 2 : 1, 2))) void dedup_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu, int Hq, int Hkv, float scale_log2, const int2* __restrict__ sched,
     const int* __restrict__ sched_count, int64_t ustride, const int32_t* __restrict__ ukeys,

@@ -237,7 +237,8 @@ int dsa_kv_append(const dsa_decode_shape* shape, const void* k_idx_new, const ui
 /* One DSA decode step (summary page sections 一 and 八): for each sequence b the newest token
  * (cache row cache_lens[b]-1, already appended) scores cache rows 0..n-1 with the indexer,
  * keeps the top-k and attends over them.  q_idx [B, H_I, d_I], w_idx fp32 [B, H_I],
- * q bf16 [B, Hq, d]; out bf16 [B, Hq, d]; topk_idx int32 [B, k] (nullable). */
+ * q bf16 [B, Hq, d]; out bf16 [B, Hq, d]; topk_idx int32 [B, k] (nullable).
+ * max_cache_len up to 2^20 rows (DSA_ERR_UNSUPPORTED beyond). */
 int dsa_decode(const dsa_decode_shape* shape, const void* q_idx, const float* w_idx,
                const uint16_t* q, const void* k_idx_cache, const uint16_t* k_cache,
                const uint16_t* v_cache, uint16_t* out, int32_t* topk_idx, void* workspace,

@@ -13,6 +13,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr int kDecodeKeysPerBlock = 256;   // cached keys per decode-indexer workgroup (one range slot each)
+constexpr int kDecodeTopkBins = 2048;      // value bins per sequence of the decode top-k histogram
+constexpr int kDecodeTopkChunk = 4096;     // scores per decode top-k chunk (one candidate list each)
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 

@@ -334,7 +334,8 @@ int check_prefill_ws(const dsa_prefill_shape* s, void* ws, size_t ws_bytes, Pref
 int check_decode(const dsa_decode_shape* s, bool need_indexer) {
   if (!s || !s->cache_lens || s->batch < 1 || s->cache_capacity < 1) return DSA_ERR_INVALID_ARGUMENT;
   if (s->max_cache_len < 1 || s->max_cache_len > s->cache_capacity) return DSA_ERR_INVALID_ARGUMENT;
-  if (s->max_cache_len > 256 * 4096) return DSA_ERR_UNSUPPORTED;
+  // the top-k finalize takes one chunk count per thread of its 256-thread workgroup
+  if (s->max_cache_len > 256 * kDecodeTopkChunk) return DSA_ERR_UNSUPPORTED;
   int rc = check_heads(s->topk, s->idx_heads, s->idx_dim, s->idx_dtype, s->q_heads, s->kv_heads, s->head_dim,
                        s->softmax_scale, need_indexer);
   if (rc) return rc;
@@ -364,8 +365,8 @@ DecodeWs decode_layout(const dsa_decode_shape* s) {
   w.opart = off; off = align_up(off + B * ns * size_t(s->q_heads) * s->head_dim * sizeof(float), 256);
   w.mlpart = off; off = align_up(off + B * ns * size_t(s->q_heads) * sizeof(float2), 256);
   w.nchunk = topk_decode_nchunk(s->max_cache_len);
-  const size_t lst = B * size_t(w.nchunk) * 4096;
-  w.ghist = off; off = align_up(off + B * 2048 * sizeof(int), 256);
+  const size_t lst = B * size_t(w.nchunk) * kDecodeTopkChunk;
+  w.ghist = off; off = align_up(off + B * kDecodeTopkBins * sizeof(int), 256);
   w.keyrange = off;
   off = align_up(off + B * size_t((s->max_cache_len + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock) * sizeof(uint2), 256);
   w.lkeys = off; off = align_up(off + lst * sizeof(uint32_t), 256);

@@ -461,7 +461,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
   const int tid = threadIdx.x;
   // the top-k after this kernel merges chunk histograms into ghist[b] with atomics: clear it
   if (blockIdx.x == 0)
-    for (int i = tid; i < 2048; i += 256) ghist[b * 2048 + i] = 0;
+    for (int i = tid; i < kDecodeTopkBins; i += 256) ghist[b * kDecodeTopkBins + i] = 0;
   if (key0 >= n) return;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   // 16-byte unit swizzle of head row h: the 16 heads an A-operand read touches (one 256-byte LDS

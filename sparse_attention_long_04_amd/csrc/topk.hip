@@ -34,7 +34,8 @@ constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kListCap = 3072;     // LDS candidate list capacity (prefill)
 constexpr int kBins = 2048;        // value bins / radix digit size
-constexpr int kChunk = 4096;       // decode chunk
+constexpr int kChunk = kDecodeTopkChunk;  // decode chunk
+static_assert(kBins == kDecodeTopkBins, "the decode histogram is sized by kBins");
 constexpr int kFinalCap = 12288;   // LDS list capacity of the decode finalize step
 
 struct TopkSmem {
@@ -223,33 +224,54 @@ __device__ void ordered_emit(const Src& src, int n, uint32_t T, int krem, Emit e
   __syncthreads();
 }
 
-// Histogram of value bins over a raw row.
-__device__ void value_hist_pass(const RowSrc& src, int n, float lo, float sc, int* hist) {
-  for (int c0 = 0; c0 < n; c0 += 4 * kTopkThreads) {
-    float x[4];
-    const int s0 = c0 + 4 * threadIdx.x;
-    src.quadf(n, s0, x);
+// ---- decode chunks: at most kChunk scores per workgroup ---------------------------------------
+// A thread's quads of the chunk are all requested before any is used, and before the kernels'
+// other reads (row range, histogram), so the chunk costs one memory round trip, not one per
+// 1024 scores.  Quad q of thread t covers positions q*1024 + 4t .. +3 of the chunk at p.
+// The decode score rows are ld floats with ld a multiple of 4 and every chunk starts below ld,
+// 16-byte aligned: a quad that starts below n lies wholly inside the row, and a quad at or past n
+// re-reads the chunk's first quad instead, so no load is predicated (a predicated load splits
+// into branches whose register reuse serialises the loads).  Elements at n and past are never
+// used.
+constexpr int kChunkQuads = kChunk / (4 * kTopkThreads);
+static_assert(kChunkQuads * 4 * kTopkThreads == kChunk, "a chunk is whole thread quads");
+typedef float ChunkRegs[kChunkQuads][4];
+
+__device__ __forceinline__ void load_chunk(const float* __restrict__ p, int n, ChunkRegs& x) {
+#pragma unroll
+  for (int q = 0; q < kChunkQuads; ++q) {
+    const int s0 = q * 4 * kTopkThreads + 4 * threadIdx.x;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(p + (s0 < n ? s0 : 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[q][e] = v[e];
+  }
+}
+
+// Histogram of value bins over a loaded chunk of n scores.
+__device__ void value_hist_chunk(const ChunkRegs& x, int n, float lo, float sc, int* hist) {
+#pragma unroll
+  for (int q = 0; q < kChunkQuads; ++q) {
+    const int s0 = q * 4 * kTopkThreads + 4 * threadIdx.x;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (s0 + e < n) atomicAdd(&hist[value_bin(x[e], lo, sc)], 1);
+      if (s0 + e < n) atomicAdd(&hist[value_bin(x[q][e], lo, sc)], 1);
   }
   __syncthreads();
 }
 
-// Ordered compaction of every element whose value bin is >= b1 (no tie limit): emit(slot, key,
-// id) in index order.  Returns the count.
+// Ordered compaction of every element of a loaded chunk whose value bin is >= b1 (no tie
+// limit): emit(slot, key, id) in index order.  Returns the count.
 template <class Emit>
-__device__ int ordered_emit_bin_ge(const RowSrc& src, int n, float lo, float sc, int b1, Emit emit, TopkSmem& sm) {
+__device__ int emit_chunk_bin_ge(const ChunkRegs& x, int n, float lo, float sc, int b1, Emit emit, TopkSmem& sm) {
   int base = 0;
-  for (int c0 = 0; c0 < n; c0 += 4 * kTopkThreads) {
-    float x[4];
-    const int s0 = c0 + 4 * threadIdx.x;
-    src.quadf(n, s0, x);
+#pragma unroll
+  for (int q = 0; q < kChunkQuads; ++q) {
+    const int s0 = q * 4 * kTopkThreads + 4 * threadIdx.x;
     bool keep[4];
     int c = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      keep[e] = s0 + e < n && value_bin(x[e], lo, sc) >= b1;
+      keep[e] = s0 + e < n && value_bin(x[q][e], lo, sc) >= b1;
       c += keep[e];
     }
     int total;
@@ -257,7 +279,7 @@ __device__ int ordered_emit_bin_ge(const RowSrc& src, int n, float lo, float sc,
     int pos = base + incl - c;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (keep[e]) emit(pos++, score_key(x[e]), s0 + e);
+      if (keep[e]) emit(pos++, score_key(x[q][e]), s0 + e);
     base += total;
   }
   __syncthreads();
@@ -714,7 +736,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_prefill_kernel(
 
 // ------------------------------------------------------------------------------------------
 // Decode: chunked top-k over rows of n = cache_lens[b] scores.
-//   blkrange [B][ceil(n/1024)] (min, max order keys per decode-indexer block), ghist [B][kBins] int
+//   blkrange [B][ceil(n/kDecodeKeysPerBlock)] (min, max order keys per decode-indexer block), ghist [B][kBins] int
 //   (cleared before the indexer), lists [B][nchunk][kChunk] (key, id), counts [B][nchunk].
 // ------------------------------------------------------------------------------------------
 struct RowRange {
@@ -759,12 +781,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_hist_kernel(
   const int b = blockIdx.y;
   const int n = cache_lens[b];
   const int c0 = blockIdx.x * kChunk;
+  const int cn = min(kChunk, n - c0);  // <= 0 past the row: nothing is loaded
+  ChunkRegs x;
+  load_chunk(scores + b * ld + c0, cn, x);
   const RowRange rr = decode_range(blkrange, blk_stride, b, n, sm);
   if (n <= K || c0 >= n || rr.flat) return;
-  const int cn = min(kChunk, n - c0);
   clear_hist(sm, kBins);
-  const RowSrc src{scores + b * ld + c0, true};
-  value_hist_pass(src, cn, rr.lo, rr.sc, sm.hist);
+  value_hist_chunk(x, cn, rr.lo, rr.sc, sm.hist);
   for (int i = threadIdx.x; i < kBins; i += kTopkThreads) {
     const int h = sm.hist[i];
     if (h) atomicAdd(&ghist[b * kBins + i], h);
@@ -779,18 +802,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_collect_kernel(
   const int b = blockIdx.y;
   const int n = cache_lens[b];
   const int c0 = blockIdx.x * kChunk;
+  const int cn = min(kChunk, n - c0);  // <= 0 past the row: nothing is loaded
+  ChunkRegs x;
+  load_chunk(scores + b * ld + c0, cn, x);
+  int hreg[kBins / kTopkThreads];
+#pragma unroll
+  for (int j = 0; j < kBins / kTopkThreads; ++j) hreg[j] = ghist[b * kBins + threadIdx.x + j * kTopkThreads];
   const RowRange rr = decode_range(blkrange, blk_stride, b, n, sm);
   if (n <= K || rr.flat) return;
   int cnt = 0;
   if (c0 < n) {
-    for (int i = threadIdx.x; i < kBins; i += kTopkThreads) sm.hist[i] = ghist[b * kBins + i];
+#pragma unroll
+    for (int j = 0; j < kBins / kTopkThreads; ++j) sm.hist[threadIdx.x + j * kTopkThreads] = hreg[j];
     __syncthreads();
     find_digit(sm, kBins, K);
     const int b1 = sm.sel_digit;
-    const int cn = min(kChunk, n - c0);
-    const RowSrc src{scores + b * ld + c0, true};
     const int64_t base = ((int64_t)b * nchunk + blockIdx.x) * kChunk;
-    cnt = ordered_emit_bin_ge(src, cn, rr.lo, rr.sc, b1, [&](int slot, uint32_t key, int id) {
+    cnt = emit_chunk_bin_ge(x, cn, rr.lo, rr.sc, b1, [&](int slot, uint32_t key, int id) {
       lkeys[base + slot] = key;
       lids[base + slot] = c0 + id;
     }, sm);
@@ -1253,11 +1281,13 @@ hipError_t launch_topk_prefill(const float* tri, const int64_t* seqoff, const in
 
 int topk_decode_nchunk(int max_len) { return (max_len + kChunk - 1) / kChunk; }
 
-// Workspace needs: ghist B*4096 ints, lists B*nchunk*kChunk*(key+id) twice (chunk lists and
-// the finalize spill area), counts B*nchunk ints.
+// Workspace needs: ghist B*kBins ints, lists B*nchunk*kChunk*(key+id) twice (chunk lists and
+// the finalize spill area), counts B*nchunk ints.  The score rows (16-byte aligned, ld floats
+// apart, ld a multiple of 4 and >= max_len) are what the chunk loads assume.
 hipError_t launch_topk_decode(const float* scores, int64_t ld, const int32_t* cache_lens, int B, int max_len,
                               int K, const uint2* blkrange, int* ghist, uint32_t* lkeys, int* lids, int* counts,
                               int* spill, int32_t* out, hipStream_t st) {
+  if ((ld & 3) != 0 || ld < max_len || (reinterpret_cast<uintptr_t>(scores) & 15) != 0) return hipErrorInvalidValue;
   const int blk_stride = (max_len + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock;
   const int nchunk = topk_decode_nchunk(max_len);
   if (nchunk > kTopkThreads) return hipErrorInvalidValue;

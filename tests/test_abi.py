@@ -128,6 +128,17 @@ def test_decode_rejects_bad_shapes():
     assert ei.value.status == 2
 
 
+def test_decode_cache_length_limit():
+    """Caches up to 2^20 rows are sized; one row more is refused as unsupported."""
+    lim = 1 << 20
+    s = dsa.decode_shape(FAKE, lim + 1, lim, batch=2, topk=2048, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3")
+    assert dsa.dsa_decode_workspace_size(s) > 2 * (lim + 1) * 4
+    s = dsa.decode_shape(FAKE, lim + 1, lim + 1, batch=2, topk=2048, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3")
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_decode_workspace_size(s)
+    assert ei.value.status == 2
+
+
 def test_schedule_rank_is_a_longest_first_permutation():
     """Host model of the device work schedule: ranks of (sequence, block) pairs ordered by
     block index descending then sequence ascending form a permutation."""

@@ -335,16 +335,18 @@ __device__ __forceinline__ bool rank_threshold_bin(uint32_t* keys, const int* id
   return true;
 }
 
-// Ordered compaction of the list entries with a non-zero key.
+// Ordered compaction of the list entries with a non-zero key, EPT entries per thread and round
+// (each round is one block scan).
+template <int EPT = 4>
 __device__ void emit_nonzero(const uint32_t* keys, const int* ids, int total, int32_t* __restrict__ out,
                              TopkSmem& sm) {
   int base = 0;
-  for (int c0 = 0; c0 < total; c0 += 4 * kTopkThreads) {
-    const int s0 = c0 + 4 * threadIdx.x;
-    bool keep[4];
+  for (int c0 = 0; c0 < total; c0 += EPT * kTopkThreads) {
+    const int s0 = c0 + EPT * threadIdx.x;
+    bool keep[EPT];
     int c = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < EPT; ++e) {
       keep[e] = (s0 + e < total) && keys[s0 + e] != 0u;
       c += keep[e];
     }
@@ -352,7 +354,7 @@ __device__ void emit_nonzero(const uint32_t* keys, const int* ids, int total, in
     const int incl = block_incl_scan(c, sm.wave_tot, &tot);
     int pos = base + incl - c;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < EPT; ++e)
       if (keep[e]) out[pos++] = ids[s0 + e];
     base += tot;
   }
@@ -878,26 +880,33 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_final_kernel(
     ids = reinterpret_cast<int*>(keys + nchunk * kChunk);
   }
   // flattened gather of the concatenated chunk lists (chunk order = index order); a batch of
-  // loads is issued into registers before any store, so the round trips overlap
+  // loads is issued into registers before any store, so the round trips overlap.  Each element
+  // finds its chunk by a fixed-step bisection written as selects (nchunk <= kTopkThreads; a read
+  // clamped to offs[nchunk] = total stops every search inside the row), so a thread's searches
+  // carry no branches and interleave; positions past the list re-read its last element, so no
+  // load is predicated.
   constexpr int PER = 16;
   for (int base = 0; base < total; base += PER * kTopkThreads) {
     uint32_t kv[PER];
     int iv[PER];
+    int ii[PER], lo[PER];  // lo: last chunk c with offs[c] <= ii
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int i = base + u * kTopkThreads + threadIdx.x;
-      kv[u] = 0u;
-      iv[u] = -1;
-      if (i < total) {
-        int lo = 0, hi = nchunk - 1;  // last chunk c with offs[c] <= i
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (sm.offs[mid] <= i) lo = mid; else hi = mid - 1;
-        }
-        const int64_t src = ((int64_t)b * nchunk + lo) * kChunk + (i - sm.offs[lo]);
-        kv[u] = gkeys[src];
-        iv[u] = gids[src];
+      ii[u] = min(base + u * kTopkThreads + (int)threadIdx.x, total - 1);
+      lo[u] = 0;
+    }
+#pragma unroll
+    for (int step = kTopkThreads / 2; step > 0; step >>= 1)  // steps outside: PER reads per wait
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int c = min(lo[u] + step, nchunk);
+        lo[u] = (sm.offs[c] <= ii[u]) ? c : lo[u];
       }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int64_t src = ((int64_t)b * nchunk + lo[u]) * kChunk + (ii[u] - sm.offs[lo[u]]);
+      kv[u] = gkeys[src];
+      iv[u] = gids[src];
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -911,7 +920,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_final_kernel(
   __syncthreads();
   auto bin_of = [&](uint32_t k) { return value_bin(key_to_score(k), rr.lo, rr.sc); };
   if (total <= kFinalCap && rank_threshold_bin(keys, ids, total, b1, K - above, bin_of, sm.f)) {
-    emit_nonzero(keys, ids, total, orow, sm.s);
+    emit_nonzero<12>(keys, ids, total, orow, sm.s);  // one round up to 3072 candidates
     return;
   }
   const ListSrc ls{keys, ids};

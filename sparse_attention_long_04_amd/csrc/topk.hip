@@ -306,14 +306,21 @@ __device__ __forceinline__ bool rank_threshold_bin(uint32_t* keys, const int* id
   constexpr int kSubCap = CAP;
   if (threadIdx.x == 0) fs.sub_n = 0;
   __syncthreads();
-  for (int i = threadIdx.x; i < total; i += kTopkThreads) {
-    const uint32_t k = keys[i];
-    if (bin_of(k) == b1) {
-      const int j = atomicAdd(&fs.sub_n, 1);
-      if (j < kSubCap) {
-        fs.sk[j] = k;
-        fs.sid[j] = ids[i];
-        fs.spos[j] = i;
+  // four list reads per wait (reads past the list are clamped to its last entry, then ignored)
+  for (int i0 = threadIdx.x; i0 < total; i0 += 4 * kTopkThreads) {
+    uint32_t kq[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kq[u] = keys[min(i0 + u * kTopkThreads, total - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kTopkThreads;
+      if (i < total && bin_of(kq[u]) == b1) {
+        const int j = atomicAdd(&fs.sub_n, 1);
+        if (j < kSubCap) {
+          fs.sk[j] = kq[u];
+          fs.sid[j] = ids[i];
+          fs.spos[j] = i;
+        }
       }
     }
   }

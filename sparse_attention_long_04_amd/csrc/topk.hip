@@ -108,16 +108,6 @@ __device__ __forceinline__ float key_to_score(uint32_t k) {
 struct RowSrc {
   const float* __restrict__ row;
   bool vec;  // 16-byte aligned
-  __device__ __forceinline__ void quadf(int n, int s0, float* x) const {
-    if (vec && s0 + 3 < n) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(row + s0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = v[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = (s0 + e < n) ? row[s0 + e] : 0.f;
-    }
-  }
   // visit elements [c0 + 4*tid, +4) of a 1024-element chunk in index order
   __device__ __forceinline__ void quad(int n, int s0, uint32_t* keys, int* ids) const {
     if (vec && s0 + 3 < n) {

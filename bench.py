@@ -48,12 +48,12 @@ def ms_between(a, b):
     return a.elapsed_time(b)
 
 
-def roof(bound, achieved, peak, unit, traffic_bytes, work, work_unit):
+def roof(bound, achieved, peak, unit, traffic_bytes, work, work_unit, **extra):
     """Roofline entry: achieved/peak in TFLOP/s or GB/s from algorithmic work per launch."""
     scale = 1e12 if unit == "TFLOP/s" else 1e9
     return {"bound": bound, "achieved": round(achieved / scale, 1), "peak": round(peak / scale, 1), "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic_bytes, "work_per_launch": work,
-            "work_unit": work_unit}
+            "work_unit": work_unit, **extra}
 
 
 def read_traffic():
@@ -124,8 +124,9 @@ def bench_prefill(name, steps, warmup, with_dense=True):
 
 
 def bench_decode(steps_total=64, stage_reps=16):
-    """The decode workload's steps back to back: a step is the append of each sequence's new
-    token (row and length) followed by dsa_decode, bracketed by one pair of events.  The per-stage
+    """The decode workload's steps back to back: each step appends every sequence's new token
+    (row and length, dsa_kv_append) and then runs dsa_decode; events around each call time
+    dsa_decode alone (the step time reported) and the append separately.  The per-stage
     split comes from a second pass of dsa_decode_timed at the final cache length (no append);
     its events between stages add small gaps, so stage times sum to a little more than a step."""
     import torch
@@ -142,15 +143,18 @@ def bench_decode(steps_total=64, stage_reps=16):
         steps.append(st_.step_dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = [timing_events(2) for _ in range(steps_total)]
+    evs = [timing_events(3) for _ in range(steps_total)]
     for i in range(steps_total):
         st_.step_dev = steps[i]
         evs[i][0].record(stream)
         st_.append()
-        st_.decode()
         evs[i][1].record(stream)
+        st_.decode()
+        evs[i][2].record(stream)
     torch.cuda.synchronize()
-    us = np.array([ms_between(e[0], e[1]) * 1e3 for e in evs])
+    us = np.array([ms_between(e[1], e[2]) * 1e3 for e in evs])          # dsa_decode alone
+    app_us = np.array([ms_between(e[0], e[1]) * 1e3 for e in evs])      # dsa_kv_append
+    both_us = np.array([ms_between(e[0], e[2]) * 1e3 for e in evs])
     sev = [timing_events(4) for _ in range(stage_reps)]
     for e in sev:
         e[0].record(stream)
@@ -169,7 +173,8 @@ def bench_decode(steps_total=64, stage_reps=16):
         torch.cuda.synchronize()
         dense_ms.append(ms_between(a, b))
     # the first step also pays one-time costs; report mean over steps 1..63 and p50 over all
-    res = dict(us_mean=float(us[1:].mean()), us_p50=float(np.median(us)), indexer_us=float(idx_us[1:].mean()),
+    res = dict(us_mean=float(us[1:].mean()), us_p50=float(np.median(us)), append_us=float(app_us[1:].mean()),
+               step_with_append_us=float(both_us[1:].mean()), indexer_us=float(idx_us[1:].mean()),
                topk_us=float(topk_us[1:].mean()), attn_us=float(attn_us[1:].mean()),
                dense_us=float(np.mean(dense_ms[1:]) * 1e3), batch=d.batch, ctx=d.ctx_len)
     n_mean = d.ctx_len + (steps_total + 1) / 2
@@ -180,7 +185,8 @@ def bench_decode(steps_total=64, stage_reps=16):
     res["indexer_gbs"] = d.batch * n_end * d.idx_dim * (1 if d.idx_dtype == "fp8_e4m3" else 2) / (
         res["indexer_us"] * 1e-6) / 1e9
     res["attn_gbs"] = d.batch * d.topk * d.kv_heads * d.head_dim * 2 * 2 / (res["attn_us"] * 1e-6) / 1e9
-    log(f"decode: {res['us_mean']:.1f} us/step (p50 {res['us_p50']:.1f}); stages indexer {res['indexer_us']:.1f} "
+    log(f"decode: dsa_decode {res['us_mean']:.1f} us/step (p50 {res['us_p50']:.1f}), append {res['append_us']:.1f}, "
+        f"both {res['step_with_append_us']:.1f}; stages indexer {res['indexer_us']:.1f} "
         f"topk {res['topk_us']:.1f} attn {res['attn_us']:.1f}; dense {res['dense_us']:.1f} us")
     del st_
     torch.cuda.empty_cache()
@@ -357,8 +363,22 @@ def bench_topk_general(reps=5):
     return dict(ms=ms, torch_topk_ms=tms, work=work, rows=rows, n=n, k=k)
 
 
-def cpu_baseline(p, seconds=15.0, max_rows=4000, seed=0):
-    """The oracle (as is) on a uniform random sample of the workload's rows, for a bounded time."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(p, gpu_tokens_per_s, seconds=20.0, max_rows=4000, seed=0):
+    """The oracle (as is) on a uniform random sample of the workload's rows, for a bounded time,
+    each of its steps timed on its own: indexer scores, top-k select, sparse attention (these
+    three are the oracle's prefill row), and dense causal attention of the same row."""
     from oracle import dsa_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -369,17 +389,41 @@ def cpu_baseline(p, seconds=15.0, max_rows=4000, seed=0):
     rng = np.random.default_rng(seed)
     rows = rng.integers(0, p.total_tokens, size=max_rows)
     o.row(int(rows[0]))  # decode the sequence's keys outside the timed part
-    t0 = time.perf_counter()
+    st = dict(scores=0.0, select=0.0, sparse_attention=0.0, dense=0.0)
+    clock = time.perf_counter
+    t0 = clock()
     n = 0
     for t in rows:
-        o.row(int(t))
+        t = int(t)
+        b, _ = o.locate(t)
+        _, K, V = o._seq(b)
+        a = clock()
+        sc = o.scores(t)
+        b_ = clock()
+        sel = O.select_topk_row(sc, o.topk)
+        c = clock()
+        s = sel[sel >= 0]
+        O.attention_row(O.decode_bf16(o.q[t]), K[s], V[s], o.scale)
+        d = clock()
+        o.dense_row(t)
+        e = clock()
+        st["scores"] += b_ - a
+        st["select"] += c - b_
+        st["sparse_attention"] += d - c
+        st["dense"] += e - d
         n += 1
-        if time.perf_counter() - t0 > seconds:
+        if clock() - t0 > seconds:
             break
-    dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="tokens/s", cores=int(cores), kind="oracle",
-                sample=f"{n} uniformly drawn rows of the 131072-token prefill (indexer + top-k + attention per "
-                       f"row, float64), {dt:.1f} s")
+    dsa_s = st["scores"] + st["select"] + st["sparse_attention"]
+    value = n / dsa_s
+    return dict(value=value, unit="tokens/s", cores=int(cores), kind="oracle",
+                cpu_model=cpu_model(), cpu_count=os.cpu_count(),
+                stage_tokens_per_s={k: round(n / v, 2) for k, v in st.items()},
+                dense_tokens_per_s=round(n / st["dense"], 2),
+                gpu_speedup=round(gpu_tokens_per_s / value, 1),
+                sample=f"{n} uniformly drawn rows of the 131072-token prefill, float64; value = rows / (scores + "
+                       f"select + sparse attention seconds) = {dsa_s:.1f} s; dense timed on the same rows "
+                       f"({st['dense']:.1f} s)")
 
 
 def main():
@@ -452,8 +496,17 @@ def main():
                                        traffic.get("indexer_prefill_kernel"), idx_flops, "flop"),
         "topk_prefill_kernel": roof("hbm", topk_bytes / (pre["topk_ms"] * 1e-3), PEAK_HBM, "GB/s",
                                     traffic.get("topk_prefill_kernel"), topk_bytes, "byte"),
-        "gather_rows_kernel": roof("hbm", attn_bytes / (pre["attn_ms"] * 1e-3), PEAK_HBM, "GB/s",
-                                        traffic.get("gather_rows_kernel"), attn_bytes, "byte"),
+        # the gather's ceiling: its MFMA work against the bf16 peak, and the bytes it moves below
+        # the L2 (counter traffic, when the profile matches the source) against the HBM peak; the
+        # algorithmic gathered bytes are mostly served by the L2 and are reported as a rate only
+        "gather_rows_kernel": roof("mfma", attn_flops / (pre["attn_ms"] * 1e-3), PEAK_BF16, "TFLOP/s",
+                                   traffic.get("gather_rows_kernel"), attn_flops, "flop",
+                                   gathered_GBps=round(attn_bytes / (pre["attn_ms"] * 1e-3) / 1e9, 1),
+                                   gathered_bytes=attn_bytes,
+                                   below_l2=None if traffic.get("gather_rows_kernel") is None else roof(
+                                       "hbm", traffic["gather_rows_kernel"] / (pre["attn_ms"] * 1e-3), PEAK_HBM,
+                                       "GB/s", traffic["gather_rows_kernel"], traffic["gather_rows_kernel"],
+                                       "byte (counter traffic below the L2)")),
     }
     stage_ms = {"indexer_prefill_kernel": pre["indexer_ms"], "topk_prefill_kernel": pre["topk_ms"],
                 "gather_rows_kernel": pre["attn_ms"]}
@@ -487,6 +540,9 @@ def main():
                                                        (pre["dense_ms"] * 1e-3) / PEAK_BF16, 4)}
         dec = bench_decode()
         line["decode"] = {"us_per_step": round(dec["us_mean"], 2), "us_p50": round(dec["us_p50"], 2),
+                          "timed": "dsa_decode alone; dsa_kv_append timed separately",
+                          "append_us": round(dec["append_us"], 2),
+                          "us_per_step_with_append": round(dec["step_with_append_us"], 2),
                           "stages_us": {"indexer": round(dec["indexer_us"], 2), "topk": round(dec["topk_us"], 2),
                                         "sparse_attention": round(dec["attn_us"], 2)},
                           "stage_timing": "separate pass at the final cache length, events between stages",
@@ -523,11 +579,30 @@ def main():
                                         "ms": round(sb["ms"], 3),
                                         "tokens_per_s": round(sb["tokens"] / (sb["ms"] * 1e-3), 1),
                                         "useful_tflops": round(sb["useful_flop"] / (sb["ms"] * 1e-3) / 1e12, 1)}
-        vl = bench_prefill(workloads.VARLEN, max(1, args.steps - 1), 1, with_dense=False)
+        vl = bench_prefill(workloads.VARLEN, max(1, args.steps - 1), 1, with_dense=True)
         line["varlen"] = {"workload": workloads.VARLEN, "tokens_per_s": round(vl["T"] / (vl["ms"] * 1e-3), 1),
-                          "ms": round(vl["ms"], 3), "lengths": vl["lengths"]}
+                          "ms": round(vl["ms"], 3), "lengths": vl["lengths"],
+                          "stages_ms": {"indexer": round(vl["indexer_ms"], 3), "topk": round(vl["topk_ms"], 3),
+                                        "sparse_attention": round(vl["attn_ms"], 3)},
+                          "dense_ms": round(vl["dense_ms"], 3),
+                          "ratio_dsa_over_dense": round(vl["ms"] / vl["dense_ms"], 4),
+                          "dense_frac_bf16_peak": round(pairs_of(vl["lengths"]) * 32 * 128 * 4 /
+                                                        (vl["dense_ms"] * 1e-3) / PEAK_BF16, 4)}
+        del vl
+        p32 = bench_prefill(workloads.P32K, args.steps, 1, with_dense=True)
+        line["prefill_32k"] = {"workload": workloads.P32K,
+                               "tokens_per_s": round(p32["T"] / (p32["ms"] * 1e-3), 1), "ms": round(p32["ms"], 3),
+                               "stages_ms": {"indexer": round(p32["indexer_ms"], 3), "topk": round(p32["topk_ms"], 3),
+                                             "sparse_attention": round(p32["attn_ms"], 3)},
+                               "indexer_frac_fp8_peak": round(pairs_of(p32["lengths"]) * 64 * 128 * 2 /
+                                                              (p32["indexer_ms"] * 1e-3) / PEAK_FP8, 4),
+                               "dense_ms": round(p32["dense_ms"], 3),
+                               "ratio_dsa_over_dense": round(p32["ms"] / p32["dense_ms"], 4),
+                               "dense_frac_bf16_peak": round(pairs_of(p32["lengths"]) * 32 * 128 * 4 /
+                                                             (p32["dense_ms"] * 1e-3) / PEAK_BF16, 4)}
+        del p32
         if not args.no_cpu:
-            line["cpu_baseline"] = cpu_baseline(pre["p"])
+            line["cpu_baseline"] = cpu_baseline(pre["p"], value)
     print(json.dumps(line), flush=True)
 
 

@@ -183,17 +183,34 @@ class Prefill:
         return np.stack([self.dense_row(int(t)) for t in ts])
 
 
+def _decoded_keys(k_idx_cache, b, n, idx_fmt, memo):
+    """Indexer keys 0..n-1 of cache b as float64.  With a ``memo`` dict the decoded rows of
+    each sequence are kept between calls and only rows appended since are decoded (the values
+    are the same either way; this only saves time over many steps)."""
+    if memo is None:
+        return decode(k_idx_cache[b, :n], idx_fmt)
+    have = memo.get(b)
+    if have is None or have.shape[0] < n:
+        start = 0 if have is None else have.shape[0]
+        new = decode(k_idx_cache[b, start:n], idx_fmt)
+        have = new if have is None else np.concatenate([have, new])
+        memo[b] = have
+    return have[:n]
+
+
 def decode_step(k_idx_cache, k_cache, v_cache, cache_lens, q_idx, w_idx, q, idx_fmt, topk, scale,
-                seqs=None):
+                seqs=None, memo=None):
     """One decode step: for each sequence b the newest token (row cache_lens[b]-1, already in
     the cache) scores all cached keys 0..n-1, keeps the top-k and attends over them.
     Returns (indices [B, k], output [B, Hq, d]) for the sequences in ``seqs``.
-    Summary page section 一 (decode cost) and section 八 (DSA decode path)."""
+    Summary page section 一 (decode cost) and section 八 (DSA decode path).
+    ``memo``: optional dict that keeps decoded indexer keys across steps (cached rows must not
+    change between calls that share it; appending rows is fine)."""
     seqs = range(len(cache_lens)) if seqs is None else seqs
     sels, outs = [], []
     for b in seqs:
         n = int(cache_lens[b])
-        sc = index_score_row(decode(q_idx[b], idx_fmt), decode(k_idx_cache[b, :n], idx_fmt),
+        sc = index_score_row(decode(q_idx[b], idx_fmt), _decoded_keys(k_idx_cache, b, n, idx_fmt, memo),
                              np.asarray(w_idx[b], dtype=np.float64))
         sel = select_topk_row(sc, topk)
         s = sel[sel >= 0]

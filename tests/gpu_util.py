@@ -43,3 +43,22 @@ def sample_rows(cu, topk, seed, n_random=32, edge=8):
             rows.update({a + f - 1, a + f, a + f + 16})
         rows.update((a + rng.integers(0, L, size=max(1, n_random // (len(cu) - 1)))).tolist())
     return np.array(sorted(r for r in rows if r < int(cu[-1])), dtype=np.int64)
+
+
+def survey_sample_rows(cu, seed, edge=2048, n_random=4096, frame=1024, text=16):
+    """The deterministic row sample of the long workloads: each sequence's first and last
+    ``edge`` rows; at every frame boundary the last row of the previous frame, the frame's first
+    (timestamp-text) row and its first vision row; and ``n_random`` seeded rows over the batch."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    T = int(cu[-1])
+    for b in range(len(cu) - 1):
+        a, e = int(cu[b]), int(cu[b + 1])
+        L = e - a
+        rows.update(range(a, a + min(edge, L)))
+        rows.update(range(max(a, e - edge), e))
+        for f in range(frame, L, frame):
+            rows.update(a + r for r in (f - 1, f, f + text) if r < L)
+    if n_random and T:
+        rows.update(rng.integers(0, T, size=n_random).tolist())
+    return np.array(sorted(rows), dtype=np.int64)

@@ -195,7 +195,7 @@ def test_topk_all_ties_prefill():
 @pytest.mark.parametrize("zero_q", [False, True])
 def test_decode_chunked_topk(zero_q):
     """Caches of ~20K rows: the decode top-k runs over several 4096-key chunks; with zero
-    queries every score ties and the candidate list spills out of LDS."""
+    queries every score is 0, the row is flat and the first k keys are kept without a select."""
     d = gen.make_decode(2, 20000, 20064, 1, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", topk=2048, seed=15)
     st = DecodeState(d)
     s = st.load_step(0)
@@ -287,10 +287,15 @@ def test_topk_two_valued_scores_prefill():
         assert np.array_equal(idx[t], O.select_topk_row(o.scores(t), p.topk)), t
 
 
-def test_topk_two_valued_scores_decode():
+@pytest.mark.parametrize("hot_frac", [0.5, 0.8])
+def test_topk_two_valued_scores_decode(hot_frac):
+    """Keys tie at two scores; a fraction ``hot_frac`` of the 20000 cached keys share the top
+    score.  At 0.5 (about 10000 tied candidates) the decode finalize keeps its candidate list in
+    LDS; at 0.8 (about 16000, more than its 12288-entry list) the list spills to the workspace
+    and the select finishes over HBM.  The row is never flat (the other keys score 0)."""
     d = gen.make_decode(2, 20000, 20064, 1, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", topk=2048, seed=42)
     rng = np.random.default_rng(1)
-    hot = rng.random(d.k_idx_cache.shape[:2]) < 0.5
+    hot = rng.random(d.k_idx_cache.shape[:2]) < hot_frac
     d.k_idx_cache[:] = 0
     d.k_idx_cache[hot] = 0x38
     st = DecodeState(d)
@@ -305,7 +310,7 @@ def test_topk_two_valued_scores_decode():
     sel, ref = O.decode_step(kc, kk, vv, st.len_host, s["q_idx"], s["w_idx"], s["q"], d.idx_dtype, d.topk,
                              d.softmax_scale)
     assert np.array_equal(st.topk_idx.cpu().numpy(), sel)
-    assert_out_close(bf16_to_float(st.out), ref, "decode two-valued")
+    assert_out_close(bf16_to_float(st.out), ref, f"decode two-valued, hot fraction {hot_frac}")
 
 
 def test_decode_unequal_cache_lengths():

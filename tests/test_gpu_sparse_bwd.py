@@ -61,6 +61,10 @@ CASES = {
     "g16": ([600], 128, 16, 1, None),
     "g4": ([450, 70], 64, 16, 4, None),
     "k_ge_L": ([300], 512, 32, 4, None),
+    # dk/dv partials are summed over 4096-row slices of a sequence: rows over 3 slices, and two
+    # sequences of 2 slices each (slices count from each sequence's start)
+    "slices_9000": ([9000], 128, 8, 1, None),
+    "slices_varlen": ([5000, 4500], 96, 8, 2, None),
 }
 
 

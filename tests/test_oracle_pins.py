@@ -398,3 +398,20 @@ def test_pin_catches_wrong_group_map():
 def test_pin_catches_missing_scale():
     bad = lambda q, k, v, s: O.attention_row(q, k, v, 1.0)
     assert not check_attention_vs_sdpa(bad)
+
+
+def test_decode_step_memo_gives_the_same_results():
+    """decode_step with a memo of decoded keys (kept across steps while rows are appended)
+    returns exactly what it returns without one."""
+    d = gen.make_decode(2, 300, 304, 3, idx_heads=4, idx_dim=128, idx_dtype="fp8_e4m3", topk=32, seed=5)
+    kc, kk, vv = d.k_idx_cache.copy(), d.k_cache.copy(), d.v_cache.copy()
+    memo = {}
+    for i in range(3):
+        s = d.step(i)
+        kc[:, 300 + i], kk[:, 300 + i], vv[:, 300 + i] = s["k_idx_new"], s["k_new"], s["v_new"]
+        lens = np.full(2, 301 + i)
+        args = (kc, kk, vv, lens, s["q_idx"], s["w_idx"], s["q"], d.idx_dtype, d.topk, d.softmax_scale)
+        a, b = O.decode_step(*args)
+        c, e = O.decode_step(*args, memo=memo)
+        assert np.array_equal(a, c) and np.array_equal(b, e)
+    assert memo[0].shape[0] == 303

@@ -31,8 +31,9 @@
  *     before anything is enqueued; on error nothing is enqueued.  Contents of device arrays
  *     (cu_seqlens, cache_lens) are the caller's contract and are not checked;
  *   - identical inputs give bit-identical outputs (no float atomics anywhere);
- *   - the library keeps no mutable global state; calls on different streams may overlap as
- *     long as they do not share output or workspace buffers.
+ *   - the library keeps no mutable global state (except the device scratch array of
+ *     dsa_decode_noalloc, below); calls on different streams may overlap as long as they do
+ *     not share output or workspace buffers.
  */
 #ifndef DSA_H
 #define DSA_H
@@ -49,7 +50,8 @@ enum dsa_status {
   DSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, inconsistent shape */
   DSA_ERR_UNSUPPORTED = 2,        /* valid but not compiled (e.g. head_dim != 128) */
   DSA_ERR_WORKSPACE_TOO_SMALL = 3,
-  DSA_ERR_HIP = 4                 /* a HIP launch failed; see dsa_last_hip_error() */
+  DSA_ERR_HIP = 4,                /* a HIP launch failed; see dsa_last_hip_error() */
+  DSA_ERR_SCRATCH_TOO_SMALL = 5   /* dsa_decode_noalloc: the shape needs more than its scratch */
 };
 
 enum dsa_idx_dtype { DSA_IDX_BF16 = 0, DSA_IDX_FP8_E4M3 = 1 };
@@ -250,6 +252,25 @@ int dsa_decode_timed(const dsa_decode_shape* shape, const void* q_idx, const flo
                      const uint16_t* q, const void* k_idx_cache, const uint16_t* k_cache,
                      const uint16_t* v_cache, uint16_t* out, int32_t* topk_idx, void* workspace,
                      size_t workspace_bytes, void* stream, void* const* events);
+
+/* Bytes of the device scratch array behind dsa_decode_noalloc (one array per GPU). */
+#define DSA_DECODE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* dsa_decode without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, results and error checks as dsa_decode; the workspace is instead a
+ * file-scope device array of DSA_DECODE_NOALLOC_SCRATCH_BYTES that every GPU the library runs
+ * on holds until the process ends.  Its address on the current device is looked up on the
+ * first call on that device (hipGetSymbolAddress); nothing is allocated or freed, ever.
+ * `stream` must belong to the current device.  A shape whose dsa_decode_workspace_size exceeds
+ * the scratch returns DSA_ERR_SCRATCH_TOO_SMALL before anything is enqueued (16 sequences of
+ * 131136 cached rows with k = 2048 fit).  All calls on one GPU share its scratch: calls that
+ * overlap in time on one GPU (different streams or threads without ordering) race and must
+ * not be made; calls ordered on one stream are fine.  The decode kernels write every scratch
+ * byte they read within the call, so nothing carries over from the previous call. */
+int dsa_decode_noalloc(const dsa_decode_shape* shape, const void* q_idx, const float* w_idx,
+                       const uint16_t* q, const void* k_idx_cache, const uint16_t* k_cache,
+                       const uint16_t* v_cache, uint16_t* out, int32_t* topk_idx, void* stream);
 
 /* Full attention of the newest token over its whole cache (decode cost reference). */
 int dense_decode_attention(const dsa_decode_shape* shape, const uint16_t* q,

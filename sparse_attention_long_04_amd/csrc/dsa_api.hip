@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/dsa.h"
 #include "common.h"
 
@@ -112,7 +114,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint8_t* __restric
 
 using namespace dsa;
 
+// Device memory of the allocation-free decode entry point: a file-scope array that each GPU the
+// library runs on holds from module load until the process ends.  In host code its name is only
+// a stand-in; the per-device address comes from hipGetSymbolAddress and is kept below.
+constexpr size_t kDecodeScratchBytes = size_t(DSA_DECODE_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 thread_local int g_last_hip_error = 0;
 
@@ -388,6 +400,7 @@ const char* dsa_status_string(int status) {
     case DSA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case DSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case DSA_ERR_HIP: return "HIP launch error";
+    case DSA_ERR_SCRATCH_TOO_SMALL: return "shape needs more than the static decode scratch";
     default: return "unknown status";
   }
 }
@@ -801,6 +814,37 @@ int dsa_decode_timed(const dsa_decode_shape* s, const void* q_idx, const float* 
                      int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream, void* const* events) {
   if (!events) return DSA_ERR_INVALID_ARGUMENT;
   return decode_impl(s, q_idx, w_idx, q, k_idx_cache, k_cache, v_cache, out, topk_idx, ws, ws_bytes, stream, events);
+}
+
+// Address of this device's copy of `scratch` (looked up once per device, with it current).
+static int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return DSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!ptr || !aligned16(ptr)) return DSA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+int dsa_decode_noalloc(const dsa_decode_shape* s, const void* q_idx, const float* w_idx, const uint16_t* q,
+                       const void* k_idx_cache, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* out,
+                       int32_t* topk_idx, void* stream) {
+  int rc = check_decode(s, true);
+  if (rc) return rc;
+  const size_t need = decode_layout(s).total;
+  if (need > kDecodeScratchBytes) return DSA_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  return decode_impl(s, q_idx, w_idx, q, k_idx_cache, k_cache, v_cache, out, topk_idx, ws, kDecodeScratchBytes,
+                     stream, nullptr);
 }
 
 int dense_decode_attention(const dsa_decode_shape* s, const uint16_t* q, const uint16_t* k_cache,

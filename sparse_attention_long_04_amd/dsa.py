@@ -57,6 +57,7 @@ EXPORTS = {
     "dsa_decode_workspace_size": ([ctypes.POINTER(DecodeShape), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "dsa_kv_append": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 8, ctypes.c_int),
     "dsa_decode": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "dsa_decode_noalloc": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 9, ctypes.c_int),
     "dense_decode_attention": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "dsa_prefill_timed": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "dsa_decode_timed": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
@@ -206,6 +207,13 @@ def dsa_decode(shape, q_idx, w_idx, q, k_idx_cache, k_cache, v_cache, out, topk_
     _check(lib().dsa_decode(ctypes.byref(shape), _ptr(q_idx), _ptr(w_idx), _ptr(q), _ptr(k_idx_cache),
                             _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(topk_idx), _ptr(workspace),
                             _nbytes(workspace), _stream(stream)), "dsa_decode")
+
+
+def dsa_decode_noalloc(shape, q_idx, w_idx, q, k_idx_cache, k_cache, v_cache, out, topk_idx, stream=None):
+    """dsa_decode on the library's static device scratch (no workspace argument)."""
+    _check(lib().dsa_decode_noalloc(ctypes.byref(shape), _ptr(q_idx), _ptr(w_idx), _ptr(q), _ptr(k_idx_cache),
+                                    _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(topk_idx), _stream(stream)),
+           "dsa_decode_noalloc")
 
 
 def dense_decode_attention(shape, q, k_cache, v_cache, out, workspace, stream=None):

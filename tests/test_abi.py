@@ -213,3 +213,21 @@ def test_indexer_kl_rejects_unsupported_shapes():
     with pytest.raises(dsa.DSAError) as ei:
         dsa.dsa_indexer_kl(ok, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, (FAKE, n - 1), stream=0)
     assert ei.value.status == 3
+
+
+def test_decode_noalloc_rejects_shapes_beyond_its_scratch_before_launch():
+    """The allocation-free decode refuses, on the host, any shape whose workspace would not fit
+    its static scratch; 16 x 131136-row caches with k = 2048 fit."""
+    assert dsa.dsa_status_string(5) == "shape needs more than the static decode scratch"
+    ok = dsa.decode_shape(FAKE, 131136, 131136, batch=16, topk=2048, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3")
+    assert dsa.dsa_decode_workspace_size(ok) <= 64 << 20
+    big = dsa.decode_shape(FAKE, 1 << 20, 1 << 20, batch=16, topk=2048, idx_heads=64, idx_dim=128,
+                           idx_dtype="fp8_e4m3")
+    assert dsa.dsa_decode_workspace_size(big) > 64 << 20
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_decode_noalloc(big, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, stream=0)
+    assert ei.value.status == 5
+    bad = dsa.decode_shape(FAKE, 1000, 900, batch=2, topk=64, idx_heads=64, idx_dim=64, idx_dtype="bf16")
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_decode_noalloc(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, stream=0)
+    assert ei.value.status == 2

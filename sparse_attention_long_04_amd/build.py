@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["dsa_api.hip", "indexer.hip", "topk.hip", "attention.hip", "dedup.hip", "indexer_kl.hip", "attention_bwd.hip", "row_order.hip"]
+SOURCES = ["dsa_api.hip", "indexer.hip", "topk.hip", "attention.hip", "dedup.hip", "indexer_kl.hip", "attention_bwd.hip", "row_order.hip", "decode_select.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -12,9 +12,15 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
-constexpr int kDecodeKeysPerBlock = 256;   // cached keys per decode-indexer workgroup (one range slot each)
-constexpr int kDecodeTopkBins = 2048;      // value bins per sequence of the decode top-k histogram
-constexpr int kDecodeTopkChunk = 4096;     // scores per decode top-k chunk (one candidate list each)
+constexpr int kDecodeKeysPerBlock = 256;   // cached keys per decode-indexer workgroup (one histogram window each)
+// Decode selection bins: bin(key) = key >> kDecodeBinShift of the order key of a score, i.e. 16
+// bins per octave of the score's magnitude.  Each decode-indexer block counts its keys in a window
+// of kDecodeWinBins bins: the octave of its largest key and the three octaves below it.
+constexpr int kDecodeBinShift = 19;
+constexpr int kDecodeWinBins = 64;
+__device__ __forceinline__ int decode_win_base(uint32_t max_key) {
+  return int((max_key >> kDecodeBinShift) & ~15u) - (kDecodeWinBins - 16);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
@@ -64,6 +70,16 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ int wave_sum_i(int v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
   return v;
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses are complete (lgkmcnt(0)), then
+// every wave meets.  Unlike __syncthreads() it does not wait for the wave's global loads and stores
+// (the workgroup-scope fence); use it where waves exchange data through LDS alone.
+__device__ __forceinline__ void lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Inclusive prefix sum across the 64 lanes of a wave.

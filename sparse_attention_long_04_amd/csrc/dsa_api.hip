@@ -17,14 +17,13 @@ hipError_t launch_indexer_prefill(bool fp8, int di, const void* q_idx, const voi
 hipError_t launch_unpack_scores(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq, int64_t T,
                                 int ldo, float* out, hipStream_t st);
 hipError_t launch_indexer_decode(const void* q_idx, const float* w, const void* k_cache, const int32_t* cache_lens,
-                                 int B, int cap, int max_len, int H, int64_t score_ld, float* scores, int* ghist,
-                                 uint2* blkrange, hipStream_t st);
+                                 int B, int cap, int max_len, int H, uint32_t* skeys, uint8_t* spos, int* wbase,
+                                 uint16_t* wcnt, hipStream_t st);
 hipError_t launch_topk_prefill(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq, int64_t T, int K,
                                const float2* rowrange, int32_t* out, hipStream_t st);
-int topk_decode_nchunk(int max_len);
-hipError_t launch_topk_decode(const float* scores, int64_t ld, const int32_t* cache_lens, int B, int max_len, int K,
-                              const uint2* blkrange, int* ghist, uint32_t* lkeys, int* lids, int* counts,
-                              int* spill, int32_t* out, hipStream_t st);
+hipError_t launch_topk_decode(const uint32_t* skeys, const uint8_t* spos, const int32_t* cache_lens, int B,
+                              int max_len, int K, const int* wbase, const uint16_t* wcnt, int blk_stride,
+                              int32_t* out, hipStream_t st);
 hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx, int K,
                                    int mode, const int32_t* cu, int nseq, const int32_t* cache_lens, int cap,
                                    int64_t rows, int Hq, int Hkv, float scale, int keys_per_split, int nsplit,
@@ -343,11 +342,12 @@ int check_prefill_ws(const dsa_prefill_shape* s, void* ws, size_t ws_bytes, Pref
   return DSA_OK;
 }
 
+constexpr int kDecodeMaxCacheLen = 1 << 20;  // longest decode cache (rows)
+
 int check_decode(const dsa_decode_shape* s, bool need_indexer) {
   if (!s || !s->cache_lens || s->batch < 1 || s->cache_capacity < 1) return DSA_ERR_INVALID_ARGUMENT;
   if (s->max_cache_len < 1 || s->max_cache_len > s->cache_capacity) return DSA_ERR_INVALID_ARGUMENT;
-  // the top-k finalize takes one chunk count per thread of its 256-thread workgroup
-  if (s->max_cache_len > 256 * kDecodeTopkChunk) return DSA_ERR_UNSUPPORTED;
+  if (s->max_cache_len > kDecodeMaxCacheLen) return DSA_ERR_UNSUPPORTED;
   int rc = check_heads(s->topk, s->idx_heads, s->idx_dim, s->idx_dtype, s->q_heads, s->kv_heads, s->head_dim,
                        s->softmax_scale, need_indexer);
   if (rc) return rc;
@@ -359,32 +359,31 @@ constexpr int kDecodeSparseSplit = 128;   // selected keys per split (decode)
 constexpr int kDecodeDenseSplit = 2048;   // cache rows per split (dense decode)
 
 struct DecodeWs {
-  size_t scores, topk, opart, mlpart, ghist, keyrange, lkeys, lids, counts, spill, total;
-  int64_t ld;
-  int nsplit_sparse, nsplit_dense, nchunk;
+  size_t skeys, spos, topk, opart, mlpart, wbase, wcnt, total;
+  int nsplit_sparse, nsplit_dense, blk_stride;
 };
 
+// Decode workspace layout (256-byte aligned), per indexer block of kDecodeKeysPerBlock cache rows:
+// bin-sorted order keys uint32 [B][blk][256] and their block positions uint8 [B][blk][256] |
+// topk int32 [B][k] | split partials (sized for the larger of the sparse and dense split counts) |
+// histogram window base int [B][blk] and counts uint16 [B][blk][kDecodeWinBins].
+// Every byte the decode kernels read is written earlier in the same call.
 DecodeWs decode_layout(const dsa_decode_shape* s) {
   DecodeWs w{};
-  w.ld = (int64_t(s->cache_capacity) + 63) / 64 * 64;
   w.nsplit_sparse = (s->topk + kDecodeSparseSplit - 1) / kDecodeSparseSplit;
   w.nsplit_dense = (s->max_cache_len + kDecodeDenseSplit - 1) / kDecodeDenseSplit;
+  w.blk_stride = (s->max_cache_len + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock;
   const int ns = w.nsplit_sparse > w.nsplit_dense ? w.nsplit_sparse : w.nsplit_dense;
   const size_t B = size_t(s->batch);
   size_t off = 0;
-  w.scores = off; off = align_up(off + B * size_t(w.ld) * sizeof(float), 256);
+  const size_t slots = B * size_t(w.blk_stride) * kDecodeKeysPerBlock;
+  w.skeys = off; off = align_up(off + slots * sizeof(uint32_t), 256);
+  w.spos = off; off = align_up(off + slots, 256);
   w.topk = off; off = align_up(off + B * size_t(s->topk) * sizeof(int32_t), 256);
   w.opart = off; off = align_up(off + B * ns * size_t(s->q_heads) * s->head_dim * sizeof(float), 256);
   w.mlpart = off; off = align_up(off + B * ns * size_t(s->q_heads) * sizeof(float2), 256);
-  w.nchunk = topk_decode_nchunk(s->max_cache_len);
-  const size_t lst = B * size_t(w.nchunk) * kDecodeTopkChunk;
-  w.ghist = off; off = align_up(off + B * kDecodeTopkBins * sizeof(int), 256);
-  w.keyrange = off;
-  off = align_up(off + B * size_t((s->max_cache_len + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock) * sizeof(uint2), 256);
-  w.lkeys = off; off = align_up(off + lst * sizeof(uint32_t), 256);
-  w.lids = off; off = align_up(off + lst * sizeof(int), 256);
-  w.counts = off; off = align_up(off + B * size_t(w.nchunk) * sizeof(int), 256);
-  w.spill = off; off = align_up(off + 2 * lst * sizeof(int), 256);
+  w.wbase = off; off = align_up(off + B * size_t(w.blk_stride) * sizeof(int), 256);
+  w.wcnt = off; off = align_up(off + B * size_t(w.blk_stride) * kDecodeWinBins * sizeof(uint16_t), 256);
   w.total = off;
   return w;
 }
@@ -560,16 +559,15 @@ int decode_impl(const dsa_decode_shape* s, const void* q_idx, const float* w_idx
   if (ws_bytes < L.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.topk);
-  float* scores = at<float>(ws, L.scores);
+  uint32_t* skeys = at<uint32_t>(ws, L.skeys);
+  uint8_t* spos = at<uint8_t>(ws, L.spos);
   if ((rc = hip_status(launch_indexer_decode(q_idx, w_idx, k_idx_cache, s->cache_lens, s->batch, s->cache_capacity,
-                                             s->max_cache_len, s->idx_heads, L.ld, scores, at<int>(ws, L.ghist),
-                                             at<uint2>(ws, L.keyrange), st))))
+                                             s->max_cache_len, s->idx_heads, skeys, spos, at<int>(ws, L.wbase),
+                                             at<uint16_t>(ws, L.wcnt), st))))
     return rc;
   if ((rc = record(ev, 0, st))) return rc;
-  if ((rc = hip_status(launch_topk_decode(scores, L.ld, s->cache_lens, s->batch, s->max_cache_len, s->topk,
-                                          at<uint2>(ws, L.keyrange), at<int>(ws, L.ghist),
-                                          at<uint32_t>(ws, L.lkeys), at<int>(ws, L.lids),
-                                          at<int>(ws, L.counts), at<int>(ws, L.spill), idx, st))))
+  if ((rc = hip_status(launch_topk_decode(skeys, spos, s->cache_lens, s->batch, s->max_cache_len, s->topk,
+                                          at<int>(ws, L.wbase), at<uint16_t>(ws, L.wcnt), L.blk_stride, idx, st))))
     return rc;
   if ((rc = record(ev, 1, st))) return rc;
   if ((rc = hip_status(launch_gather_attention(q, k_cache, v_cache, idx, s->topk, 1, nullptr, 0, s->cache_lens,

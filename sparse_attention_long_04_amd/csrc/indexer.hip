@@ -443,56 +443,70 @@ __global__ void unpack_scores_kernel(const float* __restrict__ tri, const int64_
 // Decode indexer: one query token per sequence against its whole cache.  A = the token's
 // queries (16 heads per MFMA, from LDS), B = 16 cached keys; C[i] of lane l = (head 4g+i,
 // key r).  The weighted ReLU sum over heads runs in registers, then across the 4 lane groups.
+// Each workgroup (kDecodeKeysPerBlock keys) writes its scores as order keys sorted by selection bin
+// (key >> kDecodeBinShift), highest bin first: skeys[b][blk][slot] and their positions inside the
+// block spos[b][blk][slot] (8 bits), the keys below its histogram window last.  It also writes the
+// window itself: wbase[b][blk] = decode_win_base of its largest key and wcnt[b][blk][i] = the
+// number of its keys in bins wbase + i and above (cumulative 16-bit counts, kDecodeWinBins bins;
+// keys below the window are not counted).  All plain stores: the
+// selection needs nothing cleared beforehand.  The bin sort is a counting sort: a key's rank in
+// its bin is the value its histogram atomic returned.
 // ------------------------------------------------------------------------------------------
 template <int HMAX, int NT>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(
     const uint8_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint8_t* __restrict__ k_cache, const int32_t* __restrict__ cache_lens, int cap, int H,
-    int64_t score_ld, float* __restrict__ scores, uint2* __restrict__ blkrange, int blk_stride,
-    int* __restrict__ ghist) {
-  constexpr int ROWB = 128, UNITS = 8, CH = 32;
+    uint32_t* __restrict__ skeys, uint8_t* __restrict__ spos, int* __restrict__ wbase, uint16_t* __restrict__ wcnt,
+    int blk_stride) {
+  constexpr int ROWB = 128, UNITS = 8;
   constexpr int WKEYS = kDecodeKeysPerBlock / 4;  // contiguous keys per wave
+  static_assert(WKEYS == 2 * NT * 16, "a wave's keys are two steps of NT tiles");
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[HMAX * ROWB];
   __shared__ float w_lds[HMAX];
-  __shared__ uint2 red_lds[4];
+  __shared__ uint32_t red_lds[4];
+  __shared__ int win_lds[kDecodeWinBins + 1];   // [kDecodeWinBins]: keys below the window
+  __shared__ int off_lds[kDecodeWinBins + 1];
   const int b = blockIdx.y;
   const int n = cache_lens[b];
   const int key0 = blockIdx.x * kDecodeKeysPerBlock;
   const int tid = threadIdx.x;
-  // the top-k after this kernel merges chunk histograms into ghist[b] with atomics: clear it
-  if (blockIdx.x == 0)
-    for (int i = tid; i < kDecodeTopkBins; i += 256) ghist[b * kDecodeTopkBins + i] = 0;
   if (key0 >= n) return;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  if (tid <= kDecodeWinBins) win_lds[tid] = 0;
   // 16-byte unit swizzle of head row h: the 16 heads an A-operand read touches (one 256-byte LDS
   // pass) land on 16 distinct bank groups
   auto dswz = [](int h) { return (h & 7) ^ ((h >> 3) & 1); };
   const int kw0 = key0 + wave * WKEYS;
   const int kw1 = min(n, kw0 + WKEYS);
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  // loads are clamped to the wave's own last key: the prefetch issued by its last step then
-  // re-reads cached lines instead of fetching the next wave's keys
-  const int klast = kw1 - 1;  // >= 0: n >= 1 here
+  // loads are clamped to the wave's own last key (or the block's first key for a wave past the
+  // row): the prefetch issued by its last step then re-reads cached lines instead of fetching
+  // the next wave's keys
+  const int klast = max(kw1 - 1, key0);
+  // The contraction runs over the 128 dims in a permuted order, the same for both operands: lane
+  // group g takes dims [16g, 16g + 16) and [64 + 16g, 80 + 16g).  A load instruction then reads 64
+  // contiguous bytes of each of its 16 keys (the first half of every row, then the second).
   auto load = [&](i32x8 (&dst)[NT], int kb) {
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) {
       const int key = min(kb + 16 * jt + r, klast);
-      const uint8_t* p = k_cache + ((int64_t)b * cap + key) * ROWB + g * CH;
+      const uint8_t* p = k_cache + ((int64_t)b * cap + key) * ROWB + g * 16;
       const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 64);
       dst[jt] = (i32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
-  auto step = [&](const i32x8 (&bfr)[NT], i32x8 (&nxt)[NT], int kb) {
-    load(nxt, kb + NT * 16);  // unconditional (clamped) prefetch of the next step
+  // sv[s][jt]: the score of key kw0 + 32 s + 16 jt + r (every lane group holds it after the sum)
+  float sv[2][NT] = {};
+  auto step = [&](const i32x8 (&bfr)[NT], i32x8 (&nxt)[NT], int kb, float (&out)[NT], bool prefetch) {
+    if (prefetch) load(nxt, kb + NT * 16);
     float acc[NT];
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) acc[jt] = 0.f;
     for (int hb = 0; hb < H; hb += 16) {
       const uint8_t* qa = q_lds + (hb + r) * ROWB;
       const int hr = dswz(hb + r);
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(qa + (((2 * g) ^ hr) * 16));
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(qa + (((2 * g + 1) ^ hr) * 16));
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(qa + ((g ^ hr) * 16));
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(qa + (((g + 4) ^ hr) * 16));
       const i32x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       const f32x4 wv = *reinterpret_cast<const f32x4*>(w_lds + hb + 4 * g);
 #pragma unroll
@@ -507,19 +521,14 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
       float v = acc[jt];
       v += __shfl_xor(v, 16);
       v += __shfl_xor(v, 32);
-      const int key = kb + 16 * jt + r;
-      if (g == 0 && key < kw1) {
-        scores[(int64_t)b * score_ld + key] = v;
-        const uint32_t kk = score_key(v);
-        kmin = min(kmin, kk);
-        kmax = max(kmax, kk);
-      }
+      out[jt] = v;
     }
   };
-  // the first keys, the queries and the head weights are all requested before any is used:
+  // all of the wave's keys, the queries and the head weights are requested before any is used:
   // one round trip (a load-then-store loop would wait for each of its loads in turn)
   i32x8 bA[NT], bB[NT];
   load(bA, kw0);
+  load(bB, kw0 + NT * 16);
   constexpr int QPT = HMAX * UNITS / 256;  // 16-byte query pieces per thread
   i32x4 qv[QPT];
 #pragma unroll
@@ -536,28 +545,48 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
   if (tid < H) w_lds[tid] = wv_in;
   __syncthreads();
   if (kw0 < kw1) {
-    for (int kb = kw0; kb < kw1; kb += 2 * NT * 16) {
-      step(bA, bB, kb);
-      if (kb + NT * 16 < kw1) step(bB, bA, kb + NT * 16);
-    }
+    step(bA, bB, kw0, sv[0], false);
+    if (kw0 + NT * 16 < kw1) step(bB, bA, kw0 + NT * 16, sv[1], false);
   }
-  // this block's score range (order keys) for the top-k's value binning: one slot per block,
-  // reduced by the top-k kernels (no atomics)
+  // epilogue, one key per lane: lane (r, g) owns key kw0 + 32 (g >> 1) + 16 (g & 1) + r (every
+  // lane group holds every score of the wave after the sums)
+  const int kidx = 32 * (g >> 1) + 16 * (g & 1) + r;
+  const bool kval = kw0 + kidx < kw1;
+  const float myv = g == 0 ? sv[0][0] : g == 1 ? sv[0][1] : g == 2 ? sv[1][0] : sv[1][1];
+  const uint32_t mykey = score_key(myv);
+  // the block's largest order key sets its histogram window
+  uint32_t kmax = kval ? mykey : 0u;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-  }
-  if (lane == 0) red_lds[wave] = make_uint2(kmin, kmax);
-  __syncthreads();
-  if (tid == 0) {
-    uint2 a = red_lds[0];
-    for (int w = 1; w < 4; ++w) {
-      a.x = min(a.x, red_lds[w].x);
-      a.y = max(a.y, red_lds[w].y);
+  for (int o = 1; o < 64; o <<= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+  if (lane == 0) red_lds[wave] = kmax;
+  lds_sync();
+  kmax = max(max(red_lds[0], red_lds[1]), max(red_lds[2], red_lds[3]));
+  const int base = decode_win_base(kmax);
+  // histogram window; the atomic's return value is the key's rank inside its bin
+  const int ib = int(mykey >> kDecodeBinShift) - base;
+  const int wbin = ib >= 0 ? ib : kDecodeWinBins;
+  const int rank = kval ? atomicAdd(&win_lds[wbin], 1) : 0;
+  lds_sync();
+  const int64_t slot = (int64_t)b * blk_stride + blockIdx.x;
+  if (wave == 0) {
+    // bins in descending order: the inclusive count is the window's cumulative count (keys of
+    // this bin or higher, written), the exclusive one the bin's first slot; the keys below the
+    // window follow the window's keys
+    const int c = lane < kDecodeWinBins ? win_lds[kDecodeWinBins - 1 - lane] : 0;
+    const int incl = wave_incl_scan(c);
+    if (lane < kDecodeWinBins) {
+      off_lds[kDecodeWinBins - 1 - lane] = incl - c;
+      wcnt[slot * kDecodeWinBins + kDecodeWinBins - 1 - lane] = uint16_t(incl);
     }
-    blkrange[(int64_t)b * blk_stride + blockIdx.x] = a;
+    if (lane == 63) off_lds[kDecodeWinBins] = incl;
   }
+  lds_sync();
+  if (kval) {
+    const int d = off_lds[wbin] + rank;
+    skeys[slot * kDecodeKeysPerBlock + d] = mykey;
+    spos[slot * kDecodeKeysPerBlock + d] = uint8_t(wave * WKEYS + kidx);
+  }
+  if (tid == 0) wbase[slot] = base;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -597,13 +626,12 @@ hipError_t launch_unpack_scores(const float* tri, const int64_t* seqoff, const i
 }
 
 hipError_t launch_indexer_decode(const void* q_idx, const float* w, const void* k_cache,
-                                 const int32_t* cache_lens, int B, int cap, int max_len, int H,
-                                 int64_t score_ld, float* scores, int* ghist, uint2* blkrange,
-                                 hipStream_t st) {
+                                 const int32_t* cache_lens, int B, int cap, int max_len, int H, uint32_t* skeys,
+                                 uint8_t* spos, int* wbase, uint16_t* wcnt, hipStream_t st) {
   dim3 grid((max_len + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock, B);
   indexer_decode_kernel<64, 2><<<grid, 256, 0, st>>>(static_cast<const uint8_t*>(q_idx), w,
                                                      static_cast<const uint8_t*>(k_cache), cache_lens,
-                                                     cap, H, score_ld, scores, blkrange, (int)grid.x, ghist);
+                                                     cap, H, skeys, spos, wbase, wcnt, (int)grid.x);
   return hipGetLastError();
 }
 

@@ -22,10 +22,7 @@
 // 10 bits) runs on the list.  Rows whose list would not fit in LDS (heavy ties) run the radix
 // select over HBM; rows whose scores are all equal keep their first k keys directly.
 //
-// Decode (few rows of ~10^5 keys): the row is split into 4096-key chunks handled by separate
-// workgroups -- chunk histograms of 2048 value bins are merged with integer atomics, every chunk
-// compacts its candidates into its own list, and one workgroup per row finishes the select over
-// the concatenated lists (pairwise rank of the threshold bin, radix select as the fallback).
+// Decode rows (few rows of ~10^5 keys) are selected by decode_select.hip.
 #include "common.h"
 
 namespace dsa {
@@ -34,9 +31,6 @@ constexpr int kTopkThreads = 256;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kListCap = 3072;     // LDS candidate list capacity (prefill)
 constexpr int kBins = 2048;        // value bins / radix digit size
-constexpr int kChunk = kDecodeTopkChunk;  // decode chunk
-static_assert(kBins == kDecodeTopkBins, "the decode histogram is sized by kBins");
-constexpr int kFinalCap = 12288;   // LDS list capacity of the decode finalize step
 
 struct TopkSmem {
   int hist[kBins];
@@ -212,68 +206,6 @@ __device__ void ordered_emit(const Src& src, int n, uint32_t T, int krem, Emit e
     base_eq += total >> 16;
   }
   __syncthreads();
-}
-
-// ---- decode chunks: at most kChunk scores per workgroup ---------------------------------------
-// A thread's quads of the chunk are all requested before any is used, and before the kernels'
-// other reads (row range, histogram), so the chunk costs one memory round trip, not one per
-// 1024 scores.  Quad q of thread t covers positions q*1024 + 4t .. +3 of the chunk at p.
-// The decode score rows are ld floats with ld a multiple of 4 and every chunk starts below ld,
-// 16-byte aligned: a quad that starts below n lies wholly inside the row, and a quad at or past n
-// re-reads the chunk's first quad instead, so no load is predicated (a predicated load splits
-// into branches whose register reuse serialises the loads).  Elements at n and past are never
-// used.
-constexpr int kChunkQuads = kChunk / (4 * kTopkThreads);
-static_assert(kChunkQuads * 4 * kTopkThreads == kChunk, "a chunk is whole thread quads");
-typedef float ChunkRegs[kChunkQuads][4];
-
-__device__ __forceinline__ void load_chunk(const float* __restrict__ p, int n, ChunkRegs& x) {
-#pragma unroll
-  for (int q = 0; q < kChunkQuads; ++q) {
-    const int s0 = q * 4 * kTopkThreads + 4 * threadIdx.x;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(p + (s0 < n ? s0 : 0));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[q][e] = v[e];
-  }
-}
-
-// Histogram of value bins over a loaded chunk of n scores.
-__device__ void value_hist_chunk(const ChunkRegs& x, int n, float lo, float sc, int* hist) {
-#pragma unroll
-  for (int q = 0; q < kChunkQuads; ++q) {
-    const int s0 = q * 4 * kTopkThreads + 4 * threadIdx.x;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (s0 + e < n) atomicAdd(&hist[value_bin(x[q][e], lo, sc)], 1);
-  }
-  __syncthreads();
-}
-
-// Ordered compaction of every element of a loaded chunk whose value bin is >= b1 (no tie
-// limit): emit(slot, key, id) in index order.  Returns the count.
-template <class Emit>
-__device__ int emit_chunk_bin_ge(const ChunkRegs& x, int n, float lo, float sc, int b1, Emit emit, TopkSmem& sm) {
-  int base = 0;
-#pragma unroll
-  for (int q = 0; q < kChunkQuads; ++q) {
-    const int s0 = q * 4 * kTopkThreads + 4 * threadIdx.x;
-    bool keep[4];
-    int c = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      keep[e] = s0 + e < n && value_bin(x[q][e], lo, sc) >= b1;
-      c += keep[e];
-    }
-    int total;
-    const int incl = block_incl_scan(c, sm.wave_tot, &total);
-    int pos = base + incl - c;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (keep[e]) emit(pos++, score_key(x[q][e]), s0 + e);
-    base += total;
-  }
-  __syncthreads();
-  return base;
 }
 
 // ---- finishing a candidate list ------------------------------------------------------------
@@ -734,200 +666,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_prefill_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode: chunked top-k over rows of n = cache_lens[b] scores.
-//   blkrange [B][ceil(n/kDecodeKeysPerBlock)] (min, max order keys per decode-indexer block), ghist [B][kBins] int
-//   (cleared before the indexer), lists [B][nchunk][kChunk] (key, id), counts [B][nchunk].
-// ------------------------------------------------------------------------------------------
-struct RowRange {
-  float lo, hi, sc;  // sc: kBins value bins over [lo, hi]
-  bool flat;
-};
-
-// Row range from the decode indexer's per-block (min, max) key slots (kDecodeKeysPerBlock keys
-// per slot).  Every thread of the block must call it.
-__device__ __forceinline__ RowRange decode_range(const uint2* __restrict__ blkrange, int stride, int b, int n, TopkSmem& sm) {
-  const int nblk = (n + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock;
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = threadIdx.x; i < nblk; i += kTopkThreads) {
-    const uint2 v = blkrange[(int64_t)b * stride + i];
-    mn = min(mn, v.x);
-    mx = max(mx, v.y);
-  }
-  for (int o = 1; o < 64; o <<= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-  }
-  __shared__ uint2 red[kTopkWaves];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_uint2(mn, mx);
-  __syncthreads();
-  for (int w = 0; w < kTopkWaves; ++w) {
-    mn = min(mn, red[w].x);
-    mx = max(mx, red[w].y);
-  }
-  __syncthreads();
-  RowRange rr;
-  rr.lo = key_to_score(mn);
-  rr.hi = key_to_score(mx);
-  rr.flat = !(rr.hi > rr.lo);
-  rr.sc = rr.flat ? 0.f : float(kBins) / (rr.hi - rr.lo);
-  return rr;
-}
-
-__global__ __launch_bounds__(kTopkThreads) void topk_decode_hist_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cache_lens, int K,
-    const uint2* __restrict__ blkrange, int blk_stride, int* __restrict__ ghist) {
-  __shared__ TopkSmem sm;
-  const int b = blockIdx.y;
-  const int n = cache_lens[b];
-  const int c0 = blockIdx.x * kChunk;
-  const int cn = min(kChunk, n - c0);  // <= 0 past the row: nothing is loaded
-  ChunkRegs x;
-  load_chunk(scores + b * ld + c0, cn, x);
-  const RowRange rr = decode_range(blkrange, blk_stride, b, n, sm);
-  if (n <= K || c0 >= n || rr.flat) return;
-  clear_hist(sm, kBins);
-  value_hist_chunk(x, cn, rr.lo, rr.sc, sm.hist);
-  for (int i = threadIdx.x; i < kBins; i += kTopkThreads) {
-    const int h = sm.hist[i];
-    if (h) atomicAdd(&ghist[b * kBins + i], h);
-  }
-}
-
-__global__ __launch_bounds__(kTopkThreads) void topk_decode_collect_kernel(
-    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ cache_lens, int K,
-    const uint2* __restrict__ blkrange, int blk_stride, const int* __restrict__ ghist, int nchunk,
-    uint32_t* __restrict__ lkeys, int* __restrict__ lids, int* __restrict__ counts) {
-  __shared__ TopkSmem sm;
-  const int b = blockIdx.y;
-  const int n = cache_lens[b];
-  const int c0 = blockIdx.x * kChunk;
-  const int cn = min(kChunk, n - c0);  // <= 0 past the row: nothing is loaded
-  ChunkRegs x;
-  load_chunk(scores + b * ld + c0, cn, x);
-  int hreg[kBins / kTopkThreads];
-#pragma unroll
-  for (int j = 0; j < kBins / kTopkThreads; ++j) hreg[j] = ghist[b * kBins + threadIdx.x + j * kTopkThreads];
-  const RowRange rr = decode_range(blkrange, blk_stride, b, n, sm);
-  if (n <= K || rr.flat) return;
-  int cnt = 0;
-  if (c0 < n) {
-#pragma unroll
-    for (int j = 0; j < kBins / kTopkThreads; ++j) sm.hist[threadIdx.x + j * kTopkThreads] = hreg[j];
-    __syncthreads();
-    find_digit(sm, kBins, K);
-    const int b1 = sm.sel_digit;
-    const int64_t base = ((int64_t)b * nchunk + blockIdx.x) * kChunk;
-    cnt = emit_chunk_bin_ge(x, cn, rr.lo, rr.sc, b1, [&](int slot, uint32_t key, int id) {
-      lkeys[base + slot] = key;
-      lids[base + slot] = c0 + id;
-    }, sm);
-  }
-  if (threadIdx.x == 0) counts[b * nchunk + blockIdx.x] = cnt;
-}
-
-struct TopkFinalSmem {
-  TopkSmem s;
-  FinishSmem<1024> f;
-  uint32_t lkeys[kFinalCap];
-  int lids[kFinalCap];
-  int offs[257];
-};
-
-__global__ __launch_bounds__(kTopkThreads) void topk_decode_final_kernel(
-    const int32_t* __restrict__ cache_lens, int K, const uint2* __restrict__ blkrange, int blk_stride,
-    const int* __restrict__ ghist, int nchunk, const uint32_t* __restrict__ gkeys, const int* __restrict__ gids,
-    const int* __restrict__ counts, int32_t* __restrict__ out, int* __restrict__ spill_keys_ids) {
-  __shared__ TopkFinalSmem sm;
-  const int b = blockIdx.x;
-  const int n = cache_lens[b];
-  int32_t* orow = out + (int64_t)b * K;
-  // issue the independent global reads together (histogram, chunk count) before the range
-  // reduction, which has its own read: one round trip instead of three
-  int hreg[kBins / kTopkThreads];
-#pragma unroll
-  for (int j = 0; j < kBins / kTopkThreads; ++j) hreg[j] = ghist[b * kBins + threadIdx.x + j * kTopkThreads];
-  const int c = threadIdx.x < nchunk ? counts[b * nchunk + threadIdx.x] : 0;
-  const RowRange rr = decode_range(blkrange, blk_stride, b, n, sm.s);
-  if (n <= K || rr.flat) {
-    first_k(n, K, orow);
-    return;
-  }
-  // threshold bin again (same histogram as the collect step)
-#pragma unroll
-  for (int j = 0; j < kBins / kTopkThreads; ++j) sm.s.hist[threadIdx.x + j * kTopkThreads] = hreg[j];
-  __syncthreads();
-  find_digit(sm.s, kBins, K);
-  const int b1 = sm.s.sel_digit, above = sm.s.sel_above;
-  // chunk offsets: block prefix sum of the per-chunk counts
-  {
-    int tot;
-    const int incl = block_incl_scan(c, sm.s.wave_tot, &tot);
-    if (threadIdx.x < nchunk) sm.offs[threadIdx.x] = incl - c;
-    if (threadIdx.x == 0) {
-      sm.offs[nchunk] = tot;
-      sm.s.list_n = tot;
-    }
-    __syncthreads();
-  }
-  const int total = sm.s.list_n;
-  uint32_t* keys = sm.lkeys;
-  int* ids = sm.lids;
-  if (total > kFinalCap) {  // heavy ties: work from a global spill area instead of LDS
-    keys = reinterpret_cast<uint32_t*>(spill_keys_ids) + (int64_t)b * 2 * nchunk * kChunk;
-    ids = reinterpret_cast<int*>(keys + nchunk * kChunk);
-  }
-  // flattened gather of the concatenated chunk lists (chunk order = index order); a batch of
-  // loads is issued into registers before any store, so the round trips overlap.  Each element
-  // finds its chunk by a fixed-step bisection written as selects (nchunk <= kTopkThreads; a read
-  // clamped to offs[nchunk] = total stops every search inside the row), so a thread's searches
-  // carry no branches and interleave; positions past the list re-read its last element, so no
-  // load is predicated.
-  constexpr int PER = 16;
-  for (int base = 0; base < total; base += PER * kTopkThreads) {
-    uint32_t kv[PER];
-    int iv[PER];
-    int ii[PER], lo[PER];  // lo: last chunk c with offs[c] <= ii
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      ii[u] = min(base + u * kTopkThreads + (int)threadIdx.x, total - 1);
-      lo[u] = 0;
-    }
-#pragma unroll
-    for (int step = kTopkThreads / 2; step > 0; step >>= 1)  // steps outside: PER reads per wait
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int c = min(lo[u] + step, nchunk);
-        lo[u] = (sm.offs[c] <= ii[u]) ? c : lo[u];
-      }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int64_t src = ((int64_t)b * nchunk + lo[u]) * kChunk + (ii[u] - sm.offs[lo[u]]);
-      kv[u] = gkeys[src];
-      iv[u] = gids[src];
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = base + u * kTopkThreads + threadIdx.x;
-      if (i < total) {
-        keys[i] = kv[u];
-        ids[i] = iv[u];
-      }
-    }
-  }
-  __syncthreads();
-  auto bin_of = [&](uint32_t k) { return value_bin(key_to_score(k), rr.lo, rr.sc); };
-  if (total <= kFinalCap && rank_threshold_bin(keys, ids, total, b1, K - above, bin_of, sm.f)) {
-    emit_nonzero<12>(keys, ids, total, orow, sm.s);  // one round up to 3072 candidates
-    return;
-  }
-  const ListSrc ls{keys, ids};
-  uint32_t prefix = 0, hmask = 0;
-  int krem = K;
-  radix_rest(ls, total, 0, prefix, hmask, krem, sm.s);
-  ordered_emit(ls, total, prefix, krem, [&](int slot, uint32_t, int id) { orow[slot] = id; }, sm.s);
-}
-
-// ------------------------------------------------------------------------------------------
 // Standalone top-k over general float32 rows (the deterministic stand-in for torch.topk).
 // NaN (any payload) and -inf are masked: key 0.  Every other value keeps its order-preserving
 // key, which is >= 0x00800000 (the key of -FLT_MAX), so the top 11-bit digit of a selectable
@@ -1282,27 +1020,6 @@ hipError_t launch_topk_prefill(const float* tri, const int64_t* seqoff, const in
                                int64_t T, int K, const float2* rowrange, int32_t* out, hipStream_t st) {
   if (T == 0) return hipSuccess;
   topk_prefill_kernel<<<(unsigned)T, kTopkThreads, 0, st>>>(tri, seqoff, cu, nseq, T, K, rowrange, out);
-  return hipGetLastError();
-}
-
-int topk_decode_nchunk(int max_len) { return (max_len + kChunk - 1) / kChunk; }
-
-// Workspace needs: ghist B*kBins ints, lists B*nchunk*kChunk*(key+id) twice (chunk lists and
-// the finalize spill area), counts B*nchunk ints.  The score rows (16-byte aligned, ld floats
-// apart, ld a multiple of 4 and >= max_len) are what the chunk loads assume.
-hipError_t launch_topk_decode(const float* scores, int64_t ld, const int32_t* cache_lens, int B, int max_len,
-                              int K, const uint2* blkrange, int* ghist, uint32_t* lkeys, int* lids, int* counts,
-                              int* spill, int32_t* out, hipStream_t st) {
-  if ((ld & 3) != 0 || ld < max_len || (reinterpret_cast<uintptr_t>(scores) & 15) != 0) return hipErrorInvalidValue;
-  const int blk_stride = (max_len + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock;
-  const int nchunk = topk_decode_nchunk(max_len);
-  if (nchunk > kTopkThreads) return hipErrorInvalidValue;
-  dim3 grid(nchunk, B);
-  topk_decode_hist_kernel<<<grid, kTopkThreads, 0, st>>>(scores, ld, cache_lens, K, blkrange, blk_stride, ghist);
-  topk_decode_collect_kernel<<<grid, kTopkThreads, 0, st>>>(scores, ld, cache_lens, K, blkrange, blk_stride, ghist, nchunk, lkeys,
-                                                            lids, counts);
-  topk_decode_final_kernel<<<B, kTopkThreads, 0, st>>>(cache_lens, K, blkrange, blk_stride, ghist, nchunk, lkeys,
-                                                       lids, counts, out, spill);
   return hipGetLastError();
 }
 

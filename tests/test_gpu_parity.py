@@ -11,7 +11,7 @@ from oracle import dsa_oracle as O
 from sparse_attention_long_04_amd import dsa
 from sparse_attention_long_04_amd import inputs as gen
 from sparse_attention_long_04_amd import workloads
-from sparse_attention_long_04_amd.runtime import DecodeState, PrefillBatch, bf16_to_float
+from sparse_attention_long_04_amd.runtime import DecodeState, PrefillBatch, _dev, bf16_to_float
 
 from gpu_util import assert_out_close, gpu_available
 
@@ -337,6 +337,49 @@ def test_decode_unequal_cache_lengths():
     assert_out_close(bf16_to_float(st.out), ref, "decode unequal lengths")
     dense = bf16_to_float(st.dense(out=torch.empty_like(st.out)))
     assert_out_close(dense, O.dense_decode(kk, vv, st.len_host, s["q"], d.softmax_scale), "dense unequal lengths")
+
+
+def _decode_one_step(d, setup=None):
+    """Append step 0's token and run dsa_decode; returns (indices, output, oracle indices, oracle
+    output).  ``setup(s)`` may edit the step's host tensors before they are uploaded."""
+    st = DecodeState(d)
+    s = st.load_step(0)
+    if setup is not None:
+        setup(s)
+        st.step_dev = {k: _dev(v, st.device) for k, v in s.items()}
+    st.append()
+    st.decode()
+    torch.cuda.synchronize()
+    n = d.ctx_len
+    kc, kk, vv = d.k_idx_cache.copy(), d.k_cache.copy(), d.v_cache.copy()
+    kc[:, n], kk[:, n], vv[:, n] = s["k_idx_new"], s["k_new"], s["v_new"]
+    sel, ref = O.decode_step(kc, kk, vv, st.len_host, s["q_idx"], s["w_idx"], s["q"], d.idx_dtype, d.topk,
+                             d.softmax_scale)
+    return st.topk_idx.cpu().numpy(), bf16_to_float(st.out), sel, ref
+
+
+@pytest.mark.parametrize("k", [2048, 4096])
+def test_decode_select_planted_outliers(k):
+    """A few cached keys score far above the rest (more than 16 times the k-th score, beyond the
+    four octaves each indexer block's histogram window spans), so the windows cannot place the
+    threshold and the selection takes its exact pass over the whole score row.  With k = 4096 the
+    other rows' candidate lists also exceed the LDS list more often."""
+    d = gen.make_decode(3, 30000, 30016, 1, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", topk=k, seed=57)
+    rng = np.random.default_rng(58)
+    codes = {v: int(c) for v, c in zip(range(-4, 5), gen._int_code_table("fp8_e4m3", 4))}
+    small = np.vectorize(codes.get)(rng.integers(-1, 2, size=d.k_idx_cache.shape)).astype(np.uint8)
+    d.k_idx_cache[:] = small
+    qv = rng.integers(-4, 5, size=128)
+    qv[qv == 0] = 1
+    planted = np.vectorize(codes.get)(4 * np.sign(qv)).astype(np.uint8)
+    for b in range(3):
+        d.k_idx_cache[b, rng.choice(30000, 5, replace=False)] = planted
+
+    def setup(s):
+        s["q_idx"][:] = np.vectorize(codes.get)(qv).astype(np.uint8)[None, None, :]
+    idx, out, sel, ref = _decode_one_step(d, setup)
+    assert np.array_equal(idx, sel)
+    assert_out_close(out, ref, f"decode planted outliers k={k}")
 
 
 def test_kv_append_full_cache_untouched():

@@ -123,6 +123,27 @@ def bench_prefill(name, steps, warmup, with_dense=True):
     return res
 
 
+def bench_dense(name, steps):
+    """dense_causal_attention alone on a prefill workload's inputs (profiling aid)."""
+    import torch
+    from sparse_attention_long_04_amd import workloads
+    from sparse_attention_long_04_amd.runtime import PrefillBatch, timing_events
+
+    p = workloads.make(name)
+    pb = PrefillBatch(p)
+    out = torch.empty_like(pb.out)
+    torch.cuda.synchronize()
+    a, b = timing_events(2)
+    a.record()
+    for _ in range(steps):
+        pb.dense(out=out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = ms_between(a, b) / steps
+    log(f"{name}: dense causal {ms:.2f} ms")
+    return dict(workload=name, dense_ms=ms)
+
+
 def bench_decode(steps_total=64, stage_reps=16):
     """The decode workload's steps back to back: each step appends every sequence's new token
     (row and length, dsa_kv_append) and then runs dsa_decode; events around each call time
@@ -434,8 +455,9 @@ def main():
     ap.add_argument("--quick", action="store_true", help="prefill only (no dense/decode/varlen/cpu)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--only", choices=["decode", "topk", "dedup", "kl", "bwd"], default=None,
-                    help="profiling aid: run only the decode (or standalone top-k) measurement")
+    ap.add_argument("--only", choices=["decode", "topk", "dedup", "kl", "bwd", "dense"], default=None,
+                    help="profiling aid: run only that measurement (dense: the 128K dense causal reference, "
+                         "--steps launches)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -471,6 +493,9 @@ def main():
         return
     if args.only == "bwd":
         print(json.dumps(bench_sparse_bwd()), flush=True)
+        return
+    if args.only == "dense":
+        print(json.dumps(bench_dense(args.workload or workloads.P128K, args.steps)), flush=True)
         return
     name = args.workload or workloads.P128K
     w = workloads.WORKLOADS[name]

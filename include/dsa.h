@@ -122,7 +122,10 @@ int dsa_index_topk(const dsa_prefill_shape* shape, const void* q_idx, const void
 int dsa_sparse_attention(const dsa_prefill_shape* shape, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const int32_t* topk_idx, uint16_t* out, void* stream);
 
-/* The whole prefill hot path: dsa_index_topk then dsa_sparse_attention.  topk_idx may be
+/* The whole prefill hot path (summary page section 一: the indexer scores every causal pair,
+ * each token keeps its 2048 most relevant positions, and attention runs only among them; the
+ * prefill cost is quoted against full attention): dsa_index_topk then dsa_sparse_attention.
+ * Arguments as those two calls take them; out bf16 [T, Hq, d].  topk_idx may be
  * NULL (the workspace then holds the indices).  Between the two, the rows are ordered by the
  * key block most of their selection falls in, and the attention takes them in that order
  * (better cache reuse; the results are those of the natural order, bit for bit). */

@@ -87,7 +87,8 @@ def bench_prefill(name, steps, warmup, with_dense=True):
     torch.cuda.synchronize()
     log(f"{name}: resident in HBM (workspace {pb.ws.numel() / 2**30:.1f} GiB)")
     st = torch.cuda.current_stream()
-    ev = [timing_events(4) for _ in range(steps)]
+    nev = pb.timing_events()
+    ev = [timing_events(nev) for _ in range(steps)]
     for _ in range(warmup):
         pb.prefill()
     torch.cuda.synchronize()
@@ -98,10 +99,13 @@ def bench_prefill(name, steps, warmup, with_dense=True):
     end.record(st)
     torch.cuda.synchronize()
     total_ms = ms_between(start, end)
-    # per-stage: [0]=after schedule, [1]=after indexer, [2]=after top-k, [3]=after attention
-    idx_ms = [ms_between(e[0], e[1]) for e in ev]
-    topk_ms = [ms_between(e[1], e[2]) for e in ev]
-    attn_ms = [ms_between(e[2], e[3]) for e in ev]
+    # per-stage: [0] after the schedule; chunk c: [1 + 2c] after its indexer, [2 + 2c] after its
+    # top-k; [nev - 2] after the row order, [nev - 1] after the attention
+    nch = (nev - 3) // 2
+    idx_ms = [sum(ms_between(e[2 * c], e[2 * c + 1]) for c in range(nch)) for e in ev]
+    topk_ms = [sum(ms_between(e[2 * c + 1], e[2 * c + 2]) for c in range(nch)) + ms_between(e[nev - 3], e[nev - 2])
+               for e in ev]
+    attn_ms = [ms_between(e[nev - 2], e[nev - 1]) for e in ev]
     log(f"{name}: {total_ms / steps:.2f} ms/step  indexer {np.mean(idx_ms):.2f}  topk {np.mean(topk_ms):.2f}  "
         f"attention {np.mean(attn_ms):.2f}")
     res = dict(p=p, T=p.total_tokens, lengths=[int(x) for x in p.lengths], ms=total_ms / steps,
@@ -227,10 +231,11 @@ def bench_dedup(steps=3):
     pb = PrefillBatch(p)
     st = torch.cuda.current_stream()
     res = {}
+    nev = pb.timing_events()
     for mode in ("gather", "dedup"):
         runs = []
         for it in range(steps + 1):
-            ev = timing_events(4)
+            ev = timing_events(nev)
             a, = timing_events(1)
             a.record(st)
             if mode == "gather":
@@ -238,7 +243,7 @@ def bench_dedup(steps=3):
             else:
                 pb.prefill_dedup(events=ev)
             torch.cuda.synchronize()
-            runs.append([ms_between(a, ev[3]), ms_between(ev[2], ev[3])])
+            runs.append([ms_between(a, ev[nev - 1]), ms_between(ev[nev - 2], ev[nev - 1])])
         r = np.array(runs[1:]).mean(0)
         res[mode] = dict(ms=float(r[0]), attention_ms=float(r[1]))
     pb.sparse_attention_dedup(out=torch.empty_like(pb.out))

@@ -134,9 +134,16 @@ int dsa_prefill(const dsa_prefill_shape* shape, const void* q_idx, const void* k
                 uint16_t* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
                 void* stream);
 
-/* dsa_prefill that also records caller-created hipEvent_t events[0..3] on `stream` after the
- * work schedule, the indexer, the top-k (with the row ordering) and the attention kernels
- * (per-stage timing). */
+/* Number of timing events dsa_prefill_timed and dsa_prefill_dedup record: 3 + 2 n, where n is
+ * the number of indexer chunks (the indexer scores 256 blocks of 16 query rows at a time, longest
+ * blocks first, into a reusable buffer of 256 x 16 x max_seqlen scores, and the top-k selects
+ * each chunk's rows before the next chunk reuses it). */
+int dsa_prefill_timing_events(const dsa_prefill_shape* shape, int32_t* count);
+
+/* dsa_prefill that also records caller-created hipEvent_t events on `stream` (count from
+ * dsa_prefill_timing_events): events[0] after the work schedule; for chunk c, events[1 + 2c]
+ * after its indexer scores and events[2 + 2c] after its top-k; events[1 + 2n] after the row
+ * ordering, events[2 + 2n] after the attention (per-stage timing). */
 int dsa_prefill_timed(const dsa_prefill_shape* shape, const void* q_idx, const void* k_idx,
                       const float* w_idx, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       uint16_t* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,
@@ -160,7 +167,7 @@ int dsa_sparse_attention_dedup(const dsa_prefill_shape* shape, const uint16_t* q
                                void* dedup_workspace, size_t dedup_workspace_bytes, void* stream);
 
 /* dsa_prefill whose attention stage runs through the unions.  events (nullable): as
- * dsa_prefill_timed, 4 caller-created hipEvent_t recorded after each stage. */
+ * dsa_prefill_timed, caller-created hipEvent_t recorded after each stage as there. */
 int dsa_prefill_dedup(const dsa_prefill_shape* shape, const void* q_idx, const void* k_idx,
                       const float* w_idx, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       uint16_t* out, int32_t* topk_idx, void* workspace, size_t workspace_bytes,

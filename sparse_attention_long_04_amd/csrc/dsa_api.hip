@@ -12,15 +12,17 @@ namespace dsa {
 hipError_t launch_build_schedule(const int32_t* cu, int nseq, int bq, int nb_bound, int2* sched, int* count,
                                  int64_t* seqoff, hipStream_t st);
 hipError_t launch_indexer_prefill(bool fp8, int di, const void* q_idx, const void* k_idx, const float* w,
-                                  const int32_t* cu, int H, const int2* sched, const int* count, int nb_bound,
-                                  const int64_t* seqoff, float* scores, float2* rowrange, hipStream_t st);
-hipError_t launch_unpack_scores(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq, int64_t T,
-                                int ldo, float* out, hipStream_t st);
+                                  const int32_t* cu, int H, const int2* sched, const int* count, int n0, int nblocks,
+                                  const int64_t* seqoff, int64_t slot_stride, float* scores, float2* rowrange,
+                                  hipStream_t st);
+hipError_t launch_unpack_scores(const float* buf, int64_t slot_stride, const int2* sched, const int* count, int n0,
+                                int nblocks, const int32_t* cu, int ldo, float* out, hipStream_t st);
 hipError_t launch_indexer_decode(const void* q_idx, const float* w, const void* k_cache, const int32_t* cache_lens,
                                  int B, int cap, int max_len, int H, uint32_t* skeys, uint8_t* spos, int* wbase,
                                  uint16_t* wcnt, hipStream_t st);
-hipError_t launch_topk_prefill(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq, int64_t T, int K,
-                               const float2* rowrange, int32_t* out, hipStream_t st);
+hipError_t launch_topk_prefill(const float* buf, int64_t slot_stride, const int2* sched, const int* count, int n0,
+                               int nblocks, const int32_t* cu, int K, const float2* rowrange, int32_t* out,
+                               hipStream_t st);
 hipError_t launch_topk_decode(const uint32_t* skeys, const uint8_t* spos, const int32_t* cache_lens, int B,
                               int max_len, int K, const int* wbase, const uint16_t* wcnt, int blk_stride,
                               int32_t* out, hipStream_t st);
@@ -167,38 +169,61 @@ int check_prefill(const dsa_prefill_shape* s, bool need_indexer) {
 
 // Prefill workspace layout (all offsets 256-byte aligned):
 //   counts int[64] | seqoff int64[B+1] | sched16 int2[nb16] | sched128 int2[nb128] |
-//   rowrange float2[T] | scores float[score_floats] | topk int32[T*k]
+//   rowrange float2[T] | chunk buffer float[kChunkBlocks][slot_stride] | topk int32[T*k] |
+//   row order (signatures, counts, order) | V in fp16 (dense reference only)
+// The indexer scores its 16-row blocks (longest first, as the 16-row schedule orders them) in
+// chunks of kChunkBlocks blocks, one block per slot of the chunk buffer; the top-k then selects
+// the chunk's rows before the next chunk reuses the buffer.  A slot holds a block of the longest
+// rows (16 rows of max_seqlen rounded up to 16 scores), so the buffer is kChunkBlocks x 16 x
+// max_seqlen floats (2 GiB at 131072 tokens) whatever the batch holds.
+constexpr int kChunkBlocks = 256;  // one block per compute unit; consecutive blocks have near-equal work
+
 struct PrefillWs {
   size_t counts, seqoff, sched16, sched128, rowrange, scores, topk, osig, ocnt, order, v16, total;
-  int nb16, nb128;
-  int64_t score_floats;
+  int nb16, nb128, nchunks;
+  int64_t slot_stride, score_floats;
 };
 
-PrefillWs prefill_layout(const dsa_prefill_shape* s, const int32_t* cu_host) {
-  PrefillWs w{};
-  const int64_t T = s->total_tokens;
-  const int B = s->num_seqs;
-  int64_t nb16 = 0, nb128 = 0, sq = 0;
+// Floats of the whole score triangle (16-row blocks, block j of 16(j+1) scores per row): exact
+// from host lengths, else the bound for T tokens in sequences of at most max_seqlen.
+int64_t triangle_floats(const dsa_prefill_shape* s, const int32_t* cu_host) {
+  int64_t sq = 0;
   if (cu_host) {
-    for (int b = 0; b < B; ++b) {
-      const int64_t L = cu_host[b + 1] - cu_host[b];
-      const int64_t n16 = (L + 15) / 16;
-      nb16 += n16;
-      nb128 += (L + 127) / 128;
+    for (int b = 0; b < s->num_seqs; ++b) {
+      const int64_t n16 = (int64_t(cu_host[b + 1]) - cu_host[b] + 15) / 16;
       sq += n16 * (n16 + 1);
     }
   } else {
-    nb16 = (T + 15) / 16 + B;
-    nb128 = (T + 127) / 128 + B;
+    const int64_t nb16 = (s->total_tokens + 15) / 16 + s->num_seqs;
     const int64_t M = (int64_t(s->max_seqlen) + 15) / 16;
     if (M > 0) {
       const int64_t q = nb16 / M, rem = nb16 % M;
       sq = q * M * (M + 1) + rem * (rem + 1);
     }
   }
+  return 128 * sq;
+}
+
+PrefillWs prefill_layout(const dsa_prefill_shape* s, const int32_t* cu_host) {
+  PrefillWs w{};
+  const int64_t T = s->total_tokens;
+  const int B = s->num_seqs;
+  int64_t nb16 = 0, nb128 = 0;
+  if (cu_host) {
+    for (int b = 0; b < B; ++b) {
+      const int64_t L = cu_host[b + 1] - cu_host[b];
+      nb16 += (L + 15) / 16;
+      nb128 += (L + 127) / 128;
+    }
+  } else {
+    nb16 = (T + 15) / 16 + B;
+    nb128 = (T + 127) / 128 + B;
+  }
   w.nb16 = int(nb16);
   w.nb128 = int(nb128);
-  w.score_floats = 128 * sq;
+  w.nchunks = int((nb16 + kChunkBlocks - 1) / kChunkBlocks);
+  w.slot_stride = 16 * ((int64_t(s->max_seqlen) + 15) / 16 * 16);
+  w.score_floats = int64_t(kChunkBlocks) * w.slot_stride;
   size_t off = 0;
   w.counts = off; off = align_up(off + 64 * sizeof(int), 256);
   w.seqoff = off; off = align_up(off + size_t(B + 1) * sizeof(int64_t), 256);
@@ -220,16 +245,24 @@ PrefillWs prefill_layout(const dsa_prefill_shape* s, const int32_t* cu_host) {
 template <typename T>
 T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
 
-int run_index_scores_tri(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
-                         void* ws, const PrefillWs& L, hipStream_t st) {
-  hipError_t e = launch_build_schedule(s->cu_seqlens, s->num_seqs, 16, L.nb16, at<int2>(ws, L.sched16),
-                                       at<int>(ws, L.counts), at<int64_t>(ws, L.seqoff), st);
-  if (e != hipSuccess) return hip_status(e);
-  if (L.nb16 == 0) return DSA_OK;
-  e = launch_indexer_prefill(s->idx_dtype == DSA_IDX_FP8_E4M3, s->idx_dim, q_idx, k_idx, w_idx, s->cu_seqlens,
-                             s->idx_heads, at<int2>(ws, L.sched16), at<int>(ws, L.counts), L.nb16,
-                             at<int64_t>(ws, L.seqoff), at<float>(ws, L.scores), at<float2>(ws, L.rowrange), st);
-  return hip_status(e);
+// Indexer scores of chunk c (schedule entries c * kChunkBlocks ..) into the chunk buffer.
+hipError_t index_chunk(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
+                       void* ws, const PrefillWs& L, int c, hipStream_t st) {
+  return launch_indexer_prefill(s->idx_dtype == DSA_IDX_FP8_E4M3, s->idx_dim, q_idx, k_idx, w_idx, s->cu_seqlens,
+                                s->idx_heads, at<int2>(ws, L.sched16), at<int>(ws, L.counts), c * kChunkBlocks,
+                                kChunkBlocks, nullptr, L.slot_stride, at<float>(ws, L.scores),
+                                at<float2>(ws, L.rowrange), st);
+}
+
+hipError_t topk_chunk(const dsa_prefill_shape* s, void* ws, const PrefillWs& L, int c, int32_t* idx, hipStream_t st) {
+  return launch_topk_prefill(at<float>(ws, L.scores), L.slot_stride, at<int2>(ws, L.sched16), at<int>(ws, L.counts),
+                             c * kChunkBlocks, kChunkBlocks, s->cu_seqlens, s->topk, at<float2>(ws, L.rowrange), idx,
+                             st);
+}
+
+hipError_t build_schedule16(const dsa_prefill_shape* s, void* ws, const PrefillWs& L, hipStream_t st) {
+  return launch_build_schedule(s->cu_seqlens, s->num_seqs, 16, L.nb16, at<int2>(ws, L.sched16), at<int>(ws, L.counts),
+                               at<int64_t>(ws, L.seqoff), st);
 }
 
 // Dedup workspace layout (adjacent-query union per 16-row block; 256-byte aligned):
@@ -261,8 +294,9 @@ DedupWs dedup_layout(const dsa_prefill_shape* s) {
 //   counts[8..9] (as floats) the fp16 pre-scale of the gradient weights and its inverse.
 struct KlWs {
   PrefillWs base;
-  size_t P, lse, schedR, sched256, dkpart, wpart, total;
+  size_t tri, P, lse, schedR, sched256, dkpart, wpart, total;
   int R, nbR, nb256, slices;
+  int64_t tri_floats;
 };
 
 KlWs kl_layout(const dsa_prefill_shape* s) {
@@ -273,8 +307,12 @@ KlWs kl_layout(const dsa_prefill_shape* s) {
   w.nbR = int((T + w.R - 1) / w.R + s->num_seqs);
   w.nb256 = int((T + 255) / 256 + s->num_seqs);
   w.slices = kl_dk_slices(s->max_seqlen);
+  // the objective covers every causal pair: the indexer scores and the target distribution are
+  // both whole score triangles
+  w.tri_floats = triangle_floats(s, nullptr);
   size_t off = w.base.total;
-  w.P = off; off = align_up(off + size_t(w.base.score_floats) * sizeof(float), 256);
+  w.tri = off; off = align_up(off + size_t(w.tri_floats) * sizeof(float), 256);
+  w.P = off; off = align_up(off + size_t(w.tri_floats) * sizeof(float), 256);
   w.lse = off; off = align_up(off + size_t(T) * size_t(s->q_heads) * sizeof(float), 256);
   w.schedR = off; off = align_up(off + size_t(w.nbR) * sizeof(int2), 256);
   w.sched256 = off; off = align_up(off + size_t(w.nb256) * sizeof(int2), 256);
@@ -406,6 +444,14 @@ const char* dsa_status_string(int status) {
 
 int dsa_last_hip_error(void) { return g_last_hip_error; }
 
+int dsa_prefill_timing_events(const dsa_prefill_shape* s, int32_t* count) {
+  if (!count) return DSA_ERR_INVALID_ARGUMENT;
+  int rc = check_prefill(s, false);
+  if (rc) return rc;
+  *count = 3 + 2 * prefill_layout(s, nullptr).nchunks;
+  return DSA_OK;
+}
+
 int dsa_prefill_workspace_size(const dsa_prefill_shape* s, const int32_t* cu_seqlens_host, size_t* bytes) {
   if (!bytes) return DSA_ERR_INVALID_ARGUMENT;
   int rc = check_prefill(s, false);
@@ -428,9 +474,14 @@ int dsa_index_scores(const dsa_prefill_shape* s, const void* q_idx, const void* 
   PrefillWs L;
   if ((rc = check_prefill_ws(s, ws, ws_bytes, &L))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = run_index_scores_tri(s, q_idx, k_idx, w_idx, ws, L, st))) return rc;
-  return hip_status(launch_unpack_scores(at<float>(ws, L.scores), at<int64_t>(ws, L.seqoff), s->cu_seqlens,
-                                         s->num_seqs, s->total_tokens, s->max_seqlen, scores, st));
+  hipError_t e = build_schedule16(s, ws, L, st);
+  for (int c = 0; c < L.nchunks && e == hipSuccess; ++c) {
+    e = index_chunk(s, q_idx, k_idx, w_idx, ws, L, c, st);
+    if (e == hipSuccess)
+      e = launch_unpack_scores(at<float>(ws, L.scores), L.slot_stride, at<int2>(ws, L.sched16), at<int>(ws, L.counts),
+                               c * kChunkBlocks, kChunkBlocks, s->cu_seqlens, s->max_seqlen, scores, st);
+  }
+  return hip_status(e);
 }
 
 int dsa_index_topk(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
@@ -443,9 +494,12 @@ int dsa_index_topk(const dsa_prefill_shape* s, const void* q_idx, const void* k_
   PrefillWs L;
   if ((rc = check_prefill_ws(s, ws, ws_bytes, &L))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = run_index_scores_tri(s, q_idx, k_idx, w_idx, ws, L, st))) return rc;
-  return hip_status(launch_topk_prefill(at<float>(ws, L.scores), at<int64_t>(ws, L.seqoff), s->cu_seqlens,
-                                        s->num_seqs, s->total_tokens, s->topk, at<float2>(ws, L.rowrange), topk_idx, st));
+  hipError_t e = build_schedule16(s, ws, L, st);
+  for (int c = 0; c < L.nchunks && e == hipSuccess; ++c) {
+    e = index_chunk(s, q_idx, k_idx, w_idx, ws, L, c, st);
+    if (e == hipSuccess) e = topk_chunk(s, ws, L, c, topk_idx, st);
+  }
+  return hip_status(e);
 }
 
 int dsa_sparse_attention(const dsa_prefill_shape* s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -496,8 +550,11 @@ int prefill_impl(const dsa_prefill_shape* s, const void* q_idx, const void* k_id
   if (rc) return rc;
   DedupWs D{};
   if (dedup && s->total_tokens > 0 && (rc = check_dedup_ws(s, dws, dws_bytes, &D))) return rc;
+  // timing events (dsa_prefill_timed): [0] schedule, then per chunk c [1 + 2c] indexer and
+  // [2 + 2c] top-k, then [1 + 2n] row order and [2 + 2n] attention, n = the chunk count
+  const int nch = prefill_layout(s, nullptr).nchunks;
   if (s->total_tokens == 0) {  // empty batch: nothing to compute, pointers may be null
-    for (int i = 0; i < 4 && ev; ++i)
+    for (int i = 0; i < 3 + 2 * nch && ev; ++i)
       if ((rc = record(ev, i, static_cast<hipStream_t>(stream)))) return rc;
     return DSA_OK;
   }
@@ -509,20 +566,15 @@ int prefill_impl(const dsa_prefill_shape* s, const void* q_idx, const void* k_id
   if ((rc = check_prefill_ws(s, ws, ws_bytes, &L))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* idx = topk_idx ? topk_idx : at<int32_t>(ws, L.topk);
-  hipError_t e = launch_build_schedule(s->cu_seqlens, s->num_seqs, 16, L.nb16, at<int2>(ws, L.sched16),
-                                       at<int>(ws, L.counts), at<int64_t>(ws, L.seqoff), st);
+  hipError_t e = build_schedule16(s, ws, L, st);
   if (e != hipSuccess) return hip_status(e);
   if ((rc = record(ev, 0, st))) return rc;
-  if (L.nb16 > 0) {
-    e = launch_indexer_prefill(s->idx_dtype == DSA_IDX_FP8_E4M3, s->idx_dim, q_idx, k_idx, w_idx, s->cu_seqlens,
-                               s->idx_heads, at<int2>(ws, L.sched16), at<int>(ws, L.counts), L.nb16,
-                               at<int64_t>(ws, L.seqoff), at<float>(ws, L.scores), at<float2>(ws, L.rowrange), st);
-    if (e != hipSuccess) return hip_status(e);
+  for (int c = 0; c < L.nchunks; ++c) {
+    if ((rc = hip_status(index_chunk(s, q_idx, k_idx, w_idx, ws, L, c, st)))) return rc;
+    if ((rc = record(ev, 1 + 2 * c, st))) return rc;
+    if ((rc = hip_status(topk_chunk(s, ws, L, c, idx, st)))) return rc;
+    if ((rc = record(ev, 2 + 2 * c, st))) return rc;
   }
-  if ((rc = record(ev, 1, st))) return rc;
-  if ((rc = hip_status(launch_topk_prefill(at<float>(ws, L.scores), at<int64_t>(ws, L.seqoff), s->cu_seqlens,
-                                           s->num_seqs, s->total_tokens, s->topk, at<float2>(ws, L.rowrange), idx, st))))
-    return rc;
   // the gather takes rows in the order of their dominant key block (identity when the key
   // space is too large to sort); this post-processing of the selection counts to the top-k stage
   const int32_t* order = nullptr;
@@ -532,7 +584,7 @@ int prefill_impl(const dsa_prefill_shape* s, const void* q_idx, const void* k_id
       return rc;
     order = at<int32_t>(ws, L.order);
   }
-  if ((rc = record(ev, 2, st))) return rc;
+  if ((rc = record(ev, 1 + 2 * nch, st))) return rc;
   if (dedup) {
     if ((rc = dedup_attention(s, q, k, v, idx, out, at<int2>(ws, L.sched16), at<int>(ws, L.counts), L.nb16, dws, D,
                               st)))
@@ -543,7 +595,7 @@ int prefill_impl(const dsa_prefill_shape* s, const void* q_idx, const void* k_id
                                                  1, out, nullptr, nullptr, st, nullptr, order))))
       return rc;
   }
-  return record(ev, 3, st);
+  return record(ev, 2 + 2 * nch, st);
 }
 
 int decode_impl(const dsa_decode_shape* s, const void* q_idx, const float* w_idx, const uint16_t* q,
@@ -627,10 +679,10 @@ int dsa_indexer_kl(const dsa_prefill_shape* s, const void* q_idx, const void* k_
                                  nullptr, st)) != hipSuccess)
     return hip_status(e);
   const int64_t* seqoff = at<int64_t>(ws, L.seqoff);
-  float* scores = at<float>(ws, L.scores);
+  float* scores = at<float>(ws, K.tri);
   float* P = at<float>(ws, K.P);
   if ((e = launch_indexer_prefill(true, 128, q_idx, k_idx, w_idx, s->cu_seqlens, s->idx_heads,
-                                  at<int2>(ws, L.sched16), counts, L.nb16, seqoff, scores,
+                                  at<int2>(ws, L.sched16), counts, 0, L.nb16, seqoff, 0, scores,
                                   at<float2>(ws, L.rowrange), st)) != hipSuccess ||
       (e = launch_kl_lse(q, k, s->cu_seqlens, s->q_heads, s->kv_heads, s->softmax_scale, at<int2>(ws, L.sched128),
                          counts + 1, L.nb128, at<float>(ws, K.lse), st)) != hipSuccess ||

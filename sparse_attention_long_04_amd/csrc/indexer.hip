@@ -100,8 +100,9 @@ template <bool FP8, int DI, int HMAX, int NWAVES, int NT>
 __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
     const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ w_idx, const int32_t* __restrict__ cu, int H,
-    const int2* __restrict__ sched, const int* __restrict__ sched_count,
-    const int64_t* __restrict__ seqoff, float* __restrict__ scores, float2* __restrict__ rowrange) {
+    const int2* __restrict__ sched, const int* __restrict__ sched_count, int n0,
+    const int64_t* __restrict__ seqoff, int64_t slot_stride, float* __restrict__ scores,
+    float2* __restrict__ rowrange) {
   constexpr int ROWB = DI * (FP8 ? 1 : 2);   // bytes of one d_I row
   constexpr int UNITS = ROWB / 16;           // 16-byte units per row
   constexpr int CH = ROWB / 4;               // bytes per lane group
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   // in a pass, so rows t and t + 8 (same parity, same t & 7) need different units.
   auto swz = [](int t) { return UNITS == 8 ? ((t & 7) ^ ((t >> 3) & 1)) : (t & 15); };
 
-  const int n = blockIdx.x;
+  const int n = n0 + blockIdx.x;
   if (n >= *sched_count) return;
   const int2 e = sched[n];
   const int b = e.x, j = e.y;
@@ -249,7 +250,9 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int64_t stride = 16 * (int64_t)(j + 1);
-  float* __restrict__ sblk = scores + seqoff[b] + score_block_offset(j);
+  // the block's scores: in its sequence's triangle, or in slot blockIdx.x of a chunk buffer
+  float* __restrict__ sblk = seqoff ? scores + seqoff[b] + score_block_offset(j)
+                                    : scores + (int64_t)blockIdx.x * slot_stride;
   float rmin[4], rmax[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) { rmin[i] = __builtin_inff(); rmax[i] = -__builtin_inff(); }
@@ -426,15 +429,20 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   }
 }
 
-// Expand the score triangle into a dense [T, ldo] matrix with -inf outside the causal context.
-__global__ void unpack_scores_kernel(const float* __restrict__ tri, const int64_t* __restrict__ seqoff,
-                                     const int32_t* __restrict__ cu, int nseq, int ldo,
-                                     float* __restrict__ out) {
-  const int64_t t = blockIdx.x;
-  const int b = find_seq(cu, nseq, t);
-  const int i = int(t - cu[b]);
-  const int j = i >> 4;
-  const float* src = tri + seqoff[b] + score_block_offset(j) + (i & 15) * 16 * (int64_t)(j + 1);
+// Expand the rows of one chunk of 16-row blocks (slot c of the chunk buffer holds schedule entry
+// n0 + c, rows with a stride of 16(j+1) floats) into a dense [T, ldo] matrix, -inf outside the
+// causal context.  One workgroup per (slot, row).
+__global__ void unpack_scores_kernel(const float* __restrict__ buf, int64_t slot_stride,
+                                     const int2* __restrict__ sched, const int* __restrict__ sched_count,
+                                     int n0, const int32_t* __restrict__ cu, int ldo, float* __restrict__ out) {
+  const int slot = blockIdx.x >> 4, rr = blockIdx.x & 15;
+  const int n = n0 + slot;
+  if (n >= *sched_count) return;
+  const int2 e = sched[n];
+  const int b = e.x, j = e.y, i = 16 * j + rr;
+  if (i >= cu[b + 1] - cu[b]) return;
+  const int64_t t = cu[b] + i;
+  const float* src = buf + (int64_t)slot * slot_stride + (int64_t)rr * 16 * (j + 1);
   for (int s = threadIdx.x; s < ldo; s += blockDim.x)
     out[t * ldo + s] = (s <= i) ? src[s] : -__builtin_inff();
 }
@@ -601,27 +609,34 @@ hipError_t launch_build_schedule(const int32_t* cu, int nseq, int bq, int nb_bou
   return hipGetLastError();
 }
 
+// Triangle mode (seqoff != nullptr): every schedule entry, grid nb_bound, scores at seqoff[b] +
+// score_block_offset(j).  Chunk mode (seqoff == nullptr): entries n0 .. n0 + nblocks - 1, entry
+// n0 + c into slot c (slot_stride floats apart) of the buffer `scores`.
 hipError_t launch_indexer_prefill(bool fp8, int di, const void* q_idx, const void* k_idx,
                                   const float* w, const int32_t* cu, int H, const int2* sched,
-                                  const int* count, int nb_bound, const int64_t* seqoff,
-                                  float* scores, float2* rowrange, hipStream_t st) {
+                                  const int* count, int n0, int nblocks, const int64_t* seqoff,
+                                  int64_t slot_stride, float* scores, float2* rowrange, hipStream_t st) {
   const auto* q = static_cast<const uint8_t*>(q_idx);
   const auto* k = static_cast<const uint8_t*>(k_idx);
+  if (nblocks <= 0) return hipSuccess;
   if (fp8 && di == 128)
-    indexer_prefill_kernel<true, 128, 64, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores, rowrange);
+    indexer_prefill_kernel<true, 128, 64, 8, 4><<<nblocks, 512, 0, st>>>(q, k, w, cu, H, sched, count, n0, seqoff,
+                                                                        slot_stride, scores, rowrange);
   else if (!fp8 && di == 64)
-    indexer_prefill_kernel<false, 64, 64, 8, 4><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores, rowrange);
+    indexer_prefill_kernel<false, 64, 64, 8, 4><<<nblocks, 512, 0, st>>>(q, k, w, cu, H, sched, count, n0, seqoff,
+                                                                        slot_stride, scores, rowrange);
   else if (!fp8 && di == 128)
-    indexer_prefill_kernel<false, 128, 32, 8, 1><<<nb_bound, 512, 0, st>>>(q, k, w, cu, H, sched, count, seqoff, scores, rowrange);
+    indexer_prefill_kernel<false, 128, 32, 8, 1><<<nblocks, 512, 0, st>>>(q, k, w, cu, H, sched, count, n0, seqoff,
+                                                                         slot_stride, scores, rowrange);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_unpack_scores(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq,
-                                int64_t T, int ldo, float* out, hipStream_t st) {
-  if (T == 0) return hipSuccess;
-  unpack_scores_kernel<<<(unsigned)T, 256, 0, st>>>(tri, seqoff, cu, nseq, ldo, out);
+hipError_t launch_unpack_scores(const float* buf, int64_t slot_stride, const int2* sched, const int* count, int n0,
+                                int nblocks, const int32_t* cu, int ldo, float* out, hipStream_t st) {
+  if (nblocks <= 0) return hipSuccess;
+  unpack_scores_kernel<<<(unsigned)nblocks * 16, 256, 0, st>>>(buf, slot_stride, sched, count, n0, cu, ldo, out);
   return hipGetLastError();
 }
 

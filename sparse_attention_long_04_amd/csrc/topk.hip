@@ -651,16 +651,22 @@ __device__ void select_row(const float* __restrict__ row, int n, int K, float lo
   select_row_exact(row, n, K, lo, hi, out, sm);
 }
 
-// Prefill rows: one workgroup per token, longest rows first (row t = T-1-blockIdx.x).
+// Prefill rows of one chunk of 16-row blocks: slot c of the chunk buffer holds schedule entry
+// n0 + c (rows with a stride of 16(j+1) floats); one workgroup per (slot, row), in schedule order
+// (longest blocks first).
 __global__ __launch_bounds__(kTopkThreads) void topk_prefill_kernel(
-    const float* __restrict__ tri, const int64_t* __restrict__ seqoff, const int32_t* __restrict__ cu,
-    int nseq, int64_t T, int K, const float2* __restrict__ rowrange, int32_t* __restrict__ out) {
+    const float* __restrict__ buf, int64_t slot_stride, const int2* __restrict__ sched,
+    const int* __restrict__ sched_count, int n0, const int32_t* __restrict__ cu, int K,
+    const float2* __restrict__ rowrange, int32_t* __restrict__ out) {
   __shared__ TopkRowSmem sm;
-  const int64_t t = T - 1 - (int64_t)blockIdx.x;
-  const int b = find_seq(cu, nseq, t);
-  const int i = int(t - cu[b]);
-  const int j = i >> 4;
-  const float* row = tri + seqoff[b] + score_block_offset(j) + (i & 15) * 16 * (int64_t)(j + 1);
+  const int slot = blockIdx.x >> 4, rr = blockIdx.x & 15;
+  const int n = n0 + slot;
+  if (n >= *sched_count) return;
+  const int2 e = sched[n];
+  const int b = e.x, j = e.y, i = 16 * j + rr;
+  if (i >= cu[b + 1] - cu[b]) return;
+  const int64_t t = cu[b] + i;
+  const float* row = buf + (int64_t)slot * slot_stride + (int64_t)rr * 16 * (j + 1);
   const float2 rg = rowrange[t];
   select_row(row, i + 1, K, rg.x, rg.y, out + t * K, sm);
 }
@@ -1016,10 +1022,12 @@ hipError_t launch_topk_general(const float* scores, int64_t rows, int n, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_topk_prefill(const float* tri, const int64_t* seqoff, const int32_t* cu, int nseq,
-                               int64_t T, int K, const float2* rowrange, int32_t* out, hipStream_t st) {
-  if (T == 0) return hipSuccess;
-  topk_prefill_kernel<<<(unsigned)T, kTopkThreads, 0, st>>>(tri, seqoff, cu, nseq, T, K, rowrange, out);
+hipError_t launch_topk_prefill(const float* buf, int64_t slot_stride, const int2* sched, const int* count, int n0,
+                               int nblocks, const int32_t* cu, int K, const float2* rowrange, int32_t* out,
+                               hipStream_t st) {
+  if (nblocks <= 0) return hipSuccess;
+  topk_prefill_kernel<<<(unsigned)nblocks * 16, kTopkThreads, 0, st>>>(buf, slot_stride, sched, count, n0, cu, K,
+                                                                      rowrange, out);
   return hipGetLastError();
 }
 

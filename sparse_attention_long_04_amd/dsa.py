@@ -59,6 +59,7 @@ EXPORTS = {
     "dsa_decode": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
     "dsa_decode_noalloc": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 9, ctypes.c_int),
     "dense_decode_attention": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 5 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int),
+    "dsa_prefill_timing_events": ([ctypes.POINTER(PrefillShape), ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
     "dsa_prefill_timed": ([ctypes.POINTER(PrefillShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "dsa_decode_timed": ([ctypes.POINTER(DecodeShape)] + [ctypes.c_void_p] * 9 + [ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p], ctypes.c_int),
     "dsa_dedup_workspace_size": ([ctypes.POINTER(PrefillShape), ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
@@ -227,9 +228,24 @@ def _events(events):
     return arr
 
 
+def dsa_prefill_timing_events(shape) -> int:
+    """Events dsa_prefill_timed records: 3 + 2 x (indexer chunks)."""
+    n = ctypes.c_int32(0)
+    _check(lib().dsa_prefill_timing_events(ctypes.byref(shape), ctypes.byref(n)), "dsa_prefill_timing_events")
+    return n.value
+
+
+def _prefill_events(shape, events):
+    need = dsa_prefill_timing_events(shape)
+    if len(events) < need:
+        raise ValueError(f"the prefill records {need} timing events; {len(events)} given")
+    return _events(events)
+
+
 def dsa_prefill_timed(shape, q_idx, k_idx, w_idx, q, k, v, out, topk_idx, workspace, events, stream=None):
-    """``events``: 4 recorded-once torch.cuda.Event(enable_timing=True) (or raw hipEvent_t)."""
-    ev = _events(events)
+    """``events``: dsa_prefill_timing_events(shape) recorded-once torch.cuda.Event(enable_timing=True)
+    (or raw hipEvent_t)."""
+    ev = _prefill_events(shape, events)
     _check(lib().dsa_prefill_timed(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(k),
                                    _ptr(v), _ptr(out), _ptr(topk_idx), _ptr(workspace), _nbytes(workspace),
                                    _stream(stream), ev), "dsa_prefill_timed")
@@ -263,8 +279,9 @@ def dsa_sparse_attention_dedup(shape, q, k, v, topk_idx, out, dedup_workspace, s
 
 def dsa_prefill_dedup(shape, q_idx, k_idx, w_idx, q, k, v, out, topk_idx, workspace, dedup_workspace, events=None,
                       stream=None):
-    """``events``: None, or 4 recorded-once timing events (as dsa_prefill_timed)."""
-    ev = None if events is None else _events(events)
+    """``events``: None, or dsa_prefill_timing_events(shape) recorded-once timing events (as
+    dsa_prefill_timed)."""
+    ev = None if events is None else _prefill_events(shape, events)
     _check(lib().dsa_prefill_dedup(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(w_idx), _ptr(q), _ptr(k),
                                    _ptr(v), _ptr(out), _ptr(topk_idx), _ptr(workspace), _nbytes(workspace),
                                    _ptr(dedup_workspace), _nbytes(dedup_workspace), _stream(stream), ev),

@@ -49,6 +49,10 @@ class PrefillBatch:
         dsa.dsa_prefill(self.shape, self.q_idx, self.k_idx, self.w_idx, self.q, self.k, self.v, self.out,
                         self.topk_idx, self.ws, stream)
 
+    def timing_events(self):
+        """Events a timed prefill of this batch records (3 + 2 x indexer chunks)."""
+        return dsa.dsa_prefill_timing_events(self.shape)
+
     def prefill_timed(self, events, stream=None):
         dsa.dsa_prefill_timed(self.shape, self.q_idx, self.k_idx, self.w_idx, self.q, self.k, self.v, self.out,
                               self.topk_idx, self.ws, events, stream)

@@ -78,6 +78,31 @@ def test_varlen_256k_sampled():
 
 
 @pytest.mark.timeout(900)
+def test_prefill_single_256k_sequence_sampled():
+    """One 262144-token video-like sequence (the longest context the pages name): the indexer's
+    chunked score buffer (256 blocks of 16 rows x 262144 scores) keeps the workspace to a few GiB.
+    Rows: the first 256, the last 512, every 16th frame boundary and 256 seeded rows."""
+    L = 262144
+    p = workloads.make(workloads.P128K, lengths=[L])
+    pb = PrefillBatch(p)
+    ws_gib = pb.ws.numel() / 2**30
+    print(f"[full] single 256K sequence: workspace {ws_gib:.2f} GiB", flush=True)
+    assert ws_gib < 8
+    pb.prefill()
+    rng = np.random.default_rng(262)
+    rows = np.unique(np.concatenate([np.arange(256), np.arange(L - 512, L), np.arange(1024, L, 16 * 1024) - 1,
+                                     np.arange(1024, L, 16 * 1024), rng.integers(0, L, 256)]))
+    r = torch.from_numpy(rows).to(pb.topk_idx.device)
+    idx = pb.topk_idx[r].cpu().numpy()
+    out = bf16_to_float(pb.out[r])
+    del pb, p
+    torch.cuda.empty_cache()
+    bad, eo, _ = oracle_pool.check_prefill(workloads.P128K, rows, idx, out, lengths=[L], chunk=8)
+    assert not bad, f"index mismatch on {len(bad)} rows, first {bad[:10]}"
+    _assert_bars(eo, "single 256K sequence")
+
+
+@pytest.mark.timeout(900)
 def test_decode_16x128k_every_step():
     d = workloads.make(workloads.DECODE)
     st = DecodeState(d)

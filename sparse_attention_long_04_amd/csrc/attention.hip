@@ -30,9 +30,9 @@
 //   "keys 0..n-1" (dense decode).
 //
 // dense_prefill_kernel -- FlashAttention-style causal attention: a workgroup of 8 waves owns
-//   128 query tokens x 2 query heads of one KV group; 64-key K/V tiles are double-buffered in
-//   LDS and shared by both heads; S^T and O^T use 32x32x16 MFMAs (bf16 for QK, fp16 for PV,
-//   with V converted to fp16 once beforehand).
+//   128 query tokens x 2 query heads of one KV group; 64-key K and V^T tiles are copied straight
+//   into LDS rings and shared by both heads; S^T and O^T use 32x32x16 MFMAs (bf16 for QK, fp16
+//   for PV from a V^T copy in fp16 made once per call), software-pipelined over half tiles.
 #include "attn_tiles.h"
 
 namespace dsa {
@@ -406,170 +406,361 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
 
 // ------------------------------------------------------------------------------------------
 // Dense causal prefill (FlashAttention-style), head_dim 128.
-// Workgroup = 8 waves: 128 query tokens x 2 query heads of one KV group (waves 0-3 head 2p,
-// waves 4-7 head 2p+1, 32 tokens each), so every K/V tile staged in LDS serves both heads.
-// K/V tiles of 64 keys are double-buffered: the next tile is loaded into registers while the
-// current one is computed, then written to the other LDS buffer; one barrier per tile.
-// MFMA operand layouts and the kperm / transposed-read scheme: attn_tiles.h.
+// Workgroup = 128 query tokens x HW query heads of one KV group (HW = 2 when the group size is
+// even, else 1), 4 HW waves: wave w takes tokens 32(w%4) .. +31 of head w/4.
+//
+// K and V^T tiles of 64 keys are copied from global memory straight into LDS (one 16-byte unit
+// per lane and copy instruction), each in a ring of three stages; Q stays in registers.  V is
+// read from a fp16 V^T copy (dims x keys) made once per call, so the A operand of
+// O^T += V^T P^T comes from plain 16-byte LDS reads (transposing LDS reads move under half the
+// bytes per cycle).  A K row (one key) is 256 bytes with its 16-byte unit u at unit
+// u ^ dn_swz(row); a V^T row (one dim) is 128 bytes with unit u at u ^ ((row / 2) % 8).  Both
+// layouts keep every operand read free of LDS bank conflicts (16 lanes fetch the same unit of
+// 16 consecutive rows, which land on 16 distinct bank groups).
+//
+// Software pipeline over 32-key half tiles.  Iteration t runs two half steps; each issues 8 QK
+// MFMAs of the next half (S), 8 PV MFMAs of the previous half (O^T += V^T P^T) and the 16
+// exponentials of the current half (P = 2^(S scale - m), fp16, with per-lane row sums),
+// interleaved one MFMA and one exponential per step behind scheduling barriers, so the matrix
+// cores always have work that does not wait for the vector ALUs and the exponentials spread
+// over every MFMA:
+//   half step A: S(t, keys 32..63) | P(t, keys 0..31)  | O += V(t-1, 32..63) P(t-1, 32..63)
+//   half step B: S(t+1, keys 0..31) | P(t, keys 32..63) | O += V(t, 0..31) P(t, 0..31)
+// The reference m is lazy: it is set from tile 0's row maxima and moves only when some lane's
+// sum of P over a half tile exceeds 2^15 (which keeps every P inside fp16's range); that half's
+// scores are then recomputed from K(t), still in its stage, O (holding the halves before it) and
+// the row sums rescaled to the new maxima and its P redone.
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void dense_prefill_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+constexpr int kDnTileB = 64 * 256;    // one 64-key tile of K or V^T
+constexpr int kDnKst = 0;             // K stages at 0, 16K, 32K
+constexpr int kDnVst = 3 * kDnTileB;  // V^T stages at 48K, 64K, 80K
+constexpr int kDnLds = 6 * kDnTileB;  // 96 KB
+
+__device__ __forceinline__ int dn_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// First column of sequence b (first token cub) in the V^T rows: round64(cu[b]) + 128 b -- 64-column
+// aligned, so 8-key units are 16-byte aligned, and at least 64 columns past the previous
+// sequence's last token; those 64 columns are zeros, so a key tile that runs past a sequence's
+// end reads zeros, never another sequence's values.
+__device__ __host__ __forceinline__ int64_t dn_vt_base(int64_t cub, int b) {
+  return (cub + 63) / 64 * 64 + 128 * int64_t(b);
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// 16 bytes per lane from global memory (base + off, base wave-uniform) to LDS address
+// lds_addr + 16 * lane (lds_addr wave-uniform).  Issued from asm so that the compiler's own
+// wait counting leaves it alone (for some LDS reads it would otherwise wait for every copy in
+// flight); the kernel waits for these copies itself, in dn_sync, before a stage is read.  M0
+// (the copy's LDS address) is saved and restored around it.
+__device__ __forceinline__ void dn_copy16(const void* base, uint32_t off, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(lds_addr)
+      : "memory");
+}
+
+// Workgroup barrier after every tile copy of the wave has landed in LDS (s_waitcnt vmcnt(0)
+// lgkmcnt(0)).  The compiler fences keep LDS accesses on their side of the barrier.
+__device__ __forceinline__ void dn_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int I>
+using dn_ic = std::integral_constant<int, I>;
+
+__device__ __forceinline__ i32x4 dn_ld128(const lds_u8* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(p);
+}
+
+template <int HW>
+__global__ __launch_bounds__(256 * HW) void dense_prefill_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt, int64_t tpad,
     const int32_t* __restrict__ cu, int Hq, int Hkv, float scale_log2, const int2* __restrict__ sched,
-    const int* __restrict__ sched_count, int pair, uint16_t* __restrict__ out) {
-  constexpr int D = 128, BM = 128, BN = 64;
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2][2][kKvTileB];  // [buffer][K=0/V=1]
+    const int* __restrict__ sched_count, uint16_t* __restrict__ out) {
+  constexpr int D = 128, BM = 128, BN = 64, NW = 4 * HW;
+  constexpr int CPW = 16 / NW;  // 1 KB copies per wave and tile
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kDnLds];
   const int n = blockIdx.x;
   if (n >= *sched_count) return;
   const int2 e = sched[n];
   const int b = e.x, j = e.y;
   const int G = Hq / Hkv;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  // pair != 0: waves 0-3 take head 2y, waves 4-7 head 2y+1 (same KV head since G is even);
-  // pair == 0 (odd G): one head per workgroup, waves 4-7 only help stage the tiles
-  const int h = pair ? 2 * blockIdx.y + (w >> 2) : blockIdx.y;
-  const bool active = pair || w < 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = HW * blockIdx.y + (w >> 2);  // the wave's head (the workgroup's heads share a KV head)
   const int g = h / G;
   const int64_t seq0 = cu[b];
   const int L = cu[b + 1] - cu[b];
   const int q0 = BM * j;
-  const int rows = min(BM, L - q0);
-  const int kend = q0 + rows;
+  const int kend = min(q0 + BM, L);     // keys 0 .. kend-1: the block's last query is kend-1
+  const int nt = (kend + BN - 1) / BN;  // key tiles of the workgroup
   const int qc = lane & 31, hf = lane >> 5;
   const int64_t kvs = (int64_t)Hkv * D;
-  const int my_q = q0 + 32 * (w & 3) + qc;
+  const int wq0 = q0 + 32 * (w & 3);                        // the wave's first query
+  const int my_q = min(wq0 + qc, kend - 1);                 // lanes past the end repeat the last
+  const int wlast = (wq0 < kend) ? (wq0 + 31) / BN : -1;    // the wave's last tile
+  lds_u8* const lb = (lds_u8*)lds;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lb;
 
+  // Q (B operand of S^T = K Q^T) in registers: lane (qc, hf) holds dims 16 s2 + 8 hf .. +7
   i32x4 qf[8];
   {
-    const int qq = min(my_q, kend - 1);
-    const uint16_t* qp = q + ((seq0 + qq) * Hq + h) * D + 8 * hf;
+    const uint16_t* qp = q + ((seq0 + my_q) * Hq + h) * D + 8 * hf;
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2) qf[s2] = *reinterpret_cast<const i32x4*>(qp + 16 * s2);
   }
+
+  // K tile copy: this wave fills rows 4 CPW w + 4x + lane/16 (x < CPW) of a stage, one unit per
+  // lane (keys past the block's end repeat its last key; their scores are masked).  Byte offsets
+  // from the sequence's first row fit 32 bits (the launcher checks the K/V size).
+  const int dr = 4 * CPW * w + (lane >> 4);
+  const uint32_t rowb = uint32_t(kvs) * 2;
+  const uint16_t* const kg = k + seq0 * kvs + g * D;
+  auto copy_k = [&](int stage, int tile) {
+    const uint32_t dst = lds0 + kDnKst + stage * kDnTileB + 1024 * CPW * w;
+#pragma unroll
+    for (int x = 0; x < CPW; ++x) {
+      const uint32_t r = min(tile * BN + dr + 4 * x, kend - 1);
+      dn_copy16(kg, r * rowb + 16 * ((lane & 15) ^ dn_swz(dr + 4 * x)), dst + 1024 * x);
+    }
+  };
+  // V^T tile: 128 rows (dims) of 64 keys = 128 bytes; this wave fills rows 8(CPW w + x) + lane/8.
+  // Its keys are the columns dn_vt_base(b) + 64 tile .. of the V^T rows (zeros past the sequence).
+  const uint16_t* const vg = vt + (int64_t)g * 128 * tpad + dn_vt_base(seq0, b);
+  const uint32_t vrowb = uint32_t(tpad) * 2;
+  auto copy_v = [&](int stage, int tile) {
+    const uint32_t dst = lds0 + kDnVst + stage * kDnTileB + 1024 * CPW * w;
+#pragma unroll
+    for (int x = 0; x < CPW; ++x) {
+      const int d = 8 * (CPW * w + x) + (lane >> 3);
+      dn_copy16(vg, d * vrowb + uint32_t(tile * BN) * 2 + 16 * ((lane & 7) ^ ((d >> 1) & 7)), dst + 1024 * x);
+    }
+  };
+
+  // LDS operand addresses.  K: row kperm(qc) (+32 for keys 32..63), unit 2 s2 + hf, i.e. byte
+  // kbase ^ 32 s2 with kbase = that row's unit-hf address.  V^T: row (dim) 32 db + qc, unit
+  // 2 kq + hf (keys 16 kq + 8 hf ..), i.e. byte (vbase ^ 32 kq) + 4096 db.  Stage offsets are
+  // added once per half step; half-tile and dim-block offsets are immediates.
+  int kbase, vbase;
+  {
+    const int row = kperm(qc);
+    kbase = kDnKst + 256 * row + 16 * (hf ^ dn_swz(row));
+    const int sw = (qc >> 1) & 7;
+    vbase = kDnVst + 128 * qc + 32 * (sw >> 1) + 16 * (hf ^ (sw & 1));
+  }
+
+  // S^T of one half tile (keys 32 hb ..) of the tile in K stage ks
+  auto qk_half = [&](f32x16& s, int ks, int hb) {
+    const int kb = kbase + ks * kDnTileB + 8192 * hb;
+    s = (f32x16){};
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) s = mfma_bf16_32x32x16(dn_ld128(lb + (kb ^ (32 * s2))), qf[s2], s);
+  };
+  // P = fp16 of 2^(s scale - m): p[kk2] packs registers 8 kk2 .. 8 kk2 + 7 (8 consecutive keys,
+  // the B operand of one PV k-step).  Returns the lane's sum of the fp16 P.
+  const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+  auto expo = [&](const f32x16& s, i32x4 (&p)[2], float m) -> float {
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_exp2f(fmaf(s[8 * kk2 + i], scale_log2, -m));
+      const i32x4 pk = pack_f16x8(x);
+      p[kk2] = pk;
+      ps0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[0]), one, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[1]), one, ps1, false);
+      ps0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[2]), one, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk[3]), one, ps1, false);
+    }
+    return ps0 + ps1;
+  };
+  // row maxima of raw scores (both lane halves of a query column), in log2 units
+  auto rowmax = [&](const f32x16& s) -> float {
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[i]);
+    return fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
+  };
+  // causal mask of half hb of tile t: keys past the lane's query.  Register i holds key
+  // 64t + 32hb + 8hf + c(i), c(i) = 16(i/8) + 4((i/4)%2) + i%4 (the kperm row order).
+  auto mask = [&](f32x16& s, int t, int hb) {
+    const int lim = my_q - BN * t - 32 * hb - 8 * hf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
+      if (c > lim) s[i] = -__builtin_inff();
+    }
+  };
+
+  // ---- prologue: Q, K(0), K(1), V(0) land; V stage 2 holds the pipeline's tile -1 (zeros, with
+  // P(-1) = 0); S(0, keys 0..31) and the reference maxima from all of tile 0
+  copy_k(0, 0);
+  if (nt > 1) copy_k(1, 1);
+  copy_v(0, 0);
+  {
+    i32x4* z = reinterpret_cast<i32x4*>(lds + kDnVst + 2 * kDnTileB) + CPW * tid;
+#pragma unroll
+    for (int x = 0; x < CPW; ++x) z[x] = (i32x4){0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < 8; ++s2) asm volatile("" : "+v"(qf[s2]));  // Q has landed
+  dn_sync();
+
   f32x16 o[4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db) o[db] = (f32x16){};
+  f32x16 sa, sb;       // scores: sa = S(t, keys 0..31), sb = S(t, keys 32..63)
+  i32x4 pa[2], pb[2];  // probabilities: pa = P(t, keys 0..31), pb = P(t-1 or t, keys 32..63)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m_run = -__builtin_inff(), l_run = 0.f;
-  const int wave_qmax = q0 + 32 * (w & 3) + 31;
-
-  // tile loader: 512 threads x (2 K + 2 V) 16-byte units = 64 keys x 256 B each
-  i32x4 pre[4];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int u = tid + 512 * x;  // unit 0..1023: key = u >> 4, 16-byte column c = u & 15
-      const int kk = min(kt + (u >> 4), kend - 1);
-      pre[x] = *reinterpret_cast<const i32x4*>(k + (seq0 + kk) * kvs + g * D + 8 * (u & 15));
-      pre[2 + x] = *reinterpret_cast<const i32x4*>(v + (seq0 + kk) * kvs + g * D + 8 * (u & 15));
+  for (int x = 0; x < 2; ++x) pb[x] = (i32x4){0, 0, 0, 0};
+  float m_ref = 0.f, l_run = 0.f;
+  if (wlast >= 0) {
+    qk_half(sa, 0, 0);
+    qk_half(sb, 0, 1);
+    if (wlast == 0) {
+      mask(sa, 0, 0);
+      mask(sb, 0, 1);
     }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int u = tid + 512 * x;
-      const int off = kv_off(u >> 4, 16 * (u & 15));
-      *reinterpret_cast<i32x4*>(&kv_lds[buf][0][off]) = pre[x];
-      *reinterpret_cast<i32x4*>(&kv_lds[buf][1][off]) = pre[2 + x];  // V already fp16
-    }
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  int buf = 0;
-  for (int kt = 0; kt < kend; kt += BN) {
-    const bool more = kt + BN < kend;
-    if (more) gload(kt + BN);
-    if (active && kt <= wave_qmax) {
-      const uint8_t* kl = kv_lds[buf][0];
-      const uint8_t* vl = kv_lds[buf][1];
-      // S^T for two 32-key blocks
-      f32x16 sacc[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[rb][i] = 0.f;
-        const int key = 32 * rb + kperm(qc);
-#pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2)
-          sacc[rb] = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(kl + kv_off(key, 32 * s2 + 16 * hf)), qf[s2],
-                                        sacc[rb]);
-      }
-      // mask + scale; C row (reg i, half hf) of block rb <-> key kt + 32rb + kperm(8(i/4)+4hf+i%4).
-      // Tiles wholly before the wave's first query need no mask (all but the last one or two).
-      // The max is taken on the raw scores (the scale is positive) and the scale applied once
-      // per element inside the exponent's fma.
-      float z[2][16];
-      float mt = -__builtin_inff();
-      if (kt + BN - 1 <= q0 + 32 * (w & 3)) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            z[rb][i] = sacc[rb][i];
-            mt = fmaxf(mt, z[rb][i]);
-          }
-      } else {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kt + 32 * rb + kperm(8 * (i >> 2) + 4 * hf + (i & 3));
-            const float zz = (key <= my_q) ? sacc[rb][i] : -__builtin_inff();
-            z[rb][i] = zz;
-            mt = fmaxf(mt, zz);
-          }
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
-      // lazy reference max: it moves only when the query's tile max passes it by more than 8
-      // (log2 units), so P <= 2^8 (exact enough in fp16) and the O rescale -- a round trip of
-      // the accumulators through VALU -- happens on few tiles
-      const bool move = mt > m_run + 8.f;  // false while every key so far is masked
-      if (__ballot(move)) {
-        const float alpha = move ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;  // m_run = -inf: 0
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] *= alpha;
-        m_run = move ? mt : m_run;
-      }
-      const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
-      float ps = 0.f;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(z[rb][i], scale_log2, -m_use));
-          z[rb][i] = pv;
-          ps += pv;
-        }
-      l_run += ps;
-      // O^T += V^T P^T; k-step (rb, kk2) covers keys 32rb + 16kk2 + 0..15 = registers 8kk2..8kk2+7
-      const int grp = lane >> 4, jj = lane & 15;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int kk2 = 0; kk2 < 2; ++kk2) {
-          const i32x4 pf = pack_f16x8(&z[rb][8 * kk2]);
-          const int key_a = 32 * rb + 16 * kk2 + 8 * (grp >> 1) + (jj >> 2);
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const int dim0 = 32 * db + 16 * (grp & 1) + 4 * (jj & 3);
-            const s16x4 lo = lds_tr16(vl + kv_off(key_a, 2 * dim0));
-            const s16x4 hi = lds_tr16(vl + kv_off(key_a + 4, 2 * dim0));
-            const i32x4 a = __builtin_bit_cast(i32x4, (s16x8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-            o[db] = mfma_f16_32x32x16(a, pf, o[db]);
-          }
-        }
-    }
-    if (more) lstore(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+    const float mt = fmaxf(rowmax(sa), rowmax(sb));
+    m_ref = (mt == -__builtin_inff()) ? 0.f : mt;
   }
-  float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!active || my_q >= kend) return;
-  const float inv = 1.f / l_tot;
-  uint16_t* op = out + ((seq0 + my_q) * Hq + h) * D;
+
+  // One half step: 8 QK MFMAs into sn (K stage ks, keys 32 kh ..), 8 PV MFMAs with P = pv (V^T
+  // stage vs, keys 32 vh ..), 16 exponentials of sc into pn with their row sums.  Operand reads
+  // run two MFMAs of their kind ahead; packing and the row-sum term of element pair p come two
+  // steps after its second exponential.
+  auto half = [&](f32x16& sn, int ks, int kh, const i32x4 (&pv)[2], int vs, int vh, const f32x16& sc,
+                  i32x4 (&pn)[2]) -> float {
+    const int kb = kbase + ks * kDnTileB + 8192 * kh;      // K rows 32 kh ..
+    const int vb = (vbase + vs * kDnTileB) ^ (64 * vh);    // V^T units 4 vh .. (keys 32 vh ..)
+    __builtin_amdgcn_sched_barrier(0);
+    i32x4 kop[8], vop[8];
+    auto kread = [&](auto ii) {
+      constexpr int i = decltype(ii)::value;
+      kop[i] = dn_ld128(lb + (kb ^ (32 * i)));
+    };
+    auto vread = [&](auto ii) {  // PV MFMA i: k-step i/4 of the half, O block i%4
+      constexpr int i = decltype(ii)::value;
+      vop[i] = dn_ld128(lb + (vb ^ (32 * (i >> 2))) + 4096 * (i & 3));
+    };
+    kread(dn_ic<0>{});
+    vread(dn_ic<0>{});
+    kread(dn_ic<1>{});
+    vread(dn_ic<1>{});
+    float ps0 = 0.f, ps1 = 0.f, xe[4];
+    auto pack = [&](auto pi) {  // fp16 pair of elements 2p, 2p+1 into pn, and its row-sum term
+      constexpr int pr = decltype(pi)::value;
+      const f16x2 h2 = {(_Float16)xe[2 * (pr & 1)], (_Float16)xe[2 * (pr & 1) + 1]};
+      pn[pr >> 2][pr & 3] = __builtin_bit_cast(int, h2);
+      if constexpr (pr & 1) ps1 = __builtin_amdgcn_fdot2(h2, one, ps1, false);
+      else ps0 = __builtin_amdgcn_fdot2(h2, one, ps0, false);
+    };
+    auto step = [&](auto jj) {
+      constexpr int jx = decltype(jj)::value, i = jx >> 1;
+      if constexpr ((jx & 1) == 0) {
+        if constexpr (i + 2 < 8) kread(dn_ic<i + 2>{});
+        if constexpr (i == 0) sn = mfma_bf16_32x32x16(kop[0], qf[0], (f32x16){});
+        else sn = mfma_bf16_32x32x16(kop[i], qf[i], sn);
+      } else {
+        if constexpr (i + 2 < 8) vread(dn_ic<i + 2>{});
+        o[i & 3] = mfma_f16_32x32x16(vop[i], pv[i >> 2], o[i & 3]);
+      }
+      if constexpr ((jx & 1) == 0 && jx >= 4) pack(dn_ic<(jx >> 1) - 2>{});  // frees slot jx % 4
+      xe[jx & 3] = __builtin_amdgcn_exp2f(fmaf(sc[jx], scale_log2, -m_ref));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    step(dn_ic<0>{});
+    step(dn_ic<1>{});
+    step(dn_ic<2>{});
+    step(dn_ic<3>{});
+    step(dn_ic<4>{});
+    step(dn_ic<5>{});
+    step(dn_ic<6>{});
+    step(dn_ic<7>{});
+    step(dn_ic<8>{});
+    step(dn_ic<9>{});
+    step(dn_ic<10>{});
+    step(dn_ic<11>{});
+    step(dn_ic<12>{});
+    step(dn_ic<13>{});
+    step(dn_ic<14>{});
+    step(dn_ic<15>{});
+    pack(dn_ic<6>{});
+    pack(dn_ic<7>{});
+    return ps0 + ps1;
+  };
+  // lazy-reference check of the half just exponentiated (keys 32 hb .. of tile t, K stage ks)
+  auto settle = [&](float ps, int t, int ks, int hb, i32x4 (&p)[2]) {
+    if (__builtin_amdgcn_ballot_w64(!(ps <= 32768.f))) {
+      // some P would leave fp16's range: recompute the half's scores, move the reference to the
+      // row maxima, rescale O and l, redo its P
+      f32x16 sr;
+      qk_half(sr, ks, hb);
+      if (t == wlast) mask(sr, t, hb);
+      const float m_new = fmaxf(m_ref, rowmax(sr));
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      l_run *= alpha;
+      m_ref = m_new;
+      ps = expo(sr, p, m_ref);
+    }
+    l_run += ps;
+  };
+  auto next3 = [](int x) { return x == 2 ? 0 : x + 1; };
+  auto prev3 = [](int x) { return x == 0 ? 2 : x - 1; };
+  // Iteration t (stage s = t % 3 of both rings): copies K(t+2) and V(t+1) into stage (t+2)%3 and
+  // (t+1)%3, reads K(t), K(t+1), V(t-1), V(t); the barrier ending iteration t-1 has released both
+  // stages written here.
+  auto copies = [&](int t, int st) {
+    if (t + 2 < nt) copy_k(prev3(st), t + 2);
+    if (t + 1 < nt) copy_v(next3(st), t + 1);
+  };
+  int t = 0, st = 0;
+  if (wlast >= 0) {
+    for (; t <= wlast; ++t) {
+      copies(t, st);
+      if (t == wlast && t > 0) mask(sa, t, 0);
+      // A: S(t, 32..63) | P(t, 0..31) | V(t-1, 32..63) P(t-1, 32..63)
+      float ps = half(sb, st, 1, pb, prev3(st), 1, sa, pa);
+      settle(ps, t, st, 0, pa);
+      if (t == wlast) mask(sb, t, 1);
+      // B: S(t+1, 0..31) | P(t, 32..63) | V(t, 0..31) P(t, 0..31)
+      ps = half(sa, next3(st), 0, pa, st, 0, sb, pb);
+      settle(ps, t, st, 1, pb);
+      dn_sync();  // K(t+2) and V(t+1) have landed
+      st = next3(st);
+    }
+    // iteration wlast + 1: the last half's P.V only
+    copies(t, st);
+    {
+      const int vb = (vbase + prev3(st) * kDnTileB) ^ 64;  // keys 32..63
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        o[i & 3] = mfma_f16_32x32x16(dn_ld128(lb + (vb ^ (32 * (i >> 2))) + 4096 * (i & 3)), pb[i >> 2], o[i & 3]);
+    }
+    dn_sync();
+    st = next3(st);
+    ++t;
+  }
+  // the workgroup's remaining iterations: copies and barriers only
+  for (; t <= nt; ++t) {
+    copies(t, st);
+    dn_sync();
+    st = next3(st);
+  }
+
+  if (wlast < 0 || wq0 + qc >= kend) return;
+  const float inv = 1.f / (l_run + __shfl_xor(l_run, 32));
+  uint16_t* op = out + ((seq0 + wq0 + qc) * Hq + h) * D;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -625,30 +816,86 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
   return hipGetLastError();
 }
 
-// V converted to fp16 once (exact for bf16 values in fp16's normal range) for the fp16 P.V MFMA
-// of the dense kernel, instead of once per staging workgroup (each key's V is staged by every
-// later 128-query block of its sequence).
-__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* __restrict__ in,
-                                                          uint16_t* __restrict__ out, int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const i32x4 x = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(in) + i);
-  float f[8];
+// V^T in fp16 for the dense kernel's P.V MFMA, written once (exact for bf16 values in fp16's
+// normal range) instead of by every workgroup that stages a key: vt[g][d][c] for KV head g and
+// dim d, rows of tpad columns, sequence b from column dn_vt_base(b) (see there).
+
+// One workgroup per 128-token block (b, j) of the dense schedule and KV head: two 64-token
+// halves transposed through LDS.
+__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ v, const int32_t* __restrict__ cu,
+                                                          const int2* __restrict__ sched, const int* __restrict__ count,
+                                                          int Hkv, int64_t tpad, uint16_t* __restrict__ vt) {
+  __shared__ uint16_t tile[128][64 + 2];  // [dim][token], padded against bank conflicts
+  if ((int)blockIdx.x >= *count) return;
+  const int2 e = sched[blockIdx.x];
+  const int b = e.x, g = blockIdx.y, tid = threadIdx.x;
+  const int64_t seq0 = cu[b];
+  const int L = cu[b + 1] - cu[b];
+  uint16_t* const rows = vt + (int64_t)g * 128 * tpad + dn_vt_base(seq0, b);
+  for (int half = 0; half < 2; ++half) {
+    const int i0 = 128 * e.y + 64 * half;  // first token of the half, relative to the sequence
+    if (i0 >= L) break;
+    if (half) __syncthreads();
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = bf16_to_f32(bf16_lane(x, e));
-  reinterpret_cast<i32x4*>(out)[i] = pack_f16x8(f);
+    for (int x = 0; x < 4; ++x) {
+      const int u = tid + 256 * x, tt = u >> 4, d0 = 8 * (u & 15);  // token i0+tt, dims d0 .. d0+7
+      float f[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (i0 + tt < L) {
+        const i32x4 a =
+            __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(v + ((seq0 + i0 + tt) * Hkv + g) * 128 + d0));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f[k] = bf16_to_f32(bf16_lane(a, k));
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) tile[d0 + k][tt] = __builtin_bit_cast(uint16_t, (_Float16)f[k]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int u = tid + 256 * x, d = u >> 3, c = 8 * (u & 7);  // dim d, tokens i0+c .. i0+c+7
+      if (i0 + c >= L) continue;
+      i32x4 w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = int(uint32_t(tile[d][c + 2 * k]) | (uint32_t(tile[d][c + 2 * k + 1]) << 16));
+      *reinterpret_cast<i32x4*>(rows + (int64_t)d * tpad + i0 + c) = w;  // columns past L: zeros
+    }
+  }
 }
 
-// v16: T * Hkv * 128 halves of scratch for V in fp16.
-hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* v16, int64_t T,
-                                const int32_t* cu, int Hq, int Hkv, float scale, const int2* sched, const int* count,
-                                int nb_bound, uint16_t* out, hipStream_t st) {
+// The 64 zero columns after each sequence (columns L .. L+63 past its base; the transpose
+// already wrote zeros up to the next multiple of 8), for every (KV head, dim) row.
+__global__ __launch_bounds__(256) void v_pad_zero_kernel(const int32_t* __restrict__ cu, int nseq, int Hkv, int64_t tpad,
+                                                         uint16_t* __restrict__ vt) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (sequence, row, column 0..63)
+  const int64_t rows = (int64_t)Hkv * 128;
+  if (i >= nseq * rows * 64) return;
+  const int b = int(i / (rows * 64));
+  const int64_t r = (i / 64) % rows;
+  const int col = int(i & 63);
+  vt[r * tpad + dn_vt_base(cu[b], b) + (cu[b + 1] - cu[b]) + col] = 0;
+}
+
+// Columns of the V^T rows for T tokens in nseq sequences: the last sequence ends before
+// round64(T) + 128 nseq + 64.
+int64_t dense_vt_cols(int64_t T, int nseq) { return (T + 63) / 64 * 64 + 128 * (int64_t(nseq) + 1); }
+
+// vt: Hkv * 128 * dense_vt_cols(T, nseq) halves of scratch for V^T in fp16.
+hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* vt, int64_t T,
+                                const int32_t* cu, int nseq, int Hq, int Hkv, float scale, const int2* sched,
+                                const int* count, int nb_bound, uint16_t* out, hipStream_t st) {
   if (nb_bound == 0) return hipSuccess;
-  const int64_t n8 = T * Hkv * 128 / 8;
-  bf16_to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(v, v16, n8);
-  const int pair = ((Hq / Hkv) % 2 == 0) ? 1 : 0;
-  dense_prefill_kernel<<<dim3(nb_bound, pair ? Hq / 2 : Hq), 512, 0, st>>>(
-      q, k, v16, cu, Hq, Hkv, scale * 1.4426950408889634f, sched, count, pair, out);
+  const int64_t tpad = dense_vt_cols(T, nseq);
+  // 32-bit copy offsets within a KV head's K rows and V^T rows
+  if ((uint64_t)T * Hkv * 128 * 2 > 0xFFFFFFFFull || (uint64_t)tpad * 128 * 2 > 0xFFFFFFFFull)
+    return hipErrorInvalidValue;
+  v_transpose_kernel<<<dim3(nb_bound, Hkv), 256, 0, st>>>(v, cu, sched, count, Hkv, tpad, vt);
+  const int64_t pads = (int64_t)nseq * Hkv * 128 * 64;
+  v_pad_zero_kernel<<<(unsigned)((pads + 255) / 256), 256, 0, st>>>(cu, nseq, Hkv, tpad, vt);
+  const float sl2 = scale * 1.4426950408889634f;
+  if ((Hq / Hkv) % 2 == 0)
+    dense_prefill_kernel<2><<<dim3(nb_bound, Hq / 2), 512, 0, st>>>(q, k, vt, tpad, cu, Hq, Hkv, sl2, sched, count, out);
+  else
+    dense_prefill_kernel<1><<<dim3(nb_bound, Hq), 256, 0, st>>>(q, k, vt, tpad, cu, Hq, Hkv, sl2, sched, count, out);
   return hipGetLastError();
 }
 

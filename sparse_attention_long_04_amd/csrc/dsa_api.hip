@@ -71,10 +71,10 @@ hipError_t launch_sparse_dkv(const uint16_t* q, const uint16_t* k, const uint16_
                              hipStream_t st);
 hipError_t launch_topk_general(const float* scores, int64_t rows, int n, int64_t ld, const int32_t* lens, int K,
                                int32_t* out, hipStream_t st);
-hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* v16, int64_t T,
-                                const int32_t* cu, int Hq,
-                                int Hkv, float scale, const int2* sched, const int* count, int nb_bound,
-                                uint16_t* out, hipStream_t st);
+int64_t dense_vt_cols(int64_t T, int nseq);
+hipError_t launch_dense_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* vt, int64_t T,
+                                const int32_t* cu, int nseq, int Hq, int Hkv, float scale, const int2* sched,
+                                const int* count, int nb_bound, uint16_t* out, hipStream_t st);
 
 // Copy one new token per sequence into the caches at row lens[b] and count it (lens[b] += 1);
 // a full cache (lens[b] >= cap) is left untouched.  Rows are moved in 16-byte units (VEC) when
@@ -236,8 +236,10 @@ PrefillWs prefill_layout(const dsa_prefill_shape* s, const int32_t* cu_host) {
   w.osig = off; off = align_up(off + size_t(T) * sizeof(int), 256);
   w.ocnt = off; off = align_up(off + size_t(row_order_count_ints(T, s->max_seqlen, B)) * sizeof(int), 256);
   w.order = off; off = align_up(off + size_t(T) * sizeof(int32_t), 256);
-  // V in fp16 for the dense reference (dense_causal_attention only)
-  w.v16 = off; off = align_up(off + size_t(T) * size_t(s->kv_heads) * size_t(s->head_dim) * sizeof(uint16_t), 256);
+  // V^T in fp16 for the dense reference (dense_causal_attention only), 64 zero columns after
+  // each sequence
+  w.v16 = off;
+  off = align_up(off + size_t(dense_vt_cols(T, B)) * size_t(s->kv_heads) * size_t(s->head_dim) * sizeof(uint16_t), 256);
   w.total = off;
   return w;
 }
@@ -814,7 +816,7 @@ int dense_causal_attention(const dsa_prefill_shape* s, const uint16_t* q, const 
                                        at<int>(ws, L.counts) + 1, nullptr, st);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(launch_dense_prefill(q, k, v, at<uint16_t>(ws, L.v16), s->total_tokens, s->cu_seqlens,
-                                         s->q_heads, s->kv_heads, s->softmax_scale,
+                                         s->num_seqs, s->q_heads, s->kv_heads, s->softmax_scale,
                                          at<int2>(ws, L.sched128), at<int>(ws, L.counts) + 1, L.nb128, out, st));
 }
 

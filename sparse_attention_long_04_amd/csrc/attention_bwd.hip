@@ -9,16 +9,19 @@
 // No float atomics anywhere, so results are bit-identical run to run:
 //   bwd_delta_kernel    D = rowsum(dO * O), 16 lanes per (row, head).
 //   dq: dedup_dq_kernel over the union of each 16-row block's selected keys (union_kernel):
-//     the dedup attention tile loop with S = K Q^T and dP = V dO^T (bf16 MFMA), the row masks,
-//     P = 2^(S scale - lse), dS = P (dP - D), and dq^T += K^T dS^T (bf16 MFMA, dS split hi + lo).
+//     the dedup attention tile loop with S = K Q^T and dP = V dO^T, the row masks,
+//     P = 2^(S scale - lse), dS = P (dP - D), and dq^T += K^T dS^T.
 //   dk, dv: every key needs the rows that selected it, in a fixed order.  sel_bitmap_kernel
 //     builds, per 32-row block of a sequence, one 32-bit word per key position (bit r = row r of
 //     the block selected the key), with LDS integer atomics only.  sparse_dkv_kernel then takes
 //     128 keys x one KV head (4 waves x 32 keys as MFMA columns) and a slice of the rows,
 //     streams tiles of 64 (row, head) vectors (8 rows x 8 heads for groups of 8) through LDS,
 //     skips tiles where none of its keys is selected, and accumulates dv^T += dO^T P^T and
-//     dk^T += Q^T dS^T (bf16 MFMA, transposed LDS reads, P and dS split hi + lo) into per-slice
-//     partials; dkv_reduce_kernel adds the slices in order.
+//     dk^T += Q^T dS^T into per-slice partials; dkv_reduce_kernel adds the slices in order.
+//   Both kernels run every product on fp16 MFMA: Q, K, V and dO are converted to fp16 once per
+//   call (to_f16_kernel; exact for bf16 values in fp16's normal range), and P and dS enter the
+//   accumulations rounded to fp16 (2^-11 relative), one MFMA each instead of a bf16 hi + lo
+//   pair.
 #include "attn_tiles.h"
 
 namespace dsa {
@@ -101,28 +104,17 @@ __global__ __launch_bounds__(256) void sel_bitmap_kernel(const int32_t* __restri
 }
 
 // ------------------------------------------------------------------------------------------
-// X^T G^T accumulation for one 64-row tile: X^T (dims x rows) read transposed from a bf16 LDS
-// tile, G (in the S^T register layout) split into bf16 hi + lo.
+// X^T G^T accumulation for one 64-row tile: X^T (dims x rows) read transposed from an fp16 LDS
+// tile, G (in the S^T register layout) rounded to fp16, one MFMA per step.
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ void accumulate_xt_gt_bf16(const uint8_t* xl, const float (&gz)[2][16], int lane,
-                                                      f32x16 (&o)[4]) {
+__device__ __forceinline__ void accumulate_xt_gt_f16(const uint8_t* xl, const float (&gz)[2][16], int lane,
+                                                     f32x16 (&o)[4]) {
   const int grp = lane >> 4, jj = lane & 15;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int kk2 = 0; kk2 < 2; ++kk2) {
-      uint32_t hi[8], lo[8];
-#pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) {
-        const float x = gz[rb][8 * kk2 + e2];
-        const uint32_t hb = __float_as_uint(x) & 0xFFFF0000u;  // x truncated to bf16
-        hi[e2] = hb;
-        lo[e2] = f32_to_bf16(x - __uint_as_float(hb));          // the remainder, rounded
-      }
-      const i32x4 ph = {int((hi[0] >> 16) | hi[1]), int((hi[2] >> 16) | hi[3]), int((hi[4] >> 16) | hi[5]),
-                        int((hi[6] >> 16) | hi[7])};
-      const i32x4 pl = {int(lo[0] | (lo[1] << 16)), int(lo[2] | (lo[3] << 16)), int(lo[4] | (lo[5] << 16)),
-                        int(lo[6] | (lo[7] << 16))};
+      const i32x4 ph = pack_f16x8(&gz[rb][8 * kk2]);
       const int key_a = 32 * rb + 16 * kk2 + 8 * (grp >> 1) + (jj >> 2);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
@@ -130,14 +122,26 @@ __device__ __forceinline__ void accumulate_xt_gt_bf16(const uint8_t* xl, const f
         const s16x4 a0 = lds_tr16(xl + kv_off(key_a, 2 * dim0));
         const s16x4 a1 = lds_tr16(xl + kv_off(key_a + 4, 2 * dim0));
         const i32x4 a = __builtin_bit_cast(i32x4, (s16x8_t){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
-        o[db] = mfma_bf16_32x32x16(a, ph, o[db]);
-        o[db] = mfma_bf16_32x32x16(a, pl, o[db]);
+        o[db] = mfma_f16_32x32x16(a, ph, o[db]);
       }
     }
 }
 
+// bf16 -> fp16 copy of n8 16-byte units (exact for values in fp16's normal range).
+__global__ __launch_bounds__(256) void to_f16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                     int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const i32x4 x = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(in) + i);
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = bf16_to_f32(bf16_lane(x, e));
+  reinterpret_cast<i32x4*>(out)[i] = pack_f16x8(f);
+}
+
 // ------------------------------------------------------------------------------------------
-// dedup_dq_kernel<G, SUB>: one workgroup per (16-row block, group of G query heads), G/2 waves,
+// dedup_dq_kernel<G, SUB>: q, k, v, dout are the fp16 copies.  One workgroup per (16-row block,
+// group of G query heads), G/2 waves,
 // as the dedup attention kernel (same union, masks and mapping).  SUB groups share one KV head:
 // 16 query heads per KV head run as two 8-head workgroups (one 8-wave workgroup would be
 // limited to 256 registers per wave and spill).
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
     const uint16_t* __restrict__ umask, const int* __restrict__ ucount, float* __restrict__ dq) {
   constexpr int D = 128, BN = 64, NTH = 32 * G, UPT = 1024 / NTH, RW = 32 / G;
   static_assert(G == 2 || G == 4 || G == 8 || G == 16, "a wave's 32 query vectors must span whole rows");
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2][2][kKvTileB];  // [buffer][K=0/V=1], bf16
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2][2][kKvTileB];  // [buffer][K=0/V=1], fp16
   __shared__ int upos[2][BN];
   const int n = blockIdx.x / (Hkv * SUB);
   const int gv = blockIdx.x % (Hkv * SUB);  // query-head group
@@ -253,8 +257,8 @@ __global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
       const int key = 32 * rb + kperm(qc);
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2) {
-        sacc = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(kl + kv_off(key, 32 * s2 + 16 * hf)), qf[s2], sacc);
-        pacc = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(vl + kv_off(key, 32 * s2 + 16 * hf)), df[s2], pacc);
+        sacc = mfma_f16_32x32x16(*reinterpret_cast<const i32x4*>(kl + kv_off(key, 32 * s2 + 16 * hf)), qf[s2], sacc);
+        pacc = mfma_f16_32x32x16(*reinterpret_cast<const i32x4*>(vl + kv_off(key, 32 * s2 + 16 * hf)), df[s2], pacc);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
         gz[rb][i] = p * (pacc[i] - dlt);
       }
     }
-    accumulate_xt_gt_bf16(kl, gz, lane, o);
+    accumulate_xt_gt_f16(kl, gz, lane, o);
     if (more) lstore(buf ^ 1);
     if (tid < BN) upos[t & 1][tid] = pos2;
     __syncthreads();
@@ -281,7 +285,8 @@ __global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// sparse_dkv_kernel<G>: grid (128-key blocks, KV heads, row slices), 4 waves x 32 keys.
+// sparse_dkv_kernel<G>: grid (128-key blocks, KV heads, row slices), 4 waves x 32 keys; q, k,
+// v, dout are the fp16 copies.
 // ------------------------------------------------------------------------------------------
 template <int G>
 __global__ __launch_bounds__(256) void sparse_dkv_kernel(
@@ -292,7 +297,7 @@ __global__ __launch_bounds__(256) void sparse_dkv_kernel(
     float* __restrict__ dv_part) {
   constexpr int D = 128, BN = 64, RT = BN / G;  // query vectors and rows per tile
   static_assert(G == 2 || G == 4 || G == 8 || G == 16, "tiles of whole rows inside a 32-row block");
-  __shared__ __attribute__((aligned(16))) uint8_t t_lds[2][2][kKvTileB];  // [buffer][Q=0/dO=1], bf16
+  __shared__ __attribute__((aligned(16))) uint8_t t_lds[2][2][kKvTileB];  // [buffer][Q=0/dO=1], fp16
   __shared__ float stat[2][2][BN];                                          // [buffer][lse2, D][vector]
   const int n = blockIdx.x;
   if (n >= *count) return;
@@ -392,10 +397,10 @@ __global__ __launch_bounds__(256) void sparse_dkv_kernel(
           const int vrow = 32 * rb + kperm(qc);
 #pragma unroll
           for (int s2 = 0; s2 < 8; ++s2) {
-            sacc = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(ql + kv_off(vrow, 32 * s2 + 16 * hf)), kf[s2],
-                                      sacc);
-            pacc = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(dl + kv_off(vrow, 32 * s2 + 16 * hf)), vf[s2],
-                                      pacc);
+            sacc = mfma_f16_32x32x16(*reinterpret_cast<const i32x4*>(ql + kv_off(vrow, 32 * s2 + 16 * hf)), kf[s2],
+                                     sacc);
+            pacc = mfma_f16_32x32x16(*reinterpret_cast<const i32x4*>(dl + kv_off(vrow, 32 * s2 + 16 * hf)), vf[s2],
+                                     pacc);
           }
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -406,8 +411,8 @@ __global__ __launch_bounds__(256) void sparse_dkv_kernel(
             sz[rb][i] = p * (pacc[i] - stat[buf][1][vl]);
           }
         }
-        accumulate_xt_gt_bf16(dl, pz, lane, dva);
-        accumulate_xt_gt_bf16(ql, sz, lane, dka);
+        accumulate_xt_gt_f16(dl, pz, lane, dva);
+        accumulate_xt_gt_f16(ql, sz, lane, dka);
       }
       if (more) lstore(buf ^ 1);
       __syncthreads();
@@ -491,6 +496,15 @@ hipError_t launch_dedup_dq(const uint16_t* q, const uint16_t* k, const uint16_t*
   return hipGetLastError();
 }
 
+// fp16 copy of n elements (a multiple of 8) of bf16.
+hipError_t launch_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t st) {
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  to_f16_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>(in, out, n8);
+  return hipGetLastError();
+}
+
+// q, k, v, dout: the fp16 copies.
 hipError_t launch_sparse_dkv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                              const float* lse, const float* Dlt, const int32_t* cu, int nseq, int Hq, int Hkv,
                              float scale, const int2* sched128, const int* count128, int nb128, const uint32_t* W,

@@ -64,6 +64,7 @@ hipError_t launch_dedup_dq(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const float* lse, const float* Dlt, const int32_t* cu, int Hq, int Hkv, float scale,
                            const int2* sched16, const int* count16, int nb16, int64_t ustride, const int32_t* ukeys,
                            const uint16_t* umask, const int* ucount, float* dq, hipStream_t st);
+hipError_t launch_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t st);
 hipError_t launch_sparse_dkv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                              const float* lse, const float* Dlt, const int32_t* cu, int nseq, int Hq, int Hkv,
                              float scale, const int2* sched128, const int* count128, int nb128, const uint32_t* W,
@@ -339,7 +340,8 @@ int check_kl(const dsa_prefill_shape* s) {
 // ukeys int32[nb16][16k] | umask uint16[nb16][16k] | bitmap uint32[(max_len/32 + 1) T] |
 // dk, dv partials float[slices][T][Hkv][128] each.
 struct BwdWs {
-  size_t counts, delta, sched16, sched32, sched128, ucount, ukeys, umask, bitmap, dkpart, dvpart, total;
+  size_t counts, delta, sched16, sched32, sched128, ucount, ukeys, umask, bitmap, dkpart, dvpart, qh, kh, vh, doh,
+      total;
   int nb16, nb32, nb128;
   int64_t ustride;
 };
@@ -365,6 +367,11 @@ BwdWs bwd_layout(const dsa_prefill_shape* s) {
   w.bitmap = off; off = align_up(off + size_t(s->max_seqlen / 32 + 1) * size_t(T) * sizeof(uint32_t), 256);
   w.dkpart = off; off = align_up(off + parts, 256);
   w.dvpart = off; off = align_up(off + parts, 256);
+  // fp16 copies of Q, K, V and dO for the gradient products
+  w.qh = off; off = align_up(off + size_t(T) * size_t(s->q_heads) * 128 * sizeof(uint16_t), 256);
+  w.kh = off; off = align_up(off + size_t(T) * size_t(s->kv_heads) * 128 * sizeof(uint16_t), 256);
+  w.vh = off; off = align_up(off + size_t(T) * size_t(s->kv_heads) * 128 * sizeof(uint16_t), 256);
+  w.doh = off; off = align_up(off + size_t(T) * size_t(s->q_heads) * 128 * sizeof(uint16_t), 256);
   w.total = off;
   return w;
 }
@@ -745,6 +752,8 @@ int dsa_sparse_attention_bwd(const dsa_prefill_shape* s, const uint16_t* q, cons
   int* counts = at<int>(ws, W.counts);
   const int32_t* cu = s->cu_seqlens;
   float* Dl = at<float>(ws, W.delta);
+  uint16_t *qh = at<uint16_t>(ws, W.qh), *kh = at<uint16_t>(ws, W.kh), *vh = at<uint16_t>(ws, W.vh),
+           *doh = at<uint16_t>(ws, W.doh);
   hipError_t e;
   if ((e = launch_build_schedule(cu, s->num_seqs, 16, W.nb16, at<int2>(ws, W.sched16), counts, nullptr, st)) !=
           hipSuccess ||
@@ -753,15 +762,19 @@ int dsa_sparse_attention_bwd(const dsa_prefill_shape* s, const uint16_t* q, cons
       (e = launch_build_schedule(cu, s->num_seqs, 128, W.nb128, at<int2>(ws, W.sched128), counts + 2, nullptr, st)) !=
           hipSuccess ||
       (e = launch_bwd_delta(d_out, out, s->total_tokens * s->q_heads, Dl, st)) != hipSuccess ||
+      (e = launch_to_f16(q, qh, s->total_tokens * s->q_heads * 128, st)) != hipSuccess ||
+      (e = launch_to_f16(k, kh, s->total_tokens * s->kv_heads * 128, st)) != hipSuccess ||
+      (e = launch_to_f16(v, vh, s->total_tokens * s->kv_heads * 128, st)) != hipSuccess ||
+      (e = launch_to_f16(d_out, doh, s->total_tokens * s->q_heads * 128, st)) != hipSuccess ||
       (e = launch_union(topk_idx, s->topk, cu, at<int2>(ws, W.sched16), counts, W.nb16, W.ustride,
                         at<int32_t>(ws, W.ukeys), at<uint16_t>(ws, W.umask), at<int>(ws, W.ucount), st)) !=
           hipSuccess ||
-      (e = launch_dedup_dq(q, k, v, d_out, lse, Dl, cu, s->q_heads, s->kv_heads, s->softmax_scale,
+      (e = launch_dedup_dq(qh, kh, vh, doh, lse, Dl, cu, s->q_heads, s->kv_heads, s->softmax_scale,
                            at<int2>(ws, W.sched16), counts, W.nb16, W.ustride, at<int32_t>(ws, W.ukeys),
                            at<uint16_t>(ws, W.umask), at<int>(ws, W.ucount), dq, st)) != hipSuccess ||
       (e = launch_sel_bitmap(topk_idx, s->topk, cu, at<int2>(ws, W.sched32), counts + 1, W.nb32,
                              at<uint32_t>(ws, W.bitmap), st)) != hipSuccess ||
-      (e = launch_sparse_dkv(q, k, v, d_out, lse, Dl, cu, s->num_seqs, s->q_heads, s->kv_heads, s->softmax_scale,
+      (e = launch_sparse_dkv(qh, kh, vh, doh, lse, Dl, cu, s->num_seqs, s->q_heads, s->kv_heads, s->softmax_scale,
                              at<int2>(ws, W.sched128), counts + 2, W.nb128, at<uint32_t>(ws, W.bitmap), s->max_seqlen,
                              s->total_tokens, at<float>(ws, W.dkpart), at<float>(ws, W.dvpart), dk, dv, st)) !=
           hipSuccess)

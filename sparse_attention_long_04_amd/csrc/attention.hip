@@ -446,39 +446,6 @@ __device__ __host__ __forceinline__ int64_t dn_vt_base(int64_t cub, int b) {
   return (cub + 63) / 64 * 64 + 128 * int64_t(b);
 }
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// 16 bytes per lane from global memory (base + off, base wave-uniform) to LDS address
-// lds_addr + 16 * lane (lds_addr wave-uniform).  Issued from asm so that the compiler's own
-// wait counting leaves it alone (for some LDS reads it would otherwise wait for every copy in
-// flight); the kernel waits for these copies itself, in dn_sync, before a stage is read.  M0
-// (the copy's LDS address) is saved and restored around it.
-__device__ __forceinline__ void dn_copy16(const void* base, uint32_t off, uint32_t lds_addr) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off), "s"(base), "s"(lds_addr)
-      : "memory");
-}
-
-// Workgroup barrier after every tile copy of the wave has landed in LDS (s_waitcnt vmcnt(0)
-// lgkmcnt(0)).  The compiler fences keep LDS accesses on their side of the barrier.
-__device__ __forceinline__ void dn_sync() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0070);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-template <int I>
-using dn_ic = std::integral_constant<int, I>;
-
-__device__ __forceinline__ i32x4 dn_ld128(const lds_u8* p) {
-  return *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(p);
-}
-
 template <int HW>
 __global__ __launch_bounds__(256 * HW) void dense_prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ vt, int64_t tpad,

@@ -47,9 +47,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 }
 
 // ------------------------------------------------------------------------------------------
-// Selection bitmap: for 32-row block j of sequence b, W[woff_b + j L_b + s] has bit r set when
-// row 32j + r selected key s (s <= 32j + 31).  woff_b = sum over earlier sequences of
-// ceil(L/32) L.
+// Selection bitmap: for 32-row block j of sequence b, W[woff_b + j Lp_b + s] has bit r set
+// when row 32j + r selected key s (s <= 32j + 31), Lp = L rounded up to a multiple of 4 (so
+// that every block's 128 words start 16-byte aligned).  woff_b = sum over earlier sequences of
+// ceil(L/32) Lp.
 // ------------------------------------------------------------------------------------------
 constexpr int kBitmapChunk = 16384;
 
@@ -57,7 +58,7 @@ __device__ __forceinline__ int64_t bitmap_offset(const int32_t* __restrict__ cu,
   int64_t off = 0;
   for (int x = 0; x < b; ++x) {
     const int64_t L = cu[x + 1] - cu[x];
-    off += ((L + 31) / 32) * L;
+    off += ((L + 31) / 32) * ((L + 3) & ~int64_t(3));
   }
   return off;
 }
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void sel_bitmap_kernel(const int32_t* __restri
   const int64_t seq0 = cu[b];
   const int L = cu[b + 1] - cu[b];
   const int i0 = 32 * j, nr = min(32, L - i0), plast = i0 + nr - 1;
-  uint32_t* __restrict__ wrow = W + bitmap_offset(cu, b) + (int64_t)j * L;
+  uint32_t* __restrict__ wrow = W + bitmap_offset(cu, b) + (int64_t)j * ((L + 3) & ~3);
   const int tid = threadIdx.x;
   if (tid < 32) rbeg[tid] = 0;
   for (int c0 = 0; c0 <= plast; c0 += kBitmapChunk) {
@@ -285,20 +286,108 @@ __global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// sparse_dkv_kernel<G>: grid (128-key blocks, KV heads, row slices), 4 waves x 32 keys; q, k,
-// v, dout are the fp16 copies.
+// Column layout of the dk/dv pass: vector (row t, head h) of KV group g of sequence b is column
+// bwd_col_base(cu[b], G, b) + G t + h of that group's transposed fp16 Q and dO copies
+// ([g][dim][column]) and of its statistics ([g][-lse log2 e | -D][column]).  Each sequence
+// starts on a 64-column boundary; its last 64-column tile is padded with zeros.
 // ------------------------------------------------------------------------------------------
+__device__ __host__ __forceinline__ int64_t bwd_col_base(int64_t cub, int G, int b) {
+  return (cub * G + 63) / 64 * 64 + 64 * int64_t(b);
+}
+int64_t bwd_cols(int64_t T, int G, int nseq) { return bwd_col_base(T, G, nseq); }
+
+// fp16 copies of q and dout in both layouts, and the statistics, for 64 columns of one KV group
+// (block (c, g)); thread (vg, u) converts dims 8u .. 8u+7 of the block's vectors 8vg .. 8vg+7.
+// The natural copies cover every (row, head) exactly once over the grid.
+__global__ __launch_bounds__(128) void bwd_prep_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ Dlt, const int32_t* __restrict__ cu, int nseq, int Hq, int G, int64_t ncols,
+    uint16_t* __restrict__ qh, uint16_t* __restrict__ doh, uint16_t* __restrict__ qt,
+    uint16_t* __restrict__ dot, float* __restrict__ stats) {
+  const int64_t c0 = 64 * (int64_t)blockIdx.x;
+  const int g = blockIdx.y;
+  int lo = 0, hi = nseq - 1;  // the last sequence whose columns start at or before c0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (bwd_col_base(cu[mid], G, mid) <= c0) lo = mid;
+    else hi = mid - 1;
+  }
+  const int b = lo;
+  const int64_t seq0 = cu[b];
+  const int L = cu[b + 1] - cu[b];
+  const int64_t j0 = c0 - bwd_col_base(seq0, G, b);
+  if (j0 >= ((int64_t)L * G + 63) / 64 * 64) return;  // between two sequences' columns
+  const int tid = threadIdx.x, u = tid & 15, vg = tid >> 4;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const uint16_t* __restrict__ src = pass ? dout : q;
+    uint16_t* __restrict__ nat = pass ? doh : qh;
+    uint16_t* __restrict__ tr = pass ? dot : qt;
+    float f[8][8];
+#pragma unroll
+    for (int vi = 0; vi < 8; ++vi) {
+      const int64_t j = j0 + 8 * vg + vi;
+      const int64_t t = j / G;
+      if (t < L) {
+        const int64_t off = ((seq0 + t) * Hq + g * G + int(j % G)) * 128 + 8 * u;
+        const i32x4 x = *reinterpret_cast<const i32x4*>(src + off);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[vi][e] = bf16_to_f32(bf16_lane(x, e));
+        *reinterpret_cast<i32x4*>(nat + off) = pack_f16x8(f[vi]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[vi][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float col[8];
+#pragma unroll
+      for (int vi = 0; vi < 8; ++vi) col[vi] = f[vi][e];
+      *reinterpret_cast<i32x4*>(tr + (int64_t(g) * 128 + 8 * u + e) * ncols + c0 + 8 * vg) = pack_f16x8(col);
+    }
+  }
+  if (tid < 64) {
+    const int64_t j = j0 + tid, t = j / G;
+    float a = 0.f, d = 0.f;
+    if (t < L) {
+      const int64_t r = (seq0 + t) * Hq + g * G + int(j % G);
+      a = -lse[r] * 1.4426950408889634f;
+      d = -Dlt[r];
+    }
+    stats[int64_t(g) * 2 * ncols + c0 + tid] = a;
+    stats[(int64_t(g) * 2 + 1) * ncols + c0 + tid] = d;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// sparse_dkv_kernel<G>: grid (128-key blocks, KV heads, row slices), 4 waves x 32 keys.  The
+// rows of the slice stream through LDS in half tiles of 32 (row, head) vectors, copied straight
+// from global memory into two rings: the S ring (5 slots: fp16 Q and dO rows, the A operands
+// of S^T = K Q^T and dP^T = V dO^T, plus -lse log2 e and -D of each vector and the 128 keys'
+// selection words) and the A ring (4 slots: the transposed fp16 Q^T and dO^T, the A operands of
+// dk^T += Q^T dS^T and dv^T += dO^T P^T).  Iteration h computes S and dP of half tile h+1,
+// P = 2^(S scale log2 e - lse log2 e) masked by the selection bits and dS = P (dP - D) of half
+// tile h, and the dk/dv products of half tile h; the copies run three (A) and four (S) half
+// tiles ahead; one barrier per iteration.
+// ------------------------------------------------------------------------------------------
+constexpr int kDkvS = 17408;                    // S slot: Q rows | dO rows (32 x 256 B each) | small
+constexpr int kDkvSmall = 16384;                // -lse log2 e [32] | -D [32] | words [128] | spare [64]
+constexpr int kDkvA = 16384;                    // A slot: Q^T | dO^T (128 dims x 64 B each)
+constexpr int kDkvAring = 5 * kDkvS;            // A ring offset
+constexpr int kDkvLds = kDkvAring + 4 * kDkvA;  // 152576 bytes
+constexpr int kDkvCopies = 9;                   // copies per wave and iteration
+
 template <int G>
-__global__ __launch_bounds__(256) void sparse_dkv_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dlt,
-    const int32_t* __restrict__ cu, int Hq, int Hkv, float scale_log2, float scale, const int2* __restrict__ sched,
-    const int* __restrict__ count, const uint32_t* __restrict__ W, int64_t T, float* __restrict__ dk_part,
-    float* __restrict__ dv_part) {
-  constexpr int D = 128, BN = 64, RT = BN / G;  // query vectors and rows per tile
-  static_assert(G == 2 || G == 4 || G == 8 || G == 16, "tiles of whole rows inside a 32-row block");
-  __shared__ __attribute__((aligned(16))) uint8_t t_lds[2][2][kKvTileB];  // [buffer][Q=0/dO=1], fp16
-  __shared__ float stat[2][2][BN];                                          // [buffer][lse2, D][vector]
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_dkv_kernel(
+    const uint16_t* __restrict__ qh, const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
+    const uint16_t* __restrict__ doh, const uint16_t* __restrict__ qt, const uint16_t* __restrict__ dot,
+    const float* __restrict__ stats, int64_t ncols, const int32_t* __restrict__ cu, int Hq, int Hkv,
+    float scale_log2, float scale, const int2* __restrict__ sched, const int* __restrict__ count,
+    const uint32_t* __restrict__ W, int64_t T, float* __restrict__ dk_part, float* __restrict__ dv_part) {
+  constexpr int D = 128, RH = 32 / G;  // rows per half tile
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16, "half tiles of whole rows inside a 32-row block");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kDkvLds];
   const int n = blockIdx.x;
   if (n >= *count) return;
   const int2 e = sched[n];
@@ -307,117 +396,268 @@ __global__ __launch_bounds__(256) void sparse_dkv_kernel(
   const int L = cu[b + 1] - cu[b];
   const int s0 = 128 * e.y;
   const int t_lo = max(s0, slice * kBwdSlice), t_hi = min(L, (slice + 1) * kBwdSlice);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, qc = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int my_s = s0 + 32 * w + qc;
   const bool valid = my_s < L;
-  const int srow = min(my_s, L - 1);
-  const int64_t kvs = (int64_t)Hkv * D;
-  const uint32_t* __restrict__ wseq = W + bitmap_offset(cu, b);
   f32x16 dka[4], dva[4];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dka[db][i] = 0.f;
-      dva[db][i] = 0.f;
-    }
+  for (int db = 0; db < 4; ++db) {
+    dka[db] = (f32x16){};
+    dva[db] = (f32x16){};
+  }
   if (t_lo < t_hi) {
+    const int nh = (t_hi - t_lo + RH - 1) / RH;
+    const int srow = min(my_s, L - 1);
+    const int64_t kvs = (int64_t)Hkv * D;
+    // K and V of the lane's key (B operands of S^T and dP^T): dims 16 s2 + 8 hf .. +7
     i32x4 kf[8], vf[8];
     {
-      const uint16_t* kp = k + (seq0 + srow) * kvs + g * D + 8 * hf;
-      const uint16_t* vp = v + (seq0 + srow) * kvs + g * D + 8 * hf;
+      const uint16_t* kp = kh + (seq0 + srow) * kvs + g * D + 8 * hf;
+      const uint16_t* vp = vh + (seq0 + srow) * kvs + g * D + 8 * hf;
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2) {
         kf[s2] = *reinterpret_cast<const i32x4*>(kp + 16 * s2);
         vf[s2] = *reinterpret_cast<const i32x4*>(vp + 16 * s2);
       }
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) asm volatile("" : "+v"(kf[s2]), "+v"(vf[s2]));  // landed before any copy
     }
-    i32x4 pre[8];
-    float spre[2];
-    auto gload = [&](int t0) {
+    lds_u8* const lb = (lds_u8*)lds;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)lb;
+    const int64_t cb = bwd_col_base(seq0, G, b);
+    const uint16_t* const qnb = qh + (seq0 * Hq + g * G) * D;  // row r, head hh: + (r Hq + hh) D
+    const uint16_t* const dnb = doh + (seq0 * Hq + g * G) * D;
+    const uint16_t* const qtb = qt + int64_t(g) * D * ncols + cb;  // dim d, vector j: + d ncols + j
+    const uint16_t* const dtb = dot + int64_t(g) * D * ncols + cb;
+    const float* const stb = stats + int64_t(g) * 2 * ncols + cb;
+    const int Lp = (L + 3) & ~3;
+    const uint32_t* const wb = W + bitmap_offset(cu, b) + s0;
+
+    // Copies of half tile x, clamped to the last one (the extra copies of the final iterations
+    // land in slots nobody reads again).  S slot: rows 4(2w + i) + lane/16 of the Q and dO
+    // stages, 16-byte unit (lane % 16) holding unit (lane % 16) ^ (row % 16); small region:
+    // lanes 0..15 of wave w fill bytes 256 w .. (wave 0: -lse log2 e and -D, waves 1 and 2: the
+    // words of keys 0..63 and 64..127, wave 3: a spare copy of the statistics).  A slot: dim rows
+    // 16(2w + i) + lane/4, unit (lane % 4) holding unit (lane % 4) ^ ((dim / 4) % 4).  Every wave
+    // issues 9 copies per half tile.
+    uint32_t at_off[2];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int u = tid + 256 * x;  // vector u >> 4 = (row, head) (u >> 4) / G, (u >> 4) % G
-        const int vv = u >> 4;
-        const int64_t tr = seq0 + min(t0 + vv / G, t_hi - 1);
-        const int64_t off = (tr * Hq + g * G + vv % G) * D + 8 * (u & 15);
-        pre[x] = *reinterpret_cast<const i32x4*>(q + off);
-        pre[4 + x] = *reinterpret_cast<const i32x4*>(dout + off);
-      }
-      if (tid < BN) {
-        const int64_t tr = seq0 + min(t0 + tid / G, t_hi - 1);
-        spre[0] = lse[tr * Hq + g * G + tid % G] * 1.4426950408889634f;
-        spre[1] = Dlt[tr * Hq + g * G + tid % G];
+    for (int i = 0; i < 2; ++i) {
+      const int d = 16 * (2 * w + i) + (lane >> 2);
+      at_off[i] = uint32_t(d) * uint32_t(ncols) * 2 + 16 * ((lane & 3) ^ ((d >> 2) & 3));
+    }
+    const uint32_t sm_off = (w == 1 || w == 2) ? uint32_t(256 * (w - 1) + 16 * (lane & 15))
+                                               : ((lane & 8) ? uint32_t(ncols) * 4 : 0u) + 16 * (lane & 7);
+    auto tile_row = [&](int x) { return t_lo + RH * min(x, nh - 1); };
+    auto copy_small = [&](int x) {
+      const int t0 = tile_row(x);
+      const void* src = (w == 1 || w == 2) ? (const void*)(wb + int64_t(t0 >> 5) * Lp) : (const void*)(stb + int64_t(G) * t0);
+      dn_copy16_lo16(src, sm_off, lds0 + (x % 5) * kDkvS + kDkvSmall + 256 * w);
+    };
+    auto copy_srow = [&](int x, int i) {  // Q and dO rows 4(2w + i) .. +3
+      const int t0 = tile_row(x);
+      const int vi = 4 * (2 * w + i) + (lane >> 4);
+      const int r = min(t0 + vi / G, t_hi - 1);
+      const uint32_t off = uint32_t(r * Hq + vi % G) * 256 + 16 * ((lane & 15) ^ (vi & 15));
+      const uint32_t dst = lds0 + (x % 5) * kDkvS + 1024 * (2 * w + i);
+      dn_copy16(qnb, off, dst);
+      dn_copy16(dnb, off, dst + 8192);
+    };
+    auto copy_arow = [&](int x, int i) {  // Q^T and dO^T dim rows 16(2w + i) .. +15
+      const int64_t c0 = int64_t(G) * tile_row(x);
+      const uint32_t dst = lds0 + kDkvAring + (x & 3) * kDkvA + 1024 * (2 * w + i);
+      dn_copy16(qtb + c0, at_off[i], dst);
+      dn_copy16(dtb + c0, at_off[i], dst + 8192);
+    };
+    auto copies_s = [&](int x) {
+      copy_small(x);
+      copy_srow(x, 0);
+      copy_srow(x, 1);
+    };
+    auto copies_a = [&](int x) {
+      copy_arow(x, 0);
+      copy_arow(x, 1);
+    };
+
+    // LDS read addresses.  S operands: row kperm(qc), unit 2 s2 + hf -> byte qn_off ^ 32 s2.
+    // dk/dv operands: dim row 32 db + qc, unit 2 kk + hf -> byte 2048 db + (qa_off ^ 32 kk).
+    const int vrow = kperm(qc);
+    const int qn_off = 256 * vrow + 16 * (hf ^ (vrow & 15));
+    const int qa_off = 64 * qc + 16 * (hf ^ ((qc >> 2) & 3));
+    // statistics of the lane's accumulator rows (the vectors 16(j/2) + 8 hf + 4(j%2) .. +3 of the
+    // half tile, j < 4): -lse log2 e and -D
+    float lc[16], dc[16];
+    auto load_stats = [&](int x) {
+      const lds_u8* sm = lb + (x % 5) * kDkvS + kDkvSmall;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v0 = 16 * (j >> 1) + 8 * hf + 4 * (j & 1);
+        const f32x4 a = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(sm + 4 * v0);
+        const f32x4 c = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(sm + 128 + 4 * v0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          lc[4 * j + m] = a[m];
+          dc[4 * j + m] = c[m];
+        }
       }
     };
-    auto lstore = [&](int buf) {
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int u = tid + 256 * x;
-        const int off = kv_off(u >> 4, 16 * (u & 15));
-        *reinterpret_cast<i32x4*>(&t_lds[buf][0][off]) = pre[x];
-        *reinterpret_cast<i32x4*>(&t_lds[buf][1][off]) = pre[4 + x];
-      }
-      if (tid < BN) {
-        stat[buf][0][tid] = spre[0];
-        stat[buf][1][tid] = spre[1];
-      }
+    // selection bits of the lane's key for the rows of half tile x, shifted so that bit r / G of
+    // the result belongs to accumulator register i (r = 16(i/8) + 4((i/4)%2) + i%4)
+    auto load_bits = [&](int x) -> uint32_t {
+      const int t0 = t_lo + RH * x;
+      const uint32_t word = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
+          lb + (x % 5) * kDkvS + kDkvSmall + 256 + 4 * (32 * w + qc));
+      const uint32_t keep = (valid && my_s <= 32 * (t0 >> 5) + 31) ? 0xFFFFFFFFu : 0u;
+      const uint32_t bits = (word >> (t0 & 31)) & ((1u << RH) - 1u) & keep;
+      return (G == 16) ? bits : (bits >> ((8 * hf) / G));
     };
-    // selection bits of this lane's key for the 32-row block holding row t0
-    auto bits_of = [&](int t0) -> uint32_t {
-      const int rb = t0 >> 5;
-      if (!valid || my_s > 32 * rb + 31) return 0u;
-      const uint32_t word = wseq[(int64_t)rb * L + my_s];
-      return (RT == 32) ? word : ((word >> (t0 & 31)) & ((1u << RT) - 1u));
-    };
-    gload(t_lo);
-    lstore(0);
-    uint32_t nbits = bits_of(t_lo);
-    __syncthreads();
-    int buf = 0;
-    for (int t0 = t_lo; t0 < t_hi; t0 += RT) {
-      const bool more = t0 + RT < t_hi;
-      const uint32_t mybits = nbits;
-      if (more) {
-        gload(t0 + RT);
-        nbits = bits_of(t0 + RT);
-      }
-      if (__any(mybits != 0u)) {
-        const uint8_t* ql = t_lds[buf][0];
-        const uint8_t* dl = t_lds[buf][1];
-        float pz[2][16], sz[2][16];
+
+    // prologue: S parts 0..2 and A parts 0..1 land, S part 3 and A part 2 stay in flight
+    copies_s(0);
+    copies_s(1);
+    copies_s(2);
+    copies_a(0);
+    copies_a(1);
+    copies_s(3);
+    copies_a(2);
+    lds_sync_vm<kDkvCopies>();
+    f32x16 sn, pn;  // S and dP of the next half tile (MFMA accumulators)
+    f32x16 sc, pc;  // S and dP of the current half tile (read by the exponentials)
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          f32x16 sacc, pacc;
+    for (int s2 = 0; s2 < 8; ++s2) {
+      sn = mfma_f16_32x32x16(dn_ld128(lb + (qn_off ^ (32 * s2))), kf[s2], s2 ? sn : (f32x16){});
+      pn = mfma_f16_32x32x16(dn_ld128(lb + 8192 + (qn_off ^ (32 * s2))), vf[s2], s2 ? pn : (f32x16){});
+    }
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            sacc[i] = 0.f;
-            pacc[i] = 0.f;
-          }
-          const int vrow = 32 * rb + kperm(qc);
+    for (int m = 0; m < 16; ++m) {
+      float xs = sn[m], xq = pn[m];
+      asm volatile("" : "+v"(xs), "+v"(xq));  // VGPR copies, as the loop makes them
+      sc[m] = xs;
+      pc[m] = xq;
+    }
+    load_stats(0);
+    uint32_t bits = load_bits(0);
+    i32x4 op[35];  // A operands of the MFMA slots; 32..34 are slots 0..2 of the next iteration
+
+    // Iteration h: MFMA slots 0-7 S/dP(h+1) k-steps 0-3, 8-15 dk/dv(h) kk = 0, 16-23 S/dP(h+1)
+    // k-steps 4-7, 24-31 dk/dv(h) kk = 1.  Operand reads run three slots ahead (into the next
+    // iteration: S part h+2 has landed); slots 1-5 issue the copies of S part h+4 and A part h+3.
+    // P and dS of register i are computed in slot i; slot 16 loads the statistics and selection
+    // bits of half tile h+1; slots 26-31 move S(h+1) and dP(h+1) to the registers the next
+    // iteration's exponentials read.
+    auto body = [&](int h) {
+      // slot offsets are multiples of 64: the unit XORs commute with them
+      const int sq = ((h + 1) % 5) * kDkvS + qn_off;
+      const int sq2 = ((h + 2) % 5) * kDkvS + qn_off;
+      const int aq = kDkvAring + (h & 3) * kDkvA + qa_off;
+      const uint32_t bh = bits;
+      i32x4 ppk[2], dpk[2];
+      float pv[2], dv2[2];
+      auto rd = [&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        constexpr int part = (j >> 3) & 3, k = j & 7;
+        if constexpr ((part & 1) == 0) {
+          constexpr int s2 = 4 * (part >> 1) + (k >> 1);
+          op[j] = dn_ld128(lb + (((j < 32) ? sq : sq2) ^ (32 * s2)) + ((k & 1) ? 8192 : 0));
+        } else {
+          constexpr int kk = part >> 1, db = k >> 1;
+          op[j] = dn_ld128(lb + (aq ^ (32 * kk)) + ((k & 1) ? 0 : 8192) + 2048 * db);
+        }
+      };
+      auto ev = [&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        constexpr int r = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
+        const bool on = (bh >> (r / G)) & 1u;
+        const float p = __builtin_amdgcn_exp2f(on ? fmaf(sc[i], scale_log2, lc[i]) : -__builtin_inff());
+        pv[i & 1] = p;
+        dv2[i & 1] = p * (pc[i] + dc[i]);
+        if constexpr (i & 1) {
+          const f16x2 hp = {(_Float16)pv[0], (_Float16)pv[1]};
+          const f16x2 hd = {(_Float16)dv2[0], (_Float16)dv2[1]};
+          int xp = __builtin_bit_cast(int, hp), xd = __builtin_bit_cast(int, hd);
+          asm volatile("" : "+v"(xp), "+v"(xd));  // computed in this slot
+          ppk[i >> 3][(i & 7) >> 1] = xp;
+          dpk[i >> 3][(i & 7) >> 1] = xd;
+        }
+      };
+      auto slot = [&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        constexpr int part = j >> 3, k = j & 7;
+        rd(dn_ic<j + 3>{});
+        i32x4 a;
+        if constexpr (j < 3) a = op[32 + j];
+        else a = op[j];
+        if constexpr ((part & 1) == 0) {
+          constexpr int s2 = 4 * (part >> 1) + (k >> 1);
+          if constexpr (k & 1) pn = mfma_f16_32x32x16(a, vf[s2], s2 ? pn : (f32x16){});
+          else sn = mfma_f16_32x32x16(a, kf[s2], s2 ? sn : (f32x16){});
+        } else {
+          constexpr int kk = part >> 1, db = k >> 1;
+          if constexpr (k & 1) dka[db] = mfma_f16_32x32x16(a, dpk[kk], dka[db]);
+          else dva[db] = mfma_f16_32x32x16(a, ppk[kk], dva[db]);
+        }
+        if constexpr (j == 1) copy_small(h + 4);
+        if constexpr (j == 2 || j == 3) copy_srow(h + 4, j - 2);
+        if constexpr (j == 4 || j == 5) copy_arow(h + 3, j - 4);
+        if constexpr (j < 16) ev(dn_ic<j>{});
+        if constexpr (j == 16) {
+          load_stats(h + 1);
+          bits = load_bits(h + 1);
+        }
+        if constexpr (j >= 26) {
 #pragma unroll
-          for (int s2 = 0; s2 < 8; ++s2) {
-            sacc = mfma_f16_32x32x16(*reinterpret_cast<const i32x4*>(ql + kv_off(vrow, 32 * s2 + 16 * hf)), kf[s2],
-                                     sacc);
-            pacc = mfma_f16_32x32x16(*reinterpret_cast<const i32x4*>(dl + kv_off(vrow, 32 * s2 + 16 * hf)), vf[s2],
-                                     pacc);
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int vl = 32 * rb + kperm(8 * (i >> 2) + 4 * hf + (i & 3));  // vector within the tile
-            const bool on = (mybits >> (vl / G)) & 1u;
-            const float p = on ? __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -stat[buf][0][vl])) : 0.f;
-            pz[rb][i] = p;
-            sz[rb][i] = p * (pacc[i] - stat[buf][1][vl]);
+          for (int m = 3 * (j - 26); m < 3 * (j - 26) + 3 && m < 16; ++m) {
+            float xs = sn[m], xq = pn[m];
+            asm volatile("" : "+v"(xs), "+v"(xq));  // moved in this slot
+            sc[m] = xs;
+            pc[m] = xq;
           }
         }
-        accumulate_xt_gt_f16(dl, pz, lane, dva);
-        accumulate_xt_gt_f16(ql, sz, lane, dka);
-      }
-      if (more) lstore(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      slot(dn_ic<0>{});
+      slot(dn_ic<1>{});
+      slot(dn_ic<2>{});
+      slot(dn_ic<3>{});
+      slot(dn_ic<4>{});
+      slot(dn_ic<5>{});
+      slot(dn_ic<6>{});
+      slot(dn_ic<7>{});
+      slot(dn_ic<8>{});
+      slot(dn_ic<9>{});
+      slot(dn_ic<10>{});
+      slot(dn_ic<11>{});
+      slot(dn_ic<12>{});
+      slot(dn_ic<13>{});
+      slot(dn_ic<14>{});
+      slot(dn_ic<15>{});
+      slot(dn_ic<16>{});
+      slot(dn_ic<17>{});
+      slot(dn_ic<18>{});
+      slot(dn_ic<19>{});
+      slot(dn_ic<20>{});
+      slot(dn_ic<21>{});
+      slot(dn_ic<22>{});
+      slot(dn_ic<23>{});
+      slot(dn_ic<24>{});
+      slot(dn_ic<25>{});
+      slot(dn_ic<26>{});
+      slot(dn_ic<27>{});
+      slot(dn_ic<28>{});
+      slot(dn_ic<29>{});
+      slot(dn_ic<30>{});
+      slot(dn_ic<31>{});
+      // the copies of iteration h-1 have landed (S part h+3, A part h+2) and every wave is past
+      // its reads of A part h (the slot the next iteration's copies overwrite)
+      lds_sync_vm_nolgkm<kDkvCopies>();
+    };
+    // reads of iteration 0's first slots
+    op[32] = dn_ld128(lb + (kDkvS + qn_off));
+    op[33] = dn_ld128(lb + (kDkvS + qn_off) + 8192);
+    op[34] = dn_ld128(lb + ((kDkvS + qn_off) ^ 32));
+    for (int h = 0; h < nh; ++h) body(h);
+    dn_sync();  // no copy is left in flight when the workgroup ends
   }
   if (!valid) return;
   const int64_t orow = ((int64_t)slice * T + seq0 + my_s) * Hkv + g;
@@ -504,20 +744,37 @@ hipError_t launch_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream
   return hipGetLastError();
 }
 
-// q, k, v, dout: the fp16 copies.
-hipError_t launch_sparse_dkv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
-                             const float* lse, const float* Dlt, const int32_t* cu, int nseq, int Hq, int Hkv,
-                             float scale, const int2* sched128, const int* count128, int nb128, const uint32_t* W,
-                             int max_len, int64_t T, float* dk_part, float* dv_part, float* dk, float* dv,
-                             hipStream_t st) {
+// fp16 Q and dO in both layouts and the statistics of the dk/dv pass (after launch_bwd_delta).
+hipError_t launch_bwd_prep(const uint16_t* q, const uint16_t* dout, const float* lse, const float* Dlt,
+                           const int32_t* cu, int nseq, int64_t T, int Hq, int Hkv, uint16_t* qh, uint16_t* doh,
+                           uint16_t* qt, uint16_t* dot, float* stats, hipStream_t st) {
   if (T == 0) return hipSuccess;
+  const int G = Hq / Hkv;
+  const int64_t ncols = bwd_cols(T, G, nseq);
+  bwd_prep_kernel<<<dim3((unsigned)(ncols / 64), Hkv), 128, 0, st>>>(q, dout, lse, Dlt, cu, nseq, Hq, G, ncols, qh, doh,
+                                                                   qt, dot, stats);
+  return hipGetLastError();
+}
+
+// qh, kh, vh, doh: the natural fp16 copies; qt, dot, stats: launch_bwd_prep's outputs.
+hipError_t launch_sparse_dkv(const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, const uint16_t* doh,
+                             const uint16_t* qt, const uint16_t* dot, const float* stats, const int32_t* cu, int nseq,
+                             int Hq, int Hkv, float scale, const int2* sched128, const int* count128, int nb128,
+                             const uint32_t* W, int max_len, int64_t T, float* dk_part, float* dv_part, float* dk,
+                             float* dv, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const int G = Hq / Hkv;
+  const int64_t ncols = bwd_cols(T, G, nseq);
+  // the kernel's copy offsets are 32-bit: rows of one sequence, and 128 transposed dim rows
+  if (int64_t(max_len) * Hq * 256 >= (int64_t(1) << 32) || 256 * ncols >= (int64_t(1) << 32))
+    return hipErrorInvalidValue;
   const float sl2 = scale * 1.4426950408889634f;
   const dim3 grid(nb128, Hkv, bwd_slices(max_len));
-  switch (Hq / Hkv) {
-#define DSA_DKV(GG)                                                                                                \
-  case GG:                                                                                                         \
-    sparse_dkv_kernel<GG><<<grid, 256, 0, st>>>(q, k, v, dout, lse, Dlt, cu, Hq, Hkv, sl2, scale, sched128, count128, \
-                                                W, T, dk_part, dv_part);                                           \
+  switch (G) {
+#define DSA_DKV(GG)                                                                                              \
+  case GG:                                                                                                       \
+    sparse_dkv_kernel<GG><<<grid, 256, 0, st>>>(qh, kh, vh, doh, qt, dot, stats, ncols, cu, Hq, Hkv, sl2, scale,  \
+                                                sched128, count128, W, T, dk_part, dv_part);                     \
     break;
     DSA_DKV(2)
     DSA_DKV(4)

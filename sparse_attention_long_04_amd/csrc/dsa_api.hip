@@ -65,11 +65,15 @@ hipError_t launch_dedup_dq(const uint16_t* q, const uint16_t* k, const uint16_t*
                            const int2* sched16, const int* count16, int nb16, int64_t ustride, const int32_t* ukeys,
                            const uint16_t* umask, const int* ucount, float* dq, hipStream_t st);
 hipError_t launch_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t st);
-hipError_t launch_sparse_dkv(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
-                             const float* lse, const float* Dlt, const int32_t* cu, int nseq, int Hq, int Hkv,
-                             float scale, const int2* sched128, const int* count128, int nb128, const uint32_t* W,
-                             int max_len, int64_t T, float* dk_part, float* dv_part, float* dk, float* dv,
-                             hipStream_t st);
+hipError_t launch_bwd_prep(const uint16_t* q, const uint16_t* dout, const float* lse, const float* Dlt,
+                           const int32_t* cu, int nseq, int64_t T, int Hq, int Hkv, uint16_t* qh, uint16_t* doh,
+                           uint16_t* qt, uint16_t* dot, float* stats, hipStream_t st);
+int64_t bwd_cols(int64_t T, int G, int nseq);
+hipError_t launch_sparse_dkv(const uint16_t* qh, const uint16_t* kh, const uint16_t* vh, const uint16_t* doh,
+                             const uint16_t* qt, const uint16_t* dot, const float* stats, const int32_t* cu, int nseq,
+                             int Hq, int Hkv, float scale, const int2* sched128, const int* count128, int nb128,
+                             const uint32_t* W, int max_len, int64_t T, float* dk_part, float* dv_part, float* dk,
+                             float* dv, hipStream_t st);
 hipError_t launch_topk_general(const float* scores, int64_t rows, int n, int64_t ld, const int32_t* lens, int K,
                                int32_t* out, hipStream_t st);
 int64_t dense_vt_cols(int64_t T, int nseq);
@@ -337,11 +341,12 @@ int check_kl(const dsa_prefill_shape* s) {
 
 // Sparse attention backward workspace: counts int[64] (0: 16-row, 1: 32-row, 2: 128-key
 // schedule sizes) | D float[T][Hq] | sched16 | sched32 | sched128 | ucount int[nb16] |
-// ukeys int32[nb16][16k] | umask uint16[nb16][16k] | bitmap uint32[(max_len/32 + 1) T] |
-// dk, dv partials float[slices][T][Hkv][128] each.
+// ukeys int32[nb16][16k] | umask uint16[nb16][16k] | bitmap uint32[(max_len/32 + 1)(T + 3B) + 128] |
+// dk, dv partials float[slices][T][Hkv][128] each | fp16 q, k, v, dO | transposed fp16 q, dO
+// [Hkv][128][cols] | statistics float[Hkv][2][cols] (cols = bwd_cols(T, G, B)).
 struct BwdWs {
   size_t counts, delta, sched16, sched32, sched128, ucount, ukeys, umask, bitmap, dkpart, dvpart, qh, kh, vh, doh,
-      total;
+      qt, dot, stats, total;
   int nb16, nb32, nb128;
   int64_t ustride;
 };
@@ -364,7 +369,8 @@ BwdWs bwd_layout(const dsa_prefill_shape* s) {
   w.ucount = off; off = align_up(off + size_t(w.nb16) * sizeof(int), 256);
   w.ukeys = off; off = align_up(off + size_t(w.nb16) * size_t(w.ustride) * sizeof(int32_t), 256);
   w.umask = off; off = align_up(off + size_t(w.nb16) * size_t(w.ustride) * sizeof(uint16_t), 256);
-  w.bitmap = off; off = align_up(off + size_t(s->max_seqlen / 32 + 1) * size_t(T) * sizeof(uint32_t), 256);
+  w.bitmap = off;
+  off = align_up(off + (size_t(s->max_seqlen / 32 + 1) * size_t(T + 3 * B) + 128) * sizeof(uint32_t), 256);
   w.dkpart = off; off = align_up(off + parts, 256);
   w.dvpart = off; off = align_up(off + parts, 256);
   // fp16 copies of Q, K, V and dO for the gradient products
@@ -372,6 +378,10 @@ BwdWs bwd_layout(const dsa_prefill_shape* s) {
   w.kh = off; off = align_up(off + size_t(T) * size_t(s->kv_heads) * 128 * sizeof(uint16_t), 256);
   w.vh = off; off = align_up(off + size_t(T) * size_t(s->kv_heads) * 128 * sizeof(uint16_t), 256);
   w.doh = off; off = align_up(off + size_t(T) * size_t(s->q_heads) * 128 * sizeof(uint16_t), 256);
+  const size_t cols = size_t(bwd_cols(T, s->q_heads / s->kv_heads, B));
+  w.qt = off; off = align_up(off + size_t(s->kv_heads) * 128 * cols * sizeof(uint16_t), 256);
+  w.dot = off; off = align_up(off + size_t(s->kv_heads) * 128 * cols * sizeof(uint16_t), 256);
+  w.stats = off; off = align_up(off + size_t(s->kv_heads) * 2 * cols * sizeof(float), 256);
   w.total = off;
   return w;
 }
@@ -753,7 +763,8 @@ int dsa_sparse_attention_bwd(const dsa_prefill_shape* s, const uint16_t* q, cons
   const int32_t* cu = s->cu_seqlens;
   float* Dl = at<float>(ws, W.delta);
   uint16_t *qh = at<uint16_t>(ws, W.qh), *kh = at<uint16_t>(ws, W.kh), *vh = at<uint16_t>(ws, W.vh),
-           *doh = at<uint16_t>(ws, W.doh);
+           *doh = at<uint16_t>(ws, W.doh), *qt = at<uint16_t>(ws, W.qt), *dot = at<uint16_t>(ws, W.dot);
+  float* stats = at<float>(ws, W.stats);
   hipError_t e;
   if ((e = launch_build_schedule(cu, s->num_seqs, 16, W.nb16, at<int2>(ws, W.sched16), counts, nullptr, st)) !=
           hipSuccess ||
@@ -762,10 +773,10 @@ int dsa_sparse_attention_bwd(const dsa_prefill_shape* s, const uint16_t* q, cons
       (e = launch_build_schedule(cu, s->num_seqs, 128, W.nb128, at<int2>(ws, W.sched128), counts + 2, nullptr, st)) !=
           hipSuccess ||
       (e = launch_bwd_delta(d_out, out, s->total_tokens * s->q_heads, Dl, st)) != hipSuccess ||
-      (e = launch_to_f16(q, qh, s->total_tokens * s->q_heads * 128, st)) != hipSuccess ||
+      (e = launch_bwd_prep(q, d_out, lse, Dl, cu, s->num_seqs, s->total_tokens, s->q_heads, s->kv_heads, qh, doh,
+                           qt, dot, stats, st)) != hipSuccess ||
       (e = launch_to_f16(k, kh, s->total_tokens * s->kv_heads * 128, st)) != hipSuccess ||
       (e = launch_to_f16(v, vh, s->total_tokens * s->kv_heads * 128, st)) != hipSuccess ||
-      (e = launch_to_f16(d_out, doh, s->total_tokens * s->q_heads * 128, st)) != hipSuccess ||
       (e = launch_union(topk_idx, s->topk, cu, at<int2>(ws, W.sched16), counts, W.nb16, W.ustride,
                         at<int32_t>(ws, W.ukeys), at<uint16_t>(ws, W.umask), at<int>(ws, W.ucount), st)) !=
           hipSuccess ||
@@ -774,8 +785,9 @@ int dsa_sparse_attention_bwd(const dsa_prefill_shape* s, const uint16_t* q, cons
                            at<uint16_t>(ws, W.umask), at<int>(ws, W.ucount), dq, st)) != hipSuccess ||
       (e = launch_sel_bitmap(topk_idx, s->topk, cu, at<int2>(ws, W.sched32), counts + 1, W.nb32,
                              at<uint32_t>(ws, W.bitmap), st)) != hipSuccess ||
-      (e = launch_sparse_dkv(qh, kh, vh, doh, lse, Dl, cu, s->num_seqs, s->q_heads, s->kv_heads, s->softmax_scale,
-                             at<int2>(ws, W.sched128), counts + 2, W.nb128, at<uint32_t>(ws, W.bitmap), s->max_seqlen,
+      (e = launch_sparse_dkv(qh, kh, vh, doh, qt, dot, stats, cu, s->num_seqs, s->q_heads, s->kv_heads,
+                             s->softmax_scale, at<int2>(ws, W.sched128), counts + 2, W.nb128,
+                             at<uint32_t>(ws, W.bitmap), s->max_seqlen,
                              s->total_tokens, at<float>(ws, W.dkpart), at<float>(ws, W.dvpart), dk, dv, st)) !=
           hipSuccess)
     return hip_status(e);

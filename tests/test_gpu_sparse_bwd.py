@@ -60,6 +60,7 @@ CASES = {
     "corr_1500": ([1500], 512, 32, 4, 0.95),
     "g16": ([600], 128, 16, 1, None),
     "g4": ([450, 70], 64, 16, 4, None),
+    "g2": ([333, 64], 96, 8, 4, None),
     "k_ge_L": ([300], 512, 32, 4, None),
     # dk/dv partials are summed over 4096-row slices of a sequence: rows over 3 slices, and two
     # sequences of 2 slices each (slices count from each sequence's start)

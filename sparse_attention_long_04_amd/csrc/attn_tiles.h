@@ -42,7 +42,7 @@ __device__ __forceinline__ int kperm(int rr) {
   return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + bb;
 }
 
-constexpr int kKvRowB = 288;             // bytes per K/V row in LDS (256 + 32 pad)
+constexpr int kKvRowB = 256;             // bytes per K/V row in LDS
 constexpr int kKvTileB = 64 * kKvRowB;   // one 64-key tile
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -52,9 +52,12 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
       (__attribute__((address_space(3))) s16x4*)(const_cast<uint8_t*>(p)));
 }
 
-// 16-byte unit swizzle inside a K/V row: flips unit bit 0 with key bit 3 (removes the 2-way
-// bank conflict between keys k and k+8 in the K-operand reads).
-__device__ __forceinline__ int kv_off(int key, int byte) { return key * kKvRowB + (byte ^ (((key >> 3) & 1) << 4)); }
+// 16-byte unit swizzle inside a K/V row: unit u of key r sits at u ^ (4 (r % 4) + (r / 4) % 4).
+// Conflict-free for the 16-byte operand reads of 16 consecutive keys (rows kperm(0..15) are 16
+// distinct keys mod 16) and for the transposed 8-byte reads (4 consecutive keys x 4 units).
+__device__ __forceinline__ int kv_off(int key, int byte) {
+  return key * kKvRowB + (byte ^ ((((key & 3) << 2) | ((key >> 2) & 3)) << 4));
+}
 
 // ---- direct global -> LDS copies
 typedef __attribute__((address_space(3))) uint8_t lds_u8;

@@ -105,27 +105,26 @@ __global__ __launch_bounds__(256) void sel_bitmap_kernel(const int32_t* __restri
 }
 
 // ------------------------------------------------------------------------------------------
-// X^T G^T accumulation for one 64-row tile: X^T (dims x rows) read transposed from an fp16 LDS
-// tile, G (in the S^T register layout) rounded to fp16, one MFMA per step.
+// X^T G^T accumulation for rows 32 rb .. 32 rb + 31 of a 64-row tile: X^T (dims x rows) read
+// transposed from an fp16 LDS tile, G (in the S^T register layout) rounded to fp16, one MFMA
+// per step.
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ void accumulate_xt_gt_f16(const uint8_t* xl, const float (&gz)[2][16], int lane,
+__device__ __forceinline__ void accumulate_xt_gt_f16(const uint8_t* xl, const float (&gz)[16], int rb, int lane,
                                                      f32x16 (&o)[4]) {
   const int grp = lane >> 4, jj = lane & 15;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int kk2 = 0; kk2 < 2; ++kk2) {
+    const i32x4 ph = pack_f16x8(&gz[8 * kk2]);
+    const int key_a = 32 * rb + 16 * kk2 + 8 * (grp >> 1) + (jj >> 2);
 #pragma unroll
-    for (int kk2 = 0; kk2 < 2; ++kk2) {
-      const i32x4 ph = pack_f16x8(&gz[rb][8 * kk2]);
-      const int key_a = 32 * rb + 16 * kk2 + 8 * (grp >> 1) + (jj >> 2);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int dim0 = 32 * db + 16 * (grp & 1) + 4 * (jj & 3);
-        const s16x4 a0 = lds_tr16(xl + kv_off(key_a, 2 * dim0));
-        const s16x4 a1 = lds_tr16(xl + kv_off(key_a + 4, 2 * dim0));
-        const i32x4 a = __builtin_bit_cast(i32x4, (s16x8_t){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
-        o[db] = mfma_f16_32x32x16(a, ph, o[db]);
-      }
+    for (int db = 0; db < 4; ++db) {
+      const int dim0 = 32 * db + 16 * (grp & 1) + 4 * (jj & 3);
+      const s16x4 a0 = lds_tr16(xl + kv_off(key_a, 2 * dim0));
+      const s16x4 a1 = lds_tr16(xl + kv_off(key_a + 4, 2 * dim0));
+      const i32x4 a = __builtin_bit_cast(i32x4, (s16x8_t){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
+      o[db] = mfma_f16_32x32x16(a, ph, o[db]);
     }
+  }
 }
 
 // bf16 -> fp16 copy of n8 16-byte units (exact for values in fp16's normal range).
@@ -150,16 +149,16 @@ __global__ __launch_bounds__(256) void to_f16_kernel(const uint16_t* __restrict_
 constexpr int kDqRows = 16;
 
 template <int G, int SUB>
-__global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
+__global__ __launch_bounds__(32 * G, G == 8 ? 2 : 1) void dedup_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dlt,
     const int32_t* __restrict__ cu, int Hq, int Hkv, float scale_log2, float scale, const int2* __restrict__ sched,
     const int* __restrict__ sched_count, int64_t ustride, const int32_t* __restrict__ ukeys,
     const uint16_t* __restrict__ umask, const int* __restrict__ ucount, float* __restrict__ dq) {
-  constexpr int D = 128, BN = 64, NTH = 32 * G, UPT = 1024 / NTH, RW = 32 / G;
+  constexpr int D = 128, BN = 64, NTH = 32 * G, RW = 32 / G;
   static_assert(G == 2 || G == 4 || G == 8 || G == 16, "a wave's 32 query vectors must span whole rows");
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2][2][kKvTileB];  // [buffer][K=0/V=1], fp16
-  __shared__ int upos[2][BN];
+  __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[2][2][kKvTileB];  // [buffer][K=0/V=1], fp16
+  __shared__ int upos[2][BN], umk[2][BN];  // union positions and row masks of upcoming tiles
   const int n = blockIdx.x / (Hkv * SUB);
   const int gv = blockIdx.x % (Hkv * SUB);  // query-head group
   const int g = gv / SUB;                    // its KV head
@@ -200,23 +199,25 @@ __global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
 
-  i32x4 pre[2 * UPT];
-  auto gload = [&](const int* pos) {
+  // K and V rows of the next tile, copied straight into LDS: copy x of this wave fills rows
+  // 4 (CPW w + x) + lane/16 of the tile, LDS unit lane % 16 holding unit (lane % 16) ^ s(row)
+  // (the kv_off swizzle); the positions come from upos.
+  constexpr int CPW = 16 / (NTH / 64);  // 1 KB copies per wave and matrix
+  lds_u8* const lb = (lds_u8*)&kv_lds[0][0][0];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lb;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint16_t* const kg = k + seq0 * kvs + g * D;
+  const uint16_t* const vg = v + seq0 * kvs + g * D;
+  const uint32_t rowb = uint32_t(kvs) * 2;
+  auto copies = [&](int slot, int buf) {
 #pragma unroll
-    for (int x = 0; x < UPT; ++x) {
-      const int u = tid + NTH * x;
-      const int64_t row = seq0 + pos[u >> 4];
-      pre[x] = *reinterpret_cast<const i32x4*>(k + row * kvs + g * D + 8 * (u & 15));
-      pre[UPT + x] = *reinterpret_cast<const i32x4*>(v + row * kvs + g * D + 8 * (u & 15));
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int x = 0; x < UPT; ++x) {
-      const int u = tid + NTH * x;
-      const int off = kv_off(u >> 4, 16 * (u & 15));
-      *reinterpret_cast<i32x4*>(&kv_lds[buf][0][off]) = pre[x];
-      *reinterpret_cast<i32x4*>(&kv_lds[buf][1][off]) = pre[UPT + x];
+    for (int x = 0; x < CPW; ++x) {
+      const int r = 4 * (CPW * wu + x) + (lane >> 4);
+      const int sw = ((r & 3) << 2) | ((r >> 2) & 3);
+      const uint32_t off = uint32_t(upos[slot][r]) * rowb + 16 * ((lane & 15) ^ sw);
+      const uint32_t dst = lds0 + buf * 2 * kKvTileB + 1024 * (CPW * wu + x);
+      dn_copy16(kg, off, dst);
+      dn_copy16(vg, off, dst + kKvTileB);
     }
   };
 
@@ -224,18 +225,23 @@ __global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
     if (tid < BN) {
       upos[0][tid] = uk[min(tid, U - 1)];
       upos[1][tid] = uk[min(BN + tid, U - 1)];
+      umk[0][tid] = (tid < U) ? int(um[tid]) : 0;
     }
     __syncthreads();
-    gload(upos[0]);
-    lstore(0);
+    copies(0, 0);
   }
-  __syncthreads();
-  int buf = 0, t = 0;
+  dn_sync();  // tile 0 has landed
+  int t = 0;
   for (int u0 = 0; u0 < U; u0 += BN, ++t) {
-    const bool more = u0 + BN < U;
-    if (more) gload(upos[(t + 1) & 1]);
-    const int pos2 = (tid < BN) ? uk[min(u0 + 2 * BN + tid, U - 1)] : 0;
-    const int mk = (u0 + lane < U) ? int(um[u0 + lane]) : 0;
+    const int buf = t & 1;
+    if (u0 + BN < U) copies(buf ^ 1, buf ^ 1);
+    // positions of tile t+2 and masks of tile t+1, stored at the end of the iteration
+    int pos2 = 0, mk1 = 0;
+    if (tid < BN) {
+      pos2 = uk[min(u0 + 2 * BN + tid, U - 1)];
+      mk1 = (u0 + BN + tid < U) ? int(um[u0 + BN + tid]) : 0;
+    }
+    const int mk = umk[buf][lane];
     uint64_t myword = 0;
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
@@ -246,9 +252,8 @@ __global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
     const uint32_t mlo = uint32_t(mw), mhi = uint32_t(mw >> 32);
     const uint8_t* kl = kv_lds[buf][0];
     const uint8_t* vl = kv_lds[buf][1];
-    float gz[2][16];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < 2; ++rb) {  // keys 32 rb .. 32 rb + 31 of the tile: S, dP, dS, dq^T += K^T dS^T
       f32x16 sacc, pacc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -261,19 +266,21 @@ __global__ __launch_bounds__(32 * G) void dedup_dq_kernel(
         sacc = mfma_f16_32x32x16(*reinterpret_cast<const i32x4*>(kl + kv_off(key, 32 * s2 + 16 * hf)), qf[s2], sacc);
         pacc = mfma_f16_32x32x16(*reinterpret_cast<const i32x4*>(vl + kv_off(key, 32 * s2 + 16 * hf)), df[s2], pacc);
       }
+      float gz[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const uint32_t bit = 1u << (16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3));
         const bool on = ((rb ? mhi : mlo) & bit) != 0u;
-        const float p = on ? __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -lse2)) : 0.f;
-        gz[rb][i] = p * (pacc[i] - dlt);
+        const float p = __builtin_amdgcn_exp2f(on ? fmaf(sacc[i], scale_log2, -lse2) : -__builtin_inff());
+        gz[i] = p * (pacc[i] - dlt);
       }
+      accumulate_xt_gt_f16(kl, gz, rb, lane, o);
     }
-    accumulate_xt_gt_f16(kl, gz, lane, o);
-    if (more) lstore(buf ^ 1);
-    if (tid < BN) upos[t & 1][tid] = pos2;
-    __syncthreads();
-    buf ^= 1;
+    if (tid < BN) {
+      upos[buf][tid] = pos2;
+      umk[buf ^ 1][tid] = mk1;
+    }
+    dn_sync();  // tile t+1 has landed; everyone is past tile t
   }
   if (my_r >= nr) return;
   float* op = dq + ((seq0 + i0 + my_r) * Hq + head) * D;

@@ -368,25 +368,30 @@ __global__ __launch_bounds__(128) void bwd_prep_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// sparse_dkv_kernel<G>: grid (128-key blocks, KV heads, row slices), 4 waves x 32 keys.  The
-// rows of the slice stream through LDS in half tiles of 32 (row, head) vectors, copied straight
-// from global memory into two rings: the S ring (5 slots: fp16 Q and dO rows, the A operands
-// of S^T = K Q^T and dP^T = V dO^T, plus -lse log2 e and -D of each vector and the 128 keys'
-// selection words) and the A ring (4 slots: the transposed fp16 Q^T and dO^T, the A operands of
-// dk^T += Q^T dS^T and dv^T += dO^T P^T).  Iteration h computes S and dP of half tile h+1,
-// P = 2^(S scale log2 e - lse log2 e) masked by the selection bits and dS = P (dP - D) of half
-// tile h, and the dk/dv products of half tile h; the copies run three (A) and four (S) half
-// tiles ahead; one barrier per iteration.
+// sparse_dkv_kernel<G>: grid (128-key blocks, KV heads, row slices), 8 waves: waves 0-3 (the
+// producers) and waves 4-7 (the consumers) share key group w % 4 (32 keys, the MFMA columns).
+// The rows of the slice stream through LDS in half tiles of 32 (row, head) vectors, copied
+// straight from global memory into two rings: the S ring (4 slots, filled by the producers:
+// fp16 Q and dO rows, the A operands of S^T = K Q^T and dP^T = V dO^T, plus -lse log2 e and -D
+// of each vector and the 128 keys' selection words) and the A ring (3 slots, filled by the
+// consumers: the transposed fp16 Q^T and dO^T, the A operands of dk^T += Q^T dS^T and
+// dv^T += dO^T P^T).  In iteration h a producer computes S and dP of half tile h+1 while it
+// turns S and dP of half tile h into P = 2^(S scale log2 e - lse log2 e) (masked by the
+// selection bits) and dS = P (dP - D), rounded to fp16 into an exchange buffer; its consumer
+// accumulates the dk/dv products of half tile h-1 from the other exchange buffer.  One barrier
+// per iteration; the copies run three (S) and two (A) half tiles ahead.
 // ------------------------------------------------------------------------------------------
-constexpr int kDkvS = 17408;                    // S slot: Q rows | dO rows (32 x 256 B each) | small
-constexpr int kDkvSmall = 16384;                // -lse log2 e [32] | -D [32] | words [128] | spare [64]
-constexpr int kDkvA = 16384;                    // A slot: Q^T | dO^T (128 dims x 64 B each)
-constexpr int kDkvAring = 5 * kDkvS;            // A ring offset
-constexpr int kDkvLds = kDkvAring + 4 * kDkvA;  // 152576 bytes
-constexpr int kDkvCopies = 9;                   // copies per wave and iteration
+constexpr int kDkvS = 17408;                     // S slot: Q rows | dO rows (32 x 256 B each) | small
+constexpr int kDkvSmall = 16384;                 // -lse log2 e [32] | -D [32] | words [128] | spare [64]
+constexpr int kDkvA = 16384;                     // A slot: Q^T | dO^T (128 dims x 64 B each)
+constexpr int kDkvAring = 4 * kDkvS;             // A ring offset
+constexpr int kDkvX = kDkvAring + 3 * kDkvA;     // exchange buffers: [2][key group][P0 P1 dS0 dS1][64 lanes][16 B]
+constexpr int kDkvLds = kDkvX + 2 * 4 * 4096;    // 151552 bytes
+constexpr int kDkvCopiesS = 5;                   // copies per producer and iteration
+constexpr int kDkvCopiesA = 4;                   // copies per consumer and iteration
 
 template <int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_dkv_kernel(
+__global__ __launch_bounds__(512) void sparse_dkv_kernel(
     const uint16_t* __restrict__ qh, const uint16_t* __restrict__ kh, const uint16_t* __restrict__ vh,
     const uint16_t* __restrict__ doh, const uint16_t* __restrict__ qt, const uint16_t* __restrict__ dot,
     const float* __restrict__ stats, int64_t ncols, const int32_t* __restrict__ cu, int Hq, int Hkv,
@@ -404,17 +409,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int s0 = 128 * e.y;
   const int t_lo = max(s0, slice * kBwdSlice), t_hi = min(L, (slice + 1) * kBwdSlice);
   const int tid = threadIdx.x, lane = tid & 63, qc = lane & 31, hf = lane >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = wv & 3;                 // key group
+  const bool producer = wv < 4;
   const int my_s = s0 + 32 * w + qc;
   const bool valid = my_s < L;
-  f32x16 dka[4], dva[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    dka[db] = (f32x16){};
-    dva[db] = (f32x16){};
-  }
-  if (t_lo < t_hi) {
-    const int nh = (t_hi - t_lo + RH - 1) / RH;
+  lds_u8* const lb = (lds_u8*)lds;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lb;
+  const int nh = (t_hi - t_lo + RH - 1) / RH;  // half tiles (0 if the slice holds none of the block's rows)
+  auto tile_row = [&](int x) { return t_lo + RH * min(x, nh - 1); };
+  const int64_t cb = bwd_col_base(seq0, G, b);
+
+  if (producer) {
+    if (nh <= 0) return;
     const int srow = min(my_s, L - 1);
     const int64_t kvs = (int64_t)Hkv * D;
     // K and V of the lane's key (B operands of S^T and dP^T): dims 16 s2 + 8 hf .. +7
@@ -430,73 +437,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2) asm volatile("" : "+v"(kf[s2]), "+v"(vf[s2]));  // landed before any copy
     }
-    lds_u8* const lb = (lds_u8*)lds;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)lb;
-    const int64_t cb = bwd_col_base(seq0, G, b);
     const uint16_t* const qnb = qh + (seq0 * Hq + g * G) * D;  // row r, head hh: + (r Hq + hh) D
     const uint16_t* const dnb = doh + (seq0 * Hq + g * G) * D;
-    const uint16_t* const qtb = qt + int64_t(g) * D * ncols + cb;  // dim d, vector j: + d ncols + j
-    const uint16_t* const dtb = dot + int64_t(g) * D * ncols + cb;
     const float* const stb = stats + int64_t(g) * 2 * ncols + cb;
     const int Lp = (L + 3) & ~3;
     const uint32_t* const wb = W + bitmap_offset(cu, b) + s0;
-
-    // Copies of half tile x, clamped to the last one (the extra copies of the final iterations
-    // land in slots nobody reads again).  S slot: rows 4(2w + i) + lane/16 of the Q and dO
-    // stages, 16-byte unit (lane % 16) holding unit (lane % 16) ^ (row % 16); small region:
-    // lanes 0..15 of wave w fill bytes 256 w .. (wave 0: -lse log2 e and -D, waves 1 and 2: the
-    // words of keys 0..63 and 64..127, wave 3: a spare copy of the statistics).  A slot: dim rows
-    // 16(2w + i) + lane/4, unit (lane % 4) holding unit (lane % 4) ^ ((dim / 4) % 4).  Every wave
-    // issues 9 copies per half tile.
-    uint32_t at_off[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int d = 16 * (2 * w + i) + (lane >> 2);
-      at_off[i] = uint32_t(d) * uint32_t(ncols) * 2 + 16 * ((lane & 3) ^ ((d >> 2) & 3));
-    }
+    // S part x (clamped to the last half tile): rows 4(2w + i) + lane/16 of the Q and dO stages,
+    // 16-byte unit (lane % 16) holding unit (lane % 16) ^ (row % 16); small region: lanes 0..15
+    // fill bytes 256 w .. (wave 0: -lse log2 e and -D, waves 1 and 2: the words of keys 0..63 and
+    // 64..127, wave 3: a spare copy of the statistics).  Five copies per producer.
     const uint32_t sm_off = (w == 1 || w == 2) ? uint32_t(256 * (w - 1) + 16 * (lane & 15))
                                                : ((lane & 8) ? uint32_t(ncols) * 4 : 0u) + 16 * (lane & 7);
-    auto tile_row = [&](int x) { return t_lo + RH * min(x, nh - 1); };
-    auto copy_small = [&](int x) {
-      const int t0 = tile_row(x);
-      const void* src = (w == 1 || w == 2) ? (const void*)(wb + int64_t(t0 >> 5) * Lp) : (const void*)(stb + int64_t(G) * t0);
-      dn_copy16_lo16(src, sm_off, lds0 + (x % 5) * kDkvS + kDkvSmall + 256 * w);
-    };
-    auto copy_srow = [&](int x, int i) {  // Q and dO rows 4(2w + i) .. +3
-      const int t0 = tile_row(x);
-      const int vi = 4 * (2 * w + i) + (lane >> 4);
-      const int r = min(t0 + vi / G, t_hi - 1);
-      const uint32_t off = uint32_t(r * Hq + vi % G) * 256 + 16 * ((lane & 15) ^ (vi & 15));
-      const uint32_t dst = lds0 + (x % 5) * kDkvS + 1024 * (2 * w + i);
-      dn_copy16(qnb, off, dst);
-      dn_copy16(dnb, off, dst + 8192);
-    };
-    auto copy_arow = [&](int x, int i) {  // Q^T and dO^T dim rows 16(2w + i) .. +15
-      const int64_t c0 = int64_t(G) * tile_row(x);
-      const uint32_t dst = lds0 + kDkvAring + (x & 3) * kDkvA + 1024 * (2 * w + i);
-      dn_copy16(qtb + c0, at_off[i], dst);
-      dn_copy16(dtb + c0, at_off[i], dst + 8192);
-    };
     auto copies_s = [&](int x) {
-      copy_small(x);
-      copy_srow(x, 0);
-      copy_srow(x, 1);
+      const int t0 = tile_row(x);
+      const uint32_t slot = lds0 + (x & 3) * kDkvS;
+      const void* src = (w == 1 || w == 2) ? (const void*)(wb + int64_t(t0 >> 5) * Lp) : (const void*)(stb + int64_t(G) * t0);
+      dn_copy16_lo16(src, sm_off, slot + kDkvSmall + 256 * w);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int vi = 4 * (2 * w + i) + (lane >> 4);
+        const int r = min(t0 + vi / G, t_hi - 1);
+        const uint32_t off = uint32_t(r * Hq + vi % G) * 256 + 16 * ((lane & 15) ^ (vi & 15));
+        dn_copy16(qnb, off, slot + 1024 * (2 * w + i));
+        dn_copy16(dnb, off, slot + 8192 + 1024 * (2 * w + i));
+      }
     };
-    auto copies_a = [&](int x) {
-      copy_arow(x, 0);
-      copy_arow(x, 1);
-    };
-
-    // LDS read addresses.  S operands: row kperm(qc), unit 2 s2 + hf -> byte qn_off ^ 32 s2.
-    // dk/dv operands: dim row 32 db + qc, unit 2 kk + hf -> byte 2048 db + (qa_off ^ 32 kk).
+    // S operand reads: row kperm(qc), unit 2 s2 + hf -> byte qn_off ^ 32 s2 (slot offsets are
+    // multiples of 64, so the unit XOR commutes with them)
     const int vrow = kperm(qc);
     const int qn_off = 256 * vrow + 16 * (hf ^ (vrow & 15));
-    const int qa_off = 64 * qc + 16 * (hf ^ ((qc >> 2) & 3));
-    // statistics of the lane's accumulator rows (the vectors 16(j/2) + 8 hf + 4(j%2) .. +3 of the
-    // half tile, j < 4): -lse log2 e and -D
+    // statistics of the lane's accumulator rows (vectors 16(j/2) + 8 hf + 4(j%2) .. +3, j < 4)
     float lc[16], dc[16];
     auto load_stats = [&](int x) {
-      const lds_u8* sm = lb + (x % 5) * kDkvS + kDkvSmall;
+      const lds_u8* sm = lb + (x & 3) * kDkvS + kDkvSmall;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int v0 = 16 * (j >> 1) + 8 * hf + 4 * (j & 1);
@@ -514,63 +487,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     auto load_bits = [&](int x) -> uint32_t {
       const int t0 = t_lo + RH * x;
       const uint32_t word = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
-          lb + (x % 5) * kDkvS + kDkvSmall + 256 + 4 * (32 * w + qc));
+          lb + (x & 3) * kDkvS + kDkvSmall + 256 + 4 * (32 * w + qc));
       const uint32_t keep = (valid && my_s <= 32 * (t0 >> 5) + 31) ? 0xFFFFFFFFu : 0u;
       const uint32_t bits = (word >> (t0 & 31)) & ((1u << RH) - 1u) & keep;
       return (G == 16) ? bits : (bits >> ((8 * hf) / G));
     };
-
-    // prologue: S parts 0..2 and A parts 0..1 land, S part 3 and A part 2 stay in flight
-    copies_s(0);
-    copies_s(1);
-    copies_s(2);
-    copies_a(0);
-    copies_a(1);
-    copies_s(3);
-    copies_a(2);
-    lds_sync_vm<kDkvCopies>();
-    f32x16 sn, pn;  // S and dP of the next half tile (MFMA accumulators)
-    f32x16 sc, pc;  // S and dP of the current half tile (read by the exponentials)
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
-      sn = mfma_f16_32x32x16(dn_ld128(lb + (qn_off ^ (32 * s2))), kf[s2], s2 ? sn : (f32x16){});
-      pn = mfma_f16_32x32x16(dn_ld128(lb + 8192 + (qn_off ^ (32 * s2))), vf[s2], s2 ? pn : (f32x16){});
-    }
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      float xs = sn[m], xq = pn[m];
-      asm volatile("" : "+v"(xs), "+v"(xq));  // VGPR copies, as the loop makes them
-      sc[m] = xs;
-      pc[m] = xq;
-    }
-    load_stats(0);
-    uint32_t bits = load_bits(0);
-    i32x4 op[35];  // A operands of the MFMA slots; 32..34 are slots 0..2 of the next iteration
-
-    // Iteration h: MFMA slots 0-7 S/dP(h+1) k-steps 0-3, 8-15 dk/dv(h) kk = 0, 16-23 S/dP(h+1)
-    // k-steps 4-7, 24-31 dk/dv(h) kk = 1.  Operand reads run three slots ahead (into the next
-    // iteration: S part h+2 has landed); slots 1-5 issue the copies of S part h+4 and A part h+3.
-    // P and dS of register i are computed in slot i; slot 16 loads the statistics and selection
-    // bits of half tile h+1; slots 26-31 move S(h+1) and dP(h+1) to the registers the next
-    // iteration's exponentials read.
-    auto body = [&](int h) {
-      // slot offsets are multiples of 64: the unit XORs commute with them
-      const int sq = ((h + 1) % 5) * kDkvS + qn_off;
-      const int sq2 = ((h + 2) % 5) * kDkvS + qn_off;
-      const int aq = kDkvAring + (h & 3) * kDkvA + qa_off;
-      const uint32_t bh = bits;
+    // S and dP of half tile x into (s, p), operand reads two MFMAs ahead
+    auto chains = [&](int x, f32x16& s, f32x16& p) {
+      const int sq = (x & 3) * kDkvS + qn_off;
+      i32x4 op[16];
+      auto rd = [&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        op[j] = dn_ld128(lb + (sq ^ (32 * (j >> 1))) + ((j & 1) ? 8192 : 0));
+      };
+      rd(dn_ic<0>{});
+      rd(dn_ic<1>{});
+      auto step = [&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        if constexpr (j + 2 < 16) rd(dn_ic<j + 2>{});
+        if constexpr (j & 1) p = mfma_f16_32x32x16(op[j], vf[j >> 1], (j >> 1) ? p : (f32x16){});
+        else s = mfma_f16_32x32x16(op[j], kf[j >> 1], (j >> 1) ? s : (f32x16){});
+      };
+      step(dn_ic<0>{});  step(dn_ic<1>{});  step(dn_ic<2>{});  step(dn_ic<3>{});
+      step(dn_ic<4>{});  step(dn_ic<5>{});  step(dn_ic<6>{});  step(dn_ic<7>{});
+      step(dn_ic<8>{});  step(dn_ic<9>{});  step(dn_ic<10>{}); step(dn_ic<11>{});
+      step(dn_ic<12>{}); step(dn_ic<13>{}); step(dn_ic<14>{}); step(dn_ic<15>{});
+    };
+    // one producer iteration: S, dP of half tile h+1 (16 MFMAs) with P and dS of half tile h
+    // (element i in slot i) computed between them; P and dS go to exchange buffer h % 2
+    auto body = [&](int h, const f32x16& sc, const f32x16& pc, f32x16& sn, f32x16& pn) {
+      copies_s(h + 3);
+      load_stats(h);
+      const uint32_t bh = load_bits(h);
+      const int sq = ((h + 1) & 3) * kDkvS + qn_off;
+      i32x4 op[16];
       i32x4 ppk[2], dpk[2];
       float pv[2], dv2[2];
       auto rd = [&](auto jj) {
         constexpr int j = decltype(jj)::value;
-        constexpr int part = (j >> 3) & 3, k = j & 7;
-        if constexpr ((part & 1) == 0) {
-          constexpr int s2 = 4 * (part >> 1) + (k >> 1);
-          op[j] = dn_ld128(lb + (((j < 32) ? sq : sq2) ^ (32 * s2)) + ((k & 1) ? 8192 : 0));
-        } else {
-          constexpr int kk = part >> 1, db = k >> 1;
-          op[j] = dn_ld128(lb + (aq ^ (32 * kk)) + ((k & 1) ? 0 : 8192) + 2048 * db);
-        }
+        op[j] = dn_ld128(lb + (sq ^ (32 * (j >> 1))) + ((j & 1) ? 8192 : 0));
       };
       auto ev = [&](auto ii) {
         constexpr int i = decltype(ii)::value;
@@ -588,83 +543,116 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           dpk[i >> 3][(i & 7) >> 1] = xd;
         }
       };
+      rd(dn_ic<0>{});
+      rd(dn_ic<1>{});
       auto slot = [&](auto jj) {
         constexpr int j = decltype(jj)::value;
-        constexpr int part = j >> 3, k = j & 7;
-        rd(dn_ic<j + 3>{});
-        i32x4 a;
-        if constexpr (j < 3) a = op[32 + j];
-        else a = op[j];
-        if constexpr ((part & 1) == 0) {
-          constexpr int s2 = 4 * (part >> 1) + (k >> 1);
-          if constexpr (k & 1) pn = mfma_f16_32x32x16(a, vf[s2], s2 ? pn : (f32x16){});
-          else sn = mfma_f16_32x32x16(a, kf[s2], s2 ? sn : (f32x16){});
-        } else {
-          constexpr int kk = part >> 1, db = k >> 1;
-          if constexpr (k & 1) dka[db] = mfma_f16_32x32x16(a, dpk[kk], dka[db]);
-          else dva[db] = mfma_f16_32x32x16(a, ppk[kk], dva[db]);
-        }
-        if constexpr (j == 1) copy_small(h + 4);
-        if constexpr (j == 2 || j == 3) copy_srow(h + 4, j - 2);
-        if constexpr (j == 4 || j == 5) copy_arow(h + 3, j - 4);
-        if constexpr (j < 16) ev(dn_ic<j>{});
-        if constexpr (j == 16) {
-          load_stats(h + 1);
-          bits = load_bits(h + 1);
-        }
-        if constexpr (j >= 26) {
-#pragma unroll
-          for (int m = 3 * (j - 26); m < 3 * (j - 26) + 3 && m < 16; ++m) {
-            float xs = sn[m], xq = pn[m];
-            asm volatile("" : "+v"(xs), "+v"(xq));  // moved in this slot
-            sc[m] = xs;
-            pc[m] = xq;
-          }
-        }
+        if constexpr (j + 2 < 16) rd(dn_ic<j + 2>{});
+        if constexpr (j & 1) pn = mfma_f16_32x32x16(op[j], vf[j >> 1], (j >> 1) ? pn : (f32x16){});
+        else sn = mfma_f16_32x32x16(op[j], kf[j >> 1], (j >> 1) ? sn : (f32x16){});
+        ev(dn_ic<j>{});
         __builtin_amdgcn_sched_barrier(0);
       };
-      slot(dn_ic<0>{});
-      slot(dn_ic<1>{});
-      slot(dn_ic<2>{});
-      slot(dn_ic<3>{});
-      slot(dn_ic<4>{});
-      slot(dn_ic<5>{});
-      slot(dn_ic<6>{});
-      slot(dn_ic<7>{});
-      slot(dn_ic<8>{});
-      slot(dn_ic<9>{});
-      slot(dn_ic<10>{});
-      slot(dn_ic<11>{});
-      slot(dn_ic<12>{});
-      slot(dn_ic<13>{});
-      slot(dn_ic<14>{});
-      slot(dn_ic<15>{});
-      slot(dn_ic<16>{});
-      slot(dn_ic<17>{});
-      slot(dn_ic<18>{});
-      slot(dn_ic<19>{});
-      slot(dn_ic<20>{});
-      slot(dn_ic<21>{});
-      slot(dn_ic<22>{});
-      slot(dn_ic<23>{});
-      slot(dn_ic<24>{});
-      slot(dn_ic<25>{});
-      slot(dn_ic<26>{});
-      slot(dn_ic<27>{});
-      slot(dn_ic<28>{});
-      slot(dn_ic<29>{});
-      slot(dn_ic<30>{});
-      slot(dn_ic<31>{});
-      // the copies of iteration h-1 have landed (S part h+3, A part h+2) and every wave is past
-      // its reads of A part h (the slot the next iteration's copies overwrite)
-      lds_sync_vm_nolgkm<kDkvCopies>();
+      slot(dn_ic<0>{});  slot(dn_ic<1>{});  slot(dn_ic<2>{});  slot(dn_ic<3>{});
+      slot(dn_ic<4>{});  slot(dn_ic<5>{});  slot(dn_ic<6>{});  slot(dn_ic<7>{});
+      slot(dn_ic<8>{});  slot(dn_ic<9>{});  slot(dn_ic<10>{}); slot(dn_ic<11>{});
+      slot(dn_ic<12>{}); slot(dn_ic<13>{}); slot(dn_ic<14>{}); slot(dn_ic<15>{});
+      __attribute__((address_space(3))) i32x4* xb =
+          reinterpret_cast<__attribute__((address_space(3))) i32x4*>(lb + kDkvX + (h & 1) * 16384 + 4096 * w) + lane;
+      xb[0] = ppk[0];
+      xb[64] = ppk[1];
+      xb[128] = dpk[0];
+      xb[192] = dpk[1];
+      lds_sync_vm<kDkvCopiesS>();  // S part h+2 has landed; the exchange buffer is written
     };
-    // reads of iteration 0's first slots
-    op[32] = dn_ld128(lb + (kDkvS + qn_off));
-    op[33] = dn_ld128(lb + (kDkvS + qn_off) + 8192);
-    op[34] = dn_ld128(lb + ((kDkvS + qn_off) ^ 32));
-    for (int h = 0; h < nh; ++h) body(h);
+    // prologue: S parts 0..1 land (part 2 stays in flight); S(0), dP(0)
+    copies_s(0);
+    copies_s(1);
+    copies_s(2);
+    lds_sync_vm<kDkvCopiesS>();
+    f32x16 sa, pa, sb, pb2;
+    chains(0, sa, pa);
+    int h = 0;
+    for (; h + 1 < nh; h += 2) {
+      body(h, sa, pa, sb, pb2);
+      body(h + 1, sb, pb2, sa, pa);
+    }
+    if (h < nh) {
+      body(h, sa, pa, sb, pb2);
+      ++h;
+    }
+    // iteration nh: the consumers take the last half tile
+    copies_s(nh + 3);
+    lds_sync_vm<kDkvCopiesS>();
     dn_sync();  // no copy is left in flight when the workgroup ends
+    return;
+  }
+
+  // ---- consumers: dk^T += Q^T dS^T, dv^T += dO^T P^T of half tile h-1 in iteration h
+  f32x16 dka[4], dva[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    dka[db] = (f32x16){};
+    dva[db] = (f32x16){};
+  }
+  if (nh > 0) {
+    const uint16_t* const qtb = qt + int64_t(g) * D * ncols + cb;  // dim d, vector j: + d ncols + j
+    const uint16_t* const dtb = dot + int64_t(g) * D * ncols + cb;
+    // A part x (clamped): dim rows 16(2w + i) + lane/4, unit (lane % 4) holding unit
+    // (lane % 4) ^ ((dim / 4) % 4).  Four copies per consumer.
+    uint32_t at_off[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int d = 16 * (2 * w + i) + (lane >> 2);
+      at_off[i] = uint32_t(d) * uint32_t(ncols) * 2 + 16 * ((lane & 3) ^ ((d >> 2) & 3));
+    }
+    auto copies_a = [&](int x) {
+      const int64_t c0 = int64_t(G) * tile_row(x);
+      const uint32_t slot = lds0 + kDkvAring + (x % 3) * kDkvA;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        dn_copy16(qtb + c0, at_off[i], slot + 1024 * (2 * w + i));
+        dn_copy16(dtb + c0, at_off[i], slot + 8192 + 1024 * (2 * w + i));
+      }
+    };
+    // operand reads: dim row 32 db + qc, unit 2 kk + hf -> byte 2048 db + (qa_off ^ 32 kk)
+    const int qa_off = 64 * qc + 16 * (hf ^ ((qc >> 2) & 3));
+    auto body = [&](int x) {  // the products of half tile x
+      const int aq = kDkvAring + (x % 3) * kDkvA + qa_off;
+      const __attribute__((address_space(3))) i32x4* xb =
+          reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(lb + kDkvX + (x & 1) * 16384 + 4096 * w) +
+          lane;
+      const i32x4 ppk[2] = {xb[0], xb[64]};
+      const i32x4 dpk[2] = {xb[128], xb[192]};
+      i32x4 op[16];
+      auto rd = [&](auto jj) {  // MFMA j: kk = j / 8, db = (j % 8) / 2, dv (j even, dO^T) or dk (Q^T)
+        constexpr int j = decltype(jj)::value;
+        op[j] = dn_ld128(lb + (aq ^ (32 * (j >> 3))) + ((j & 1) ? 0 : 8192) + 2048 * ((j & 7) >> 1));
+      };
+      rd(dn_ic<0>{});
+      rd(dn_ic<1>{});
+      rd(dn_ic<2>{});
+      auto step = [&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        constexpr int kk = j >> 3, db = (j & 7) >> 1;
+        if constexpr (j + 3 < 16) rd(dn_ic<j + 3>{});
+        if constexpr (j & 1) dka[db] = mfma_f16_32x32x16(op[j], dpk[kk], dka[db]);
+        else dva[db] = mfma_f16_32x32x16(op[j], ppk[kk], dva[db]);
+      };
+      step(dn_ic<0>{});  step(dn_ic<1>{});  step(dn_ic<2>{});  step(dn_ic<3>{});
+      step(dn_ic<4>{});  step(dn_ic<5>{});  step(dn_ic<6>{});  step(dn_ic<7>{});
+      step(dn_ic<8>{});  step(dn_ic<9>{});  step(dn_ic<10>{}); step(dn_ic<11>{});
+      step(dn_ic<12>{}); step(dn_ic<13>{}); step(dn_ic<14>{}); step(dn_ic<15>{});
+    };
+    // prologue: A part 0 in flight (it lands by the end of iteration 0)
+    copies_a(0);
+    lds_sync_vm<kDkvCopiesA>();
+    for (int h = 0; h <= nh; ++h) {
+      copies_a(h + 1);
+      if (h > 0) body(h - 1);
+      lds_sync_vm<kDkvCopiesA>();  // A part h has landed; this wave is past exchange buffer h-1
+    }
+    dn_sync();
   }
   if (!valid) return;
   const int64_t orow = ((int64_t)slice * T + seq0 + my_s) * Hkv + g;
@@ -780,7 +768,7 @@ hipError_t launch_sparse_dkv(const uint16_t* qh, const uint16_t* kh, const uint1
   switch (G) {
 #define DSA_DKV(GG)                                                                                              \
   case GG:                                                                                                       \
-    sparse_dkv_kernel<GG><<<grid, 256, 0, st>>>(qh, kh, vh, doh, qt, dot, stats, ncols, cu, Hq, Hkv, sl2, scale,  \
+    sparse_dkv_kernel<GG><<<grid, 512, 0, st>>>(qh, kh, vh, doh, qt, dot, stats, ncols, cu, Hq, Hkv, sl2, scale,  \
                                                 sched128, count128, W, T, dk_part, dv_part);                     \
     break;
     DSA_DKV(2)

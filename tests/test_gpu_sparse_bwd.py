@@ -3,11 +3,12 @@ dsa_sparse_attention_bwd, through the C ABI) against the float64 oracle
 (oracle/sparse_attention_bwd.py).
 
 Tolerances: the gradients use D = dO . O from the bf16 forward output (as the API takes it),
-whose rounding (2^-9 relative) reaches dS = P (dP - D) at ~1e-3 of its scale; P and dP are fp32
-(bf16 products, fp32 MFMA accumulation) and dS, P enter the final products split into bf16
-hi + lo (2^-16).  Bars: each gradient within 1e-2 of its largest reference magnitude element by
-element, and within mean-relative 3e-3; lse within 1e-4 absolute; out as the forward (max-abs
-1e-2, mean-rel 2e-3)."""
+whose rounding (2^-9 relative) reaches dS = P (dP - D) at ~1e-3 of its scale; S and dP are fp32
+(fp16 copies of the bf16 inputs, exact in fp16's normal range, and fp32 MFMA accumulation) and
+P and dS enter the final products rounded to fp16 (2^-11 relative, unbiased, so the mean error
+of a sum over many keys shrinks with their count).  Bars: each gradient within 1e-2 of its
+largest reference magnitude element by element, and within mean-relative 3e-3; lse within 1e-4
+absolute; out as the forward (max-abs 1e-2, mean-rel 2e-3)."""
 import numpy as np
 import pytest
 import torch

@@ -52,6 +52,11 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
       (__attribute__((address_space(3))) s16x4*)(const_cast<uint8_t*>(p)));
 }
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ s16x4 lds_tr16_l(const lds_u8* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(const_cast<lds_u8*>(p)));
+}
+
 // 16-byte unit swizzle inside a K/V row: unit u of key r sits at u ^ (4 (r % 4) + (r / 4) % 4).
 // Conflict-free for the 16-byte operand reads of 16 consecutive keys (rows kperm(0..15) are 16
 // distinct keys mod 16) and for the transposed 8-byte reads (4 consecutive keys x 4 units).
@@ -60,7 +65,6 @@ __device__ __forceinline__ int kv_off(int key, int byte) {
 }
 
 // ---- direct global -> LDS copies
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // 16 bytes per lane from global memory (base + off, base wave-uniform) to LDS address
 // lds_addr + 16 * lane (lds_addr wave-uniform).  Issued from asm so that the compiler's own

@@ -36,7 +36,7 @@ hipError_t launch_row_order(const int32_t* idx, int K, const int32_t* cu, int ns
                             int* sig, int* cnt, int32_t* order, hipStream_t st);
 hipError_t launch_union(const int32_t* idx, int K, const int32_t* cu, const int2* sched, const int* count,
                         int nb_bound, int64_t ustride, int32_t* ukeys, uint16_t* umask, int* ucount, hipStream_t st);
-hipError_t launch_dedup_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu, int Hq,
+hipError_t launch_dedup_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vh, const int32_t* cu, int Hq,
                                   int Hkv, float scale, const int2* sched, const int* count, int nb_bound,
                                   int64_t ustride, const int32_t* ukeys, const uint16_t* umask, const int* ucount,
                                   uint16_t* out, hipStream_t st);
@@ -273,9 +273,10 @@ hipError_t build_schedule16(const dsa_prefill_shape* s, void* ws, const PrefillW
 }
 
 // Dedup workspace layout (adjacent-query union per 16-row block; 256-byte aligned):
-//   counts int[64] | sched16 int2[nb16] | ucount int[nb16] | ukeys int32[nb16][16k] | umask uint16[nb16][16k]
+//   counts int[64] | sched16 int2[nb16] | ucount int[nb16] | ukeys int32[nb16][16k] | umask uint16[nb16][16k] |
+//   fp16 copy of V [T][Hkv][128]
 struct DedupWs {
-  size_t counts, sched16, ucount, ukeys, umask, total;
+  size_t counts, sched16, ucount, ukeys, umask, vh, total;
   int nb16;
   int64_t ustride;
 };
@@ -290,6 +291,7 @@ DedupWs dedup_layout(const dsa_prefill_shape* s) {
   w.ucount = off; off = align_up(off + size_t(w.nb16) * sizeof(int), 256);
   w.ukeys = off; off = align_up(off + size_t(w.nb16) * size_t(w.ustride) * sizeof(int32_t), 256);
   w.umask = off; off = align_up(off + size_t(w.nb16) * size_t(w.ustride) * sizeof(uint16_t), 256);
+  w.vh = off; off = align_up(off + size_t(s->total_tokens) * size_t(s->kv_heads) * 128 * sizeof(uint16_t), 256);
   w.total = off;
   return w;
 }
@@ -548,7 +550,9 @@ int dedup_attention(const dsa_prefill_shape* s, const uint16_t* q, const uint16_
                                     at<int32_t>(dws, D.ukeys), at<uint16_t>(dws, D.umask), at<int>(dws, D.ucount),
                                     st))))
     return rc;
-  return hip_status(launch_dedup_attention(q, k, v, s->cu_seqlens, s->q_heads, s->kv_heads, s->softmax_scale,
+  uint16_t* vh = at<uint16_t>(dws, D.vh);
+  if ((rc = hip_status(launch_to_f16(v, vh, s->total_tokens * s->kv_heads * 128, st)))) return rc;
+  return hip_status(launch_dedup_attention(q, k, vh, s->cu_seqlens, s->q_heads, s->kv_heads, s->softmax_scale,
                                            sched16, count, nb16, D.ustride, at<int32_t>(dws, D.ukeys),
                                            at<uint16_t>(dws, D.umask), at<int>(dws, D.ucount), out, st));
 }

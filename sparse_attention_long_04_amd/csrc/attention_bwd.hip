@@ -712,8 +712,10 @@ hipError_t launch_sel_bitmap(const int32_t* idx, int K, const int32_t* cu, const
 hipError_t launch_dedup_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                            const float* lse, const float* Dlt, const int32_t* cu, int Hq, int Hkv, float scale,
                            const int2* sched16, const int* count16, int nb16, int64_t ustride, const int32_t* ukeys,
-                           const uint16_t* umask, const int* ucount, float* dq, hipStream_t st) {
+                           const uint16_t* umask, const int* ucount, float* dq, int max_len, hipStream_t st) {
   if (nb16 == 0) return hipSuccess;
+  // the K/V copy offsets are 32-bit byte offsets from the sequence's first row
+  if (int64_t(max_len) * Hkv * 256 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
   const float sl2 = scale * 1.4426950408889634f;
   const unsigned grid = (unsigned)(nb16 * Hkv);
   switch (Hq / Hkv) {

@@ -365,8 +365,10 @@ hipError_t launch_union(const int32_t* idx, int K, const int32_t* cu, const int2
 hipError_t launch_dedup_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vh, const int32_t* cu, int Hq,
                                   int Hkv, float scale, const int2* sched, const int* count, int nb_bound,
                                   int64_t ustride, const int32_t* ukeys, const uint16_t* umask, const int* ucount,
-                                  uint16_t* out, hipStream_t st) {
+                                  uint16_t* out, int max_len, hipStream_t st) {
   if (nb_bound == 0) return hipSuccess;
+  // the K/V copy offsets are 32-bit byte offsets from the sequence's first row
+  if (int64_t(max_len) * Hkv * 256 >= (int64_t(1) << 32)) return hipErrorInvalidValue;
   const float sl2 = scale * 1.4426950408889634f;
   const unsigned grid = (unsigned)(nb_bound * Hkv);
   switch (Hq / Hkv) {

@@ -39,7 +39,7 @@ hipError_t launch_union(const int32_t* idx, int K, const int32_t* cu, const int2
 hipError_t launch_dedup_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vh, const int32_t* cu, int Hq,
                                   int Hkv, float scale, const int2* sched, const int* count, int nb_bound,
                                   int64_t ustride, const int32_t* ukeys, const uint16_t* umask, const int* ucount,
-                                  uint16_t* out, hipStream_t st);
+                                  uint16_t* out, int max_len, hipStream_t st);
 hipError_t launch_kl_lse(const uint16_t* q, const uint16_t* k, const int32_t* cu, int Hq, int Hkv, float scale,
                          const int2* sched128, const int* count128, int nb128, float* lse, hipStream_t st);
 hipError_t launch_kl_target(const uint16_t* q, const uint16_t* k, const int32_t* cu, int Hq, int Hkv, float scale,
@@ -63,7 +63,7 @@ hipError_t launch_sel_bitmap(const int32_t* idx, int K, const int32_t* cu, const
 hipError_t launch_dedup_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                            const float* lse, const float* Dlt, const int32_t* cu, int Hq, int Hkv, float scale,
                            const int2* sched16, const int* count16, int nb16, int64_t ustride, const int32_t* ukeys,
-                           const uint16_t* umask, const int* ucount, float* dq, hipStream_t st);
+                           const uint16_t* umask, const int* ucount, float* dq, int max_len, hipStream_t st);
 hipError_t launch_to_f16(const uint16_t* in, uint16_t* out, int64_t n, hipStream_t st);
 hipError_t launch_bwd_prep(const uint16_t* q, const uint16_t* dout, const float* lse, const float* Dlt,
                            const int32_t* cu, int nseq, int64_t T, int Hq, int Hkv, uint16_t* qh, uint16_t* doh,
@@ -554,7 +554,8 @@ int dedup_attention(const dsa_prefill_shape* s, const uint16_t* q, const uint16_
   if ((rc = hip_status(launch_to_f16(v, vh, s->total_tokens * s->kv_heads * 128, st)))) return rc;
   return hip_status(launch_dedup_attention(q, k, vh, s->cu_seqlens, s->q_heads, s->kv_heads, s->softmax_scale,
                                            sched16, count, nb16, D.ustride, at<int32_t>(dws, D.ukeys),
-                                           at<uint16_t>(dws, D.umask), at<int>(dws, D.ucount), out, st));
+                                           at<uint16_t>(dws, D.umask), at<int>(dws, D.ucount), out, s->max_seqlen,
+                                           st));
 }
 
 int check_dedup_ws(const dsa_prefill_shape* s, void* dws, size_t dws_bytes, DedupWs* D) {
@@ -786,7 +787,7 @@ int dsa_sparse_attention_bwd(const dsa_prefill_shape* s, const uint16_t* q, cons
           hipSuccess ||
       (e = launch_dedup_dq(qh, kh, vh, doh, lse, Dl, cu, s->q_heads, s->kv_heads, s->softmax_scale,
                            at<int2>(ws, W.sched16), counts, W.nb16, W.ustride, at<int32_t>(ws, W.ukeys),
-                           at<uint16_t>(ws, W.umask), at<int>(ws, W.ucount), dq, st)) != hipSuccess ||
+                           at<uint16_t>(ws, W.umask), at<int>(ws, W.ucount), dq, s->max_seqlen, st)) != hipSuccess ||
       (e = launch_sel_bitmap(topk_idx, s->topk, cu, at<int2>(ws, W.sched32), counts + 1, W.nb32,
                              at<uint32_t>(ws, W.bitmap), st)) != hipSuccess ||
       (e = launch_sparse_dkv(qh, kh, vh, doh, qt, dot, stats, cu, s->num_seqs, s->q_heads, s->kv_heads,

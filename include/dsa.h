@@ -155,7 +155,8 @@ int dsa_prefill_timed(const dsa_prefill_shape* shape, const void* q_idx, const v
  * per-(row, key) mask).  Same results as dsa_sparse_attention / dsa_prefill up to the order of
  * fp32 sums; fastest when adjacent rows' selections overlap.  Needs Hq/Hkv in {2, 4, 8, 16}
  * (DSA_ERR_UNSUPPORTED otherwise).  A separate "dedup workspace" (DEVICE, 16-byte aligned)
- * holds the block schedule and the unions (about T * k * 6 bytes).
+ * holds the block schedule, the unions (about T * k * 6 bytes) and an fp16 copy of V
+ * (T * Hkv * 256 bytes).
  * ------------------------------------------------------------------------------------- */
 
 /* Dedup workspace bytes for this shape (host only). */

@@ -395,7 +395,9 @@ __global__ __launch_bounds__(512) void kl_dq_kernel(const uint8_t* __restrict__ 
                                                     const float* __restrict__ gsc, float* __restrict__ dq,
                                                     float* __restrict__ dw) {
   constexpr int D = 128, BN = 64, R = 256 / HI;
+  static_assert(R % 4 == 0, "G rows are copied four at a time");
   __shared__ __attribute__((aligned(16))) uint8_t t_lds[2][2][kKvTileB];
+  __shared__ __attribute__((aligned(16))) float g_lds[2][R][BN];  // G of the block's rows for a key tile
   const int n = blockIdx.x;
   if (n >= *count) return;
   const int2 e = sched[n];
@@ -417,7 +419,22 @@ __global__ __launch_bounds__(512) void kl_dq_kernel(const uint8_t* __restrict__ 
   }
   const float wq = wgt[(seq0 + trow) * HI + head];
   const float wqs = wq * gsc[0], unscale = gsc[1];
-  const float* grow = tri_row(Gt, seqoff[b], trow);
+  // G[t][kt .. kt+63] of the block's rows for key tile kt, copied into g_lds[gb] one tile ahead:
+  // wave w < R/4 fills rows 4w .. 4w+3, 16 lanes per row (rows past the block end repeat its
+  // last row and chunks past a row's stored width re-read its last chunk: both masked later)
+  const int64_t soff = seqoff[b];
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t glds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&g_lds[0][0][0];
+  auto gcopy = [&](int kt, int gb) {
+    if (wu < R / 4) {
+      const int t = min(r0 + 4 * wu + (lane >> 4), kend - 1);
+      const int width = 16 * ((t >> 4) + 1);  // stored floats of row t
+      const int c = min(kt + 4 * (lane & 15), width - 4);
+      const float* base = tri_row(Gt, soff, min(r0 + 4 * wu, kend - 1));
+      const uint32_t off = uint32_t((tri_row(Gt, soff, t) - base) + c) * 4;
+      dn_copy16(base, off, glds0 + (gb * R + 4 * wu) * BN * 4);
+    }
+  };
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -429,12 +446,16 @@ __global__ __launch_bounds__(512) void kl_dq_kernel(const uint8_t* __restrict__ 
     pre = *reinterpret_cast<const uint4*>(k_idx + (seq0 + min(kt + (tid >> 3), kend - 1)) * D + 16 * (tid & 7));
   };
   gload(0);
+  gcopy(0, 0);
   fp8_tile_store(t_lds[0][0], t_lds[0][1], pre, tid);
-  __syncthreads();
+  dn_sync();
   int buf = 0;
   for (int kt = 0; kt < kend; kt += BN) {
     const bool more = kt + BN < kend;
-    if (more) gload(kt + BN);
+    if (more) {
+      gload(kt + BN);
+      gcopy(kt + BN, buf ^ 1);
+    }
     if (kt <= wave_tmax) {
       float gz[2][16];
 #pragma unroll
@@ -452,7 +473,7 @@ __global__ __launch_bounds__(512) void kl_dq_kernel(const uint8_t* __restrict__ 
         for (int a = 0; a < 4; ++a) {
           const int k0 = kt + 32 * rb + kperm(8 * a + 4 * hf);
           f32x4 g4 = {0.f, 0.f, 0.f, 0.f};
-          if (valid && k0 <= my_t) g4 = *reinterpret_cast<const f32x4*>(grow + k0);
+          if (valid && k0 <= my_t) g4 = *reinterpret_cast<const f32x4*>(&g_lds[buf][my_t - r0][k0 - kt]);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const float s = sacc[4 * a + c];
@@ -465,7 +486,7 @@ __global__ __launch_bounds__(512) void kl_dq_kernel(const uint8_t* __restrict__ 
       accumulate_xt_gt(t_lds[buf][1], gz, lane, o);
     }
     if (more) fp8_tile_store(t_lds[buf ^ 1][0], t_lds[buf ^ 1][1], pre, tid);
-    __syncthreads();
+    dn_sync();  // the next tile's G has landed
     buf ^= 1;
   }
   dwacc += __shfl_xor(dwacc, 32);
@@ -498,6 +519,7 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(const uint8_t* __restrict__ 
   constexpr int D = 128, BN = 64, RPT = BN / HI;  // rows per tile
   __shared__ __attribute__((aligned(16))) uint8_t t_lds[2][2][kKvTileB];
   __shared__ float w_lds[2][BN];
+  __shared__ __attribute__((aligned(16))) float g_lds[2][RPT][256];  // G of a tile's rows for the block's keys
   const int n = blockIdx.x;
   if (n >= *count) return;
   const int2 e = sched[n];
@@ -525,6 +547,20 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(const uint8_t* __restrict__ 
       for (int s2 = 0; s2 < 8; ++s2) kf[s2] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(kp + 16 * s2));
     }
     const int64_t v_begin = (int64_t)t_lo * HI, v_end = (int64_t)t_hi * HI;  // vectors of this slice
+    // G[t][s0 .. s0+255] of the tile's rows, copied into g_lds[gb] one tile ahead: wave w < RPT
+    // fills row w, 4 keys per lane (rows past the slice repeat its last row and chunks past a
+    // row's stored width re-read its last chunk: both masked later)
+    const int64_t soff = seqoff[b];
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const uint32_t glds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&g_lds[0][0][0];
+    auto gcopy = [&](int64_t v0, int gb) {
+      if (wu < RPT) {
+        const int tr = min(int(v0 / HI) + wu, t_hi - 1);
+        const int width = 16 * ((tr >> 4) + 1);  // stored floats of row tr
+        const int c = min(s0 + 4 * lane, width - 4);
+        dn_copy16(tri_row(Gt, soff, tr), uint32_t(c) * 4, glds0 + (gb * RPT + wu) * 1024);
+      }
+    };
     uint4 pre;
     float wpre = 0.f;
     auto gload = [&](int64_t v0) {
@@ -537,12 +573,16 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(const uint8_t* __restrict__ 
       if (tid < BN) w_lds[buf][tid] = wpre;
     };
     gload(v_begin);
+    gcopy(v_begin, 0);
     lstore(0);
-    __syncthreads();
+    dn_sync();
     int buf = 0;
     for (int64_t v0 = v_begin; v0 < v_end; v0 += BN) {
       const bool more = v0 + BN < v_end;
-      if (more) gload(v0 + BN);
+      if (more) {
+        gload(v0 + BN);
+        gcopy(v0 + BN, buf ^ 1);
+      }
       const int tt0 = int(v0 / HI);  // first row of the tile
       if (tt0 + RPT - 1 >= s0 + 32 * w) {  // some row of the tile sees some key of this wave
         // g[t, s] for the tile's rows (s <= t)
@@ -550,7 +590,7 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(const uint8_t* __restrict__ 
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
           const int tr = tt0 + r;
-          gr[r] = (valid && tr < t_hi && my_s <= tr) ? tri_row(Gt, seqoff[b], tr)[my_s] : 0.f;
+          gr[r] = (valid && tr < t_hi && my_s <= tr) ? g_lds[buf][r][32 * w + qc] : 0.f;
         }
         float gz[2][16];
 #pragma unroll
@@ -575,7 +615,7 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(const uint8_t* __restrict__ 
         accumulate_xt_gt(t_lds[buf][1], gz, lane, o);
       }
       if (more) lstore(buf ^ 1);
-      __syncthreads();
+      dn_sync();  // the next tile's G has landed
       buf ^= 1;
     }
   }

@@ -194,8 +194,10 @@ def test_dedup_workspace_layout_and_unsupported_groups():
     s = shape(T=4096, max_seqlen=4096, topk=2048)
     n = dsa.dsa_dedup_workspace_size(s)
     nb16 = 4096 // 16 + 1
-    assert n >= nb16 * 16 * 2048 * 6
-    assert n < nb16 * 16 * 2048 * 6 + (1 << 20)
+    unions = nb16 * 16 * 2048 * 6          # key positions (int32) and row masks (uint16) per block
+    vh = 4096 * s.kv_heads * 128 * 2       # the fp16 copy of V the masked products read
+    assert n >= unions + vh
+    assert n < unions + vh + (1 << 20)
     with pytest.raises(dsa.DSAError) as ei:
         dsa.dsa_dedup_workspace_size(shape(q_heads=24, kv_heads=4))   # G = 6
     assert ei.value.status == 2

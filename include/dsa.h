@@ -186,7 +186,7 @@ int dsa_prefill_dedup(const dsa_prefill_shape* shape, const void* q_idx, const v
  * c = q_I[t,h] . k_I[s]:  dw[t,h] = sum_s g max(0, c);  dq_I[t,h] = w[t,h] sum_s g [c>0] k_I[s];
  * dk_I[s] = sum_{t>=s} sum_h g w[t,h] [c>0] q_I[t,h].
  * Inputs as dsa_prefill (q, k bf16; V is not used); indexer e4m3 with d_I = 128 and
- * H_I in {16, 32, 64}; Hkv in {1, 2, 4}; Hq even (DSA_ERR_UNSUPPORTED otherwise).
+ * H_I in {16, 32, 64}; Hkv in {1, 2, 4} (DSA_ERR_UNSUPPORTED otherwise).
  * Outputs (DEVICE fp32): kl [T], dq_idx [T, H_I, d_I], dk_idx [T, d_I], dw_idx [T, H_I].
  * Deterministic (no float atomics).  Workspace: dsa_indexer_kl_workspace_size.
  * ------------------------------------------------------------------------------------- */

@@ -337,7 +337,6 @@ int check_kl(const dsa_prefill_shape* s) {
   if (s->idx_dtype != DSA_IDX_FP8_E4M3 || s->idx_dim != 128) return DSA_ERR_UNSUPPORTED;
   if (s->idx_heads != 16 && s->idx_heads != 32 && s->idx_heads != 64) return DSA_ERR_UNSUPPORTED;
   if (s->kv_heads != 1 && s->kv_heads != 2 && s->kv_heads != 4) return DSA_ERR_UNSUPPORTED;
-  if (s->q_heads % 2 != 0) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 

@@ -156,10 +156,14 @@ __global__ __launch_bounds__(256) void kl_lse_kernel(const uint16_t* __restrict_
 }
 
 // ------------------------------------------------------------------------------------------
-// kl_target_kernel: grid (128-row blocks, key chunks of kKlTargetChunk), 4 waves x 32 query
-// rows, all heads; 32-key tiles of the HKV KV heads double-buffered in LDS.
+// kl_target_kernel: grid (256-key chunks, 128-row blocks; chunks vary fastest, so the
+// workgroups resident together read the same rows' queries from L2), 4 waves x 32 query rows.
+// The chunk's p sums stay in registers (8 tiles x 16 per lane) for all Hq heads: per KV head,
+// its 256 K rows are copied into LDS (two buffers, the next KV head's copy in flight during the
+// current one), and every query head of the group takes its Q fragment from global memory once
+// per chunk (the next head's prefetched) for the 8 tiles.  Any Hq / HKV works.
 // ------------------------------------------------------------------------------------------
-constexpr int kKlTargetChunk = 2048;
+constexpr int kKlTargetChunk = 256;
 
 template <int HKV>
 __global__ __launch_bounds__(256) void kl_target_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -167,9 +171,9 @@ __global__ __launch_bounds__(256) void kl_target_kernel(const uint16_t* __restri
                                                         const int2* __restrict__ sched, const int* __restrict__ count,
                                                         const float* __restrict__ lse,
                                                         const int64_t* __restrict__ seqoff, float* __restrict__ P) {
-  constexpr int D = 128, BN = 32, TB = BN * kKvRowB, UPT = 2 * HKV;
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][HKV][TB];
-  const int n = blockIdx.x;
+  constexpr int D = 128, BN = 32, KC = kKlTargetChunk, NT = KC / BN, TB = KC * kKvRowB;
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][TB];
+  const int n = blockIdx.y;
   if (n >= *count) return;
   const int2 e = sched[n];
   const int b = e.x;
@@ -178,91 +182,108 @@ __global__ __launch_bounds__(256) void kl_target_kernel(const uint16_t* __restri
   const int L = cu[b + 1] - cu[b];
   const int q0 = 128 * e.y, kend = min(L, q0 + 128);
   // this workgroup's key chunk (the rows' outputs are independent across key ranges)
-  const int kbeg = kKlTargetChunk * blockIdx.y;
+  const int kbeg = KC * blockIdx.x;
   if (kbeg >= kend) return;
-  const int kstop = min(kend, kbeg + kKlTargetChunk);
+  const int kstop = min(kend, kbeg + KC);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 31, hf = lane >> 5;
   const int my_q = q0 + 32 * w + qc;
   const int qrow = min(my_q, kend - 1);
-  const int wave_qmax = q0 + 32 * w + 31;
-  const int64_t kvs = (int64_t)HKV * D;
-  const float inv_hq = 1.f / float(Hq);
-  i32x4 pre[UPT];
-  auto gload = [&](int kt) {
+  // tiles of the chunk that reach this wave's rows (none for a wave entirely before the chunk)
+  const int wlast = min(q0 + 32 * w + 31, kstop - 1);
+  const int nt = wlast < kbeg ? 0 : (wlast - kbeg) / BN + 1;
+  // K copy: wave w fills rows 64 w + 4 x + lane / 16 of a buffer, one 16-byte unit per lane, for
+  // the tiles any wave reads (rows past the sequence's end repeat its last key; their scores
+  // are never written).  Byte offsets from the sequence's first row fit 32 bits (the launcher
+  // checks the K size).
+  const int crows = BN * ((kstop - kbeg + BN - 1) / BN);
+  const uint32_t rowb = uint32_t(HKV * D * 2);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&k_lds[0][0];
+  const int ws = __builtin_amdgcn_readfirstlane(w);
+  auto copy_k = [&](int g, int kb) {
+    const uint16_t* kg = k + seq0 * (HKV * D) + g * D;
 #pragma unroll
-    for (int x = 0; x < UPT; ++x) {
-      const int u = tid + 256 * x;  // head u / 512, key (u % 512) >> 4, column u & 15
-      const int gg = u >> 9, kk = min(kt + ((u & 511) >> 4), kend - 1);
-      pre[x] = *reinterpret_cast<const i32x4*>(k + (seq0 + kk) * kvs + gg * D + 8 * (u & 15));
+    for (int x = 0; x < 16; ++x) {
+      const int r = 64 * w + 4 * x + (lane >> 4);
+      if (64 * ws + 4 * x < crows) {
+        const uint32_t kr = uint32_t(min(kbeg + r, kend - 1));
+        const int swz = ((r & 3) << 2) | ((r >> 2) & 3);
+        dn_copy16(kg, kr * rowb + 16 * ((lane & 15) ^ swz), lds0 + kb * TB + 1024 * (16 * ws + x));
+      }
     }
   };
-  auto lstore = [&](int buf) {
+  // queries of head h for this lane's row: 8 x 16 bytes (dims 16 s2 + 8 hf ..), and its lse
+  const uint16_t* const qrow_p = q + (seq0 + qrow) * Hq * D + 8 * hf;
+  const float* const lse_row = lse + (seq0 + qrow) * Hq;
+  auto qload = [&](i32x4 (&dst)[8], float& ls, int h) {
 #pragma unroll
-    for (int x = 0; x < UPT; ++x) {
-      const int u = tid + 256 * x;
-      *reinterpret_cast<i32x4*>(&k_lds[buf][u >> 9][kv_off((u & 511) >> 4, 16 * (u & 15))]) = pre[x];
-    }
+    for (int s2 = 0; s2 < 8; ++s2) dst[s2] = *reinterpret_cast<const i32x4*>(qrow_p + h * D + 16 * s2);
+    ls = lse_row[h];
   };
-  const float* lse_row = lse + (seq0 + qrow) * Hq;
-  float* prow = const_cast<float*>(tri_row(P, seqoff[b], qrow));
-  gload(kbeg);
-  lstore(0);
-  __syncthreads();
-  int buf = 0;
-  for (int kt = kbeg; kt < kstop; kt += BN) {
-    const bool more = kt + BN < kstop;
-    if (more) gload(kt + BN);
-    if (kt <= wave_qmax) {
-      float pacc[16];
+  float pacc[NT][16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pacc[i] = 0.f;
-      const int key = kperm(qc);
-      i32x4 qa[8], qb[8];
-      auto qload = [&](i32x4 (&dst)[8], int h) {
-        const uint16_t* qp = q + ((seq0 + qrow) * Hq + h) * D + 8 * hf;
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2) dst[s2] = *reinterpret_cast<const i32x4*>(qp + 16 * s2);
-      };
-      auto head = [&](const i32x4 (&qf)[8], int h) {
-        const uint8_t* kl = k_lds[buf][h / G];
+    for (int i = 0; i < 16; ++i) pacc[t][i] = 0.f;
+  const int key = kperm(qc);
+  auto head = [&](const i32x4 (&qf)[8], float ls, int kb) {
+    const uint8_t* kl = k_lds[kb];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < nt) {
         f32x16 sacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2)
-          sacc = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(kl + kv_off(key, 32 * s2 + 16 * hf)), qf[s2],
-                                    sacc);
-        const float ls = lse_row[h];
+          sacc = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(kl + kv_off(BN * t + key, 32 * s2 + 16 * hf)),
+                                    qf[s2], sacc);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pacc[i] += __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -ls));
-      };
-      // heads in pairs, the next pair's queries loaded while the current one is computed
-      qload(qa, 0);
-      for (int h = 0; h < Hq; h += 2) {
-        qload(qb, h + 1);
-        head(qa, h);
-        if (h + 2 < Hq) qload(qa, h + 2);
-        head(qb, h + 1);
+        for (int i = 0; i < 16; ++i) pacc[t][i] += __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -ls));
       }
-      // C row (reg i, half hf) <-> key kt + kperm(8(i/4) + 4hf + i%4): runs of 4 consecutive keys
-      if (my_q < kend) {
+    }
+  };
+  // heads in order (each one's successor loaded while it is computed); at the first head of KV
+  // group g, its K rows have landed and every wave is done with the other buffer, which then
+  // receives group g + 1's rows
+  auto step = [&](int h, const i32x4 (&cur)[8], float lc, i32x4 (&nxt)[8], float& ln) {
+    const int g = h / G;
+    if (h % G == 0) {
+      dn_sync();
+      if (g + 1 < HKV) copy_k(g + 1, (g + 1) & 1);
+    }
+    qload(nxt, ln, min(h + 1, Hq - 1));
+    head(cur, lc, g & 1);
+  };
+  i32x4 qa[8], qb[8];
+  float la, lb;
+  copy_k(0, 0);
+  qload(qa, la, 0);
+  for (int h = 0; h < Hq; h += 2) {
+    step(h, qa, la, qb, lb);
+    if (h + 1 < Hq) step(h + 1, qb, lb, qa, la);
+  }
+  // C row (reg i, half hf) <-> key kbeg + 32 t + kperm(8(i/4) + 4hf + i%4): runs of 4 keys
+  if (my_q < kend) {
+    const float inv_hq = 1.f / float(Hq);
+    float* prow = const_cast<float*>(tri_row(P, seqoff[b], qrow));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < nt) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const int k0 = kt + kperm(8 * a + 4 * hf);
+          const int k0 = kbeg + BN * t + kperm(8 * a + 4 * hf);
           if (k0 + 3 <= my_q) {
-            *reinterpret_cast<f32x4*>(prow + k0) = (f32x4){pacc[4 * a] * inv_hq, pacc[4 * a + 1] * inv_hq,
-                                                           pacc[4 * a + 2] * inv_hq, pacc[4 * a + 3] * inv_hq};
+            *reinterpret_cast<f32x4*>(prow + k0) =
+                (f32x4){pacc[t][4 * a] * inv_hq, pacc[t][4 * a + 1] * inv_hq, pacc[t][4 * a + 2] * inv_hq,
+                        pacc[t][4 * a + 3] * inv_hq};
           } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-              if (k0 + c <= my_q) prow[k0 + c] = pacc[4 * a + c] * inv_hq;
+              if (k0 + c <= my_q) prow[k0 + c] = pacc[t][4 * a + c] * inv_hq;
           }
         }
       }
     }
-    if (more) lstore(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
   }
 }
 
@@ -657,7 +678,8 @@ hipError_t launch_kl_target(const uint16_t* q, const uint16_t* k, const int32_t*
                             const int64_t* seqoff, float* P, hipStream_t st) {
   if (nb128 == 0) return hipSuccess;
   const float sl2 = scale * 1.4426950408889634f;
-  const dim3 grid(nb128, (max_len + kKlTargetChunk - 1) / kKlTargetChunk);
+  if ((int64_t)max_len * Hkv * 256 > 0xFFFFFFFFll) return hipErrorInvalidValue;  // 32-bit K copy offsets
+  const dim3 grid((max_len + kKlTargetChunk - 1) / kKlTargetChunk, nb128);
   switch (Hkv) {
     case 1: kl_target_kernel<1><<<grid, 256, 0, st>>>(q, k, cu, Hq, sl2, sched128, count128, lse, seqoff, P); break;
     case 2: kl_target_kernel<2><<<grid, 256, 0, st>>>(q, k, cu, Hq, sl2, sched128, count128, lse, seqoff, P); break;

@@ -52,6 +52,10 @@ CASES = {
     "h16_gqa2": ([520], 16, 16, 2, False, 1.0),
     "h32_mha1": ([260, 33], 32, 8, 1, True, 1.0),
     "long_2k": ([2100], 64, 32, 4, True, 1.0),
+    # three query heads per KV head, and an odd head count (the target kernel walks the heads of
+    # each KV group in turn)
+    "g3": ([600, 45], 64, 6, 2, True, 1.0),
+    "h3_mqa": ([290], 16, 3, 1, False, 1.0),
     # head weights scaled by 2^-8 (still exact): indexer scores of order 1, so r is not one-hot
     "soft_scores": ([700, 150], 64, 32, 4, True, 2.0 ** -8),
 }

@@ -296,11 +296,11 @@ def bench_indexer_kl(reps=3):
     torch.cuda.synchronize()
     ms = ms_between(a, b) / reps
     pairs = pairs_of([L])
-    # MFMA work executed per call: two passes of QK^T over all query heads (log-sum-exp, target),
-    # the fp8 indexer scores, and per gradient kernel one S recompute plus the contraction twice
-    # (fp16 hi + lo)
-    bf16_flop = 2 * 32 * 128 * 2 * pairs + 2 * (H * 128 * 2 * pairs * 3)
-    fp8_flop = H * 128 * 2 * pairs
+    # MFMA work executed per call: two bf16 passes of QK^T over all query heads (log-sum-exp,
+    # target), the fp8 indexer scores, and per gradient kernel an fp8 recompute of the indexer
+    # products plus the G contraction twice (bf16 hi + lo)
+    bf16_flop = 2 * 32 * 128 * 2 * pairs + 2 * (H * 128 * 2 * pairs * 2)
+    fp8_flop = 3 * H * 128 * 2 * pairs
     log(f"indexer KL 32K: {ms:.2f} ms per call (forward + gradients)")
     del pb, ws, dq
     torch.cuda.empty_cache()

@@ -47,14 +47,13 @@ hipError_t launch_kl_target(const uint16_t* q, const uint16_t* k, const int32_t*
                             const int64_t* seqoff, float* P, hipStream_t st);
 hipError_t launch_kl_rows(const float* I, float* P, const int64_t* seqoff, const int32_t* cu, int nseq, int64_t T,
                           const float2* rowrange, float* kl, hipStream_t st);
-hipError_t launch_kl_gscale(const float* w, int64_t n, float* part, float* gsc, hipStream_t st);
 hipError_t launch_kl_dq(int H, const uint8_t* q_idx, const uint8_t* k_idx, const float* w, const float* G,
                         const int64_t* seqoff, const int32_t* cu, const int2* schedR, const int* countR, int nbR,
-                        const float* gsc, float* dq, float* dw, hipStream_t st);
+                        float* dq, float* dw, hipStream_t st);
 int kl_dk_slices(int max_len);
 hipError_t launch_kl_dk(int H, const uint8_t* q_idx, const uint8_t* k_idx, const float* w, const float* G,
                         const int64_t* seqoff, const int32_t* cu, int nseq, const int2* sched256,
-                        const int* count256, int nb256, int max_len, int64_t T, const float* gsc, float* dk_part,
+                        const int* count256, int nb256, int max_len, int64_t T, float* dk_part,
                         float* dk, hipStream_t st);
 int bwd_slices(int max_len);
 hipError_t launch_bwd_delta(const uint16_t* dout, const uint16_t* out, int64_t pairs, float* D, hipStream_t st);
@@ -303,7 +302,7 @@ DedupWs dedup_layout(const dsa_prefill_shape* s) {
 //   counts[8..9] (as floats) the fp16 pre-scale of the gradient weights and its inverse.
 struct KlWs {
   PrefillWs base;
-  size_t tri, P, lse, schedR, sched256, dkpart, wpart, total;
+  size_t tri, P, lse, schedR, sched256, dkpart, total;
   int R, nbR, nb256, slices;
   int64_t tri_floats;
 };
@@ -326,7 +325,6 @@ KlWs kl_layout(const dsa_prefill_shape* s) {
   w.schedR = off; off = align_up(off + size_t(w.nbR) * sizeof(int2), 256);
   w.sched256 = off; off = align_up(off + size_t(w.nb256) * sizeof(int2), 256);
   w.dkpart = off; off = align_up(off + size_t(w.slices) * size_t(T) * 128 * sizeof(float), 256);
-  w.wpart = off; off = align_up(off + 256 * sizeof(float), 256);
   w.total = off;
   return w;
 }
@@ -714,15 +712,12 @@ int dsa_indexer_kl(const dsa_prefill_shape* s, const void* q_idx, const void* k_
                             P, st)) != hipSuccess ||
       (e = launch_kl_rows(scores, P, seqoff, s->cu_seqlens, s->num_seqs, s->total_tokens,
                           at<float2>(ws, L.rowrange), kl, st)) != hipSuccess ||
-      (e = launch_kl_gscale(w_idx, s->total_tokens * s->idx_heads, at<float>(ws, K.wpart),
-                            reinterpret_cast<float*>(counts + 8), st)) != hipSuccess ||
       (e = launch_kl_dq(s->idx_heads, static_cast<const uint8_t*>(q_idx), static_cast<const uint8_t*>(k_idx), w_idx,
-                        P, seqoff, s->cu_seqlens, at<int2>(ws, K.schedR), counts + 2, K.nbR,
-                        reinterpret_cast<const float*>(counts + 8), dq_idx, dw_idx, st)) != hipSuccess ||
+                        P, seqoff, s->cu_seqlens, at<int2>(ws, K.schedR), counts + 2, K.nbR, dq_idx, dw_idx,
+                        st)) != hipSuccess ||
       (e = launch_kl_dk(s->idx_heads, static_cast<const uint8_t*>(q_idx), static_cast<const uint8_t*>(k_idx), w_idx,
                         P, seqoff, s->cu_seqlens, s->num_seqs, at<int2>(ws, K.sched256), counts + 3, K.nb256,
-                        s->max_seqlen, s->total_tokens, reinterpret_cast<const float*>(counts + 8),
-                        at<float>(ws, K.dkpart), dk_idx, st)) != hipSuccess)
+                        s->max_seqlen, s->total_tokens, at<float>(ws, K.dkpart), dk_idx, st)) != hipSuccess)
     return hip_status(e);
   return DSA_OK;
 }

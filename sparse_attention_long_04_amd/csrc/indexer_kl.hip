@@ -16,17 +16,20 @@
 // Kernels (all rows of one sequence; packed sequences via cu_seqlens):
 //   kl_lse_kernel     per (128 query rows, query head): log-sum-exp of the scaled scores (log2
 //                     units) -- the dense kernel's S^T = K Q^T tile loop with an online max/sum.
-//   kl_target_kernel  per 128 query rows: for each 32-key tile, p += 2^(S_h - lse_h) summed over
-//                     all Hq heads (every KV head's K tile staged in LDS), written once into a
-//                     score-shaped triangle (16-row blocks, as the indexer's scores).
+//   kl_target_kernel  per 256-key chunk x 128 query rows: p += 2^(S_h - lse_h) summed over all
+//                     Hq heads in registers (one KV head's K rows staged in LDS at a time),
+//                     written once into a score-shaped triangle (16-row blocks, as the indexer's
+//                     scores).
 //   kl_row_kernel     per row: softmax statistics of the indexer row, KL_t, then g = r - p in
 //                     place of p.
 //   kl_dq_kernel      per block of 256/H_I rows: the dense kernel's loop over 64-key tiles with
-//                     the H_I x rows query vectors as MFMA columns; S^T = k_I q_I^T (bf16 MFMA,
-//                     exact for e4m3 inputs), G = g w [S > 0] in registers, dq^T += k_I^T G^T
-//                     (fp16 MFMA, G split hi + lo), dw accumulated from the same registers.
+//                     the H_I x rows query vectors as MFMA columns; S^T = k_I q_I^T (fp8 MFMA on
+//                     the e4m3 codes, exact), G = g [S > 0] in registers, dq^T += k_I^T G^T (bf16
+//                     MFMA, G split hi + lo), dw accumulated from the same registers; the head
+//                     weight scales the finished row.
 //   kl_dk_kernel      roles swapped: per 256 keys x a slice of the query rows, 64-vector tiles of
-//                     (row, head) pairs; dk^T += q_I^T G^T into per-slice partials.
+//                     (row, head) pairs, G = g w [S > 0]; dk^T += q_I^T G^T into per-slice
+//                     partials.
 //   kl_dk_reduce_kernel  sums the partials in slice order (deterministic; no float atomics).
 #include "attn_tiles.h"
 
@@ -39,30 +42,25 @@ __device__ __forceinline__ const float* tri_row(const float* tri, int64_t off, i
   return tri + off + score_block_offset(j) + (i & 15) * 16 * (int64_t)(j + 1);
 }
 
-// 8 e4m3 codes (a uint2) -> 8 bf16 (exact), packed as 4 dwords.
-__device__ __forceinline__ i32x4 e4m3x8_to_bf16(uint2 v) {
-  i32x4 r;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t word = p < 2 ? v.x : v.y;
-    const uint32_t b0 = (word >> (16 * (p & 1))) & 0xFFu, b1 = (word >> (16 * (p & 1) + 8)) & 0xFFu;
-    r[p] = int((__float_as_uint(e4m3_decode(b0)) >> 16) | (__float_as_uint(e4m3_decode(b1)) & 0xFFFF0000u));
-  }
-  return r;
+// e4m3 (OCP, bias 7) codes are exact in fp32 and bf16.  The conversions below use the hardware's
+// fp8 -> fp32 pair conversion (two codes of a 16-bit half of a dword), then keep the upper halves
+// of the two floats (bf16, an exact truncation).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <bool UPPER>
+__device__ __forceinline__ f32x2_t e4m3x2_to_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(int(word), UPPER);
+}
+__device__ __forceinline__ int bf16_pair(f32x2_t f) {
+  return int(__builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u));
 }
 
-// 16 e4m3 codes (a uint4) -> 16 bf16 and 16 fp16 (both exact), 2 x 4 dwords each.
-__device__ __forceinline__ void e4m3x16_convert(uint4 v, i32x4 (&bf)[2], i32x4 (&hf)[2]) {
+// 16 e4m3 codes (a uint4) -> 16 bf16, 2 x 4 dwords (code order).
+__device__ __forceinline__ void e4m3x16_to_bf16(uint4 v, i32x4 (&bf)[2]) {
   const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = e4m3_decode((w4[2 * half + (e >> 2)] >> (8 * (e & 3))) & 0xFFu);
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      bf[half][p] = int((__float_as_uint(f[2 * p]) >> 16) | (__float_as_uint(f[2 * p + 1]) & 0xFFFF0000u));
-    hf[half] = pack_f16x8(f);
+  for (int wi = 0; wi < 4; ++wi) {
+    bf[wi >> 1][2 * (wi & 1)] = bf16_pair(e4m3x2_to_f32<false>(w4[wi]));
+    bf[wi >> 1][2 * (wi & 1) + 1] = bf16_pair(e4m3x2_to_f32<true>(w4[wi]));
   }
 }
 
@@ -328,54 +326,66 @@ __global__ __launch_bounds__(256) void kl_row_kernel(const float* __restrict__ I
 
 // ------------------------------------------------------------------------------------------
 // Shared by the two gradient kernels: a 64-row tile of e4m3 rows (128 codes each) staged in LDS
-// as bf16 (copy 0, MFMA A operand rows) and fp16 (copy 1, transposed second operand).
-// 512 threads: thread -> row tid / 8, 16 codes at column 16 (tid % 8).
+// twice -- the raw codes (128 bytes per row: the fp8 MFMA operand of the score recompute) and
+// the same rows as bf16 (256 bytes per row in the K/V layout: read transposed as the first
+// operand of the G contraction).  Unit u (16 bytes) of a raw row r sits at u ^ ((r / 2) % 8), so
+// the 16 rows that a quarter wave reads at one unit fall on 16 distinct bank groups.
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ void fp8_tile_store(uint8_t* lds0, uint8_t* lds1, uint4 v, int tid) {
-  i32x4 bf[2], hfv[2];
-  e4m3x16_convert(v, bf, hfv);
+constexpr int kF8RowB = 128, kF8TileB = 64 * kF8RowB;
+__device__ __forceinline__ int f8_off(int row, int unit) { return row * kF8RowB + 16 * (unit ^ ((row >> 1) & 7)); }
+
+// 512 threads: thread -> row tid / 8, 16 codes (unit tid % 8).
+__device__ __forceinline__ void fp8_tile_store(uint8_t* f8, uint8_t* bf, uint4 v, int tid) {
   const int r = tid >> 3, c = tid & 7;
+  *reinterpret_cast<uint4*>(f8 + f8_off(r, c)) = v;
+  i32x4 b[2];
+  e4m3x16_to_bf16(v, b);
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    *reinterpret_cast<i32x4*>(lds0 + kv_off(r, 32 * c + 16 * x)) = bf[x];
-    *reinterpret_cast<i32x4*>(lds1 + kv_off(r, 32 * c + 16 * x)) = hfv[x];
+  for (int x = 0; x < 2; ++x) *reinterpret_cast<i32x4*>(bf + kv_off(r, 32 * c + 16 * x)) = b[x];
+}
+
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 32 e4m3 codes at p (16-byte aligned) as one fp8 MFMA operand.
+__device__ __forceinline__ i32x8 load_f8x32(const uint8_t* p) {
+  const i32x4 a = *reinterpret_cast<const i32x4*>(p), b = *reinterpret_cast<const i32x4*>(p + 16);
+  return (i32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// S = (tile row `row`) . (lane column) over the 128 dims in two fp8 MFMAs: for step m, lane
+// (c, hf) supplies dims 64 m + 32 hf .. + 31 of both operands (the same dims on both sides, so
+// the sum does not depend on how the instruction orders them).
+__device__ __forceinline__ f32x16 s_tile_f8(const uint8_t* f8, int row, int hf, const i32x8 (&col)[2]) {
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const i32x4 a0 = *reinterpret_cast<const i32x4*>(f8 + f8_off(row, 4 * m + 2 * hf));
+    const i32x4 a1 = *reinterpret_cast<const i32x4*>(f8 + f8_off(row, 4 * m + 2 * hf + 1));
+    acc = mfma_fp8_32x32x64((i32x8){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]}, col[m], acc);
+  }
+  return acc;
+}
+
+// 8 floats -> bf16 hi (each float's upper 16 bits) and lo (the exact remainder x - hi, again
+// truncated to bf16), as packed pairs.  hi + lo keeps 16 or more significant bits of x, at any
+// magnitude (bf16 has fp32's exponent range).
+__device__ __forceinline__ void split_bf16x8(const float* x, i32x4& ph, i32x4& pl) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t u0 = __float_as_uint(x[2 * p]), u1 = __float_as_uint(x[2 * p + 1]);
+    ph[p] = int(__builtin_amdgcn_perm(u1, u0, 0x07060302u));
+    const float l0 = x[2 * p] - __uint_as_float(u0 & 0xFFFF0000u);
+    const float l1 = x[2 * p + 1] - __uint_as_float(u1 & 0xFFFF0000u);
+    pl[p] = int(__builtin_amdgcn_perm(__float_as_uint(l1), __float_as_uint(l0), 0x07060302u));
   }
 }
 
-// Power-of-two pre-scale for the fp16 hi + lo split of G = g w [c > 0] (|g| <= 1): 2^(14 - e)
-// with 2^e >= max |w|, so |G| scale <= 2^14 stays below fp16's maximum and small values stay
-// normal.  gsc[0] = scale, gsc[1] = 1 / scale (both exact).  Two stages: kGscaleBlocks partial
-// maxima, then one workgroup.
-constexpr int kGscaleBlocks = 256;
-
-__global__ __launch_bounds__(256) void kl_wmax_kernel(const float* __restrict__ w, int64_t n, float* __restrict__ part) {
-  __shared__ float red[4];
-  float m = 0.f;
-  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += 256 * kGscaleBlocks) m = fmaxf(m, fabsf(w[i]));
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-
-__global__ __launch_bounds__(256) void kl_gscale_kernel(const float* __restrict__ part, float* __restrict__ gsc) {
-  __shared__ float red[4];
-  float m = part[threadIdx.x];
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    int e = 0;
-    if (m > 0.f && m < __builtin_inff()) frexpf(m, &e);  // m = f 2^e, f in [1/2, 1): 2^e >= m
-    e = max(-100, min(100, e));
-    gsc[0] = ldexpf(1.f, 14 - e);
-    gsc[1] = ldexpf(1.f, e - 14);
-  }
-}
-
-// O^T += X^T G^T for one 64-key tile: X^T (dims x keys) read transposed from the fp16 tile, G (in
-// the S^T register layout, already multiplied by the pre-scale) split into fp16 hi + lo.
+// O^T += X^T G^T for one 64-key tile: X^T (dims x keys) read transposed from the bf16 tile, G (in
+// the S^T register layout) split into bf16 hi + lo.
 __device__ __forceinline__ void accumulate_xt_gt(const uint8_t* xl, const float (&gz)[2][16], int lane,
                                                  f32x16 (&o)[4]) {
   const int grp = lane >> 4, jj = lane & 15;
@@ -383,14 +393,8 @@ __device__ __forceinline__ void accumulate_xt_gt(const uint8_t* xl, const float 
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int kk2 = 0; kk2 < 2; ++kk2) {
-      float hi[8], lo[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = gz[rb][8 * kk2 + e];
-        hi[e] = float(_Float16(x));
-        lo[e] = x - hi[e];
-      }
-      const i32x4 ph = pack_f16x8(hi), pl = pack_f16x8(lo);
+      i32x4 ph, pl;
+      split_bf16x8(&gz[rb][8 * kk2], ph, pl);
       const int key_a = 32 * rb + 16 * kk2 + 8 * (grp >> 1) + (jj >> 2);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
@@ -398,26 +402,27 @@ __device__ __forceinline__ void accumulate_xt_gt(const uint8_t* xl, const float 
         const s16x4 a0 = lds_tr16(xl + kv_off(key_a, 2 * dim0));
         const s16x4 a1 = lds_tr16(xl + kv_off(key_a + 4, 2 * dim0));
         const i32x4 a = __builtin_bit_cast(i32x4, (s16x8_t){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]});
-        o[db] = mfma_f16_32x32x16(a, ph, o[db]);
-        o[db] = mfma_f16_32x32x16(a, pl, o[db]);
+        o[db] = mfma_bf16_32x32x16(a, ph, o[db]);
+        o[db] = mfma_bf16_32x32x16(a, pl, o[db]);
       }
     }
 }
 
 // ------------------------------------------------------------------------------------------
 // kl_dq_kernel<HI>: grid (blocks of 256/HI rows), 8 waves; lane column = query vector
-// v = 32 wave + c -> (row v / HI, head v % HI).
+// v = 32 wave + c -> (row v / HI, head v % HI).  The head weight is applied once at the end
+// (dq = w sum_s g [c > 0] k), so G here is g [c > 0].
 // ------------------------------------------------------------------------------------------
 template <int HI>
 __global__ __launch_bounds__(512) void kl_dq_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx,
                                                     const float* __restrict__ wgt, const float* __restrict__ Gt,
                                                     const int64_t* __restrict__ seqoff, const int32_t* __restrict__ cu,
                                                     const int2* __restrict__ sched, const int* __restrict__ count,
-                                                    const float* __restrict__ gsc, float* __restrict__ dq,
-                                                    float* __restrict__ dw) {
+                                                    float* __restrict__ dq, float* __restrict__ dw) {
   constexpr int D = 128, BN = 64, R = 256 / HI;
   static_assert(R % 4 == 0, "G rows are copied four at a time");
-  __shared__ __attribute__((aligned(16))) uint8_t t_lds[2][2][kKvTileB];
+  __shared__ __attribute__((aligned(16))) uint8_t f8_lds[2][kF8TileB];
+  __shared__ __attribute__((aligned(16))) uint8_t bf_lds[2][kKvTileB];
   __shared__ __attribute__((aligned(16))) float g_lds[2][R][BN];  // G of the block's rows for a key tile
   const int n = blockIdx.x;
   if (n >= *count) return;
@@ -427,24 +432,27 @@ __global__ __launch_bounds__(512) void kl_dq_kernel(const uint8_t* __restrict__ 
   const int L = cu[b + 1] - cu[b];
   const int r0 = R * e.y, kend = min(L, r0 + R);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 31, hf = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int v = 32 * w + qc;
   const int my_t = r0 + v / HI, head = v % HI;
   const bool valid = my_t < kend;
   const int trow = min(my_t, kend - 1);
-  const int wave_tmax = min(kend - 1, r0 + (32 * w + 31) / HI);
-  i32x4 qf[8];
+  const int wave_tmax = min(kend - 1, r0 + (32 * wu + 31) / HI);
+  // a tile needs no key mask for this wave when all its vectors are rows of the sequence and its
+  // last key precedes the wave's first row
+  const int wave_tmin = r0 + (32 * wu) / HI;
+  const bool wave_full = r0 + (32 * wu + 31) / HI < kend;
+  i32x8 qf[2];
   {
-    const uint8_t* qp = q_idx + ((seq0 + trow) * HI + head) * D + 8 * hf;
+    const uint8_t* qp = q_idx + ((seq0 + trow) * HI + head) * D + 32 * hf;
 #pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) qf[s2] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(qp + 16 * s2));
+    for (int m = 0; m < 2; ++m) qf[m] = load_f8x32(qp + 64 * m);
   }
   const float wq = wgt[(seq0 + trow) * HI + head];
-  const float wqs = wq * gsc[0], unscale = gsc[1];
   // G[t][kt .. kt+63] of the block's rows for key tile kt, copied into g_lds[gb] one tile ahead:
   // wave w < R/4 fills rows 4w .. 4w+3, 16 lanes per row (rows past the block end repeat its
   // last row and chunks past a row's stored width re-read its last chunk: both masked later)
   const int64_t soff = seqoff[b];
-  const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint32_t glds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) float*)&g_lds[0][0][0];
   auto gcopy = [&](int kt, int gb) {
     if (wu < R / 4) {
@@ -468,7 +476,7 @@ __global__ __launch_bounds__(512) void kl_dq_kernel(const uint8_t* __restrict__ 
   };
   gload(0);
   gcopy(0, 0);
-  fp8_tile_store(t_lds[0][0], t_lds[0][1], pre, tid);
+  fp8_tile_store(f8_lds[0], bf_lds[0], pre, tid);
   dn_sync();
   int buf = 0;
   for (int kt = 0; kt < kend; kt += BN) {
@@ -478,35 +486,32 @@ __global__ __launch_bounds__(512) void kl_dq_kernel(const uint8_t* __restrict__ 
       gcopy(kt + BN, buf ^ 1);
     }
     if (kt <= wave_tmax) {
+      const bool full = wave_full && kt + BN - 1 <= wave_tmin;
       float gz[2][16];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        f32x16 sacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-        const int key = 32 * rb + kperm(qc);
-#pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2)
-          sacc = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(&t_lds[buf][0][kv_off(key, 32 * s2 + 16 * hf)]),
-                                    qf[s2], sacc);
-        // registers 4a .. 4a+3 <-> keys k0 .. k0+3 (consecutive)
+        const f32x16 s = s_tile_f8(f8_lds[buf], 32 * rb + kperm(qc), hf, qf);
+        // registers 4a .. 4a+3 <-> keys kt + kl0 .. kt + kl0 + 3 (consecutive)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const int k0 = kt + 32 * rb + kperm(8 * a + 4 * hf);
-          f32x4 g4 = {0.f, 0.f, 0.f, 0.f};
-          if (valid && k0 <= my_t) g4 = *reinterpret_cast<const f32x4*>(&g_lds[buf][my_t - r0][k0 - kt]);
+          const int kl0 = 32 * rb + kperm(8 * a + 4 * hf);
+          f32x4 g4 = *reinterpret_cast<const f32x4*>(&g_lds[buf][trow - r0][kl0]);
+          if (!full) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (!valid || kt + kl0 + c > my_t) g4[c] = 0.f;
+          }
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const float s = sacc[4 * a + c];
-            const bool on = valid && (k0 + c <= my_t) && s > 0.f;
-            gz[rb][4 * a + c] = on ? g4[c] * wqs : 0.f;
-            dwacc += on ? g4[c] * s : 0.f;
+            const float x = s[4 * a + c] > 0.f ? g4[c] : 0.f;
+            gz[rb][4 * a + c] = x;
+            dwacc = fmaf(x, s[4 * a + c], dwacc);  // g max(0, c)
           }
         }
       }
-      accumulate_xt_gt(t_lds[buf][1], gz, lane, o);
+      accumulate_xt_gt(bf_lds[buf], gz, lane, o);
     }
-    if (more) fp8_tile_store(t_lds[buf ^ 1][0], t_lds[buf ^ 1][1], pre, tid);
+    if (more) fp8_tile_store(f8_lds[buf ^ 1], bf_lds[buf ^ 1], pre, tid);
     dn_sync();  // the next tile's G has landed
     buf ^= 1;
   }
@@ -519,14 +524,13 @@ __global__ __launch_bounds__(512) void kl_dq_kernel(const uint8_t* __restrict__ 
 #pragma unroll
     for (int a = 0; a < 4; ++a)
       *reinterpret_cast<f32x4*>(op + 32 * db + 8 * a + 4 * hf) =
-          (f32x4){o[db][4 * a] * unscale, o[db][4 * a + 1] * unscale, o[db][4 * a + 2] * unscale,
-                  o[db][4 * a + 3] * unscale};
+          (f32x4){o[db][4 * a] * wq, o[db][4 * a + 1] * wq, o[db][4 * a + 2] * wq, o[db][4 * a + 3] * wq};
 }
 
 // ------------------------------------------------------------------------------------------
 // kl_dk_kernel<HI>: grid (256-key blocks, query-row slices of kDkSlice rows), 8 waves; lane
 // column = key s = s0 + 32 wave + c; tiles of 64 consecutive (row, head) vectors of the slice.
-// Writes partial dk [slice][T][128].
+// G = g w [c > 0].  Writes partial dk [slice][T][128].
 // ------------------------------------------------------------------------------------------
 constexpr int kDkSlice = 1024;
 
@@ -535,11 +539,12 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(const uint8_t* __restrict__ 
                                                     const float* __restrict__ wgt, const float* __restrict__ Gt,
                                                     const int64_t* __restrict__ seqoff, const int32_t* __restrict__ cu,
                                                     const int2* __restrict__ sched, const int* __restrict__ count,
-                                                    int64_t T, const float* __restrict__ gsc,
-                                                    float* __restrict__ dk_part) {
+                                                    int64_t T, float* __restrict__ dk_part) {
   constexpr int D = 128, BN = 64, RPT = BN / HI;  // rows per tile
-  __shared__ __attribute__((aligned(16))) uint8_t t_lds[2][2][kKvTileB];
-  __shared__ float w_lds[2][BN];
+  static_assert(HI >= 16 && HI <= 64, "a run of 4 vectors never crosses a row");
+  __shared__ __attribute__((aligned(16))) uint8_t f8_lds[2][kF8TileB];
+  __shared__ __attribute__((aligned(16))) uint8_t bf_lds[2][kKvTileB];
+  __shared__ __attribute__((aligned(16))) float w_lds[2][BN];
   __shared__ __attribute__((aligned(16))) float g_lds[2][RPT][256];  // G of a tile's rows for the block's keys
   const int n = blockIdx.x;
   if (n >= *count) return;
@@ -554,18 +559,17 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(const uint8_t* __restrict__ 
   const bool valid = my_s < send;
   const int srow = min(my_s, send - 1);
   float* op = dk_part + ((int64_t)slice * T + seq0 + srow) * D;
-  const float gs = gsc[0], unscale = gsc[1];
   f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   if (t_lo < t_hi) {
-    i32x4 kf[8];
+    i32x8 kf[2];
     {
-      const uint8_t* kp = k_idx + (seq0 + srow) * D + 8 * hf;
+      const uint8_t* kp = k_idx + (seq0 + srow) * D + 32 * hf;
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2) kf[s2] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(kp + 16 * s2));
+      for (int m = 0; m < 2; ++m) kf[m] = load_f8x32(kp + 64 * m);
     }
     const int64_t v_begin = (int64_t)t_lo * HI, v_end = (int64_t)t_hi * HI;  // vectors of this slice
     // G[t][s0 .. s0+255] of the tile's rows, copied into g_lds[gb] one tile ahead: wave w < RPT
@@ -590,7 +594,7 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(const uint8_t* __restrict__ 
       if (tid < BN) wpre = wgt[seq0 * HI + min(v0 + tid, v_end - 1)];
     };
     auto lstore = [&](int buf) {
-      fp8_tile_store(t_lds[buf][0], t_lds[buf][1], pre, tid);
+      fp8_tile_store(f8_lds[buf], bf_lds[buf], pre, tid);
       if (tid < BN) w_lds[buf][tid] = wpre;
     };
     gload(v_begin);
@@ -616,24 +620,18 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(const uint8_t* __restrict__ 
         float gz[2][16];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          f32x16 sacc;
+          const f32x16 s = s_tile_f8(f8_lds[buf], 32 * rb + kperm(qc), hf, kf);
+          // registers 4a .. 4a+3 <-> vectors vl0 .. vl0 + 3 of the tile, all of row r
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-          const int vrow = 32 * rb + kperm(qc);
+          for (int a = 0; a < 4; ++a) {
+            const int vl0 = 32 * rb + kperm(8 * a + 4 * hf);
+            const int r = (32 * rb + 16 * (a >> 1) + 4 * (a & 1)) / HI;  // = vl0 / HI (8 hf < HI)
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(&w_lds[buf][vl0]);
 #pragma unroll
-          for (int s2 = 0; s2 < 8; ++s2)
-            sacc = mfma_bf16_32x32x16(
-                *reinterpret_cast<const i32x4*>(&t_lds[buf][0][kv_off(vrow, 32 * s2 + 16 * hf)]), kf[s2], sacc);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int vl = 32 * rb + kperm(8 * (i >> 2) + 4 * hf + (i & 3));  // vector within the tile
-            const int r = vl / HI;
-            const float gv = gr[r];
-            const float s = sacc[i];
-            gz[rb][i] = (s > 0.f) ? gv * (w_lds[buf][vl] * gs) : 0.f;
+            for (int c = 0; c < 4; ++c) gz[rb][4 * a + c] = s[4 * a + c] > 0.f ? gr[r] * w4[c] : 0.f;
           }
         }
-        accumulate_xt_gt(t_lds[buf][1], gz, lane, o);
+        accumulate_xt_gt(bf_lds[buf], gz, lane, o);
       }
       if (more) lstore(buf ^ 1);
       dn_sync();  // the next tile's G has landed
@@ -646,8 +644,7 @@ __global__ __launch_bounds__(512) void kl_dk_kernel(const uint8_t* __restrict__ 
 #pragma unroll
     for (int a = 0; a < 4; ++a)
       *reinterpret_cast<f32x4*>(op + 32 * db + 8 * a + 4 * hf) =
-          (f32x4){o[db][4 * a] * unscale, o[db][4 * a + 1] * unscale, o[db][4 * a + 2] * unscale,
-                  o[db][4 * a + 3] * unscale};
+          (f32x4){o[db][4 * a], o[db][4 * a + 1], o[db][4 * a + 2], o[db][4 * a + 3]};
 }
 
 // dk[row] = sum over the row's slices (fixed order).  Slices that do not reach a row (all of
@@ -696,20 +693,14 @@ hipError_t launch_kl_rows(const float* I, float* P, const int64_t* seqoff, const
   return hipGetLastError();
 }
 
-hipError_t launch_kl_gscale(const float* w, int64_t n, float* part, float* gsc, hipStream_t st) {
-  kl_wmax_kernel<<<kGscaleBlocks, 256, 0, st>>>(w, n, part);
-  kl_gscale_kernel<<<1, 256, 0, st>>>(part, gsc);
-  return hipGetLastError();
-}
-
 hipError_t launch_kl_dq(int H, const uint8_t* q_idx, const uint8_t* k_idx, const float* w, const float* G,
                         const int64_t* seqoff, const int32_t* cu, const int2* schedR, const int* countR, int nbR,
-                        const float* gsc, float* dq, float* dw, hipStream_t st) {
+                        float* dq, float* dw, hipStream_t st) {
   if (nbR == 0) return hipSuccess;
   switch (H) {
-    case 16: kl_dq_kernel<16><<<nbR, 512, 0, st>>>(q_idx, k_idx, w, G, seqoff, cu, schedR, countR, gsc, dq, dw); break;
-    case 32: kl_dq_kernel<32><<<nbR, 512, 0, st>>>(q_idx, k_idx, w, G, seqoff, cu, schedR, countR, gsc, dq, dw); break;
-    case 64: kl_dq_kernel<64><<<nbR, 512, 0, st>>>(q_idx, k_idx, w, G, seqoff, cu, schedR, countR, gsc, dq, dw); break;
+    case 16: kl_dq_kernel<16><<<nbR, 512, 0, st>>>(q_idx, k_idx, w, G, seqoff, cu, schedR, countR, dq, dw); break;
+    case 32: kl_dq_kernel<32><<<nbR, 512, 0, st>>>(q_idx, k_idx, w, G, seqoff, cu, schedR, countR, dq, dw); break;
+    case 64: kl_dq_kernel<64><<<nbR, 512, 0, st>>>(q_idx, k_idx, w, G, seqoff, cu, schedR, countR, dq, dw); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -719,14 +710,14 @@ int kl_dk_slices(int max_len) { return (max_len + kDkSlice - 1) / kDkSlice; }
 
 hipError_t launch_kl_dk(int H, const uint8_t* q_idx, const uint8_t* k_idx, const float* w, const float* G,
                         const int64_t* seqoff, const int32_t* cu, int nseq, const int2* sched256,
-                        const int* count256, int nb256, int max_len, int64_t T, const float* gsc, float* dk_part,
+                        const int* count256, int nb256, int max_len, int64_t T, float* dk_part,
                         float* dk, hipStream_t st) {
   if (T == 0) return hipSuccess;
   const dim3 grid(nb256, kl_dk_slices(max_len));
   switch (H) {
-    case 16: kl_dk_kernel<16><<<grid, 512, 0, st>>>(q_idx, k_idx, w, G, seqoff, cu, sched256, count256, T, gsc, dk_part); break;
-    case 32: kl_dk_kernel<32><<<grid, 512, 0, st>>>(q_idx, k_idx, w, G, seqoff, cu, sched256, count256, T, gsc, dk_part); break;
-    case 64: kl_dk_kernel<64><<<grid, 512, 0, st>>>(q_idx, k_idx, w, G, seqoff, cu, sched256, count256, T, gsc, dk_part); break;
+    case 16: kl_dk_kernel<16><<<grid, 512, 0, st>>>(q_idx, k_idx, w, G, seqoff, cu, sched256, count256, T, dk_part); break;
+    case 32: kl_dk_kernel<32><<<grid, 512, 0, st>>>(q_idx, k_idx, w, G, seqoff, cu, sched256, count256, T, dk_part); break;
+    case 64: kl_dk_kernel<64><<<grid, 512, 0, st>>>(q_idx, k_idx, w, G, seqoff, cu, sched256, count256, T, dk_part); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t err = hipGetLastError();

@@ -179,13 +179,20 @@ __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, co
       i32x4 vf[8];
       int sv[8];
     };
+    // Gather addresses: the head's K/V base is wave-uniform and a key's byte offset from it,
+    // index * row bytes, fits 32 bits (the launchers check the sequence / cache length), so each
+    // load takes a scalar base plus one 24-bit multiply-add per lane.
+    const uint32_t rowb = uint32_t(kvs) * 2;
+    const char* const kgb = reinterpret_cast<const char*>(kg_base);
+    const char* const vgb = reinterpret_cast<const char*>(vg_base);
+    const uint32_t klane = 2 * (32 * lg + 8 * (lr & 3)), vlane = 16 * lr;
     auto issue = [&](VTile& t, int tl) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const i32x4 sk = *reinterpret_cast<const i32x4*>(il + tl + 8 * (lr >> 2) + 4 * h);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          __builtin_amdgcn_global_load_lds(kg_base + (int64_t)max(sk[c], 0) * kvs + 32 * lg + 8 * (lr & 3),
+          __builtin_amdgcn_global_load_lds(kgb + (__umul24(uint32_t(max(sk[c], 0)), rowb) + klane),
                                            kb + (4 * h + c) * kKRegion, 16, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the K loads ahead of the V loads (vmcnt order)
@@ -195,12 +202,12 @@ __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, co
       for (int m = 0; m < 4; ++m) { t.sv[m] = s0[m]; t.sv[4 + m] = s1[m]; }
 #pragma unroll
       for (int m = 0; m < 8; ++m)
-        t.vf[m] = *reinterpret_cast<const i32x4*>(vg_base + (int64_t)max(t.sv[m], 0) * kvs + 8 * lr);
+        t.vf[m] = *reinterpret_cast<const i32x4*>(vgb + (__umul24(uint32_t(max(t.sv[m], 0)), rowb) + vlane));
     };
     const __attribute__((address_space(3))) uint8_t* kr = kb + (lr & 3) * kKRegion + (4 * (lr >> 2) + 16 * lg) * 16;
-    VTile vc, vn;
-    if (cnt32 > 0) issue(vc, 0);
-    for (int tl = 0; tl < cnt32; tl += 32) {
+    // tile tl: its V rows are in `cur` (loaded during the previous tile), the next tile's go to
+    // `nxt`; the loop alternates the two register sets instead of copying one into the other
+    auto step = [&](int tl, const VTile& cur, VTile& nxt) {
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(kWaitVm8);  // this tile's K is in LDS
       i32x4 kf[2][4];
@@ -212,10 +219,15 @@ __device__ __forceinline__ void attend_staged(const uint16_t* __restrict__ q, co
       if (tl + 32 < cnt32) {
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the read-back has landed
         __builtin_amdgcn_sched_barrier(0);
-        issue(vn, tl + 32);
+        issue(nxt, tl + 32);
       }
-      compute(kf, vc.vf, vc.sv);
-      vc = vn;
+      compute(kf, cur.vf, cur.sv);
+    };
+    VTile va, vb;
+    if (cnt32 > 0) issue(va, 0);
+    for (int tl = 0; tl < cnt32; tl += 64) {
+      step(tl, va, vb);
+      if (tl + 32 < cnt32) step(tl + 32, vb, va);
     }
   }
   l_tot = l_run;
@@ -251,7 +263,7 @@ __global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t kb_all[NW][kKTileLds];  // K tiles (LDS path)
   const int64_t r = blockIdx.x;
   const int split = blockIdx.y;
-  const int g = threadIdx.x >> 6;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int G = Hq / Hkv;
   const RowInfo ri = row_info(mode, r, cu, nseq, cache_lens, cap);
@@ -330,10 +342,11 @@ __global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
   // row groups are dealt to the 8 / hp XCDs of a head in chunks of kGatherChunk consecutive groups
   const int64_t slot = bid >> 3;
   const int64_t group = (slot / kGatherChunk) * (8 / hp) * kGatherChunk + (xcd / hp) * kGatherChunk + slot % kGatherChunk;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rslot = group * NW + wave;
   if (rslot >= rows) return;  // waves are independent: no workgroup barrier below
-  const int64_t r = order ? (int64_t)order[rslot] : rslot;  // the row this slot serves
+  // the row this slot serves (wave-uniform)
+  const int64_t r = order ? (int64_t)__builtin_amdgcn_readfirstlane(order[rslot]) : rslot;
   const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int G = Hq / Hkv;
   const RowInfo ri = row_info(0, r, cu, nseq, nullptr, 0);
@@ -748,6 +761,9 @@ hipError_t launch_gather_attention(const uint16_t* q, const uint16_t* k, const u
                                    float* o_part, float2* ml_part, hipStream_t st, float* lse_out,
                                    const int32_t* order) {
   if (rows == 0) return hipSuccess;
+  // 32-bit gather offsets: a key index (below its sequence's length <= rows, or below cap) times
+  // Hkv x 128 x 2 bytes
+  if ((uint64_t)(mode == 0 ? rows : cap) * Hkv * 128 * 2 > 0xFFFFFFFFull) return hipErrorInvalidValue;
   const float scale_log2 = scale * 1.4426950408889634f;
   if (mode == 0 && nsplit == 1 && idx && K <= kRowKeys && 8 % Hkv == 0) {
     constexpr int NWR = 4;

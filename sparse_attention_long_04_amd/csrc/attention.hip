@@ -252,7 +252,7 @@ __device__ __forceinline__ void store_out_bf16(uint16_t* __restrict__ out, int64
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void gather_attention_kernel(
+__global__ __launch_bounds__(64 * NW, (8 + NW - 1) / NW) void gather_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, int K, int mode, const int32_t* __restrict__ cu, int nseq,
     const int32_t* __restrict__ cache_lens, int cap, int Hq, int Hkv, float scale_log2,
@@ -327,7 +327,7 @@ constexpr int kGatherHeadsPerPhase = 1;
 constexpr int kGatherChunk = 128;
 
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void gather_rows_kernel(
+__global__ __launch_bounds__(64 * NW, (8 + NW - 1) / NW) void gather_rows_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, int K, const int32_t* __restrict__ cu, int nseq, int64_t rows, int Hq,
     int Hkv, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse_out, int hp,

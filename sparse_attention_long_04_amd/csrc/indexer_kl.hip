@@ -16,7 +16,7 @@
 // Kernels (all rows of one sequence; packed sequences via cu_seqlens):
 //   kl_lse_kernel     per (128 query rows, query head): log-sum-exp of the scaled scores (log2
 //                     units) -- the dense kernel's S^T = K Q^T tile loop with an online max/sum.
-//   kl_target_kernel  per 256-key chunk x 128 query rows: p += 2^(S_h - lse_h) summed over all
+//   kl_target_kernel  per 128-key chunk x 128 query rows: p += 2^(S_h - lse_h) summed over all
 //                     Hq heads in registers (one KV head's K rows staged in LDS at a time),
 //                     written once into a score-shaped triangle (16-row blocks, as the indexer's
 //                     scores).
@@ -67,7 +67,7 @@ __device__ __forceinline__ void e4m3x16_to_bf16(uint4 v, i32x4 (&bf)[2]) {
 // ------------------------------------------------------------------------------------------
 // kl_lse_kernel: grid (128-row blocks, Hq), 4 waves x 32 query rows of one head.
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void kl_lse_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(256, 2) void kl_lse_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                      const int32_t* __restrict__ cu, int Hq, int Hkv, float scale_log2,
                                                      const int2* __restrict__ sched, const int* __restrict__ count,
                                                      float* __restrict__ lse) {
@@ -83,6 +83,7 @@ __global__ __launch_bounds__(256) void kl_lse_kernel(const uint16_t* __restrict_
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 31, hf = lane >> 5;
   const int my_q = q0 + 32 * w + qc;
   const int wave_qmax = q0 + 32 * w + 31;
+  const int wave_qmin = q0 + 32 * __builtin_amdgcn_readfirstlane(w);  // tiles ending before it need no mask
   const int64_t kvs = (int64_t)Hkv * D;
   i32x4 qf[8];
   {
@@ -115,34 +116,41 @@ __global__ __launch_bounds__(256) void kl_lse_kernel(const uint16_t* __restrict_
     const bool more = kt + BN < kend;
     if (more) gload(kt + BN);
     if (kt <= wave_qmax) {
-      float z[2][16];
-      float mt = -__builtin_inff();
+      // raw scores; the running max is kept in raw units (scale > 0), so each score costs one
+      // fma before its exponential, and keys are masked only on tiles that reach the diagonal
+      f32x16 z[2];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        f32x16 sacc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+        for (int i = 0; i < 16; ++i) z[rb][i] = 0.f;
         const int key = 32 * rb + kperm(qc);
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2)
-          sacc = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(&k_lds[buf][kv_off(key, 32 * s2 + 16 * hf)]),
-                                    qf[s2], sacc);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kk = kt + 32 * rb + kperm(8 * (i >> 2) + 4 * hf + (i & 3));
-          z[rb][i] = (kk <= my_q) ? sacc[i] * scale_log2 : -__builtin_inff();
-          mt = fmaxf(mt, z[rb][i]);
-        }
+          z[rb] = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(&k_lds[buf][kv_off(key, 32 * s2 + 16 * hf)]),
+                                     qf[s2], z[rb]);
       }
+      if (kt + BN - 1 > wave_qmin) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (kt + 32 * rb + kperm(8 * (i >> 2) + 4 * hf + (i & 3)) > my_q) z[rb][i] = -__builtin_inff();
+      }
+      float mt = fmaxf(z[0][0], z[1][0]);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mt = fmaxf(mt, z[rb][i]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float m_new = fmaxf(m_run, mt);
       const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+      const float msc = m_use * scale_log2;
       float ps = 0.f;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ps += __builtin_amdgcn_exp2f(z[rb][i] - m_use);
-      l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_use) + ps;
+        for (int i = 0; i < 16; ++i) ps += __builtin_amdgcn_exp2f(fmaf(z[rb][i], scale_log2, -msc));
+      l_run = l_run * __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2) + ps;
       m_run = m_new;
     }
     if (more) lstore(buf ^ 1);
@@ -150,21 +158,21 @@ __global__ __launch_bounds__(256) void kl_lse_kernel(const uint16_t* __restrict_
     buf ^= 1;
   }
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (my_q < kend && hf == 0) lse[(seq0 + my_q) * Hq + h] = m_run + __log2f(l_tot);
+  if (my_q < kend && hf == 0) lse[(seq0 + my_q) * Hq + h] = m_run * scale_log2 + __log2f(l_tot);
 }
 
 // ------------------------------------------------------------------------------------------
-// kl_target_kernel: grid (256-key chunks, 128-row blocks; chunks vary fastest, so the
-// workgroups resident together read the same rows' queries from L2), 4 waves x 32 query rows.
-// The chunk's p sums stay in registers (8 tiles x 16 per lane) for all Hq heads: per KV head,
-// its 256 K rows are copied into LDS (two buffers, the next KV head's copy in flight during the
-// current one), and every query head of the group takes its Q fragment from global memory once
-// per chunk (the next head's prefetched) for the 8 tiles.  Any Hq / HKV works.
+// kl_target_kernel: grid (128-key chunks, 128-row blocks; chunks vary fastest, so the
+// workgroups resident together read the same rows' queries from L2), 4 waves x 32 query rows,
+// two workgroups per CU.  The chunk's p sums stay in registers (4 tiles x 16 per lane) for all
+// Hq heads: per KV head, its 128 K rows are copied into LDS (two buffers, the next KV head's copy
+// in flight during the current one), and every query head of the group takes its Q fragment from
+// global memory once per chunk (the next head's prefetched) for the 4 tiles.  Any Hq / HKV works.
 // ------------------------------------------------------------------------------------------
-constexpr int kKlTargetChunk = 256;
+constexpr int kKlTargetChunk = 128;
 
 template <int HKV>
-__global__ __launch_bounds__(256) void kl_target_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(256, 2) void kl_target_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                         const int32_t* __restrict__ cu, int Hq, float scale_log2,
                                                         const int2* __restrict__ sched, const int* __restrict__ count,
                                                         const float* __restrict__ lse,
@@ -187,25 +195,26 @@ __global__ __launch_bounds__(256) void kl_target_kernel(const uint16_t* __restri
   const int my_q = q0 + 32 * w + qc;
   const int qrow = min(my_q, kend - 1);
   // tiles of the chunk that reach this wave's rows (none for a wave entirely before the chunk)
-  const int wlast = min(q0 + 32 * w + 31, kstop - 1);
+  const int ws = __builtin_amdgcn_readfirstlane(w);
+  const int wlast = min(q0 + 32 * ws + 31, kstop - 1);
   const int nt = wlast < kbeg ? 0 : (wlast - kbeg) / BN + 1;
-  // K copy: wave w fills rows 64 w + 4 x + lane / 16 of a buffer, one 16-byte unit per lane, for
+  // K copy: wave w fills rows KC w / 4 + 4 x + lane / 16 of a buffer, one 16-byte unit per lane, for
   // the tiles any wave reads (rows past the sequence's end repeat its last key; their scores
   // are never written).  Byte offsets from the sequence's first row fit 32 bits (the launcher
   // checks the K size).
   const int crows = BN * ((kstop - kbeg + BN - 1) / BN);
   const uint32_t rowb = uint32_t(HKV * D * 2);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&k_lds[0][0];
-  const int ws = __builtin_amdgcn_readfirstlane(w);
+  constexpr int CPW = KC / 16;  // 4-row copies per wave
   auto copy_k = [&](int g, int kb) {
     const uint16_t* kg = k + seq0 * (HKV * D) + g * D;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int r = 64 * w + 4 * x + (lane >> 4);
-      if (64 * ws + 4 * x < crows) {
+    for (int x = 0; x < CPW; ++x) {
+      const int r = 4 * CPW * w + 4 * x + (lane >> 4);
+      if (4 * CPW * ws + 4 * x < crows) {
         const uint32_t kr = uint32_t(min(kbeg + r, kend - 1));
         const int swz = ((r & 3) << 2) | ((r >> 2) & 3);
-        dn_copy16(kg, kr * rowb + 16 * ((lane & 15) ^ swz), lds0 + kb * TB + 1024 * (16 * ws + x));
+        dn_copy16(kg, kr * rowb + 16 * ((lane & 15) ^ swz), lds0 + kb * TB + 1024 * (CPW * ws + x));
       }
     }
   };
@@ -225,19 +234,35 @@ __global__ __launch_bounds__(256) void kl_target_kernel(const uint16_t* __restri
   const int key = kperm(qc);
   auto head = [&](const i32x4 (&qf)[8], float ls, int kb) {
     const uint8_t* kl = k_lds[kb];
+    auto scores = [&](int t) {
+      f32x16 sacc;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t < nt) {
-        f32x16 sacc;
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+      for (int s2 = 0; s2 < 8; ++s2)
+        sacc = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(kl + kv_off(BN * t + key, 32 * s2 + 16 * hf)),
+                                  qf[s2], sacc);
+      return sacc;
+    };
+    auto accumulate = [&](int t, const f32x16& sacc) {
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2)
-          sacc = mfma_bf16_32x32x16(*reinterpret_cast<const i32x4*>(kl + kv_off(BN * t + key, 32 * s2 + 16 * hf)),
-                                    qf[s2], sacc);
+      for (int i = 0; i < 16; ++i) pacc[t][i] += __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -ls));
+    };
+    if (nt == NT) {
+      // every tile: tile t + 1's products are issued before tile t's exponentials, so the
+      // matrix core and the vector unit overlap
+      f32x16 cur = scores(0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pacc[t][i] += __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, -ls));
+      for (int t = 0; t < NT; ++t) {
+        f32x16 nxt;
+        if (t + 1 < NT) nxt = scores(t + 1);
+        accumulate(t, cur);
+        if (t + 1 < NT) cur = nxt;
       }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (t < nt) accumulate(t, scores(t));
     }
   };
   // heads in order (each one's successor loaded while it is computed); at the first head of KV

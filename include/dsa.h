@@ -48,7 +48,10 @@ extern "C" {
 enum dsa_status {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad size, inconsistent shape */
-  DSA_ERR_UNSUPPORTED = 2,        /* valid but not compiled (e.g. head_dim != 128) */
+  DSA_ERR_UNSUPPORTED = 2,        /* valid but not compiled (e.g. head_dim != 128), or past a size
+                                     limit: calls that run attention address K/V rows with 32-bit
+                                     byte offsets, so total_tokens (prefill) or cache_capacity
+                                     (decode) x Hkv x head_dim x 2 bytes must stay below 4 GiB */
   DSA_ERR_WORKSPACE_TOO_SMALL = 3,
   DSA_ERR_HIP = 4,                /* a HIP launch failed; see dsa_last_hip_error() */
   DSA_ERR_SCRATCH_TOO_SMALL = 5   /* dsa_decode_noalloc: the shape needs more than its scratch */
@@ -251,7 +254,8 @@ int dsa_kv_append(const dsa_decode_shape* shape, const void* k_idx_new, const ui
  * (cache row cache_lens[b]-1, already appended) scores cache rows 0..n-1 with the indexer,
  * keeps the top-k and attends over them.  q_idx [B, H_I, d_I], w_idx fp32 [B, H_I],
  * q bf16 [B, Hq, d]; out bf16 [B, Hq, d]; topk_idx int32 [B, k] (nullable).
- * max_cache_len up to 2^20 rows (DSA_ERR_UNSUPPORTED beyond). */
+ * max_cache_len up to 2^20 rows and cache_capacity x Hkv x head_dim x 2 bytes below 4 GiB
+ * (DSA_ERR_UNSUPPORTED beyond). */
 int dsa_decode(const dsa_decode_shape* shape, const void* q_idx, const float* w_idx,
                const uint16_t* q, const void* k_idx_cache, const uint16_t* k_cache,
                const uint16_t* v_cache, uint16_t* out, int32_t* topk_idx, void* workspace,

@@ -161,14 +161,24 @@ int check_heads(int32_t topk, int32_t H, int32_t dI, int32_t dtype, int32_t Hq, 
   return DSA_OK;
 }
 
-int check_prefill(const dsa_prefill_shape* s, bool need_indexer) {
+// K/V rows are addressed with 32-bit byte offsets from a sequence's (or a cache's) first row:
+// rows x Hkv x head_dim x 2 bytes must stay below 4 GiB.
+bool kv_span_fits(int64_t rows, int kv_heads, int head_dim) {
+  return uint64_t(rows) * uint64_t(kv_heads) * uint64_t(head_dim) * 2 <= 0xFFFFFFFFull;
+}
+
+// uses_kv: the entry point runs attention kernels (everything but the index-only calls)
+int check_prefill(const dsa_prefill_shape* s, bool need_indexer, bool uses_kv = true) {
   if (!s || !s->cu_seqlens || s->num_seqs < 1 || s->total_tokens < 0 || s->max_seqlen < 0)
     return DSA_ERR_INVALID_ARGUMENT;
   if (s->total_tokens > 0 && s->max_seqlen < 1) return DSA_ERR_INVALID_ARGUMENT;
   if (s->max_seqlen > s->total_tokens) return DSA_ERR_INVALID_ARGUMENT;
   if (s->total_tokens > (int64_t(1) << 31) - 1) return DSA_ERR_UNSUPPORTED;
-  return check_heads(s->topk, s->idx_heads, s->idx_dim, s->idx_dtype, s->q_heads, s->kv_heads, s->head_dim,
-                     s->softmax_scale, need_indexer);
+  const int rc = check_heads(s->topk, s->idx_heads, s->idx_dim, s->idx_dtype, s->q_heads, s->kv_heads, s->head_dim,
+                             s->softmax_scale, need_indexer);
+  if (rc) return rc;
+  if (uses_kv && !kv_span_fits(s->total_tokens, s->kv_heads, s->head_dim)) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
 }
 
 // Prefill workspace layout (all offsets 256-byte aligned):
@@ -408,6 +418,7 @@ int check_decode(const dsa_decode_shape* s, bool need_indexer) {
                        s->softmax_scale, need_indexer);
   if (rc) return rc;
   if (need_indexer && s->idx_dtype != DSA_IDX_FP8_E4M3) return DSA_ERR_UNSUPPORTED;
+  if (!kv_span_fits(s->cache_capacity, s->kv_heads, s->head_dim)) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 
@@ -464,7 +475,7 @@ int dsa_last_hip_error(void) { return g_last_hip_error; }
 
 int dsa_prefill_timing_events(const dsa_prefill_shape* s, int32_t* count) {
   if (!count) return DSA_ERR_INVALID_ARGUMENT;
-  int rc = check_prefill(s, false);
+  int rc = check_prefill(s, false, false);
   if (rc) return rc;
   *count = 3 + 2 * prefill_layout(s, nullptr).nchunks;
   return DSA_OK;
@@ -472,7 +483,7 @@ int dsa_prefill_timing_events(const dsa_prefill_shape* s, int32_t* count) {
 
 int dsa_prefill_workspace_size(const dsa_prefill_shape* s, const int32_t* cu_seqlens_host, size_t* bytes) {
   if (!bytes) return DSA_ERR_INVALID_ARGUMENT;
-  int rc = check_prefill(s, false);
+  int rc = check_prefill(s, false, false);
   if (rc) return rc;
   if (s->total_tokens == 0) return DSA_OK;  // empty batch: nothing to do, pointers may be null
   *bytes = prefill_layout(s, cu_seqlens_host).total;
@@ -484,7 +495,7 @@ int dsa_prefill_workspace_size(const dsa_prefill_shape* s, const int32_t* cu_seq
 
 int dsa_index_scores(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
                      float* scores, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_prefill(s, true);
+  int rc = check_prefill(s, true, false);
   if (rc) return rc;
   if (s->total_tokens == 0) return DSA_OK;  // empty batch: nothing to do, pointers may be null
   if (!q_idx || !k_idx || !w_idx || !scores) return DSA_ERR_INVALID_ARGUMENT;
@@ -504,7 +515,7 @@ int dsa_index_scores(const dsa_prefill_shape* s, const void* q_idx, const void* 
 
 int dsa_index_topk(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
                    int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_prefill(s, true);
+  int rc = check_prefill(s, true, false);
   if (rc) return rc;
   if (s->total_tokens == 0) return DSA_OK;  // empty batch: nothing to do, pointers may be null
   if (!q_idx || !k_idx || !w_idx || !topk_idx) return DSA_ERR_INVALID_ARGUMENT;

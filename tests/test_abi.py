@@ -73,6 +73,23 @@ def test_prefill_rejects_bad_shapes_before_launch(kw, code):
     assert ei.value.status == code
 
 
+def test_kv_spans_past_32bit_offsets_are_refused_before_launch():
+    """The attention kernels address K/V rows with 32-bit byte offsets from a sequence's (or a
+    cache's) first row.  A batch of 4.2M tokens with 4 KV heads of 128 dims (4.3 GB of K) is
+    refused as unsupported before any launch by the calls that run attention, while the
+    workspace query (shared with the index-only calls) still answers; a decode cache of 5M rows
+    is refused the same way."""
+    big = shape(T=4_200_000, max_seqlen=4096, num_seqs=1100)
+    assert dsa.dsa_prefill_workspace_size(big) > 0
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_prefill(big, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, WS, stream=0)
+    assert ei.value.status == 2
+    d = dsa.decode_shape(FAKE, 5_000_000, 1000, batch=2, topk=64, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3")
+    with pytest.raises(dsa.DSAError) as ei:
+        dsa.dsa_decode(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, WS, stream=0)
+    assert ei.value.status == 2
+
+
 def test_prefill_rejects_null_and_misaligned_pointers():
     s = shape()
     with pytest.raises(dsa.DSAError) as ei:

@@ -307,9 +307,8 @@ DedupWs dedup_layout(const dsa_prefill_shape* s) {
 
 // Warm-up KL workspace: the prefill layout (schedules, row ranges, indexer score triangle) then
 //   P triangle float[score_floats] | lse float[T][Hq] | schedR int2[nbR] | sched256 int2[nb256] |
-//   dk partials float[slices][T][128] | w max partials float[256].  counts[2] / counts[3] hold the
-//   R-row / 256-row schedule sizes;
-//   counts[8..9] (as floats) the fp16 pre-scale of the gradient weights and its inverse.
+//   dk partials float[slices][T][128].  counts[2] / counts[3] hold the R-row / 256-row schedule
+//   sizes.
 struct KlWs {
   PrefillWs base;
   size_t tri, P, lse, schedR, sched256, dkpart, total;

@@ -3,8 +3,10 @@ the float64 oracle (oracle/indexer_kl.py).
 
 Tolerances (derived from the arithmetic): the target p is built from fp32 exponentials of
 exact bf16 products summed in fp32 (relative error ~1e-6); the indexer scores are exact; the
-gradients multiply g = r - p (fp32) by exact inputs, with g w split into fp16 hi + lo (relative
-error 2^-22) and fp32 accumulation over up to T keys.  Bars: |kl - ref| <= 1e-4 * max(1, |ref|)
+gradients multiply g = r - p (fp32) by exact inputs, with G = g [c > 0] (dq, dw) or g w [c > 0]
+(dk) split into bf16 hi + lo, both truncated (16 or more significant bits: a CPU simulation of
+the split on these cases gives 1.4e-5 of the largest dq and 0.8e-5 of the largest dk), and fp32
+accumulation over up to T keys.  Bars: |kl - ref| <= 1e-4 * max(1, |ref|)
 per token; each gradient within 2e-4 of its largest reference magnitude, element by element."""
 import numpy as np
 import pytest

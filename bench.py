@@ -58,7 +58,8 @@ def roof(bound, achieved, peak, unit, traffic_bytes, work, work_unit, **extra):
 
 def read_traffic():
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from the committed profile
-    summary; a kernel whose source changed since the counters were taken gets no entry."""
+    summary; a kernel whose sources (its own, and for the gather the row order that shapes its
+    traffic) changed since the counters were taken gets no entry."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "prefill_128k_video_traffic.md")
     out = {}
@@ -68,10 +69,14 @@ def read_traffic():
         if not line.startswith("traffic "):
             continue
         f = dict(kv.split("=", 1) for kv in line.split()[2:])
-        src = os.path.join(ROOT, "sparse_attention_long_04_amd", "csrc", f["source"])
-        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != f["sha256"]:
-            continue
-        out[line.split()[1]] = int(f["fetch_bytes"]) + int(f["write_bytes"])
+        # source=a.hip,b.hip sha256=h1,h2: every listed source must be unchanged
+        current = True
+        for name, digest in zip(f["source"].split(","), f["sha256"].split(",")):
+            src = os.path.join(ROOT, "sparse_attention_long_04_amd", "csrc", name)
+            if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != digest:
+                current = False
+        if current:
+            out[line.split()[1]] = int(f["fetch_bytes"]) + int(f["write_bytes"])
     return out
 
 

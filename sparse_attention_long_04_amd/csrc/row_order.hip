@@ -9,7 +9,7 @@
 // row is computed on its own and written to its own output row.
 //
 // For long contexts (a sequence of 64K tokens or more) the key is two-level: the dominant
-// block, then the block holding the second-most of the row's selection (in up to 64 buckets),
+// block, then the block holding the second-most of the row's selection (in up to 128 buckets),
 // so that rows taken together share their second busiest stretch of keys too.
 //
 // A counting sort of the rows by that key, with no global atomics (neighbouring rows rarely
@@ -35,7 +35,7 @@ namespace dsa {
 constexpr int kSigBins = 1024;          // histogram bins per row (4 KiB of LDS per wave)
 constexpr int kSigRowsPerWave = 4;      // consecutive rows per wave of the signature kernel
 constexpr int kOrderMaxKeys = 32768;    // LDS counters per chunk (128 KiB); beyond: identity order
-constexpr int kSigSubBitsMax = 6;       // second-level buckets per dominant block: up to 64
+constexpr int kSigSubBitsMax = 7;       // second-level buckets per dominant block: up to 128
 constexpr int kSigSubMinSeq = 65536;    // longest sequence below this: first level only
 constexpr int kOrderCountMax = 1 << 20; // [chunk][key] matrix entries (4 MiB of workspace)
 constexpr int kOrderMaxChunks = 1024;

@@ -8,17 +8,18 @@
 // context run together and share those keys' lines.  The order changes nothing else -- every
 // row is computed on its own and written to its own output row.
 //
-// For long contexts (a sequence of 64K tokens or more) the key is two-level: the dominant
-// block, then the block holding the second-most of the row's selection (in up to 128 buckets),
-// so that rows taken together share their second busiest stretch of keys too.
+// For long contexts (a sequence of 64K tokens or more) the key is two-level: the two blocks
+// holding most of the row's selection, as an unordered pair (the lower block, then the higher
+// one in up to 128 buckets), so that rows taken together share their two busiest stretches of
+// keys.
 //
 // A counting sort of the rows by that key, with no global atomics (neighbouring rows rarely
 // share a key, and device-wide atomics on a few hundred counters serialise):
 //   row_signature_kernel  one wave per row (four consecutive rows per wave): LDS histogram of
 //                         its selected positions >> shift, the fullest bin and the next
 //                         fullest (lowest on ties; the fullest again when no other bin is
-//                         used), key = (global block of the first) * 2^sub_bits + the second's
-//                         bucket
+//                         used), key = (global block of the lower) * 2^sub_bits + the higher
+//                         one's bucket
 //   row_order_count       one workgroup per chunk of rows: LDS count per key, written out as
 //                         the chunk's row of a [chunk][key] matrix
 //   row_order_colscan    one thread per key: each (chunk, key) entry becomes the key's rows in
@@ -174,8 +175,11 @@ __global__ __launch_bounds__(256) void row_signature_kernel(const int32_t* __res
     wave_best(sec_c, sec_b);
     if (sec_c <= 0) sec_b = best_b;   // the whole selection in one block
     __builtin_amdgcn_wave_barrier();  // every lane has read h before the next row clears it
-    const int first = int((int64_t(cu[b]) + (int64_t(best_b) << shift)) >> shift) + b;
-    if (lane == 0) sig[t] = (first << sub_bits) | (sec_b >> sub_shift);
+    // the two busiest blocks as an unordered pair: the lower one's global block, then the
+    // higher one's bucket
+    const int lo_b = min(best_b, sec_b), hi_b = max(best_b, sec_b);
+    const int first = int((int64_t(cu[b]) + (int64_t(lo_b) << shift)) >> shift) + b;
+    if (lane == 0) sig[t] = (first << sub_bits) | (hi_b >> sub_shift);
   }
 }
 

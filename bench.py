@@ -66,7 +66,7 @@ def read_traffic():
     if not os.path.exists(path):
         return out
     for line in open(path):
-        if not line.startswith("traffic "):
+        if not line.startswith("traffic ") or "fetch_bytes=" not in line:
             continue
         f = dict(kv.split("=", 1) for kv in line.split()[2:])
         # source=a.hip,b.hip sha256=h1,h2: every listed source must be unchanged

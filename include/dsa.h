@@ -138,9 +138,10 @@ int dsa_prefill(const dsa_prefill_shape* shape, const void* q_idx, const void* k
                 void* stream);
 
 /* Number of timing events dsa_prefill_timed and dsa_prefill_dedup record: 3 + 2 n, where n is
- * the number of indexer chunks (the indexer scores 256 blocks of 16 query rows at a time, longest
- * blocks first, into a reusable buffer of 256 x 16 x max_seqlen scores, and the top-k selects
- * each chunk's rows before the next chunk reuses it). */
+ * the number of indexer chunks (the indexer scores 512 blocks of 16 query rows at a time -- the
+ * next 256 longest blocks of the schedule and 256 from its short end -- into a reusable buffer
+ * of 512 x 16 x max_seqlen scores, and the top-k selects each chunk's rows before the next chunk
+ * reuses it). */
 int dsa_prefill_timing_events(const dsa_prefill_shape* shape, int32_t* count);
 
 /* dsa_prefill that also records caller-created hipEvent_t events on `stream` (count from

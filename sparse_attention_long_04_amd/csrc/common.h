@@ -102,6 +102,20 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int nseq
   return lo;
 }
 
+// Order of the chunked prefill loop over the longest-first schedule of N 16-row blocks: position
+// p -> schedule rank.  Every complete chunk of 2 * kPairHalf positions takes the next kPairHalf
+// longest blocks and then, longest first, the kPairHalf blocks as far from the short end of the
+// schedule; blocks left in the middle follow in schedule order.  With one indexer workgroup per
+// compute unit, a unit that finishes one of the chunk's long blocks early is the next to take a
+// short block, and the longest of them: per unit, long plus short comes to about the same work.
+constexpr int kPairHalf = 256;
+__device__ __forceinline__ int chunk_entry(int p, int N) {
+  const int C = N / (2 * kPairHalf);  // complete chunks
+  const int c = p / (2 * kPairHalf), q = p - c * (2 * kPairHalf);
+  if (c >= C) return kPairHalf * C + (p - 2 * kPairHalf * C);
+  return q < kPairHalf ? kPairHalf * c + q : N - kPairHalf * (c + 1) + (q - kPairHalf);
+}
+
 // Offset (in floats) of 16-row score block j of a sequence inside its score triangle:
 // block j holds rows 16j..16j+15, each with a stride of 16(j+1) floats.
 __device__ __forceinline__ int64_t score_block_offset(int64_t j) { return 128 * j * (j + 1); }

@@ -185,12 +185,14 @@ int check_prefill(const dsa_prefill_shape* s, bool need_indexer, bool uses_kv = 
 //   counts int[64] | seqoff int64[B+1] | sched16 int2[nb16] | sched128 int2[nb128] |
 //   rowrange float2[T] | chunk buffer float[kChunkBlocks][slot_stride] | topk int32[T*k] |
 //   row order (signatures, counts, order) | V in fp16 (dense reference only)
-// The indexer scores its 16-row blocks (longest first, as the 16-row schedule orders them) in
-// chunks of kChunkBlocks blocks, one block per slot of the chunk buffer; the top-k then selects
-// the chunk's rows before the next chunk reuses the buffer.  A slot holds a block of the longest
-// rows (16 rows of max_seqlen rounded up to 16 scores), so the buffer is kChunkBlocks x 16 x
-// max_seqlen floats (2 GiB at 131072 tokens) whatever the batch holds.
-constexpr int kChunkBlocks = 256;  // one block per compute unit; consecutive blocks have near-equal work
+// The indexer scores its 16-row blocks in chunks of kChunkBlocks blocks, one block per slot of
+// the chunk buffer, in the order chunk_entry gives (each chunk: the next kPairHalf longest blocks
+// of the longest-first schedule, then kPairHalf from its short end, so a compute unit that
+// finishes a long block early takes the longest short one); the top-k then selects the chunk's
+// rows before the next chunk reuses the buffer.  A slot holds a block of the longest rows (16
+// rows of max_seqlen rounded up to 16 scores), so the buffer is kChunkBlocks x 16 x max_seqlen
+// floats (4 GiB at 131072 tokens) whatever the batch holds.
+constexpr int kChunkBlocks = 2 * kPairHalf;  // the long and the short half of a chunk (chunk_entry)
 
 struct PrefillWs {
   size_t counts, seqoff, sched16, sched128, rowrange, scores, topk, osig, ocnt, order, v16, total;
@@ -261,7 +263,7 @@ PrefillWs prefill_layout(const dsa_prefill_shape* s, const int32_t* cu_host) {
 template <typename T>
 T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
 
-// Indexer scores of chunk c (schedule entries c * kChunkBlocks ..) into the chunk buffer.
+// Indexer scores of chunk c (loop positions c * kChunkBlocks .., chunk_entry) into the chunk buffer.
 hipError_t index_chunk(const dsa_prefill_shape* s, const void* q_idx, const void* k_idx, const float* w_idx,
                        void* ws, const PrefillWs& L, int c, hipStream_t st) {
   return launch_indexer_prefill(s->idx_dtype == DSA_IDX_FP8_E4M3, s->idx_dim, q_idx, k_idx, w_idx, s->cu_seqlens,

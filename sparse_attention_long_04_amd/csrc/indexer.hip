@@ -125,8 +125,10 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   auto swz = [](int t) { return UNITS == 8 ? ((t & 7) ^ ((t >> 3) & 1)) : (t & 15); };
 
   const int n = n0 + blockIdx.x;
-  if (n >= *sched_count) return;
-  const int2 e = sched[n];
+  const int N = *sched_count;
+  if (n >= N) return;
+  // triangle mode: schedule order; chunk mode: the chunked loop's order
+  const int2 e = sched[seqoff ? n : chunk_entry(n, N)];
   const int b = e.x, j = e.y;
   const int64_t seq0 = cu[b];
   const int L = cu[b + 1] - cu[b];
@@ -429,16 +431,18 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
   }
 }
 
-// Expand the rows of one chunk of 16-row blocks (slot c of the chunk buffer holds schedule entry
-// n0 + c, rows with a stride of 16(j+1) floats) into a dense [T, ldo] matrix, -inf outside the
+// Expand the rows of one chunk of 16-row blocks (slot c of the chunk buffer holds the block at
+// position n0 + c of the chunked loop, schedule entry chunk_entry(n0 + c), rows with a stride of
+// 16(j+1) floats) into a dense [T, ldo] matrix, -inf outside the
 // causal context.  One workgroup per (slot, row).
 __global__ void unpack_scores_kernel(const float* __restrict__ buf, int64_t slot_stride,
                                      const int2* __restrict__ sched, const int* __restrict__ sched_count,
                                      int n0, const int32_t* __restrict__ cu, int ldo, float* __restrict__ out) {
   const int slot = blockIdx.x >> 4, rr = blockIdx.x & 15;
   const int n = n0 + slot;
-  if (n >= *sched_count) return;
-  const int2 e = sched[n];
+  const int N = *sched_count;
+  if (n >= N) return;
+  const int2 e = sched[chunk_entry(n, N)];
   const int b = e.x, j = e.y, i = 16 * j + rr;
   if (i >= cu[b + 1] - cu[b]) return;
   const int64_t t = cu[b] + i;
@@ -610,8 +614,9 @@ hipError_t launch_build_schedule(const int32_t* cu, int nseq, int bq, int nb_bou
 }
 
 // Triangle mode (seqoff != nullptr): every schedule entry, grid nb_bound, scores at seqoff[b] +
-// score_block_offset(j).  Chunk mode (seqoff == nullptr): entries n0 .. n0 + nblocks - 1, entry
-// n0 + c into slot c (slot_stride floats apart) of the buffer `scores`.
+// score_block_offset(j).  Chunk mode (seqoff == nullptr): positions n0 .. n0 + nblocks - 1 of the
+// chunked loop (chunk_entry), position n0 + c into slot c (slot_stride floats apart) of the
+// buffer `scores`.
 hipError_t launch_indexer_prefill(bool fp8, int di, const void* q_idx, const void* k_idx,
                                   const float* w, const int32_t* cu, int H, const int2* sched,
                                   const int* count, int n0, int nblocks, const int64_t* seqoff,

@@ -651,9 +651,9 @@ __device__ void select_row(const float* __restrict__ row, int n, int K, float lo
   select_row_exact(row, n, K, lo, hi, out, sm);
 }
 
-// Prefill rows of one chunk of 16-row blocks: slot c of the chunk buffer holds schedule entry
-// n0 + c (rows with a stride of 16(j+1) floats); one workgroup per (slot, row), in schedule order
-// (longest blocks first).
+// Prefill rows of one chunk of 16-row blocks: slot c of the chunk buffer holds the block at
+// position n0 + c of the chunked loop (schedule entry chunk_entry(n0 + c), rows with a stride of
+// 16(j+1) floats); one workgroup per (slot, row), in slot order.
 __global__ __launch_bounds__(kTopkThreads) void topk_prefill_kernel(
     const float* __restrict__ buf, int64_t slot_stride, const int2* __restrict__ sched,
     const int* __restrict__ sched_count, int n0, const int32_t* __restrict__ cu, int K,
@@ -661,8 +661,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_prefill_kernel(
   __shared__ TopkRowSmem sm;
   const int slot = blockIdx.x >> 4, rr = blockIdx.x & 15;
   const int n = n0 + slot;
-  if (n >= *sched_count) return;
-  const int2 e = sched[n];
+  const int N = *sched_count;
+  if (n >= N) return;
+  const int2 e = sched[chunk_entry(n, N)];
   const int b = e.x, j = e.y, i = 16 * j + rr;
   if (i >= cu[b + 1] - cu[b]) return;
   const int64_t t = cu[b] + i;

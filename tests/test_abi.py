@@ -109,19 +109,21 @@ def test_workspace_too_small_is_reported():
 
 
 def test_workspace_is_bounded_by_the_chunk_buffer():
-    """The indexer scores 256 blocks of 16 rows at a time into a reusable buffer of 256 x 16 x
-    max_seqlen floats; the prefill workspace is that buffer plus O(T k) of indices and per-row
-    state -- a few GiB at 128K and 256K tokens, not the score triangle."""
+    """The indexer scores 512 blocks of 16 rows at a time (256 long and 256 short ones) into a
+    reusable buffer of 512 x 16 x max_seqlen floats; the prefill workspace is that buffer plus
+    O(T k) of indices and per-row state -- a few GiB at 128K and 256K tokens, not the score
+    triangle."""
     for T in (131072, 262144):
         s = shape(T=T, max_seqlen=T)
         n = dsa.dsa_prefill_workspace_size(s, np.array([0, T]))
-        chunk = 256 * 16 * T * 4
+        chunk = 512 * 16 * T * 4
         idx = T * 2048 * 4
         dense_v = T * 4 * 128 * 2
         assert chunk + idx + dense_v <= n < chunk + idx + dense_v + T * 64 + (1 << 22)
         nb = T // 16
         assert n < 128 * nb * (nb + 1) * 4 / 4          # well under the whole triangle
-    assert dsa.dsa_prefill_timing_events(shape(T=131072, max_seqlen=131072)) == 3 + 2 * 33
+    # 8193 blocks bound the 16-row schedule of one 131072-token sequence: 17 chunks of 512
+    assert dsa.dsa_prefill_timing_events(shape(T=131072, max_seqlen=131072)) == 3 + 2 * 17
 
 
 def test_varlen_workspace_bound_holds_for_any_split():

@@ -80,14 +80,15 @@ def test_varlen_256k_sampled():
 @pytest.mark.timeout(900)
 def test_prefill_single_256k_sequence_sampled():
     """One 262144-token video-like sequence (the longest context the pages name): the indexer's
-    chunked score buffer (256 blocks of 16 rows x 262144 scores) keeps the workspace to a few GiB.
+    chunked score buffer (512 blocks of 16 rows x 262144 scores, 8 GiB) bounds the workspace to
+    about 10 GiB instead of the 137 GB score triangle.
     Rows: the first 256, the last 512, every 16th frame boundary and 256 seeded rows."""
     L = 262144
     p = workloads.make(workloads.P128K, lengths=[L])
     pb = PrefillBatch(p)
     ws_gib = pb.ws.numel() / 2**30
     print(f"[full] single 256K sequence: workspace {ws_gib:.2f} GiB", flush=True)
-    assert ws_gib < 8
+    assert ws_gib < 12
     pb.prefill()
     rng = np.random.default_rng(262)
     rows = np.unique(np.concatenate([np.arange(256), np.arange(L - 512, L), np.arange(1024, L, 16 * 1024) - 1,

@@ -191,13 +191,24 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_prefill_kernel(
       for (int h = 0; h < H; ++h) {  // H is a multiple of 16
         const i32x4 val = *reinterpret_cast<const i32x4*>(q_lds + (h * 16 + t) * ROWB + ((u ^ swz(t)) * 16));
         const float wv = w_lds[h * 16 + t];
+        if constexpr (FP8) {
+          // the hardware's e4m3 -> fp32 pair conversion (exact): two codes per instruction
 #pragma unroll
-        for (int x = 0; x < EPU; ++x) {
-          const uint32_t word = uint32_t(val[x / (EPU / 4)]);
-          float qv;
-          if constexpr (FP8) qv = e4m3_decode((word >> (8 * (x & 3))) & 0xFFu);
-          else qv = bf16_to_f32(uint16_t((x & 1) ? (word >> 16) : (word & 0xFFFFu)));
-          lin[x] = fmaf(wv, qv, lin[x]);
+          for (int wd = 0; wd < 4; ++wd) {
+            typedef float f32x2_t __attribute__((ext_vector_type(2)));
+            const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(val[wd], false);
+            const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(val[wd], true);
+            lin[4 * wd + 0] = fmaf(wv, lo.x, lin[4 * wd + 0]);
+            lin[4 * wd + 1] = fmaf(wv, lo.y, lin[4 * wd + 1]);
+            lin[4 * wd + 2] = fmaf(wv, hi.x, lin[4 * wd + 2]);
+            lin[4 * wd + 3] = fmaf(wv, hi.y, lin[4 * wd + 3]);
+          }
+        } else {
+#pragma unroll
+          for (int x = 0; x < EPU; ++x) {
+            const uint32_t word = uint32_t(val[x / (EPU / 4)]);
+            lin[x] = fmaf(wv, bf16_to_f32(uint16_t((x & 1) ? (word >> 16) : (word & 0xFFFFu))), lin[x]);
+          }
         }
       }
     }

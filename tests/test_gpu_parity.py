@@ -305,12 +305,14 @@ def test_topk_two_valued_scores_prefill():
         assert np.array_equal(idx[t], O.select_topk_row(o.scores(t), p.topk)), t
 
 
-@pytest.mark.parametrize("hot_frac", [0.5, 0.8])
+@pytest.mark.parametrize("hot_frac", [0.3, 0.5, 0.8])
 def test_topk_two_valued_scores_decode(hot_frac):
     """Keys tie at two scores; a fraction ``hot_frac`` of the 20000 cached keys share the top
-    score.  At 0.5 (about 10000 tied candidates) the decode finalize keeps its candidate list in
-    LDS; at 0.8 (about 16000, more than its 12288-entry list) the list spills to the workspace
-    and the select finishes over HBM.  The row is never flat (the other keys score 0)."""
+    score, so the threshold bin holds all of them.  At 0.3 (about 6000 tied keys) the selection's
+    candidate list fits its 8192 LDS entries, and the tie group, larger than the 1024 entries
+    ranked directly, goes through the second radix digit and the emit's lowest-positions-first
+    rule; at 0.5 and 0.8 (about 10000 and 16000) the list would overflow and the select runs over
+    the blocks' lists in HBM.  The row is never flat (the other keys score 0)."""
     d = gen.make_decode(2, 20000, 20064, 1, idx_heads=64, idx_dim=128, idx_dtype="fp8_e4m3", topk=2048, seed=42)
     rng = np.random.default_rng(1)
     hot = rng.random(d.k_idx_cache.shape[:2]) < hot_frac

@@ -29,7 +29,10 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelCap = 8192;                          // LDS candidate list entries
 constexpr int kSelMaxBlocks = 4096;                    // indexer blocks per row (2^20 keys)
-constexpr int kStageWins = 512;                        // histogram windows staged in LDS per round
+// histogram windows staged in LDS per round: 640 x 128 bytes fill the union with the emit
+// bitmaps, so a row of up to 163840 keys (a 128K context plus its generated tokens) sums its
+// windows in one round (at 512, a 131136-key row paid a second round for its 513th window)
+constexpr int kStageWins = 640;
 constexpr int kEmitPos = 5 * 32 * 1024;                 // positions per emit round (5 words per thread)
 constexpr int kEmitWords = kEmitPos / 32;
 constexpr int kEmitWordsPerThread = kEmitWords / kSelThreads;
